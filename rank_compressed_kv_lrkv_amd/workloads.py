@@ -1,0 +1,169 @@
+"""Seeded synthetic workloads for LRKV compressed-cache attention.
+
+This module draws inputs and nothing else: it holds none of the method's
+arithmetic, so the float64 oracle and the HIP path can both be fed from it
+without sharing any computation.  Every array is produced on the host with
+``numpy.random.default_rng(seed)``; bf16 workloads are drawn in float32 and
+rounded once to bfloat16 (round to nearest, ties to even), so both sides see
+the identical rounded values (the oracle upcasts them exactly).
+
+Value distributions follow the LRKV cache definition (Low-Rank Key Value
+Attention, slide "Cache shared features and compact per-head latents",
+Eqs. (4)-(5)): queries, shared bases K_s/V_s and per-head latents R_h are
+N(0, 1); the per-head factors B_h are N(0, 1/r) (variance 1/r), so that
+B_h z has unit variance per element, like the base.
+
+Draw order (fixed, part of the workload definition):
+  decode : lengths (ragged workloads only), q, then per sequence b in order
+           K_s[b,:len], V_s[b,:len], Z^K[b,:len], Z^V[b,:len]; then B^K, B^V.
+  prefill: Q, K_s, V_s, Z^K, Z^V, B^K, B^V.
+Cache slots at or beyond a sequence's length are zero.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "DecodeWorkload", "PrefillWorkload", "DECODE_WORKLOADS", "PREFILL_WORKLOADS",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "decode_inputs", "prefill_inputs",
+    "append_inputs", "as_f64",
+]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def as_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 view of a stored array (float32 values, or bf16 bit patterns)."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(arr).astype(np.float64)
+    return np.asarray(arr, dtype=np.float64)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    batch: int
+    heads: int
+    head_dim: int
+    rank: int
+    capacity: int                 # cache slots per sequence (row stride)
+    dtype: str                    # "f32" or "bf16"
+    seed: int
+    ragged: Optional[tuple] = None   # (lo, hi) inclusive length range, else every length == capacity
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    batch: int
+    seq_len: int
+    heads: int
+    head_dim: int
+    rank: int
+    dtype: str
+    seed: int
+
+
+DECODE_WORKLOADS = {
+    w.name: w for w in [
+        DecodeWorkload("tiny_f32_T64", 1, 4, 16, 4, 64, "f32", 20261202),
+        DecodeWorkload("small_bf16_T2k", 8, 8, 64, 8, 2048, "bf16", 20261203),
+        DecodeWorkload("mid_bf16_T8k", 32, 32, 128, 16, 8192, "bf16", 20261204),
+        DecodeWorkload("ragged_bf16_T1k_64k", 16, 32, 128, 32, 65536, "bf16", 20261205,
+                       ragged=(1024, 65536)),
+    ]
+}
+
+PREFILL_WORKLOADS = {
+    w.name: w for w in [
+        PrefillWorkload("prefill_bf16_L4k", 4, 4096, 32, 128, 16, "bf16", 20261206),
+    ]
+}
+
+
+def _store(x32: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x32) if dtype == "bf16" else np.ascontiguousarray(x32, dtype=np.float32)
+
+
+def _b_factor(rng, H, d_h, r):
+    b = rng.standard_normal((H, d_h, r), dtype=np.float32)
+    if r > 0:
+        b *= np.float32(1.0 / np.sqrt(r))
+    return b
+
+
+def decode_inputs(wl: DecodeWorkload, *, batch: Optional[int] = None, seed: Optional[int] = None,
+                  capacity: Optional[int] = None, lens: Optional[np.ndarray] = None) -> dict:
+    """Draw one decode workload.  ``batch``/``capacity``/``lens``/``seed`` override the
+    workload's values (used for reduced-size parity cases of the same distribution)."""
+    B = wl.batch if batch is None else batch
+    T = wl.capacity if capacity is None else capacity
+    H, d_h, r, dt = wl.heads, wl.head_dim, wl.rank, wl.dtype
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    if lens is not None:
+        seq_lens = np.asarray(lens, dtype=np.int32)
+    elif wl.ragged is not None:
+        lo, hi = wl.ragged
+        seq_lens = rng.integers(min(lo, T), min(hi, T), size=B, endpoint=True).astype(np.int32)
+    else:
+        seq_lens = np.full(B, T, dtype=np.int32)
+    assert seq_lens.shape == (B,) and int(seq_lens.max(initial=0)) <= T
+    q = rng.standard_normal((B, H, d_h), dtype=np.float32)
+    sdt = np.uint16 if dt == "bf16" else np.float32
+    k_s = np.zeros((B, T, d_h), sdt)
+    v_s = np.zeros((B, T, d_h), sdt)
+    z_k = np.zeros((B, T, H, r), sdt)
+    z_v = np.zeros((B, T, H, r), sdt)
+    for b in range(B):
+        L = int(seq_lens[b])
+        k_s[b, :L] = _store(rng.standard_normal((L, d_h), dtype=np.float32), dt)
+        v_s[b, :L] = _store(rng.standard_normal((L, d_h), dtype=np.float32), dt)
+        z_k[b, :L] = _store(rng.standard_normal((L, H, r), dtype=np.float32), dt)
+        z_v[b, :L] = _store(rng.standard_normal((L, H, r), dtype=np.float32), dt)
+    b_k = _b_factor(rng, H, d_h, r)
+    b_v = _b_factor(rng, H, d_h, r)
+    return dict(q=_store(q, dt), k_s=k_s, v_s=v_s, z_k=z_k, z_v=z_v,
+                b_k=_store(b_k, dt), b_v=_store(b_v, dt), seq_lens=seq_lens,
+                dtype=dt, heads=H, head_dim=d_h, rank=r, capacity=T)
+
+
+def prefill_inputs(wl: PrefillWorkload, *, batch: Optional[int] = None, seq_len: Optional[int] = None,
+                   seed: Optional[int] = None) -> dict:
+    B = wl.batch if batch is None else batch
+    L = wl.seq_len if seq_len is None else seq_len
+    H, d_h, r, dt = wl.heads, wl.head_dim, wl.rank, wl.dtype
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    q = rng.standard_normal((B, L, H, d_h), dtype=np.float32)
+    k_s = rng.standard_normal((B, L, d_h), dtype=np.float32)
+    v_s = rng.standard_normal((B, L, d_h), dtype=np.float32)
+    z_k = rng.standard_normal((B, L, H, r), dtype=np.float32)
+    z_v = rng.standard_normal((B, L, H, r), dtype=np.float32)
+    b_k = _b_factor(rng, H, d_h, r)
+    b_v = _b_factor(rng, H, d_h, r)
+    return dict(q=_store(q, dt), k_s=_store(k_s, dt), v_s=_store(v_s, dt), z_k=_store(z_k, dt),
+                z_v=_store(z_v, dt), b_k=_store(b_k, dt), b_v=_store(b_v, dt),
+                dtype=dt, heads=H, head_dim=d_h, rank=r, seq_len=L)
+
+
+def append_inputs(B: int, n: int, H: int, d_h: int, r: int, dtype: str, seed: int) -> dict:
+    """New-token rows for a cache append: K_s/V_s rows [B,n,d_h], latents [B,n,H,r]."""
+    rng = np.random.default_rng(seed)
+    k_s = rng.standard_normal((B, n, d_h), dtype=np.float32)
+    v_s = rng.standard_normal((B, n, d_h), dtype=np.float32)
+    z_k = rng.standard_normal((B, n, H, r), dtype=np.float32)
+    z_v = rng.standard_normal((B, n, H, r), dtype=np.float32)
+    return dict(k_s=_store(k_s, dtype), v_s=_store(v_s, dtype), z_k=_store(z_k, dtype),
+                z_v=_store(z_v, dtype), dtype=dtype)
