@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Throughput of LRKV compressed-cache decode on one MI355X.
+
+A step is one lrkv_decode over the whole batch: the split-K scan
+(lrkv_decode_partial) followed by the merge and B^V epilogue
+(lrkv_decode_combine), on seeded synthetic inputs already resident in HBM.
+The default workload is the 8K-context bf16 decode: 32 sequences x 8192
+cached tokens, H=32 heads, d_h=128, r=16 (cache 671 MB, larger than the
+256 MB Infinity Cache, so every step streams it from HBM).
+
+Prints one JSON line.  `value` is cache tokens per second for the whole
+step; `roofline` prices the dominant kernel (the scan) against the HBM
+peak using the algorithmic bytes of one launch and its average duration
+from HIP events recorded around it on the launch stream; `cpu_baseline`
+times the float64 oracle on a bounded sample of the same workload on the
+host cores and reports its agreement with the GPU on that sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_SRC = os.path.join(ROOT, "rank_compressed_kv_lrkv_amd", "csrc", "decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mid_bf16_T8k")
+    ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, split):
+    """HBM bytes per scan launch from committed rocprofv3 counter summaries,
+    if they were taken on the current kernel source for this workload."""
+    path = os.path.join(PROFILES, "decode_scan_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_digest(DECODE_SRC) or rec.get("workload") != workload:
+        return None
+    if rec.get("split_tokens") != split:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def thread_count():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info()]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the LRKV decode path here is single-GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rank_compressed_kv_lrkv_amd as L
+    from rank_compressed_kv_lrkv_amd.workloads import DECODE_WORKLOADS, as_f64, decode_inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    L.library()     # fails loudly if the HIP library is missing
+    wl = DECODE_WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    d = decode_inputs(wl)
+    t_gen = time.perf_counter() - t_gen
+    dt = torch.bfloat16 if d["dtype"] == "bf16" else torch.float32
+
+    def dev(a):
+        if d["dtype"] == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+    cache = L.LrkvCache(dev(d["k_s"]), dev(d["v_s"]), dev(d["z_k"]), dev(d["z_v"]))
+    q, b_k, b_v = dev(d["q"]), dev(d["b_k"]), dev(d["b_v"])
+    lens_np = np.asarray(d["seq_lens"], np.int32)
+    lens = torch.from_numpy(lens_np).cuda()
+    max_len = int(d["capacity"])
+    out = torch.empty_like(q)
+    ws = L.decode_workspace(cache, max_len, args.split_tokens)
+    B, H, d_h, r = wl.batch, wl.heads, wl.head_dim, wl.rank
+    es = 2 if d["dtype"] == "bf16" else 4
+    tokens = int(np.minimum(lens_np, max_len).sum())
+
+    def scan():
+        L.lrkv_decode(cache, lens, max_len, q, b_k, b_v, split_tokens=args.split_tokens, out=out,
+                      workspace=ws, phase="partial")
+
+    def combine():
+        L.lrkv_decode(cache, lens, max_len, q, b_k, b_v, split_tokens=args.split_tokens, out=out,
+                      workspace=ws, phase="combine")
+
+    for _ in range(args.warmup):
+        scan()
+        combine()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()       # the library launches on torch's current stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        scan()
+        e1.record(stream)
+        combine()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    comb_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+
+    cache_bytes = tokens * 2 * (d_h + H * r) * es
+    scan_bytes = cache_bytes + B * H * d_h * es + H * d_h * r * es          # cache + q + B^K
+    step_bytes = cache_bytes + 2 * B * H * d_h * es + 2 * H * d_h * r * es  # + out + B^V
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(wl.name, args.split_tokens)
+
+    rec = {
+        "metric": "compressed-cache decode: cache tokens/s and achieved HBM GB/s (% of peak)",
+        "value": tokens / (step_ms * 1e-3),
+        "unit": "cache tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if d["dtype"] == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) queries, bases and latents; B ~ N(0, 1/r))",
+        "config": {"workload": wl.name, "batch": B, "heads": H, "head_dim": d_h, "rank": r,
+                   "context": max_len, "cache_tokens": tokens, "split_tokens": args.split_tokens or "default",
+                   "cache_MB": cache_bytes / 1e6},
+        "hbm_GBps_step": step_bytes / (step_ms * 1e-3) / 1e9,
+        "hbm_frac_step": step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "kernels_ms": {"decode_split_kernel": scan_ms, "decode_merge_kernel": comb_ms},
+        "wall_s_timed": wall,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic,
+                     "kernel": "decode_split_kernel", "algorithmic_bytes_per_launch": scan_bytes},
+    }
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(d, out, args.cpu_seconds, as_f64)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(d, out_dev, budget_s, as_f64):
+    """Time the float64 oracle, one whole sequence (all heads) at a time, on
+    the host cores until the budget is spent; compare with the GPU output."""
+    sys.path.insert(0, ROOT)
+    import oracle as O
+    got = out_dev.float().cpu().numpy().astype(np.float64)
+    dt = d["dtype"]
+    f = lambda k: as_f64(d[k], dt)
+    bk, bv = f("b_k"), f("b_v")
+    q = f("q")
+    lens = np.asarray(d["seq_lens"])
+    toks, secs, errs, done = 0, 0.0, [], 0
+    for b in range(len(lens)):
+        L_ = int(lens[b])
+        args = (q[b:b + 1], as_f64(d["k_s"][b:b + 1, :L_], dt), as_f64(d["v_s"][b:b + 1, :L_], dt),
+                as_f64(d["z_k"][b:b + 1, :L_], dt), as_f64(d["z_v"][b:b + 1, :L_], dt), bk, bv, lens[b:b + 1])
+        t = time.perf_counter()
+        want = O.decode(*args)
+        secs += time.perf_counter() - t
+        toks += L_
+        done += 1
+        errs.append(float(np.max(np.abs(got[b] - want[0])) / max(np.max(np.abs(want[0])), 1e-30)))
+        if secs >= budget_s:
+            break
+    return {"value": toks / secs, "unit": "cache tokens/s", "cores": thread_count(), "kind": "oracle",
+            "sample": f"{done} of {len(lens)} sequences, all heads ({toks} cache tokens), float64 numpy, "
+                      f"{secs:.1f} s",
+            "gpu_vs_oracle_max_err_over_inf_norm": max(errs)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * lrkv.h - C ABI of liblrkv: attention over an LRKV compressed KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: Low-Rank Key Value Attention (O'Neill, Clancy, Matskevichus, Reid,
+ * arXiv:2601.11471v3), in the slide discussion of that paper:
+ *   - every head's K/V projection is a shared base plus a rank-r correction,
+ *     W_h = W_shared + U_h B_h^T (slide "LRKV constrains differences between
+ *     heads", Eqs. (2)-(3));
+ *   - the cache stores, per token, one shared key row k_s and value row v_s of
+ *     width d_h and, per head h, rank-r latents z^K_h and z^V_h; B_h are
+ *     weights, not cache entries (slide "Cache shared features and compact
+ *     per-head latents", Eqs. (4)-(5)); that is 2(d_h + H r) elements per
+ *     token per layer (slide "Can heads share storage while keeping distinct
+ *     K/V features?");
+ *   - attention never expands per-head keys or values: the logits are
+ *     q_h.k_s + (B^K_h^T q_h).z^K_h, scaled by 1/sqrt(d_h) and softmaxed
+ *     (slide "Compute logits without expanding historical keys", Eq. (6)),
+ *     and the output is a V_s + B^V_h (a R^V_h) (slide "Aggregate values
+ *     before the residual up-projection", Eq. (7)).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library allocates no device memory, keeps no per-call state, never
+ *     synchronises, and enqueues all work on `stream` (a hipStream_t passed
+ *     as void*; NULL is the default stream).  Results are ready when the
+ *     stream has drained.
+ *   - `dtype` (lrkv_dtype) is the storage type of q, the cache, B^K, B^V,
+ *     the new rows and the output, one type per call.  Arithmetic is fp32
+ *     (bf16 products accumulate in fp32).
+ *   - Dense row-major layouts (innermost index last):
+ *       shared cache rows  k_shared, v_shared  [batch][capacity][head_dim]
+ *       latent cache rows  z_k, z_v            [batch][capacity][num_heads][rank]
+ *       residual factors   b_k, b_v            [num_heads][head_dim][rank]
+ *     so the cache holds exactly 2(head_dim + num_heads*rank) elements per
+ *     token slot.
+ *   - Every pointer must be 16-byte aligned, and head_dim and rank must make
+ *     rows whole 16-byte units: head_dim*elem_bytes % 16 == 0 and
+ *     rank*elem_bytes % 16 == 0 (rank == 0 is allowed and is MQA).
+ *   - Supported envelope: head_dim in {16, 32, 64, 128}; rank in
+ *     {0, 4, 8, 16, 32, 64} (bf16 needs rank % 8 == 0); 1 <= num_heads <= 64
+ *     (num_heads <= 32 unless rank == 4).  Anything else returns
+ *     LRKV_ERR_SHAPE before any launch.
+ *   - Validation happens on the host before anything is enqueued; a call
+ *     that returns an error has launched nothing.  A failed launch returns
+ *     LRKV_ERR_DEVICE (from hipGetLastError).  No exception or abort crosses
+ *     this interface.
+ */
+#ifndef LRKV_H
+#define LRKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lrkv_status {
+  LRKV_OK = 0,
+  LRKV_ERR_NULL = 1,       /* a required pointer is NULL */
+  LRKV_ERR_SHAPE = 2,      /* a size is invalid or outside the supported envelope */
+  LRKV_ERR_DTYPE = 3,      /* dtype is not an lrkv_dtype */
+  LRKV_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned */
+  LRKV_ERR_CAPACITY = 5,   /* max_len or seq_len exceeds capacity */
+  LRKV_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than lrkv_decode_workspace_size */
+  LRKV_ERR_DEVICE = 7      /* a HIP runtime call or kernel launch failed */
+} lrkv_status;
+
+typedef enum lrkv_dtype {
+  LRKV_F32 = 0,            /* IEEE binary32 */
+  LRKV_BF16 = 1            /* bfloat16; outputs rounded to nearest-even */
+} lrkv_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* lrkv_status_string(int32_t status);
+
+/* Cache elements per token per layer, 2(head_dim + num_heads*rank)
+ * (slide "Can heads share storage while keeping distinct K/V features?",
+ * and Eq. (9) of slide "The rank directly sets the theoretical cache
+ * budget").  Returns -1 if an argument is negative or num_heads/head_dim is 0. */
+int64_t lrkv_cache_elems_per_token(int32_t num_heads, int32_t head_dim, int32_t rank);
+
+/* Append n_new tokens per sequence to the cache (slide "Cache shared
+ * features and compact per-head latents", Eqs. (4)-(5): the shared rows
+ * and the per-head latents are stored; B_h is not).
+ *   pos      device int32 [batch]: first slot written for sequence b.
+ *   new_k_s, new_v_s  [batch][n_new][head_dim];  new_z_k, new_z_v
+ *   [batch][n_new][num_heads][rank].
+ * Slot pos[b]+i of every cache array receives row i of sequence b,
+ * bit-exactly; no other slot is touched.  Rows whose slot falls outside
+ * [0, capacity) are dropped (pos is device data, so this cannot be
+ * reported).  n_new == 0 is a no-op. */
+lrkv_status lrkv_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                        int32_t rank, int64_t capacity,
+                        void* k_shared, void* v_shared, void* z_k, void* z_v,
+                        const int32_t* pos, int32_t n_new,
+                        const void* new_k_s, const void* new_v_s,
+                        const void* new_z_k, const void* new_z_v, void* stream);
+
+/* Bytes of device workspace lrkv_decode needs for these sizes and this
+ * split (split_tokens == 0 selects the library's default for the device
+ * that is current).  Written to *bytes.  The workspace holds the split-K
+ * partial softmax states (fp32). */
+lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num_heads,
+                                       int32_t head_dim, int32_t rank, int64_t capacity,
+                                       int64_t max_len, int32_t split_tokens, size_t* bytes);
+
+/* One decode step: for every sequence b and head h,
+ *   out[b][h] = softmax_t( scale * (q_bh.k_s[t] + (B^K_h^T q_bh).z^K[t][h]) )
+ *               applied to  v_s[t] + B^V_h z^V[t][h],   t < seq_lens[b],
+ * computed in the absorbed form of Eqs. (6)-(7) without forming K_h, V_h.
+ *   seq_lens  device int32 [batch]; each length is clamped to [0, max_len].
+ *             A sequence of length 0 gets an all-zero output.
+ *   max_len   host upper bound on the lengths, <= capacity (sizes the grid).
+ *   q         [batch][num_heads][head_dim];   out [batch][num_heads][head_dim].
+ *   b_k, b_v  [num_heads][head_dim][rank].
+ *   scale     softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *   split_tokens  tokens per split-K partition (0 = default; otherwise a
+ *             positive multiple of 64).  The partial states of all
+ *             partitions are merged by a log-sum-exp combine.
+ *   workspace device scratch of at least lrkv_decode_workspace_size bytes
+ *             for the same arguments; contents on entry are ignored.
+ * Every query attends to all of its sequence's cached tokens (the current
+ * token is appended before the call); nothing inside the cache is masked. */
+lrkv_status lrkv_decode(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                        int32_t rank, int64_t capacity,
+                        const void* k_shared, const void* v_shared,
+                        const void* z_k, const void* z_v,
+                        const int32_t* seq_lens, int64_t max_len,
+                        const void* q, const void* b_k, const void* b_v, float scale,
+                        int32_t split_tokens, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two phases of lrkv_decode, for callers that schedule them apart (for
+ * instance to time the scan alone, or to move the partial states between
+ * devices before combining).  Both take exactly the arguments of
+ * lrkv_decode; each ignores the ones it does not use (partial: b_v, out;
+ * combine: the cache pointers, q, b_k, scale).  lrkv_decode_partial runs the
+ * split-K scan and leaves, in the workspace, one partial softmax state per
+ * (sequence, partition, head): running max, running sum and the unnormalised
+ * sums of a*v_s and a*z^V (Eqs. (6)-(7) restricted to the partition).
+ * lrkv_decode_combine merges those states by log-sum-exp and applies B^V_h
+ * once per head.  The same sizes, seq_lens, max_len and split_tokens must be
+ * passed to both, and the workspace must not change in between. */
+lrkv_status lrkv_decode_partial(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                int32_t rank, int64_t capacity,
+                                const void* k_shared, const void* v_shared,
+                                const void* z_k, const void* z_v,
+                                const int32_t* seq_lens, int64_t max_len,
+                                const void* q, const void* b_k, const void* b_v, float scale,
+                                int32_t split_tokens, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+lrkv_status lrkv_decode_combine(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                int32_t rank, int64_t capacity,
+                                const void* k_shared, const void* v_shared,
+                                const void* z_k, const void* z_v,
+                                const int32_t* seq_lens, int64_t max_len,
+                                const void* q, const void* b_k, const void* b_v, float scale,
+                                int32_t split_tokens, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Causal prefill of seq_len fresh tokens per sequence (slides "Compute
+ * logits without expanding historical keys" and "Aggregate values before
+ * the residual up-projection" with seq_len queries; query i sees keys
+ * j <= i):
+ *   q   [batch][seq_len][num_heads][head_dim];  out same shape.
+ *   k_s, v_s [batch][seq_len][head_dim];  z_k, z_v [batch][seq_len][num_heads][rank].
+ * Only dtype LRKV_BF16 is supported (bf16 MFMA with fp32 accumulation).
+ * If the four cache pointers are all non-NULL the tokens are also written,
+ * bit-exactly, to cache slots [0, seq_len) of every sequence (seq_len must
+ * then be <= capacity); if all four are NULL the cache is not touched. */
+lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                         int32_t rank, int64_t capacity,
+                         void* k_shared, void* v_shared, void* z_k, void* z_v,
+                         int32_t seq_len, const void* q,
+                         const void* k_s, const void* v_s, const void* z_k_new, const void* z_v_new,
+                         const void* b_k, const void* b_v, float scale, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRKV_H */

@@ -1,0 +1,246 @@
+"""ctypes binding of liblrkv: the C entry points under the same names.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of liblrkv.so.  Tensors are torch tensors on a ROCm device; their
+data pointers and torch's current stream are handed to the library.  There
+is no fallback: if the library is missing, or a tensor is not on the GPU,
+the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch  # imported before the library so both share one HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "liblrkv.so")
+
+LRKV_F32 = 0
+LRKV_BF16 = 1
+STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DTYPE", 4: "LRKV_ERR_ALIGN",
+          5: "LRKV_ERR_CAPACITY", 6: "LRKV_ERR_WORKSPACE", 7: "LRKV_ERR_DEVICE"}
+
+EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
+            "lrkv_decode_workspace_size", "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_combine",
+            "lrkv_prefill")
+
+
+class LrkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({lrkv_status_string(status)})")
+
+
+_lib = None
+
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+def library() -> ctypes.CDLL:
+    """Load liblrkv.so (built in-tree by ``rank_compressed_kv_lrkv_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m rank_compressed_kv_lrkv_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.lrkv_status_string.argtypes = [_i32]
+        lib.lrkv_status_string.restype = ctypes.c_char_p
+        lib.lrkv_cache_elems_per_token.argtypes = [_i32, _i32, _i32]
+        lib.lrkv_cache_elems_per_token.restype = _i64
+        lib.lrkv_append.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i32,
+                                    _vp, _vp, _vp, _vp, _vp]
+        lib.lrkv_append.restype = _i32
+        lib.lrkv_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _i64, _i32,
+                                                   ctypes.POINTER(_sz)]
+        lib.lrkv_decode_workspace_size.restype = _i32
+        for fn in (lib.lrkv_decode, lib.lrkv_decode_partial, lib.lrkv_decode_combine):
+            fn.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64,
+                           _vp, _vp, _vp, _f32, _i32, _vp, _vp, _sz, _vp]
+            fn.restype = _i32
+        lib.lrkv_prefill.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _i32,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp]
+        lib.lrkv_prefill.restype = _i32
+        _lib = lib
+    return _lib
+
+
+def lrkv_status_string(status: int) -> str:
+    return library().lrkv_status_string(int(status)).decode()
+
+
+def lrkv_cache_elems_per_token(num_heads: int, head_dim: int, rank: int) -> int:
+    return int(library().lrkv_cache_elems_per_token(num_heads, head_dim, rank))
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return LRKV_BF16
+    if t == torch.float32:
+        return LRKV_F32
+    raise LrkvError(3, f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype] = None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _shape(t: Optional[torch.Tensor], name: str, want: tuple) -> None:
+    if t is not None and tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise LrkvError(status, where)
+
+
+@dataclass
+class LrkvCache:
+    """Caller-owned cache tensors: shared rows [B, T, d_h] and latents [B, T, H, r]."""
+    k_s: torch.Tensor
+    v_s: torch.Tensor
+    z_k: torch.Tensor
+    z_v: torch.Tensor
+
+    @property
+    def batch(self) -> int: return self.k_s.shape[0]
+    @property
+    def capacity(self) -> int: return self.k_s.shape[1]
+    @property
+    def head_dim(self) -> int: return self.k_s.shape[2]
+    @property
+    def heads(self) -> int: return self.z_k.shape[2]
+    @property
+    def rank(self) -> int: return self.z_k.shape[3]
+    @property
+    def dtype(self) -> torch.dtype: return self.k_s.dtype
+
+    @staticmethod
+    def empty(batch, heads, head_dim, rank, capacity, dtype=torch.bfloat16, device="cuda", zero=True):
+        mk = torch.zeros if zero else torch.empty
+        return LrkvCache(mk((batch, capacity, head_dim), dtype=dtype, device=device),
+                         mk((batch, capacity, head_dim), dtype=dtype, device=device),
+                         mk((batch, capacity, heads, rank), dtype=dtype, device=device),
+                         mk((batch, capacity, heads, rank), dtype=dtype, device=device))
+
+    def check(self):
+        B, T, d_h = self.k_s.shape
+        H, r = self.z_k.shape[2], self.z_k.shape[3]
+        _shape(self.v_s, "v_s", (B, T, d_h))
+        _shape(self.z_k, "z_k", (B, T, H, r))
+        _shape(self.z_v, "z_v", (B, T, H, r))
+        for t, n in ((self.v_s, "v_s"), (self.z_k, "z_k"), (self.z_v, "z_v")):
+            if t.dtype != self.dtype or t.device != self.k_s.device:
+                raise ValueError(f"cache tensor {n} differs in dtype/device from k_s")
+
+    def pointers(self):
+        self.check()
+        dt = self.dtype
+        return (_ptr(self.k_s, "k_s", dt), _ptr(self.v_s, "v_s", dt), _ptr(self.z_k, "z_k", dt),
+                _ptr(self.z_v, "z_v", dt))
+
+
+def lrkv_append(cache: LrkvCache, pos: torch.Tensor, new_k_s, new_v_s, new_z_k, new_z_v) -> None:
+    dt = cache.dtype
+    B, n_new = new_k_s.shape[0], new_k_s.shape[1]
+    if B != cache.batch:
+        raise ValueError("new rows and cache differ in batch")
+    _shape(new_k_s, "new_k_s", (B, n_new, cache.head_dim))
+    _shape(new_v_s, "new_v_s", (B, n_new, cache.head_dim))
+    _shape(new_z_k, "new_z_k", (B, n_new, cache.heads, cache.rank))
+    _shape(new_z_v, "new_z_v", (B, n_new, cache.heads, cache.rank))
+    _shape(pos, "pos", (B,))
+    _check(library().lrkv_append(_dtype_code(dt), cache.batch, cache.heads, cache.head_dim, cache.rank,
+                                 cache.capacity, *cache.pointers(), _ptr(pos, "pos", torch.int32), n_new,
+                                 _ptr(new_k_s, "new_k_s", dt), _ptr(new_v_s, "new_v_s", dt),
+                                 _ptr(new_z_k, "new_z_k", dt), _ptr(new_z_v, "new_z_v", dt), _stream()),
+           "lrkv_append")
+
+
+def lrkv_decode_workspace_size(dtype: torch.dtype, batch: int, heads: int, head_dim: int, rank: int,
+                               capacity: int, max_len: int, split_tokens: int = 0) -> int:
+    n = _sz(0)
+    _check(library().lrkv_decode_workspace_size(_dtype_code(dtype), batch, heads, head_dim, rank, capacity,
+                                                max_len, split_tokens, ctypes.byref(n)),
+           "lrkv_decode_workspace_size")
+    return int(n.value)
+
+
+def decode_workspace(cache: LrkvCache, max_len: int, split_tokens: int = 0) -> torch.Tensor:
+    nbytes = lrkv_decode_workspace_size(cache.dtype, cache.batch, cache.heads, cache.head_dim, cache.rank,
+                                        cache.capacity, max_len, split_tokens)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=cache.k_s.device)
+
+
+def lrkv_decode(cache: LrkvCache, seq_lens: torch.Tensor, max_len: int, q: torch.Tensor, b_k: torch.Tensor,
+                b_v: torch.Tensor, scale: Optional[float] = None, split_tokens: int = 0,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                phase: str = "both") -> torch.Tensor:
+    """phase: "both" (lrkv_decode), "partial" (lrkv_decode_partial) or "combine" (lrkv_decode_combine)."""
+    dt = cache.dtype
+    B, H, d_h, r = cache.batch, cache.heads, cache.head_dim, cache.rank
+    _shape(q, "q", (B, H, d_h))
+    _shape(b_k, "b_k", (H, d_h, r))
+    _shape(b_v, "b_v", (H, d_h, r))
+    _shape(seq_lens, "seq_lens", (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", (B, H, d_h))
+    if workspace is None:
+        workspace = decode_workspace(cache, max_len, split_tokens)
+    fn = {"both": library().lrkv_decode, "partial": library().lrkv_decode_partial,
+          "combine": library().lrkv_decode_combine}[phase]
+    _check(fn(_dtype_code(dt), cache.batch, cache.heads, cache.head_dim, cache.rank,
+                                 cache.capacity, *cache.pointers(), _ptr(seq_lens, "seq_lens", torch.int32),
+                                 max_len, _ptr(q, "q", dt), _ptr(b_k, "b_k", dt), _ptr(b_v, "b_v", dt),
+                                 0.0 if scale is None else float(scale), split_tokens, _ptr(out, "out", dt),
+                                 _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                 _stream()),
+           "lrkv_decode")
+    return out
+
+
+def lrkv_prefill(q, k_s, v_s, z_k, z_v, b_k, b_v, scale: Optional[float] = None,
+                 cache: Optional[LrkvCache] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dt = q.dtype
+    B, L, H, d_h = q.shape
+    r = z_k.shape[-1]
+    _shape(k_s, "k_s", (B, L, d_h))
+    _shape(v_s, "v_s", (B, L, d_h))
+    _shape(z_k, "z_k", (B, L, H, r))
+    _shape(z_v, "z_v", (B, L, H, r))
+    _shape(b_k, "b_k", (H, d_h, r))
+    _shape(b_v, "b_v", (H, d_h, r))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", (B, L, H, d_h))
+    if cache is not None and (cache.batch, cache.heads, cache.head_dim, cache.rank) != (B, H, d_h, r):
+        raise ValueError("cache dimensions differ from the prefill inputs")
+    cptr = cache.pointers() if cache is not None else (None, None, None, None)
+    cap = cache.capacity if cache is not None else max(L, 1)
+    _check(library().lrkv_prefill(_dtype_code(dt), B, H, d_h, r, cap, *cptr, L, _ptr(q, "q", dt),
+                                  _ptr(k_s, "k_s", dt), _ptr(v_s, "v_s", dt), _ptr(z_k, "z_k", dt),
+                                  _ptr(z_v, "z_v", dt), _ptr(b_k, "b_k", dt), _ptr(b_v, "b_v", dt),
+                                  0.0 if scale is None else float(scale), _ptr(out, "out", dt), _stream()),
+           "lrkv_prefill")
+    return out
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

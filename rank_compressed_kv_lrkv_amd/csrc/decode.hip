@@ -1,0 +1,530 @@
+// LRKV decode over the compressed cache: split-K scan + log-sum-exp merge.
+//
+// Method (Low-Rank Key Value Attention, slide discussion of arXiv:2601.11471v3):
+//   logits  s_t = ( q_h.k_{s,t} + (B^K_h^T q_h).z^K_{t,h} ) / sqrt(d_h)     slide
+//           "Compute logits without expanding historical keys", Eq. (6);
+//   output  o_h = sum_t a_t v_{s,t} + B^V_h ( sum_t a_t z^V_{t,h} )           slide
+//           "Aggregate values before the residual up-projection", Eq. (7).
+// Per-head keys and values are never formed.  The shared rows k_s/v_s of a
+// token are staged once in LDS and serve all H heads of the workgroup; the
+// per-head latents stream from HBM straight into the lanes that own the head.
+//
+// Work decomposition (one workgroup = 256 lanes = 4 wave64):
+//   grid.x = split index (a run of split_tokens tokens), grid.y = sequence.
+//   Lane -> (slot, head h, g) with g in [0, G).  The G lanes of a head form an
+//   aligned group inside one wave.  Tokens are processed in batches of G: in a
+//   batch, lane g scores token g of the batch (the full d_h + r dot product,
+//   no cross-lane reduction), then every lane of the group folds all G tokens
+//   into its slice of the accumulators (d_h/G shared dims, r/G latent dims).
+//   When H*G < 256 the workgroup runs several independent token streams
+//   ("slots"), each producing its own partial state.
+// Numerics: bf16 products accumulate in fp32 via v_dot2_f32_bf16; the
+// absorbed query B^K_h^T q_h is formed in fp32 and fed as a hi+lo pair of
+// bf16 values (error ~2^-17 relative); softmax runs in the log2 domain with
+// running max m and sum l; softmax weights enter the value sums as bf16 and
+// l sums the same rounded weights.  fp32 storage runs all-fp32 FMAs.
+#include "lrkv_device.h"
+#include "lrkv_internal.h"
+
+#include <utility>
+
+namespace lrkv {
+
+template <class E, int DH, int R, int G>
+struct DecodeShape {
+  using T = typename E::T;
+  using Pair = typename E::Pair;
+  static constexpr int ES = E::kBytes;
+  static constexpr int PB = 2 * ES;                    // bytes per pair
+  static constexpr int ROW_BYTES = DH * ES;            // one k_s / v_s row
+  static constexpr int ROW_CH = ROW_BYTES / 16;        // 16-byte chunks per row
+  static constexpr int KS_STRIDE = ROW_BYTES + 16;     // padded LDS row (bank spread)
+  static constexpr int VP_STRIDE = DH * PB;            // two tokens interleaved per LDS row
+  static constexpr int DPL = DH / G;                   // head dims owned per lane
+  static constexpr int SLICE_BYTES = DPL * ES;         // a lane's slice of a k_s row
+  static constexpr int VSLICE_BYTES = DPL * PB;        // a lane's slice of an interleaved v row
+  static constexpr int CPS = VSLICE_BYTES / 16;        // 16-byte chunks per v slice (0 if < 16 B)
+  static constexpr int RPL = R / G;                    // latent-value dims per lane
+  static constexpr int RP = R / 2;                     // latent pairs
+  static constexpr int ZK_BYTES = R * ES;              // one head's key latent row
+  static constexpr int ZV_BYTES = RPL * ES;            // one lane's slice of a value latent row
+  static constexpr bool SPLIT_QT = (ES == 2);          // absorbed query as bf16 hi+lo
+  static constexpr int NBT = kDecodeTile / G;          // batches per tile
+  static constexpr int KV_CH = kDecodeTile * ROW_CH;   // 16-byte chunks of one K (or V) tile
+  static constexpr int K_PER_LANE = (KV_CH + kDecodeThreads - 1) / kDecodeThreads;
+  static constexpr int VPAIR_ITEMS = (kDecodeTile / 2) * ROW_CH;  // (pair row, chunk) items
+  static constexpr int V_PER_LANE = (VPAIR_ITEMS + kDecodeThreads - 1) / kDecodeThreads;
+  static_assert(DH % G == 0 && (R == 0 || R % G == 0), "dims per lane");
+  static_assert(ROW_BYTES % 16 == 0 && ZK_BYTES % 16 == 0, "16-byte rows");
+  static_assert(G % 2 == 0 && DPL % 2 == 0, "pairs");
+  // Physical 16-byte chunk of logical chunk L of an interleaved v row: the
+  // chunks of each lane's slice are rotated so that the G lanes of a group,
+  // reading chunk c of their slices together, hit distinct LDS banks.
+  __device__ static __forceinline__ int vchunk(int L) {
+    if constexpr (CPS >= 2) {
+      const int j = L / CPS;
+      const int rot = ((j * CPS) / 8) & (CPS - 1);
+      return (L & ~(CPS - 1)) | (((L & (CPS - 1)) + rot) & (CPS - 1));
+    } else {
+      return L;
+    }
+  }
+};
+
+struct DecodeKernelParams {
+  const void* k_s; const void* v_s; const void* z_k; const void* z_v;
+  const int32_t* seq_lens;
+  const void* q; const void* b_k;
+  float scale_log2;
+  int heads, heads_pow2, slots, partials;
+  int64_t capacity;
+  int max_len, split_tokens;
+  float* ws_ml; float* ws_acc;
+};
+
+// One tile of shared rows in registers: 64 K rows, and V rows taken two at a
+// time so they can be interleaved token-wise.  Rows at or beyond `nvalid`
+// are zero (never read from memory).
+template <class S>
+struct TileRegs {
+  uint4 k[S::K_PER_LANE];
+  uint4 va[S::V_PER_LANE];
+  uint4 vb[S::V_PER_LANE];
+};
+
+template <class S>
+__device__ __forceinline__ void tile_load(TileRegs<S>& tr, const unsigned char* kbase,
+                                          const unsigned char* vbase, int nvalid, int tid) {
+#pragma unroll
+  for (int i = 0; i < S::K_PER_LANE; ++i) {
+    const int c = tid + i * kDecodeThreads;
+    const int row = c / S::ROW_CH;
+    tr.k[i] = make_uint4(0, 0, 0, 0);
+    if (c < S::KV_CH && row < nvalid) tr.k[i] = *reinterpret_cast<const uint4*>(kbase + size_t(c) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < S::V_PER_LANE; ++i) {
+    const int it = tid + i * kDecodeThreads;
+    const int pr = it / S::ROW_CH, ch = it % S::ROW_CH;
+    const int r0 = 2 * pr;
+    tr.va[i] = make_uint4(0, 0, 0, 0);
+    tr.vb[i] = make_uint4(0, 0, 0, 0);
+    if (it < S::VPAIR_ITEMS && r0 < nvalid)
+      tr.va[i] = *reinterpret_cast<const uint4*>(vbase + size_t(r0) * S::ROW_BYTES + ch * 16);
+    if (it < S::VPAIR_ITEMS && r0 + 1 < nvalid)
+      tr.vb[i] = *reinterpret_cast<const uint4*>(vbase + size_t(r0 + 1) * S::ROW_BYTES + ch * 16);
+  }
+}
+
+// Interleave two 16-byte row chunks element-wise into 32 bytes of pairs.
+template <class E>
+__device__ __forceinline__ void zip16(const uint4& a, const uint4& b, uint4& o0, uint4& o1) {
+  if constexpr (E::kBytes == 2) {
+    auto z = [](uint32_t x, uint32_t y, uint32_t& lo, uint32_t& hi) {
+      lo = __builtin_amdgcn_perm(y, x, 0x05040100u);   // (x.lo, y.lo)
+      hi = __builtin_amdgcn_perm(y, x, 0x07060302u);   // (x.hi, y.hi)
+    };
+    z(a.x, b.x, o0.x, o0.y);
+    z(a.y, b.y, o0.z, o0.w);
+    z(a.z, b.z, o1.x, o1.y);
+    z(a.w, b.w, o1.z, o1.w);
+  } else {
+    o0 = make_uint4(a.x, b.x, a.y, b.y);
+    o1 = make_uint4(a.z, b.z, a.w, b.w);
+  }
+}
+
+template <class S, class E>
+__device__ __forceinline__ void tile_store(const TileRegs<S>& tr, unsigned char* ks, unsigned char* vp, int tid) {
+#pragma unroll
+  for (int i = 0; i < S::K_PER_LANE; ++i) {
+    const int c = tid + i * kDecodeThreads;
+    if (c < S::KV_CH) {
+      const int row = c / S::ROW_CH, ch = c % S::ROW_CH;
+      *reinterpret_cast<uint4*>(ks + row * S::KS_STRIDE + ch * 16) = tr.k[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < S::V_PER_LANE; ++i) {
+    const int it = tid + i * kDecodeThreads;
+    if (it < S::VPAIR_ITEMS) {
+      const int pr = it / S::ROW_CH, ch = it % S::ROW_CH;
+      uint4 o0, o1;
+      zip16<E>(tr.va[i], tr.vb[i], o0, o1);
+      unsigned char* row = vp + pr * S::VP_STRIDE;
+      *reinterpret_cast<uint4*>(row + S::vchunk(2 * ch) * 16) = o0;
+      *reinterpret_cast<uint4*>(row + S::vchunk(2 * ch + 1) * 16) = o1;
+    }
+  }
+}
+
+// Latents of one batch for one lane: its own token's key latent row (all r
+// dims, for the logit) and, for each of the G tokens, its r/G-dim slice of
+// that token's value latent row (for the aggregation), as 32-bit words.
+template <class S>
+struct ZRegs {
+  static constexpr int ZKW = S::ZK_BYTES / 4 > 0 ? S::ZK_BYTES / 4 : 1;
+  static constexpr int ZVW = S::ZV_BYTES >= 4 ? S::ZV_BYTES / 4 : 1;
+  uint32_t zk[ZKW];
+  uint32_t zv[8][ZVW];   // [token of the batch][words]  (G <= 8)
+};
+
+template <class S, int G>
+__device__ __forceinline__ void z_load(ZRegs<S>& zr, const unsigned char* zk_seq, const unsigned char* zv_seq,
+                                       int tb, int t1, int H, int h, int g) {
+  if constexpr (S::ZK_BYTES > 0) {
+    const int tok = tb + g;
+    if (tok < t1) {
+      load_words<S::ZK_BYTES>(zr.zk, zk_seq + (size_t(tok) * H + h) * S::ZK_BYTES);
+    } else {
+#pragma unroll
+      for (int i = 0; i < ZRegs<S>::ZKW; ++i) zr.zk[i] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int tj = tb + j;
+      if (tj < t1) {
+        load_words<S::ZV_BYTES>(zr.zv[j], zv_seq + (size_t(tj) * H + h) * S::ZK_BYTES + g * S::ZV_BYTES);
+      } else {
+#pragma unroll
+        for (int i = 0; i < ZRegs<S>::ZVW; ++i) zr.zv[j][i] = 0u;
+      }
+    }
+  }
+}
+
+// XOR-ordered reduce-scatter of per-lane partial sums within an aligned
+// group of G lanes.  On entry part[i] of lane g is the partial sum of item
+// (i ^ g) over lane g's slice; on exit part[0] of lane g is the complete sum
+// of item g.  Stage masks (G=8: 7, 2, 1; G=4: 3, 1; G=2: 1) keep the register
+// index exchanged the same in every lane, so each stage is a DPP add.
+template <int G>
+__device__ __forceinline__ void xor_reduce_scatter(float* part) {
+  if constexpr (G == 8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) part[k] += dpp_mov<kDppHalfMirror>(part[k ^ 7]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) part[k] += dpp_mov<kDppSwap2>(part[k ^ 2]);
+    part[0] += dpp_mov<kDppSwap1>(part[1]);
+  } else if constexpr (G == 4) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) part[k] += dpp_mov<kDppRev4>(part[k ^ 3]);
+    part[0] += dpp_mov<kDppSwap1>(part[1]);
+  } else {
+    static_assert(G == 2, "group size");
+    part[0] += dpp_mov<kDppSwap1>(part[1]);
+  }
+}
+
+template <class E, int DH, int R, int G>
+__global__ __attribute__((amdgpu_flat_work_group_size(kDecodeThreads, kDecodeThreads), amdgpu_waves_per_eu(2)))
+void decode_split_kernel(DecodeKernelParams p) {
+  using S = DecodeShape<E, DH, R, G>;
+  using T = typename S::T;
+  using Pair = typename S::Pair;
+
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[kDecodeTile * S::KS_STRIDE];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[(kDecodeTile / 2) * S::VP_STRIDE];
+
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int H = p.heads;
+  const int g = tid % G;
+  const int h = (tid / G) % p.heads_pow2;
+  const int slot = tid / (G * p.heads_pow2);
+  const bool active = (h < H) && (slot < p.slots);
+
+  int len = p.seq_lens[b];
+  len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+  const int t0 = split * p.split_tokens;
+  if (t0 >= len) return;                                   // whole workgroup: uniform exit
+  const int t1 = min(t0 + p.split_tokens, len);
+
+  const unsigned char* kseq = static_cast<const unsigned char*>(p.k_s) + size_t(b) * p.capacity * S::ROW_BYTES;
+  const unsigned char* vseq = static_cast<const unsigned char*>(p.v_s) + size_t(b) * p.capacity * S::ROW_BYTES;
+  const unsigned char* zkseq = static_cast<const unsigned char*>(p.z_k) + size_t(b) * p.capacity * H * S::ZK_BYTES;
+  const unsigned char* zvseq = static_cast<const unsigned char*>(p.z_v) + size_t(b) * p.capacity * H * S::ZK_BYTES;
+
+  // ---- prologue: this lane's slice of q_h, and the absorbed query B^K_h^T q_h ----
+  const int hq = active ? h : 0;
+  const T* qrow = static_cast<const T*>(p.q) + (size_t(b) * H + hq) * DH;
+  Pair qs[S::DPL / 2];
+  {
+    uint32_t qw[S::SLICE_BYTES / 4];
+    load_words<S::SLICE_BYTES>(qw, qrow + g * S::DPL);
+#pragma unroll
+    for (int i = 0; i < S::DPL / 2; ++i) qs[i] = pair_at<E>(qw, i);
+  }
+  Pair qt_hi[S::RP > 0 ? S::RP : 1], qt_lo[S::RP > 0 ? S::RP : 1];
+  if constexpr (R > 0) {
+    // lane g sums rows d in its slice of B^K_h, then the group adds up.
+    float part[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) part[i] = 0.f;
+    const T* bk = static_cast<const T*>(p.b_k) + size_t(hq) * DH * R;
+#pragma unroll
+    for (int dd = 0; dd < S::DPL; ++dd) {
+      const int d = g * S::DPL + dd;
+      const float qd = (dd & 1) ? E::hi(qs[dd / 2]) : E::lo(qs[dd / 2]);
+      uint32_t rw[S::ZK_BYTES / 4];
+      load_words<S::ZK_BYTES>(rw, bk + size_t(d) * R);
+#pragma unroll
+      for (int i = 0; i < R; ++i) part[i] = __builtin_fmaf(qd, E::to_f32(elem_at<E>(rw, i)), part[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < S::RP; ++i) {
+      const float a = group_sum<G>(part[2 * i]);
+      const float c = group_sum<G>(part[2 * i + 1]);
+      qt_hi[i] = E::make_pair(a, c);
+      if constexpr (S::SPLIT_QT) qt_lo[i] = E::make_pair(a - E::lo(qt_hi[i]), c - E::hi(qt_hi[i]));
+    }
+  }
+
+  // ---- running state ----
+  float m = -INFINITY, l = 0.f;
+  float acc_s[S::DPL];
+  float acc_z[S::RPL > 0 ? S::RPL : 1];
+#pragma unroll
+  for (int i = 0; i < S::DPL; ++i) acc_s[i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < (S::RPL > 0 ? S::RPL : 1); ++i) acc_z[i] = 0.f;
+
+  TileRegs<S> tr;
+  tile_load<S>(tr, kseq + size_t(t0) * S::ROW_BYTES, vseq + size_t(t0) * S::ROW_BYTES, t1 - t0, tid);
+
+  ZRegs<S> zcur;
+  if (active && slot < S::NBT) z_load<S, G>(zcur, zkseq, zvseq, t0 + slot * G, t1, H, h, g);
+
+  for (int ts = t0; ts < t1; ts += kDecodeTile) {
+    __syncthreads();                                         // previous tile fully consumed
+    tile_store<S, E>(tr, s_k, s_v, tid);
+    __syncthreads();
+    const int tn = ts + kDecodeTile;
+    if (tn < t1) tile_load<S>(tr, kseq + size_t(tn) * S::ROW_BYTES, vseq + size_t(tn) * S::ROW_BYTES, t1 - tn, tid);
+
+    if (active) {
+      for (int bi = slot; bi < S::NBT; bi += p.slots) {
+        const int tb = ts + bi * G;
+        if (tb >= t1) break;
+        // prefetch the latents of this slot's next batch
+        ZRegs<S> znext;
+        int nbi = bi + p.slots, nts = ts;
+        if (nbi >= S::NBT) { nbi = slot; nts = ts + kDecodeTile; }
+        const int ntb = nts + nbi * G;
+        if (ntb < t1) z_load<S, G>(znext, zkseq, zvseq, ntb, t1, H, h, g);
+
+        // -- logits (Eq. (6)): shared path by slices + reduce-scatter, then the latent path --
+        float part[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+          uint32_t kw[S::SLICE_BYTES / 4];
+          load_words<S::SLICE_BYTES>(kw, s_k + (bi * G + (i ^ g)) * S::KS_STRIDE + g * S::SLICE_BYTES);
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < S::DPL / 2; ++j) a = E::dot2(a, qs[j], pair_at<E>(kw, j));
+          part[i] = a;
+        }
+        xor_reduce_scatter<G>(part);
+        float sz = 0.f;
+        if constexpr (R > 0) {
+#pragma unroll
+          for (int i = 0; i < S::RP; ++i) {
+            const Pair zp = pair_at<E>(zcur.zk, i);
+            sz = E::dot2(sz, qt_hi[i], zp);
+            if constexpr (S::SPLIT_QT) sz = E::dot2(sz, qt_lo[i], zp);
+          }
+        }
+        const bool tok_ok = (tb + g) < t1;
+        const float s = tok_ok ? (part[0] + sz) * p.scale_log2 : -INFINITY;
+
+        // -- online softmax over the batch --
+        const float m_new = fmaxf(m, group_max<G>(s));      // finite: token tb is valid
+        const float alpha = fast_exp2(m - m_new);
+        const float pe = fast_exp2(s - m_new);
+        m = m_new;
+        // pair up the weights of tokens (2k, 2k+1); both lanes of a pair hold it
+        const float pnb = dpp_mov<kDppSwap1>(pe);
+        const bool even = (g & 1) == 0;
+        const Pair pp = even ? E::make_pair(pe, pnb) : E::make_pair(pnb, pe);
+        const float p_own = even ? E::lo(pp) : E::hi(pp);   // the weight as it enters the sums
+        l = l * alpha + p_own;
+#pragma unroll
+        for (int i = 0; i < S::DPL; ++i) acc_s[i] *= alpha;
+#pragma unroll
+        for (int i = 0; i < S::RPL; ++i) acc_z[i] *= alpha;
+
+        // -- aggregation (Eq. (7)): shared values and value latents --
+        auto fold = [&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          Pair pk;
+          if constexpr (S::PB == 4) {
+            pk = __builtin_bit_cast(Pair, group_bcast<G, 2 * k>(__builtin_bit_cast(uint32_t, pp)));
+          } else {
+            const float2 f = __builtin_bit_cast(float2, pp);
+            pk = make_float2(__uint_as_float(group_bcast<G, 2 * k>(__float_as_uint(f.x))),
+                             __uint_as_float(group_bcast<G, 2 * k>(__float_as_uint(f.y))));
+          }
+          const unsigned char* vrow = s_v + (bi * (G / 2) + k) * S::VP_STRIDE;
+          uint32_t vw[S::VSLICE_BYTES / 4];
+          if constexpr (S::CPS >= 1) {
+#pragma unroll
+            for (int c = 0; c < S::CPS; ++c)
+              load_words<16>(vw + 4 * c, vrow + S::vchunk(g * S::CPS + c) * 16);
+          } else {
+            load_words<S::VSLICE_BYTES>(vw, vrow + g * S::VSLICE_BYTES);
+          }
+#pragma unroll
+          for (int i = 0; i < S::DPL; ++i) acc_s[i] = E::dot2(acc_s[i], pk, pair_at<E>(vw, i));
+          if constexpr (R > 0) {
+#pragma unroll
+            for (int i = 0; i < S::RPL; ++i)
+              acc_z[i] = E::dot2(acc_z[i], pk, E::zip(elem_at<E>(zcur.zv[2 * k], i), elem_at<E>(zcur.zv[2 * k + 1], i)));
+          }
+        };
+        [&]<int... K>(std::integer_sequence<int, K...>) {
+          (fold(std::integral_constant<int, K>{}), ...);
+        }(std::make_integer_sequence<int, G / 2>{});
+
+        if (ntb < t1) zcur = znext;
+      }
+    }
+  }
+
+  if (!active) return;
+  // ---- partial state of this (split, slot, head) ----
+  const float l_tot = group_sum<G>(l);
+  const size_t pidx = (size_t(b) * p.partials + size_t(split) * p.slots + slot) * H + h;
+  if (g == 0) {
+    p.ws_ml[2 * pidx] = m;
+    p.ws_ml[2 * pidx + 1] = l_tot;
+  }
+  float* dst = p.ws_acc + pidx * (DH + R);
+#pragma unroll
+  for (int i = 0; i < S::DPL; ++i) dst[g * S::DPL + i] = acc_s[i];
+#pragma unroll
+  for (int i = 0; i < S::RPL; ++i) dst[DH + g * S::RPL + i] = acc_z[i];
+}
+
+// Merge the partial states of one (sequence, head) and apply the residual
+// up-projection once: o = (sum_j w_j acc_s_j + B^V_h sum_j w_j acc_z_j) / L,
+// w_j = 2^(m_j - M), L = sum_j w_j l_j (Eq. (7): the latent sums are linear in
+// the weights, so B^V is applied after the merge).
+template <class E, int DH, int R>
+__global__ __launch_bounds__(128) void decode_merge_kernel(const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+                                                           const int32_t* __restrict__ seq_lens, const void* b_v,
+                                                           void* out, int heads, int partials, int slots,
+                                                           int split_tokens, int max_len) {
+  using T = typename E::T;
+  constexpr int NT = 128;
+  __shared__ float s_z[R > 0 ? R : 1];
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  int len = seq_lens[b];
+  len = len < 0 ? 0 : (len > max_len ? max_len : len);
+  T* o = static_cast<T*>(out) + (size_t(b) * heads + h) * DH;
+  if (len == 0) {
+    for (int d = tid; d < DH; d += NT) o[d] = E::from_f32(0.f);
+    return;
+  }
+  const int n = ((len + split_tokens - 1) / split_tokens) * slots;   // partials written for this sequence
+  const float* ml = ws_ml + (size_t(b) * partials * heads + h) * 2;
+  const size_t mls = size_t(heads) * 2;
+  const float* acc = ws_acc + (size_t(b) * partials * heads + h) * (DH + R);
+  const size_t as = size_t(heads) * (DH + R);
+  float M = -INFINITY;
+  for (int j = 0; j < n; ++j) M = fmaxf(M, ml[j * mls]);
+  float L = 0.f;
+  for (int j = 0; j < n; ++j) L += fast_exp2(ml[j * mls] - M) * ml[j * mls + 1];   // empty partial: m = -inf
+  if constexpr (R > 0) {
+    for (int i = tid; i < R; i += NT) {
+      float z = 0.f;
+      for (int j = 0; j < n; ++j) z += fast_exp2(ml[j * mls] - M) * acc[j * as + DH + i];
+      s_z[i] = z;
+    }
+    __syncthreads();
+  }
+  const float invL = 1.f / L;
+  const T* bv = static_cast<const T*>(b_v) + size_t(h) * DH * R;
+  for (int d = tid; d < DH; d += NT) {
+    float a = 0.f;
+    for (int j = 0; j < n; ++j) a += fast_exp2(ml[j * mls] - M) * acc[j * as + d];
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) a = __builtin_fmaf(E::to_f32(bv[size_t(d) * R + i]), s_z[i], a);
+    }
+    o[d] = E::from_f32(a * invL);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch over the compiled envelope.
+// ---------------------------------------------------------------------------
+template <class E, int DH, int R, int G>
+static hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
+  DecodeKernelParams kp;
+  kp.k_s = a.k_s; kp.v_s = a.v_s; kp.z_k = a.z_k; kp.z_v = a.z_v;
+  kp.seq_lens = a.seq_lens; kp.q = a.q; kp.b_k = a.b_k;
+  kp.scale_log2 = a.scale_log2;
+  kp.heads = pl.heads; kp.heads_pow2 = pl.heads_pow2; kp.slots = pl.slots; kp.partials = pl.partials;
+  kp.capacity = pl.capacity; kp.max_len = pl.max_len; kp.split_tokens = pl.split_tokens;
+  kp.ws_ml = a.ws_ml; kp.ws_acc = a.ws_acc;
+  if ((phase & 1) && pl.n_splits > 0) {
+    hipLaunchKernelGGL((decode_split_kernel<E, DH, R, G>), dim3(pl.n_splits, pl.batch), dim3(kDecodeThreads), 0, st, kp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!(phase & 2)) return hipSuccess;
+  hipLaunchKernelGGL((decode_merge_kernel<E, DH, R>), dim3(pl.heads, pl.batch), dim3(128), 0, st,
+                     a.ws_ml, a.ws_acc, a.seq_lens, a.b_v, a.out, pl.heads, pl.partials, pl.slots,
+                     pl.split_tokens, pl.max_len);
+  return hipGetLastError();
+}
+
+template <class E, int DH, int R, int G>
+static hipError_t launch_if_valid(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
+  if constexpr ((R * E::kBytes) % 16 == 0 && DH % G == 0 && (R == 0 || R % G == 0)) {
+    return launch_decode_t<E, DH, R, G>(pl, a, phase, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <class E, int DH>
+static hipError_t dispatch_rank(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
+  const bool g4 = pl.group == 4;
+  switch (pl.rank) {
+#define LRKV_RANK_CASE(RV)                                                                          \
+    case RV: return g4 ? launch_if_valid<E, DH, RV, 4>(pl, a, phase, st) : launch_if_valid<E, DH, RV, 8>(pl, a, phase, st);
+    LRKV_RANK_CASE(0) LRKV_RANK_CASE(4) LRKV_RANK_CASE(8) LRKV_RANK_CASE(16) LRKV_RANK_CASE(32) LRKV_RANK_CASE(64)
+#undef LRKV_RANK_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class E>
+static hipError_t dispatch_dim(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
+  switch (pl.head_dim) {
+    case 16: return dispatch_rank<E, 16>(pl, a, phase, st);
+    case 32: return dispatch_rank<E, 32>(pl, a, phase, st);
+    case 64: return dispatch_rank<E, 64>(pl, a, phase, st);
+    case 128: return dispatch_rank<E, 128>(pl, a, phase, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool decode_supported(int dtype, int head_dim, int rank, int heads) {
+  if (dtype != 0 && dtype != 1) return false;
+  if (!(head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128)) return false;
+  if (!(rank == 0 || rank == 4 || rank == 8 || rank == 16 || rank == 32 || rank == 64)) return false;
+  if (dtype == 1 && rank % 8 != 0) return false;           // 16-byte latent rows in bf16
+  if (heads < 1 || heads > 64) return false;
+  if (heads > 32 && rank == 0) return true;                 // G = 4
+  if (heads > 32 && rank % 4 != 0) return false;
+  return true;
+}
+
+hipError_t launch_decode(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
+  return pl.dtype == 1 ? dispatch_dim<BF16>(pl, a, phase, st) : dispatch_dim<F32>(pl, a, phase, st);
+}
+
+}  // namespace lrkv

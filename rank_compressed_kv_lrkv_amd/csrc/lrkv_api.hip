@@ -1,0 +1,227 @@
+// C ABI of liblrkv: host-side validation, planning and dispatch.
+// Every check runs before anything is enqueued; a call that returns an error
+// has launched nothing.  No memory is allocated and nothing synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/lrkv.h"
+#include "lrkv_internal.h"
+
+namespace {
+
+using lrkv::DecodePlan;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+int elem_bytes(int32_t dtype) { return dtype == LRKV_BF16 ? 2 : 4; }
+
+// Compute units of the current device, queried once per device.
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+lrkv_status check_sizes(int32_t dtype, int32_t batch, int32_t heads, int32_t head_dim, int32_t rank,
+                        int64_t capacity) {
+  if (dtype != LRKV_F32 && dtype != LRKV_BF16) return LRKV_ERR_DTYPE;
+  if (batch < 0 || heads < 1 || head_dim < 1 || rank < 0 || capacity < 1) return LRKV_ERR_SHAPE;
+  if (capacity > INT32_MAX) return LRKV_ERR_SHAPE;
+  const int es = elem_bytes(dtype);
+  if ((int64_t(head_dim) * es) % 16 != 0 || (int64_t(rank) * es) % 16 != 0) return LRKV_ERR_SHAPE;
+  return LRKV_OK;
+}
+
+lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t head_dim, int32_t rank,
+                        int64_t capacity, int64_t max_len, int32_t split_tokens, DecodePlan* pl) {
+  lrkv_status st = check_sizes(dtype, batch, heads, head_dim, rank, capacity);
+  if (st != LRKV_OK) return st;
+  if (!lrkv::decode_supported(dtype, head_dim, rank, heads)) return LRKV_ERR_SHAPE;
+  if (max_len < 0 || split_tokens < 0) return LRKV_ERR_SHAPE;
+  if (max_len > capacity) return LRKV_ERR_CAPACITY;
+  if (split_tokens != 0 && split_tokens % lrkv::kDecodeTile != 0) return LRKV_ERR_SHAPE;
+
+  pl->batch = batch; pl->heads = heads; pl->head_dim = head_dim; pl->rank = rank; pl->dtype = dtype;
+  pl->capacity = capacity; pl->max_len = int(max_len);
+  pl->group = (rank == 4 || heads > 32) ? 4 : 8;
+  int hp = 1;
+  while (hp < heads) hp <<= 1;
+  pl->heads_pow2 = hp;
+  pl->slots = lrkv::kDecodeThreads / (hp * pl->group);
+  if (pl->slots < 1) return LRKV_ERR_SHAPE;
+
+  const int tile = lrkv::kDecodeTile;
+  int split = split_tokens;
+  if (split == 0) {
+    // Aim for about two resident workgroups per compute unit over the whole batch.
+    const int64_t total = int64_t(batch) * max_len;
+    const int64_t target = 2 * int64_t(device_cu_count());
+    int64_t s = (total + target - 1) / (target > 0 ? target : 1);
+    s = (s + tile - 1) / tile * tile;
+    if (s < tile) s = tile;
+    const int64_t cap = (max_len + tile - 1) / tile * tile;
+    if (s > cap) s = cap < tile ? tile : cap;
+    split = int(s);
+  }
+  pl->split_tokens = split;
+  pl->n_splits = int((max_len + split - 1) / split);
+  pl->partials = pl->n_splits * pl->slots;
+  const size_t states = size_t(batch) * size_t(pl->partials) * size_t(heads);
+  pl->ws_ml_bytes = (states * 2 * sizeof(float) + 255) / 256 * 256;
+  pl->ws_acc_bytes = (states * size_t(head_dim + rank) * sizeof(float) + 255) / 256 * 256;
+  return LRKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lrkv_status_string(int32_t s) {
+  switch (s) {
+    case LRKV_OK: return "ok";
+    case LRKV_ERR_NULL: return "null pointer";
+    case LRKV_ERR_SHAPE: return "invalid or unsupported shape";
+    case LRKV_ERR_DTYPE: return "invalid dtype";
+    case LRKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case LRKV_ERR_CAPACITY: return "length exceeds cache capacity";
+    case LRKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case LRKV_ERR_DEVICE: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+int64_t lrkv_cache_elems_per_token(int32_t num_heads, int32_t head_dim, int32_t rank) {
+  if (num_heads < 1 || head_dim < 1 || rank < 0) return -1;
+  return 2 * (int64_t(head_dim) + int64_t(num_heads) * int64_t(rank));
+}
+
+lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                       int32_t rank, int64_t capacity, int64_t max_len, int32_t split_tokens,
+                                       size_t* bytes) {
+  if (!bytes) return LRKV_ERR_NULL;
+  DecodePlan pl;
+  const lrkv_status st = plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl);
+  if (st != LRKV_OK) return st;
+  *bytes = pl.ws_ml_bytes + pl.ws_acc_bytes;
+  return LRKV_OK;
+}
+
+static lrkv_status decode_phases(int phase, int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                 int32_t rank, int64_t capacity, const void* k_shared, const void* v_shared,
+                                 const void* z_k, const void* z_v, const int32_t* seq_lens, int64_t max_len,
+                                 const void* q, const void* b_k, const void* b_v, float scale, int32_t split_tokens,
+                                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  DecodePlan pl;
+  const lrkv_status st = plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl);
+  if (st != LRKV_OK) return st;
+  if (batch == 0) return LRKV_OK;
+  const bool scan = phase & 1, combine = phase & 2;
+  if (!seq_lens) return LRKV_ERR_NULL;
+  if (scan && (!k_shared || !v_shared || !q)) return LRKV_ERR_NULL;
+  if (scan && rank > 0 && (!z_k || !z_v || !b_k)) return LRKV_ERR_NULL;
+  if (combine && (!out || (rank > 0 && !b_v))) return LRKV_ERR_NULL;
+  const size_t need = pl.ws_ml_bytes + pl.ws_acc_bytes;
+  if (!workspace || workspace_bytes < need) return LRKV_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned4(seq_lens)) return LRKV_ERR_ALIGN;
+  if (scan && (!aligned16(k_shared) || !aligned16(v_shared) || !aligned16(q))) return LRKV_ERR_ALIGN;
+  if (scan && rank > 0 && (!aligned16(z_k) || !aligned16(z_v) || !aligned16(b_k))) return LRKV_ERR_ALIGN;
+  if (combine && (!aligned16(out) || (rank > 0 && !aligned16(b_v)))) return LRKV_ERR_ALIGN;
+
+  const float sc = (scale > 0.f && std::isfinite(scale)) ? scale : 1.0f / std::sqrt(float(head_dim));
+  lrkv::DecodeArgs a;
+  a.k_s = k_shared; a.v_s = v_shared; a.z_k = z_k; a.z_v = z_v;
+  a.seq_lens = seq_lens; a.q = q; a.b_k = b_k; a.b_v = b_v;
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.out = out;
+  a.ws_ml = static_cast<float*>(workspace);
+  a.ws_acc = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + pl.ws_ml_bytes);
+  const hipError_t e = lrkv::launch_decode(pl, a, phase, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+}
+
+#define LRKV_DECODE_ARGS                                                                                        \
+  int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank, int64_t capacity,         \
+      const void *k_shared, const void *v_shared, const void *z_k, const void *z_v, const int32_t *seq_lens,   \
+      int64_t max_len, const void *q, const void *b_k, const void *b_v, float scale, int32_t split_tokens,     \
+      void *out, void *workspace, size_t workspace_bytes, void *stream
+#define LRKV_DECODE_PASS                                                                                   \
+  dtype, batch, num_heads, head_dim, rank, capacity, k_shared, v_shared, z_k, z_v, seq_lens, max_len, q, b_k, \
+      b_v, scale, split_tokens, out, workspace, workspace_bytes, stream
+
+lrkv_status lrkv_decode(LRKV_DECODE_ARGS) { return decode_phases(3, LRKV_DECODE_PASS); }
+lrkv_status lrkv_decode_partial(LRKV_DECODE_ARGS) { return decode_phases(1, LRKV_DECODE_PASS); }
+lrkv_status lrkv_decode_combine(LRKV_DECODE_ARGS) { return decode_phases(2, LRKV_DECODE_PASS); }
+
+lrkv_status lrkv_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
+                        int64_t capacity, void* k_shared, void* v_shared, void* z_k, void* z_v,
+                        const int32_t* pos, int32_t n_new, const void* new_k_s, const void* new_v_s,
+                        const void* new_z_k, const void* new_z_v, void* stream) {
+  const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, capacity);
+  if (st != LRKV_OK) return st;
+  if (n_new < 0) return LRKV_ERR_SHAPE;
+  if (batch == 0 || n_new == 0) return LRKV_OK;
+  if (!k_shared || !v_shared || !pos || !new_k_s || !new_v_s) return LRKV_ERR_NULL;
+  if (rank > 0 && (!z_k || !z_v || !new_z_k || !new_z_v)) return LRKV_ERR_NULL;
+  if (!aligned16(k_shared) || !aligned16(v_shared) || !aligned16(new_k_s) || !aligned16(new_v_s) ||
+      !aligned4(pos))
+    return LRKV_ERR_ALIGN;
+  if (rank > 0 && (!aligned16(z_k) || !aligned16(z_v) || !aligned16(new_z_k) || !aligned16(new_z_v)))
+    return LRKV_ERR_ALIGN;
+  lrkv::AppendArgs a;
+  a.dtype = dtype; a.batch = batch; a.heads = num_heads; a.head_dim = head_dim; a.rank = rank;
+  a.capacity = capacity; a.k_s = k_shared; a.v_s = v_shared; a.z_k = z_k; a.z_v = z_v;
+  a.pos = pos; a.n_new = n_new;
+  a.new_k_s = new_k_s; a.new_v_s = new_v_s; a.new_z_k = new_z_k; a.new_z_v = new_z_v;
+  const hipError_t e = lrkv::launch_append(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+}
+
+lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
+                         int64_t capacity, void* k_shared, void* v_shared, void* z_k, void* z_v, int32_t seq_len,
+                         const void* q, const void* k_s, const void* v_s, const void* z_k_new,
+                         const void* z_v_new, const void* b_k, const void* b_v, float scale, void* out,
+                         void* stream) {
+  const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, capacity);
+  if (st != LRKV_OK) return st;
+  if (!lrkv::prefill_supported(dtype, head_dim, rank, num_heads)) return LRKV_ERR_SHAPE;
+  if (seq_len < 0) return LRKV_ERR_SHAPE;
+  const int ncache = (k_shared != nullptr) + (v_shared != nullptr) + (z_k != nullptr) + (z_v != nullptr);
+  const bool write_cache = ncache == 4;
+  if (ncache != 0 && ncache != 4) return LRKV_ERR_NULL;
+  if (write_cache && seq_len > capacity) return LRKV_ERR_CAPACITY;
+  if (batch == 0 || seq_len == 0) return LRKV_OK;
+  if (!q || !k_s || !v_s || !out) return LRKV_ERR_NULL;
+  if (rank > 0 && (!z_k_new || !z_v_new || !b_k || !b_v)) return LRKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_s) || !aligned16(v_s) || !aligned16(out)) return LRKV_ERR_ALIGN;
+  if (rank > 0 && (!aligned16(z_k_new) || !aligned16(z_v_new) || !aligned16(b_k) || !aligned16(b_v)))
+    return LRKV_ERR_ALIGN;
+  if (write_cache && (!aligned16(k_shared) || !aligned16(v_shared) || !aligned16(z_k) || !aligned16(z_v)))
+    return LRKV_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (write_cache) {
+    lrkv::AppendArgs a;
+    a.dtype = dtype; a.batch = batch; a.heads = num_heads; a.head_dim = head_dim; a.rank = rank;
+    a.capacity = capacity; a.k_s = k_shared; a.v_s = v_shared; a.z_k = z_k; a.z_v = z_v;
+    a.pos = nullptr; a.n_new = seq_len;
+    a.new_k_s = k_s; a.new_v_s = v_s; a.new_z_k = z_k_new; a.new_z_v = z_v_new;
+    if (lrkv::launch_append(a, s) != hipSuccess) return LRKV_ERR_DEVICE;
+  }
+  const float sc = (scale > 0.f && std::isfinite(scale)) ? scale : 1.0f / std::sqrt(float(head_dim));
+  lrkv::PrefillArgs p;
+  p.batch = batch; p.heads = num_heads; p.head_dim = head_dim; p.rank = rank; p.seq_len = seq_len;
+  p.q = q; p.k_s = k_s; p.v_s = v_s; p.z_k = z_k_new; p.z_v = z_v_new; p.b_k = b_k; p.b_v = b_v;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.out = out;
+  return lrkv::launch_prefill(p, s) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// Device helpers for the LRKV kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrkv {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// Round to nearest even; gfx950 has a native packed convert for this.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) { return uint16_t(pack_bf16x2(x, 0.f) & 0xffffu); }
+
+// Element traits.  A "pair" is two consecutive elements used as one operand
+// of a 2-wide dot product; for bf16 that is one 32-bit register feeding
+// v_dot2_f32_bf16, for fp32 a float2 evaluated as two FMAs.
+struct F32 {
+  using T = float;
+  using Pair = float2;
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ float dot2(float acc, Pair a, Pair b) {
+    return __builtin_fmaf(a.y, b.y, __builtin_fmaf(a.x, b.x, acc));
+  }
+  __device__ static __forceinline__ Pair make_pair(float lo, float hi) { return make_float2(lo, hi); }
+  __device__ static __forceinline__ float lo(Pair p) { return p.x; }
+  __device__ static __forceinline__ float hi(Pair p) { return p.y; }
+  __device__ static __forceinline__ float to_f32(T x) { return x; }
+  __device__ static __forceinline__ T from_f32(float x) { return x; }
+  // Interleave element i of a and element i of b.
+  __device__ static __forceinline__ Pair zip(T a, T b) { return make_float2(a, b); }
+};
+
+struct BF16 {
+  using T = uint16_t;
+  using Pair = uint32_t;
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ float dot2(float acc, Pair a, Pair b) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+  }
+  __device__ static __forceinline__ Pair make_pair(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  __device__ static __forceinline__ float lo(Pair p) { return __uint_as_float(p << 16); }
+  __device__ static __forceinline__ float hi(Pair p) { return __uint_as_float(p & 0xffff0000u); }
+  __device__ static __forceinline__ float to_f32(T x) { return bf16_to_f32(x); }
+  __device__ static __forceinline__ T from_f32(float x) { return f32_to_bf16(x); }
+  __device__ static __forceinline__ Pair zip(T a, T b) { return uint32_t(a) | (uint32_t(b) << 16); }
+};
+
+// Pair i (compile-time) of registers viewed as consecutive 32-bit words.
+template <class E>
+__device__ __forceinline__ typename E::Pair pair_at(const uint32_t* w, int i);
+template <>
+__device__ __forceinline__ BF16::Pair pair_at<BF16>(const uint32_t* w, int i) { return w[i]; }
+template <>
+__device__ __forceinline__ F32::Pair pair_at<F32>(const uint32_t* w, int i) {
+  return make_float2(__uint_as_float(w[2 * i]), __uint_as_float(w[2 * i + 1]));
+}
+// Element i (compile-time) of registers viewed as consecutive 32-bit words.
+template <class E>
+__device__ __forceinline__ typename E::T elem_at(const uint32_t* w, int i);
+template <>
+__device__ __forceinline__ BF16::T elem_at<BF16>(const uint32_t* w, int i) {
+  return uint16_t((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu));
+}
+template <>
+__device__ __forceinline__ F32::T elem_at<F32>(const uint32_t* w, int i) { return __uint_as_float(w[i]); }
+
+// Load NB bytes (NB == 2 or a multiple of 4) into 32-bit words w[0..ceil(NB/4)),
+// using 16-, 8- and 4-byte accesses; p must be aligned to min(NB, 16).
+template <int NB>
+__device__ __forceinline__ void load_words(uint32_t* w, const void* p) {
+  if constexpr (NB == 2) {
+    w[0] = *reinterpret_cast<const uint16_t*>(p);
+  } else {
+    static_assert(NB % 4 == 0, "load size");
+    const unsigned char* c = static_cast<const unsigned char*>(p);
+    int o = 0;
+#pragma unroll
+    for (; o + 16 <= NB; o += 16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(c + o);
+      w[o / 4] = v.x; w[o / 4 + 1] = v.y; w[o / 4 + 2] = v.z; w[o / 4 + 3] = v.w;
+    }
+    if constexpr (NB % 16 >= 8) {
+      constexpr int o8 = NB / 16 * 16;
+      const uint2 v = *reinterpret_cast<const uint2*>(c + o8);
+      w[o8 / 4] = v.x; w[o8 / 4 + 1] = v.y;
+    }
+    if constexpr (NB % 8 == 4) {
+      constexpr int o4 = NB / 8 * 8;
+      w[o4 / 4] = *reinterpret_cast<const uint32_t*>(c + o4);
+    }
+  }
+}
+
+// Byte-sized vector type for loads of NB bytes (NB in {2, 4, 8, 16}).
+template <int NB> struct VecBytes;
+template <> struct VecBytes<2> { using V = uint16_t; };
+template <> struct VecBytes<4> { using V = uint32_t; };
+template <> struct VecBytes<8> { using V = uint2; };
+template <> struct VecBytes<16> { using V = uint4; };
+
+// Copy NB bytes (a multiple of 8, or 2/4) from p to dst using the widest
+// aligned accesses; p and dst must be aligned to min(NB, 16).
+template <int NB>
+__device__ __forceinline__ void copy_bytes(void* dst, const void* p) {
+  if constexpr (NB >= 16) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i)
+      reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(p)[i];
+  } else {
+    *reinterpret_cast<typename VecBytes<NB>::V*>(dst) = *reinterpret_cast<const typename VecBytes<NB>::V*>(p);
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void zero_bytes(void* dst) {
+  if constexpr (NB >= 16) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) reinterpret_cast<uint4*>(dst)[i] = make_uint4(0, 0, 0, 0);
+  } else {
+    *reinterpret_cast<typename VecBytes<NB>::V*>(dst) = typename VecBytes<NB>::V{};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Reductions inside aligned groups of G lanes (G in {2, 4, 8}) with DPP:
+// quad_perm swaps for distances 1 and 2, row_half_mirror to pair the two
+// quads of an 8-lane group.  After the calls every lane of the group holds
+// the group result.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kDppSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kDppRev4 = 0x1B;        // quad_perm [3,2,1,0]
+
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  if constexpr (G >= 2) v = fmaxf(v, dpp_mov<kDppSwap1>(v));
+  if constexpr (G >= 4) v = fmaxf(v, dpp_mov<kDppSwap2>(v));
+  if constexpr (G >= 8) v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  if constexpr (G >= 2) v += dpp_mov<kDppSwap1>(v);
+  if constexpr (G >= 4) v += dpp_mov<kDppSwap2>(v);
+  if constexpr (G >= 8) v += dpp_mov<kDppHalfMirror>(v);
+  return v;
+}
+
+// Value held by lane `src` (0 <= src < G) of this lane's aligned G-group,
+// through the LDS crossbar swizzle (bit-mask mode, no memory traffic).
+template <int G, int SRC>
+__device__ __forceinline__ uint32_t group_bcast(uint32_t v) {
+  constexpr int and_mask = 0x1F & ~(G - 1);
+  constexpr int pattern = and_mask | (SRC << 5);
+  return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), pattern));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace lrkv

@@ -1,0 +1,61 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lrkv {
+
+constexpr int kDecodeThreads = 256;  // one workgroup = 4 wave64
+constexpr int kDecodeTile = 64;      // cache tokens staged in LDS per step
+
+struct DecodePlan {
+  int batch, heads, head_dim, rank, dtype;
+  int64_t capacity;
+  int max_len;
+  int split_tokens;   // tokens per split (multiple of kDecodeTile)
+  int n_splits;       // ceil(max_len / split_tokens)
+  int group;          // lanes per head (G)
+  int heads_pow2;     // heads rounded up to a power of two
+  int slots;          // independent token streams per workgroup
+  int partials;       // n_splits * slots partial states per (sequence, head)
+  size_t ws_ml_bytes, ws_acc_bytes;
+};
+
+struct DecodeArgs {
+  const void* k_s; const void* v_s; const void* z_k; const void* z_v;
+  const int32_t* seq_lens;
+  const void* q; const void* b_k; const void* b_v;
+  float scale_log2;   // softmax scale times log2(e)
+  void* out;
+  float* ws_ml;       // [batch][partials][heads] x (m, l)
+  float* ws_acc;      // [batch][partials][heads][head_dim + rank]
+};
+
+// Returns false if (dtype, head_dim, rank, heads) is outside the compiled envelope.
+bool decode_supported(int dtype, int head_dim, int rank, int heads);
+// phase: 1 = split-K scan only, 2 = combine only, 3 = both.
+hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int phase, hipStream_t stream);
+
+struct AppendArgs {
+  int dtype, batch, heads, head_dim, rank;
+  int64_t capacity;
+  void* k_s; void* v_s; void* z_k; void* z_v;
+  const int32_t* pos;      // device [batch], or NULL: slot 0 for every sequence
+  int n_new;
+  const void* new_k_s; const void* new_v_s; const void* new_z_k; const void* new_z_v;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  int batch, heads, head_dim, rank, seq_len;
+  const void* q; const void* k_s; const void* v_s; const void* z_k; const void* z_v;
+  const void* b_k; const void* b_v;
+  float scale_log2;
+  void* out;
+};
+bool prefill_supported(int dtype, int head_dim, int rank, int heads);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace lrkv
