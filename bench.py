@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after timing, run `steps` plain device copies of this many MB (untimed), "
+                         "a known-size reference for the HBM byte counters")
     return ap.parse_args()
 
 
@@ -172,6 +175,14 @@ def main():
                      "traffic": traffic,
                      "kernel": "decode_split_kernel", "algorithmic_bytes_per_launch": scan_bytes},
     }
+
+    if args.copy_mb > 0:
+        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_reference_bytes"] = args.copy_mb << 20
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(d, out, args.cpu_seconds, as_f64)

@@ -169,22 +169,25 @@ struct ZRegs {
   uint32_t zv[8][ZVW];   // [token of the batch][words]  (G <= 8)
 };
 
-template <class S, int G>
-__device__ __forceinline__ void z_load(ZRegs<S>& zr, const unsigned char* zk_seq, const unsigned char* zv_seq,
-                                       int tb, int t1, int H, int h, int g) {
+// Load the latents of the batch whose first token (for slot 0) sits at byte
+// offset `zbase` of the sequence's latent arrays.  Lane offsets are
+// precomputed; `ztok` is the latent bytes of one token (H * r * elem).  FULL
+// batches skip the per-token bounds test.
+template <class S, int G, bool FULL>
+__device__ __forceinline__ void z_load(ZRegs<S>& zr, const unsigned char* zk_batch, const unsigned char* zv_batch,
+                                       uint32_t zk_lane, uint32_t zv_lane, uint32_t ztok, int tb, int t1, int g) {
   if constexpr (S::ZK_BYTES > 0) {
-    const int tok = tb + g;
-    if (tok < t1) {
-      load_words<S::ZK_BYTES>(zr.zk, zk_seq + (size_t(tok) * H + h) * S::ZK_BYTES);
+    if (FULL || tb + g < t1) {
+      load_words<S::ZK_BYTES>(zr.zk, zk_batch + zk_lane);
     } else {
 #pragma unroll
       for (int i = 0; i < ZRegs<S>::ZKW; ++i) zr.zk[i] = 0u;
     }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const int tj = tb + j;
-      if (tj < t1) {
-        load_words<S::ZV_BYTES>(zr.zv[j], zv_seq + (size_t(tj) * H + h) * S::ZK_BYTES + g * S::ZV_BYTES);
+      if (FULL || tb + j < t1) {
+        const unsigned char* row_j = zv_batch + j * ztok;   // uniform: scalar address arithmetic
+        load_words<S::ZV_BYTES>(zr.zv[j], row_j + zv_lane);
       } else {
 #pragma unroll
         for (int i = 0; i < ZRegs<S>::ZVW; ++i) zr.zv[j][i] = 0u;
@@ -243,8 +246,18 @@ void decode_split_kernel(DecodeKernelParams p) {
 
   const unsigned char* kseq = static_cast<const unsigned char*>(p.k_s) + size_t(b) * p.capacity * S::ROW_BYTES;
   const unsigned char* vseq = static_cast<const unsigned char*>(p.v_s) + size_t(b) * p.capacity * S::ROW_BYTES;
-  const unsigned char* zkseq = static_cast<const unsigned char*>(p.z_k) + size_t(b) * p.capacity * H * S::ZK_BYTES;
-  const unsigned char* zvseq = static_cast<const unsigned char*>(p.z_v) + size_t(b) * p.capacity * H * S::ZK_BYTES;
+  const uint32_t ztok = uint32_t(H) * S::ZK_BYTES;           // latent bytes per token
+  const unsigned char* zkseq = static_cast<const unsigned char*>(p.z_k) + size_t(b) * p.capacity * ztok;
+  const unsigned char* zvseq = static_cast<const unsigned char*>(p.z_v) + size_t(b) * p.capacity * ztok;
+
+  // Batches: slot s of the workgroup takes tokens [tb, tb+G) with
+  // tb = t0 + n*step + s*G, n = 0, 1, ...; `step` tokens per round, a power of
+  // two that divides the 64-token tile.
+  const int step = min(p.slots * G, kDecodeTile);
+  const int nb = (t1 - t0 + step - 1) / step;
+  const bool slot_in_round = slot * G < step;
+  const uint32_t zk_lane = uint32_t((slot * G + g) * H + h) * S::ZK_BYTES;
+  const uint32_t zv_lane = uint32_t(slot * G) * ztok + uint32_t(h) * S::ZK_BYTES + uint32_t(g) * S::ZV_BYTES;
 
   // ---- prologue: this lane's slice of q_h, and the absorbed query B^K_h^T q_h ----
   const int hq = active ? h : 0;
@@ -293,102 +306,113 @@ void decode_split_kernel(DecodeKernelParams p) {
   TileRegs<S> tr;
   tile_load<S>(tr, kseq + size_t(t0) * S::ROW_BYTES, vseq + size_t(t0) * S::ROW_BYTES, t1 - t0, tid);
 
-  ZRegs<S> zcur;
-  if (active && slot < S::NBT) z_load<S, G>(zcur, zkseq, zvseq, t0 + slot * G, t1, H, h, g);
+  auto fetch = [&](ZRegs<S>& zr, int n) {
+    const int tbu = t0 + n * step;
+    const int tb = tbu + slot * G;
+    if (!(active && slot_in_round && tb < t1)) return;
+    const unsigned char* zkb = zkseq + size_t(tbu) * ztok;
+    const unsigned char* zvb = zvseq + size_t(tbu) * ztok;
+    if (tb + G <= t1) z_load<S, G, true>(zr, zkb, zvb, zk_lane, zv_lane, ztok, tb, t1, g);
+    else z_load<S, G, false>(zr, zkb, zvb, zk_lane, zv_lane, ztok, tb, t1, g);
+  };
 
-  for (int ts = t0; ts < t1; ts += kDecodeTile) {
-    __syncthreads();                                         // previous tile fully consumed
-    tile_store<S, E>(tr, s_k, s_v, tid);
-    __syncthreads();
-    const int tn = ts + kDecodeTile;
-    if (tn < t1) tile_load<S>(tr, kseq + size_t(tn) * S::ROW_BYTES, vseq + size_t(tn) * S::ROW_BYTES, t1 - tn, tid);
+  // One batch: logits of tokens [tb, tb+G), online softmax, aggregation.
+  auto process = [&](const ZRegs<S>& zc, int n) {
+    const int tbu = t0 + n * step;
+    const int off = tbu - t0;
+    if ((off & (kDecodeTile - 1)) == 0) {                    // first batch of a tile: stage it
+      __syncthreads();                                       // previous tile fully consumed
+      tile_store<S, E>(tr, s_k, s_v, tid);
+      __syncthreads();
+      const int tn = tbu + kDecodeTile;
+      if (tn < t1) tile_load<S>(tr, kseq + size_t(tn) * S::ROW_BYTES, vseq + size_t(tn) * S::ROW_BYTES, t1 - tn, tid);
+    }
+    const int tb = tbu + slot * G;
+    if (!(active && slot_in_round && tb < t1)) return;
+    const int brow = (off & (kDecodeTile - 1)) + slot * G;   // first tile row of this batch
 
-    if (active) {
-      for (int bi = slot; bi < S::NBT; bi += p.slots) {
-        const int tb = ts + bi * G;
-        if (tb >= t1) break;
-        // prefetch the latents of this slot's next batch
-        ZRegs<S> znext;
-        int nbi = bi + p.slots, nts = ts;
-        if (nbi >= S::NBT) { nbi = slot; nts = ts + kDecodeTile; }
-        const int ntb = nts + nbi * G;
-        if (ntb < t1) z_load<S, G>(znext, zkseq, zvseq, ntb, t1, H, h, g);
-
-        // -- logits (Eq. (6)): shared path by slices + reduce-scatter, then the latent path --
-        float part[G];
+    // -- logits (Eq. (6)): shared path by slices + reduce-scatter, then the latent path --
+    float part[G];
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-          uint32_t kw[S::SLICE_BYTES / 4];
-          load_words<S::SLICE_BYTES>(kw, s_k + (bi * G + (i ^ g)) * S::KS_STRIDE + g * S::SLICE_BYTES);
-          float a = 0.f;
+    for (int i = 0; i < G; ++i) {
+      uint32_t kw[S::SLICE_BYTES / 4];
+      load_words<S::SLICE_BYTES>(kw, s_k + (brow + (i ^ g)) * S::KS_STRIDE + g * S::SLICE_BYTES);
+      float a = 0.f;
 #pragma unroll
-          for (int j = 0; j < S::DPL / 2; ++j) a = E::dot2(a, qs[j], pair_at<E>(kw, j));
-          part[i] = a;
-        }
-        xor_reduce_scatter<G>(part);
-        float sz = 0.f;
-        if constexpr (R > 0) {
+      for (int j = 0; j < S::DPL / 2; ++j) a = E::dot2(a, qs[j], pair_at<E>(kw, j));
+      part[i] = a;
+    }
+    xor_reduce_scatter<G>(part);
+    float sz = 0.f;
+    if constexpr (R > 0) {
 #pragma unroll
-          for (int i = 0; i < S::RP; ++i) {
-            const Pair zp = pair_at<E>(zcur.zk, i);
-            sz = E::dot2(sz, qt_hi[i], zp);
-            if constexpr (S::SPLIT_QT) sz = E::dot2(sz, qt_lo[i], zp);
-          }
-        }
-        const bool tok_ok = (tb + g) < t1;
-        const float s = tok_ok ? (part[0] + sz) * p.scale_log2 : -INFINITY;
-
-        // -- online softmax over the batch --
-        const float m_new = fmaxf(m, group_max<G>(s));      // finite: token tb is valid
-        const float alpha = fast_exp2(m - m_new);
-        const float pe = fast_exp2(s - m_new);
-        m = m_new;
-        // pair up the weights of tokens (2k, 2k+1); both lanes of a pair hold it
-        const float pnb = dpp_mov<kDppSwap1>(pe);
-        const bool even = (g & 1) == 0;
-        const Pair pp = even ? E::make_pair(pe, pnb) : E::make_pair(pnb, pe);
-        const float p_own = even ? E::lo(pp) : E::hi(pp);   // the weight as it enters the sums
-        l = l * alpha + p_own;
-#pragma unroll
-        for (int i = 0; i < S::DPL; ++i) acc_s[i] *= alpha;
-#pragma unroll
-        for (int i = 0; i < S::RPL; ++i) acc_z[i] *= alpha;
-
-        // -- aggregation (Eq. (7)): shared values and value latents --
-        auto fold = [&](auto kc) {
-          constexpr int k = decltype(kc)::value;
-          Pair pk;
-          if constexpr (S::PB == 4) {
-            pk = __builtin_bit_cast(Pair, group_bcast<G, 2 * k>(__builtin_bit_cast(uint32_t, pp)));
-          } else {
-            const float2 f = __builtin_bit_cast(float2, pp);
-            pk = make_float2(__uint_as_float(group_bcast<G, 2 * k>(__float_as_uint(f.x))),
-                             __uint_as_float(group_bcast<G, 2 * k>(__float_as_uint(f.y))));
-          }
-          const unsigned char* vrow = s_v + (bi * (G / 2) + k) * S::VP_STRIDE;
-          uint32_t vw[S::VSLICE_BYTES / 4];
-          if constexpr (S::CPS >= 1) {
-#pragma unroll
-            for (int c = 0; c < S::CPS; ++c)
-              load_words<16>(vw + 4 * c, vrow + S::vchunk(g * S::CPS + c) * 16);
-          } else {
-            load_words<S::VSLICE_BYTES>(vw, vrow + g * S::VSLICE_BYTES);
-          }
-#pragma unroll
-          for (int i = 0; i < S::DPL; ++i) acc_s[i] = E::dot2(acc_s[i], pk, pair_at<E>(vw, i));
-          if constexpr (R > 0) {
-#pragma unroll
-            for (int i = 0; i < S::RPL; ++i)
-              acc_z[i] = E::dot2(acc_z[i], pk, E::zip(elem_at<E>(zcur.zv[2 * k], i), elem_at<E>(zcur.zv[2 * k + 1], i)));
-          }
-        };
-        [&]<int... K>(std::integer_sequence<int, K...>) {
-          (fold(std::integral_constant<int, K>{}), ...);
-        }(std::make_integer_sequence<int, G / 2>{});
-
-        if (ntb < t1) zcur = znext;
+      for (int i = 0; i < S::RP; ++i) {
+        const Pair zp = pair_at<E>(zc.zk, i);
+        sz = E::dot2(sz, qt_hi[i], zp);
+        if constexpr (S::SPLIT_QT) sz = E::dot2(sz, qt_lo[i], zp);
       }
     }
+    const float s = (tb + g < t1) ? (part[0] + sz) * p.scale_log2 : -INFINITY;
+
+    // -- online softmax over the batch; rescale only when the running max grows --
+    const float m_new = fmaxf(m, group_max<G>(s));          // finite: token tb is valid
+    if (m_new > m) {
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < S::DPL; ++i) acc_s[i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < S::RPL; ++i) acc_z[i] *= alpha;
+      m = m_new;
+    }
+    const float pe = fast_exp2(s - m);
+    // pair up the weights of tokens (2k, 2k+1); both lanes of a pair hold it
+    const float pnb = dpp_mov<kDppSwap1>(pe);
+    const bool even = (g & 1) == 0;
+    const Pair pp = even ? E::make_pair(pe, pnb) : E::make_pair(pnb, pe);
+    l += even ? E::lo(pp) : E::hi(pp);                       // the weight as it enters the sums
+
+    // -- aggregation (Eq. (7)): shared values and value latents --
+    auto fold = [&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      Pair pk;
+      if constexpr (S::PB == 4) {
+        pk = __builtin_bit_cast(Pair, group_bcast<G, 2 * k>(__builtin_bit_cast(uint32_t, pp)));
+      } else {
+        const float2 f = __builtin_bit_cast(float2, pp);
+        pk = make_float2(__uint_as_float(group_bcast<G, 2 * k>(__float_as_uint(f.x))),
+                         __uint_as_float(group_bcast<G, 2 * k>(__float_as_uint(f.y))));
+      }
+      const unsigned char* vrow = s_v + (brow / 2 + k) * S::VP_STRIDE;
+      uint32_t vw[S::VSLICE_BYTES / 4];
+      if constexpr (S::CPS >= 1) {
+#pragma unroll
+        for (int c = 0; c < S::CPS; ++c)
+          load_words<16>(vw + 4 * c, vrow + S::vchunk(g * S::CPS + c) * 16);
+      } else {
+        load_words<S::VSLICE_BYTES>(vw, vrow + g * S::VSLICE_BYTES);
+      }
+#pragma unroll
+      for (int i = 0; i < S::DPL; ++i) acc_s[i] = E::dot2(acc_s[i], pk, pair_at<E>(vw, i));
+      if constexpr (R > 0) {
+#pragma unroll
+        for (int i = 0; i < S::RPL; ++i)
+          acc_z[i] = E::dot2(acc_z[i], pk, E::zip(elem_at<E>(zc.zv[2 * k], i), elem_at<E>(zc.zv[2 * k + 1], i)));
+      }
+    };
+    [&]<int... K>(std::integer_sequence<int, K...>) {
+      (fold(std::integral_constant<int, K>{}), ...);
+    }(std::make_integer_sequence<int, G / 2>{});
+  };
+
+  // Latents double-buffered in registers: batch n+1 loads while n computes.
+  ZRegs<S> za, zb;
+  fetch(za, 0);
+  for (int n = 0; n < nb; n += 2) {
+    if (n + 1 < nb) fetch(zb, n + 1);
+    process(za, n);
+    if (n + 2 < nb) fetch(za, n + 2);
+    if (n + 1 < nb) process(zb, n + 1);
   }
 
   if (!active) return;
@@ -409,50 +433,78 @@ void decode_split_kernel(DecodeKernelParams p) {
 // Merge the partial states of one (sequence, head) and apply the residual
 // up-projection once: o = (sum_j w_j acc_s_j + B^V_h sum_j w_j acc_z_j) / L,
 // w_j = 2^(m_j - M), L = sum_j w_j l_j (Eq. (7): the latent sums are linear in
-// the weights, so B^V is applied after the merge).
+// the weights, so B^V is applied after the merge).  Threads [0, DH) own the
+// shared-value dims, threads [DH, DH+R) the latent dims; the weights are
+// computed once into LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeChunk = 256;      // partial states handled per pass
+
 template <class E, int DH, int R>
-__global__ __launch_bounds__(128) void decode_merge_kernel(const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
-                                                           const int32_t* __restrict__ seq_lens, const void* b_v,
-                                                           void* out, int heads, int partials, int slots,
-                                                           int split_tokens, int max_len) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
+    const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, const int32_t* __restrict__ seq_lens,
+    const void* b_v, void* out, int heads, int partials, int slots, int split_tokens, int max_len) {
+  static_assert(DH + R <= kMergeThreads, "one thread per merged dimension");
   using T = typename E::T;
-  constexpr int NT = 128;
+  __shared__ float s_w[kMergeChunk];
+  __shared__ float s_red[kMergeThreads / 64];
   __shared__ float s_z[R > 0 ? R : 1];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   int len = seq_lens[b];
   len = len < 0 ? 0 : (len > max_len ? max_len : len);
   T* o = static_cast<T*>(out) + (size_t(b) * heads + h) * DH;
   if (len == 0) {
-    for (int d = tid; d < DH; d += NT) o[d] = E::from_f32(0.f);
+    if (tid < DH) o[tid] = E::from_f32(0.f);
     return;
   }
   const int n = ((len + split_tokens - 1) / split_tokens) * slots;   // partials written for this sequence
-  const float* ml = ws_ml + (size_t(b) * partials * heads + h) * 2;
-  const size_t mls = size_t(heads) * 2;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + size_t(b) * partials * heads + h;
   const float* acc = ws_acc + (size_t(b) * partials * heads + h) * (DH + R);
   const size_t as = size_t(heads) * (DH + R);
-  float M = -INFINITY;
-  for (int j = 0; j < n; ++j) M = fmaxf(M, ml[j * mls]);
-  float L = 0.f;
-  for (int j = 0; j < n; ++j) L += fast_exp2(ml[j * mls] - M) * ml[j * mls + 1];   // empty partial: m = -inf
-  if constexpr (R > 0) {
-    for (int i = tid; i < R; i += NT) {
-      float z = 0.f;
-      for (int j = 0; j < n; ++j) z += fast_exp2(ml[j * mls] - M) * acc[j * as + DH + i];
-      s_z[i] = z;
+
+  // M = max_j m_j
+  float mx = -INFINITY;
+  for (int j = tid; j < n; j += kMergeThreads) mx = fmaxf(mx, ml[size_t(j) * heads].x);
+  for (int o2 = 32; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  float M = s_red[0];
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
+  __syncthreads();
+
+  float Lpart = 0.f, a = 0.f;
+  const int col = tid;                                       // merged dimension owned by this thread
+  for (int j0 = 0; j0 < n; j0 += kMergeChunk) {
+    const int cnt = min(kMergeChunk, n - j0);
+    if (tid < cnt) {
+      const float2 v = ml[size_t(j0 + tid) * heads];
+      const float w = fast_exp2(v.x - M);                    // empty partial: m = -inf -> 0
+      s_w[tid] = w;
+      Lpart += w * v.y;
+    }
+    __syncthreads();
+    if (col < DH + R) {
+      const float* src = acc + size_t(j0) * as + col;
+#pragma unroll 8
+      for (int j = 0; j < cnt; ++j) a = __builtin_fmaf(s_w[j], src[size_t(j) * as], a);
     }
     __syncthreads();
   }
-  const float invL = 1.f / L;
-  const T* bv = static_cast<const T*>(b_v) + size_t(h) * DH * R;
-  for (int d = tid; d < DH; d += NT) {
-    float a = 0.f;
-    for (int j = 0; j < n; ++j) a += fast_exp2(ml[j * mls] - M) * acc[j * as + d];
+  for (int o2 = 32; o2 > 0; o2 >>= 1) Lpart += __shfl_xor(Lpart, o2);
+  if (lane == 0) s_red[wave] = Lpart;
+  if (R > 0 && col >= DH && col < DH + R) s_z[col - DH] = a;
+  __syncthreads();
+  float L = 0.f;
+  for (int w = 0; w < kMergeThreads / 64; ++w) L += s_red[w];
+  if (col < DH) {
     if constexpr (R > 0) {
+      const T* bv = static_cast<const T*>(b_v) + (size_t(h) * DH + col) * R;
+      uint32_t bw[(R * E::kBytes) / 4];
+      load_words<R * E::kBytes>(bw, bv);
 #pragma unroll
-      for (int i = 0; i < R; ++i) a = __builtin_fmaf(E::to_f32(bv[size_t(d) * R + i]), s_z[i], a);
+      for (int i = 0; i < R; ++i) a = __builtin_fmaf(E::to_f32(elem_at<E>(bw, i)), s_z[i], a);
     }
-    o[d] = E::from_f32(a * invL);
+    o[col] = E::from_f32(a / L);
   }
 }
 
@@ -474,7 +526,7 @@ static hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, int
     if (e != hipSuccess) return e;
   }
   if (!(phase & 2)) return hipSuccess;
-  hipLaunchKernelGGL((decode_merge_kernel<E, DH, R>), dim3(pl.heads, pl.batch), dim3(128), 0, st,
+  hipLaunchKernelGGL((decode_merge_kernel<E, DH, R>), dim3(pl.heads, pl.batch), dim3(kMergeThreads), 0, st,
                      a.ws_ml, a.ws_acc, a.seq_lens, a.b_v, a.out, pl.heads, pl.partials, pl.slots,
                      pl.split_tokens, pl.max_len);
   return hipGetLastError();
