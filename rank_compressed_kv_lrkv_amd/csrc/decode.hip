@@ -21,8 +21,9 @@
 // Numerics: bf16 products accumulate in fp32 via v_dot2_f32_bf16; the
 // absorbed query B^K_h^T q_h is formed in fp32 and fed as a hi+lo pair of
 // bf16 values (error ~2^-17 relative); softmax runs in the log2 domain with
-// running max m and sum l; softmax weights enter the value sums as bf16 and
-// l sums the same rounded weights.  fp32 storage runs all-fp32 FMAs.
+// running max m and sum l (fp32 weights); the weights enter the value sums
+// rounded to bf16 (relative error <= 2^-9 each, unbiased).  fp32 storage runs
+// all-fp32 FMAs.
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -71,6 +72,9 @@ struct DecodeShape {
   }
 };
 
+// Batches of latents in flight ahead of the one being computed.
+constexpr int kZDepth = 1;
+
 struct DecodeKernelParams {
   const void* k_s; const void* v_s; const void* z_k; const void* z_v;
   const int32_t* seq_lens;
@@ -87,50 +91,51 @@ struct DecodeKernelParams {
 // are zero (never read from memory).
 template <class S>
 struct TileRegs {
-  uint4 k[S::K_PER_LANE];
-  uint4 va[S::V_PER_LANE];
-  uint4 vb[S::V_PER_LANE];
+  u32x4 k[S::K_PER_LANE];
+  u32x4 va[S::V_PER_LANE];
+  u32x4 vb[S::V_PER_LANE];
 };
 
+// Stage the 64-token tile starting at token `base` into registers.  Rows past
+// the split's last token `last` re-read row `last` (valid, finite data whose
+// logit is masked and whose weight is zero), so every load is unconditional.
 template <class S>
-__device__ __forceinline__ void tile_load(TileRegs<S>& tr, const unsigned char* kbase,
-                                          const unsigned char* vbase, int nvalid, int tid) {
+__device__ __forceinline__ void tile_load(TileRegs<S>& tr, const unsigned char* kseq, const unsigned char* vseq,
+                                          int base, int last, int tid) {
+  const unsigned char* kbase = kseq + size_t(base) * S::ROW_BYTES;
+  const unsigned char* vbase = vseq + size_t(base) * S::ROW_BYTES;
+  const int lim = last - base;
 #pragma unroll
   for (int i = 0; i < S::K_PER_LANE; ++i) {
     const int c = tid + i * kDecodeThreads;
-    const int row = c / S::ROW_CH;
-    tr.k[i] = make_uint4(0, 0, 0, 0);
-    if (c < S::KV_CH && row < nvalid) tr.k[i] = *reinterpret_cast<const uint4*>(kbase + size_t(c) * 16);
+    if (c < S::KV_CH) {
+      const int row = min(c / S::ROW_CH, lim), ch = c % S::ROW_CH;
+      tr.k[i] = *reinterpret_cast<const u32x4*>(kbase + row * S::ROW_BYTES + ch * 16);
+    }
   }
 #pragma unroll
   for (int i = 0; i < S::V_PER_LANE; ++i) {
     const int it = tid + i * kDecodeThreads;
-    const int pr = it / S::ROW_CH, ch = it % S::ROW_CH;
-    const int r0 = 2 * pr;
-    tr.va[i] = make_uint4(0, 0, 0, 0);
-    tr.vb[i] = make_uint4(0, 0, 0, 0);
-    if (it < S::VPAIR_ITEMS && r0 < nvalid)
-      tr.va[i] = *reinterpret_cast<const uint4*>(vbase + size_t(r0) * S::ROW_BYTES + ch * 16);
-    if (it < S::VPAIR_ITEMS && r0 + 1 < nvalid)
-      tr.vb[i] = *reinterpret_cast<const uint4*>(vbase + size_t(r0 + 1) * S::ROW_BYTES + ch * 16);
+    if (it < S::VPAIR_ITEMS) {
+      const int pr = it / S::ROW_CH, ch = it % S::ROW_CH;
+      const int r0 = min(2 * pr, lim), r1 = min(2 * pr + 1, lim);
+      tr.va[i] = *reinterpret_cast<const u32x4*>(vbase + r0 * S::ROW_BYTES + ch * 16);
+      tr.vb[i] = *reinterpret_cast<const u32x4*>(vbase + r1 * S::ROW_BYTES + ch * 16);
+    }
   }
 }
 
 // Interleave two 16-byte row chunks element-wise into 32 bytes of pairs.
 template <class E>
-__device__ __forceinline__ void zip16(const uint4& a, const uint4& b, uint4& o0, uint4& o1) {
+__device__ __forceinline__ void zip16(const u32x4& a, const u32x4& b, u32x4& o0, u32x4& o1) {
   if constexpr (E::kBytes == 2) {
-    auto z = [](uint32_t x, uint32_t y, uint32_t& lo, uint32_t& hi) {
-      lo = __builtin_amdgcn_perm(y, x, 0x05040100u);   // (x.lo, y.lo)
-      hi = __builtin_amdgcn_perm(y, x, 0x07060302u);   // (x.hi, y.hi)
-    };
-    z(a.x, b.x, o0.x, o0.y);
-    z(a.y, b.y, o0.z, o0.w);
-    z(a.z, b.z, o1.x, o1.y);
-    z(a.w, b.w, o1.z, o1.w);
+    auto lo = [](uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); };  // (x.lo, y.lo)
+    auto hi = [](uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); };  // (x.hi, y.hi)
+    o0 = u32x4{lo(a.x, b.x), hi(a.x, b.x), lo(a.y, b.y), hi(a.y, b.y)};
+    o1 = u32x4{lo(a.z, b.z), hi(a.z, b.z), lo(a.w, b.w), hi(a.w, b.w)};
   } else {
-    o0 = make_uint4(a.x, b.x, a.y, b.y);
-    o1 = make_uint4(a.z, b.z, a.w, b.w);
+    o0 = u32x4{a.x, b.x, a.y, b.y};
+    o1 = u32x4{a.z, b.z, a.w, b.w};
   }
 }
 
@@ -141,7 +146,7 @@ __device__ __forceinline__ void tile_store(const TileRegs<S>& tr, unsigned char*
     const int c = tid + i * kDecodeThreads;
     if (c < S::KV_CH) {
       const int row = c / S::ROW_CH, ch = c % S::ROW_CH;
-      *reinterpret_cast<uint4*>(ks + row * S::KS_STRIDE + ch * 16) = tr.k[i];
+      *reinterpret_cast<u32x4*>(ks + row * S::KS_STRIDE + ch * 16) = tr.k[i];
     }
   }
 #pragma unroll
@@ -149,11 +154,11 @@ __device__ __forceinline__ void tile_store(const TileRegs<S>& tr, unsigned char*
     const int it = tid + i * kDecodeThreads;
     if (it < S::VPAIR_ITEMS) {
       const int pr = it / S::ROW_CH, ch = it % S::ROW_CH;
-      uint4 o0, o1;
+      u32x4 o0, o1;
       zip16<E>(tr.va[i], tr.vb[i], o0, o1);
       unsigned char* row = vp + pr * S::VP_STRIDE;
-      *reinterpret_cast<uint4*>(row + S::vchunk(2 * ch) * 16) = o0;
-      *reinterpret_cast<uint4*>(row + S::vchunk(2 * ch + 1) * 16) = o1;
+      *reinterpret_cast<u32x4*>(row + S::vchunk(2 * ch) * 16) = o0;
+      *reinterpret_cast<u32x4*>(row + S::vchunk(2 * ch + 1) * 16) = o1;
     }
   }
 }
@@ -169,28 +174,32 @@ struct ZRegs {
   uint32_t zv[8][ZVW];   // [token of the batch][words]  (G <= 8)
 };
 
-// Load the latents of the batch whose first token (for slot 0) sits at byte
-// offset `zbase` of the sequence's latent arrays.  Lane offsets are
-// precomputed; `ztok` is the latent bytes of one token (H * r * elem).  FULL
-// batches skip the per-token bounds test.
-template <class S, int G, bool FULL>
-__device__ __forceinline__ void z_load(ZRegs<S>& zr, const unsigned char* zk_batch, const unsigned char* zv_batch,
-                                       uint32_t zk_lane, uint32_t zv_lane, uint32_t ztok, int tb, int t1, int g) {
+// Load the latents of the batch of tokens [tb, tb+G).  A full batch (all G
+// tokens before the split end) uses a (for single-slot waves uniform) base
+// plus precomputed lane offsets; the split's last, partial batch (CLAMP)
+// clamps token indices to the last valid token, whose data is finite and
+// whose weight is zero there.  Every load is unconditional.
+template <class S, int G, bool CLAMP>
+__device__ __forceinline__ void z_load(ZRegs<S>& zr, const unsigned char* zk_seq, const unsigned char* zv_seq,
+                                       int tb, uint32_t zk_lane, uint32_t zv_lane, uint32_t ztok, int last,
+                                       int g) {
   if constexpr (S::ZK_BYTES > 0) {
-    if (FULL || tb + g < t1) {
-      load_words<S::ZK_BYTES>(zr.zk, zk_batch + zk_lane);
-    } else {
+    if constexpr (!CLAMP) {
+      const unsigned char* zkb = zk_seq + size_t(tb) * ztok;
+      const unsigned char* zvb = zv_seq + size_t(tb) * ztok;
+      load_words<S::ZK_BYTES>(zr.zk, zkb + zk_lane);
 #pragma unroll
-      for (int i = 0; i < ZRegs<S>::ZKW; ++i) zr.zk[i] = 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      if (FULL || tb + j < t1) {
-        const unsigned char* row_j = zv_batch + j * ztok;   // uniform: scalar address arithmetic
+      for (int j = 0; j < G; ++j) {
+        const unsigned char* row_j = zvb + j * ztok;
         load_words<S::ZV_BYTES>(zr.zv[j], row_j + zv_lane);
-      } else {
+      }
+    } else {
+      const int tok = min(tb + g, last);
+      load_words<S::ZK_BYTES>(zr.zk, zk_seq + size_t(tok) * ztok + (zk_lane - uint32_t(g) * ztok));
 #pragma unroll
-        for (int i = 0; i < ZRegs<S>::ZVW; ++i) zr.zv[j][i] = 0u;
+      for (int j = 0; j < G; ++j) {
+        const int tj = min(tb + j, last);
+        load_words<S::ZV_BYTES>(zr.zv[j], zv_seq + size_t(tj) * ztok + zv_lane);
       }
     }
   }
@@ -219,45 +228,35 @@ __device__ __forceinline__ void xor_reduce_scatter(float* part) {
   }
 }
 
+// Per-lane running state of one (slot, head) and the loop over a split.
+//
+// Placement.  Rounds n = 0, 1, ... cover tokens [t0 + n*step, t0 + (n+1)*step)
+// (step = min(slots*G, 64)); slot s takes the G tokens starting at
+// tb = t0 + n*step + s*G (even, so token pairs line up with the interleaved
+// value rows).  64-token tiles are staged in LDS at 64-token boundaries.  Rows
+// and latents past the split end are clamped to its last token, so no load
+// is predicated; those tokens' logits are masked.
 template <class E, int DH, int R, int G>
-__global__ __attribute__((amdgpu_flat_work_group_size(kDecodeThreads, kDecodeThreads), amdgpu_waves_per_eu(2)))
-void decode_split_kernel(DecodeKernelParams p) {
+__device__ __forceinline__ void decode_split_body(
+    const DecodeKernelParams& p, unsigned char* s_k, unsigned char* s_v, int tid, int b, int split,
+    int t0, int t1, int g, int h, int slot, bool active, float& m, float& l, float* acc_s, float* acc_z) {
   using S = DecodeShape<E, DH, R, G>;
   using T = typename S::T;
   using Pair = typename S::Pair;
-
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[kDecodeTile * S::KS_STRIDE];
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[(kDecodeTile / 2) * S::VP_STRIDE];
-
-  const int tid = threadIdx.x;
-  const int split = blockIdx.x;
-  const int b = blockIdx.y;
   const int H = p.heads;
-  const int g = tid % G;
-  const int h = (tid / G) % p.heads_pow2;
-  const int slot = tid / (G * p.heads_pow2);
-  const bool active = (h < H) && (slot < p.slots);
-
-  int len = p.seq_lens[b];
-  len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
-  const int t0 = split * p.split_tokens;
-  if (t0 >= len) return;                                   // whole workgroup: uniform exit
-  const int t1 = min(t0 + p.split_tokens, len);
-
   const unsigned char* kseq = static_cast<const unsigned char*>(p.k_s) + size_t(b) * p.capacity * S::ROW_BYTES;
   const unsigned char* vseq = static_cast<const unsigned char*>(p.v_s) + size_t(b) * p.capacity * S::ROW_BYTES;
   const uint32_t ztok = uint32_t(H) * S::ZK_BYTES;           // latent bytes per token
   const unsigned char* zkseq = static_cast<const unsigned char*>(p.z_k) + size_t(b) * p.capacity * ztok;
   const unsigned char* zvseq = static_cast<const unsigned char*>(p.z_v) + size_t(b) * p.capacity * ztok;
 
-  // Batches: slot s of the workgroup takes tokens [tb, tb+G) with
-  // tb = t0 + n*step + s*G, n = 0, 1, ...; `step` tokens per round, a power of
-  // two that divides the 64-token tile.
   const int step = min(p.slots * G, kDecodeTile);
-  const int nb = (t1 - t0 + step - 1) / step;
+  const int nb = (t1 - t0 + step - 1) / step;                 // rounds
   const bool slot_in_round = slot * G < step;
-  const uint32_t zk_lane = uint32_t((slot * G + g) * H + h) * S::ZK_BYTES;
-  const uint32_t zv_lane = uint32_t(slot * G) * ztok + uint32_t(h) * S::ZK_BYTES + uint32_t(g) * S::ZV_BYTES;
+  const int last = t1 - 1;
+  const int ntiles = (t1 - t0 + kDecodeTile - 1) / kDecodeTile;
+  const uint32_t zk_lane = uint32_t(g) * ztok + uint32_t(h) * S::ZK_BYTES;
+  const uint32_t zv_lane = uint32_t(h) * S::ZK_BYTES + uint32_t(g) * S::ZV_BYTES;
 
   // ---- prologue: this lane's slice of q_h, and the absorbed query B^K_h^T q_h ----
   const int hq = active ? h : 0;
@@ -294,42 +293,29 @@ void decode_split_kernel(DecodeKernelParams p) {
     }
   }
 
-  // ---- running state ----
-  float m = -INFINITY, l = 0.f;
-  float acc_s[S::DPL];
-  float acc_z[S::RPL > 0 ? S::RPL : 1];
-#pragma unroll
-  for (int i = 0; i < S::DPL; ++i) acc_s[i] = 0.f;
-#pragma unroll
-  for (int i = 0; i < (S::RPL > 0 ? S::RPL : 1); ++i) acc_z[i] = 0.f;
-
   TileRegs<S> tr;
-  tile_load<S>(tr, kseq + size_t(t0) * S::ROW_BYTES, vseq + size_t(t0) * S::ROW_BYTES, t1 - t0, tid);
+  tile_load<S>(tr, kseq, vseq, t0, last, tid);
 
   auto fetch = [&](ZRegs<S>& zr, int n) {
-    const int tbu = t0 + n * step;
-    const int tb = tbu + slot * G;
+    const int tb = t0 + n * step + slot * G;
     if (!(active && slot_in_round && tb < t1)) return;
-    const unsigned char* zkb = zkseq + size_t(tbu) * ztok;
-    const unsigned char* zvb = zvseq + size_t(tbu) * ztok;
-    if (tb + G <= t1) z_load<S, G, true>(zr, zkb, zvb, zk_lane, zv_lane, ztok, tb, t1, g);
-    else z_load<S, G, false>(zr, zkb, zvb, zk_lane, zv_lane, ztok, tb, t1, g);
+    if (tb + G <= t1) z_load<S, G, false>(zr, zkseq, zvseq, tb, zk_lane, zv_lane, ztok, last, g);
+    else z_load<S, G, true>(zr, zkseq, zvseq, tb, zk_lane, zv_lane, ztok, last, g);
   };
 
   // One batch: logits of tokens [tb, tb+G), online softmax, aggregation.
   auto process = [&](const ZRegs<S>& zc, int n) {
-    const int tbu = t0 + n * step;
-    const int off = tbu - t0;
-    if ((off & (kDecodeTile - 1)) == 0) {                    // first batch of a tile: stage it
+    const int off = n * step;
+    const int tile = off / kDecodeTile;
+    if ((off & (kDecodeTile - 1)) == 0) {                    // first round of a tile: stage it
       __syncthreads();                                       // previous tile fully consumed
       tile_store<S, E>(tr, s_k, s_v, tid);
       __syncthreads();
-      const int tn = tbu + kDecodeTile;
-      if (tn < t1) tile_load<S>(tr, kseq + size_t(tn) * S::ROW_BYTES, vseq + size_t(tn) * S::ROW_BYTES, t1 - tn, tid);
+      if (tile + 1 < ntiles) tile_load<S>(tr, kseq, vseq, t0 + (tile + 1) * kDecodeTile, last, tid);
     }
-    const int tb = tbu + slot * G;
+    const int tb = t0 + n * step + slot * G;
     if (!(active && slot_in_round && tb < t1)) return;
-    const int brow = (off & (kDecodeTile - 1)) + slot * G;   // first tile row of this batch
+    const int brow = (off & (kDecodeTile - 1)) + slot * G;   // first tile row of this batch (even)
 
     // -- logits (Eq. (6)): shared path by slices + reduce-scatter, then the latent path --
     float part[G];
@@ -343,16 +329,16 @@ void decode_split_kernel(DecodeKernelParams p) {
       part[i] = a;
     }
     xor_reduce_scatter<G>(part);
-    float sz = 0.f;
+    float sc = part[0];
     if constexpr (R > 0) {
 #pragma unroll
       for (int i = 0; i < S::RP; ++i) {
         const Pair zp = pair_at<E>(zc.zk, i);
-        sz = E::dot2(sz, qt_hi[i], zp);
-        if constexpr (S::SPLIT_QT) sz = E::dot2(sz, qt_lo[i], zp);
+        sc = E::dot2(sc, qt_hi[i], zp);
+        if constexpr (S::SPLIT_QT) sc = E::dot2(sc, qt_lo[i], zp);
       }
     }
-    const float s = (tb + g < t1) ? (part[0] + sz) * p.scale_log2 : -INFINITY;
+    const float s = (tb + g < t1) ? sc * p.scale_log2 : -INFINITY;
 
     // -- online softmax over the batch; rescale only when the running max grows --
     const float m_new = fmaxf(m, group_max<G>(s));          // finite: token tb is valid
@@ -366,11 +352,9 @@ void decode_split_kernel(DecodeKernelParams p) {
       m = m_new;
     }
     const float pe = fast_exp2(s - m);
-    // pair up the weights of tokens (2k, 2k+1); both lanes of a pair hold it
-    const float pnb = dpp_mov<kDppSwap1>(pe);
-    const bool even = (g & 1) == 0;
-    const Pair pp = even ? E::make_pair(pe, pnb) : E::make_pair(pnb, pe);
-    l += even ? E::lo(pp) : E::hi(pp);                       // the weight as it enters the sums
+    l += pe;
+    // weights of tokens (2k, 2k+1) as one pair, held by both lanes of the pair
+    const Pair pp = E::make_pair(dpp_mov<kDppEven>(pe), dpp_mov<kDppOdd>(pe));
 
     // -- aggregation (Eq. (7)): shared values and value latents --
     auto fold = [&](auto kc) {
@@ -383,7 +367,7 @@ void decode_split_kernel(DecodeKernelParams p) {
         pk = make_float2(__uint_as_float(group_bcast<G, 2 * k>(__float_as_uint(f.x))),
                          __uint_as_float(group_bcast<G, 2 * k>(__float_as_uint(f.y))));
       }
-      const unsigned char* vrow = s_v + (brow / 2 + k) * S::VP_STRIDE;
+      const unsigned char* vrow = s_v + ((brow >> 1) + k) * S::VP_STRIDE;
       uint32_t vw[S::VSLICE_BYTES / 4];
       if constexpr (S::CPS >= 1) {
 #pragma unroll
@@ -397,7 +381,7 @@ void decode_split_kernel(DecodeKernelParams p) {
       if constexpr (R > 0) {
 #pragma unroll
         for (int i = 0; i < S::RPL; ++i)
-          acc_z[i] = E::dot2(acc_z[i], pk, E::zip(elem_at<E>(zc.zv[2 * k], i), elem_at<E>(zc.zv[2 * k + 1], i)));
+          acc_z[i] = E::dot2(acc_z[i], pk, zip_at<E>(zc.zv[2 * k], zc.zv[2 * k + 1], i));
       }
     };
     [&]<int... K>(std::integer_sequence<int, K...>) {
@@ -405,15 +389,53 @@ void decode_split_kernel(DecodeKernelParams p) {
     }(std::make_integer_sequence<int, G / 2>{});
   };
 
-  // Latents double-buffered in registers: batch n+1 loads while n computes.
-  ZRegs<S> za, zb;
-  fetch(za, 0);
-  for (int n = 0; n < nb; n += 2) {
-    if (n + 1 < nb) fetch(zb, n + 1);
-    process(za, n);
-    if (n + 2 < nb) fetch(za, n + 2);
-    if (n + 1 < nb) process(zb, n + 1);
+  // Latents prefetched kZDepth rounds ahead through kZDepth+1 register
+  // buffers used round-robin (the loop is unrolled so each index is static).
+  constexpr int NBUF = kZDepth + 1;
+  ZRegs<S> zbuf[NBUF];
+#pragma unroll
+  for (int i = 0; i < kZDepth; ++i)
+    if (i < nb) fetch(zbuf[i], i);
+  for (int n = 0; n < nb; n += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      if (n + u + kZDepth < nb) fetch(zbuf[(u + kZDepth) % NBUF], n + u + kZDepth);
+      if (n + u < nb) process(zbuf[u], n + u);
+    }
   }
+}
+
+template <class E, int DH, int R, int G>
+__global__ __attribute__((amdgpu_flat_work_group_size(kDecodeThreads, kDecodeThreads), amdgpu_waves_per_eu(2)))
+void decode_split_kernel(DecodeKernelParams p) {
+  using S = DecodeShape<E, DH, R, G>;
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[kDecodeTile * S::KS_STRIDE];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[(kDecodeTile / 2) * S::VP_STRIDE];
+
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const int b = blockIdx.y;
+  const int H = p.heads;
+  const int g = tid % G;
+  const int h = (tid / G) % p.heads_pow2;
+  const int slot = tid / (G * p.heads_pow2);
+  const bool active = (h < H) && (slot < p.slots);
+
+  int len = p.seq_lens[b];
+  len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+  const int t0 = split * p.split_tokens;
+  if (t0 >= len) return;                                   // whole workgroup: uniform exit
+  const int t1 = min(t0 + p.split_tokens, len);
+
+  float m = -INFINITY, l = 0.f;
+  float acc_s[S::DPL];
+  float acc_z[S::RPL > 0 ? S::RPL : 1];
+#pragma unroll
+  for (int i = 0; i < S::DPL; ++i) acc_s[i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < (S::RPL > 0 ? S::RPL : 1); ++i) acc_z[i] = 0.f;
+
+  decode_split_body<E, DH, R, G>(p, s_k, s_v, tid, b, split, t0, t1, g, h, slot, active, m, l, acc_s, acc_z);
 
   if (!active) return;
   // ---- partial state of this (split, slot, head) ----

@@ -8,6 +8,8 @@ namespace lrkv {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+// Native 128-bit vector: register-resident copies of it never go through memory.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 
@@ -84,7 +86,7 @@ __device__ __forceinline__ void load_words(uint32_t* w, const void* p) {
     int o = 0;
 #pragma unroll
     for (; o + 16 <= NB; o += 16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(c + o);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(c + o);
       w[o / 4] = v.x; w[o / 4 + 1] = v.y; w[o / 4 + 2] = v.z; w[o / 4 + 3] = v.w;
     }
     if constexpr (NB % 16 >= 8) {
@@ -97,6 +99,19 @@ __device__ __forceinline__ void load_words(uint32_t* w, const void* p) {
       w[o4 / 4] = *reinterpret_cast<const uint32_t*>(c + o4);
     }
   }
+}
+
+// Pair (element i of word array a, element i of word array b), i compile-time.
+template <class E>
+__device__ __forceinline__ typename E::Pair zip_at(const uint32_t* a, const uint32_t* b, int i);
+template <>
+__device__ __forceinline__ BF16::Pair zip_at<BF16>(const uint32_t* a, const uint32_t* b, int i) {
+  return (i & 1) ? __builtin_amdgcn_perm(b[i >> 1], a[i >> 1], 0x07060302u)
+                 : __builtin_amdgcn_perm(b[i >> 1], a[i >> 1], 0x05040100u);
+}
+template <>
+__device__ __forceinline__ F32::Pair zip_at<F32>(const uint32_t* a, const uint32_t* b, int i) {
+  return make_float2(__uint_as_float(a[i]), __uint_as_float(b[i]));
 }
 
 // Byte-sized vector type for loads of NB bytes (NB in {2, 4, 8, 16}).
@@ -144,6 +159,8 @@ constexpr int kDppSwap1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kDppSwap2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
 constexpr int kDppRev4 = 0x1B;        // quad_perm [3,2,1,0]
+constexpr int kDppEven = 0xA0;        // quad_perm [0,0,2,2]: value of the even lane of each pair
+constexpr int kDppOdd = 0xF5;         // quad_perm [1,1,3,3]: value of the odd lane of each pair
 
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
