@@ -114,13 +114,8 @@ def main():
     es = 2 if d["dtype"] == "bf16" else 4
     tokens = int(np.minimum(lens_np, max_len).sum())
 
-    def scan():
-        L.lrkv_decode(cache, lens, max_len, q, b_k, b_v, split_tokens=args.split_tokens, out=out,
-                      workspace=ws, phase="partial")
-
-    def combine():
-        L.lrkv_decode(cache, lens, max_len, q, b_k, b_v, split_tokens=args.split_tokens, out=out,
-                      workspace=ws, phase="combine")
+    call = L.DecodeCall(cache, lens, max_len, q, b_k, b_v, split_tokens=args.split_tokens, out=out, workspace=ws)
+    scan, combine = call.partial, call.combine
 
     for _ in range(args.warmup):
         scan()

@@ -5,7 +5,7 @@ kernels); this package is its Python binding plus the seeded synthetic
 workload generator used by the tests and the benchmark.
 """
 from .binding import (  # noqa: F401
-    EXPORTED, LRKV_BF16, LRKV_F32, LrkvCache, LrkvError, decode_workspace, default_scale, library,
+    DecodeCall, EXPORTED, LRKV_BF16, LRKV_F32, LrkvCache, LrkvError, decode_workspace, default_scale, library,
     lrkv_append, lrkv_cache_elems_per_token, lrkv_decode, lrkv_decode_workspace_size, lrkv_prefill,
     lrkv_status_string,
 )

@@ -216,6 +216,45 @@ def lrkv_decode(cache: LrkvCache, seq_lens: torch.Tensor, max_len: int, q: torch
     return out
 
 
+class DecodeCall:
+    """A decode whose arguments are marshalled once: the three methods call
+    lrkv_decode, lrkv_decode_partial and lrkv_decode_combine with the same
+    tensors on torch's current stream at the time of each call.  The tensors
+    must stay alive and keep their shapes; this only removes the per-call
+    argument checking from loops that repeat the same decode."""
+
+    def __init__(self, cache: LrkvCache, seq_lens, max_len, q, b_k, b_v, scale=None, split_tokens=0,
+                 out=None, workspace=None):
+        self.out = out if out is not None else torch.empty_like(q)
+        self.workspace = workspace if workspace is not None else decode_workspace(cache, max_len, split_tokens)
+        # validate once through the regular path (a real call), then freeze the argument tuple
+        lrkv_decode(cache, seq_lens, max_len, q, b_k, b_v, scale, split_tokens, self.out, self.workspace,
+                    phase="partial")
+        dt = cache.dtype
+        self._keep = (cache, seq_lens, q, b_k, b_v)
+        self._args = (_dtype_code(dt), cache.batch, cache.heads, cache.head_dim, cache.rank, cache.capacity,
+                      *cache.pointers(), _ptr(seq_lens, "seq_lens", torch.int32), max_len, _ptr(q, "q", dt),
+                      _ptr(b_k, "b_k", dt), _ptr(b_v, "b_v", dt), 0.0 if scale is None else float(scale),
+                      split_tokens, _ptr(self.out, "out", dt), _ptr(self.workspace, "workspace"),
+                      self.workspace.numel())
+        lib = library()
+        self._fns = (lib.lrkv_decode, lib.lrkv_decode_partial, lib.lrkv_decode_combine)
+
+    def _call(self, i):
+        st = self._fns[i](*self._args, torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise LrkvError(st, ("lrkv_decode", "lrkv_decode_partial", "lrkv_decode_combine")[i])
+
+    def both(self):
+        self._call(0)
+
+    def partial(self):
+        self._call(1)
+
+    def combine(self):
+        self._call(2)
+
+
 def lrkv_prefill(q, k_s, v_s, z_k, z_v, b_k, b_v, scale: Optional[float] = None,
                  cache: Optional[LrkvCache] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     dt = q.dtype
