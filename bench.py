@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mid_bf16_T8k")
+    ap.add_argument("--mode", choices=("decode", "prefill"), default="decode",
+                    help="decode (the headline line) or the causal-prefill MFMA path")
+    ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -92,7 +94,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     L.library()     # fails loudly if the HIP library is missing
-    wl = DECODE_WORKLOADS[args.workload]
+    if args.mode == "prefill":
+        return bench_prefill(args)
+    wl = DECODE_WORKLOADS[args.workload or "mid_bf16_T8k"]
     t_gen = time.perf_counter()
     d = decode_inputs(wl)
     t_gen = time.perf_counter() - t_gen
@@ -181,6 +185,69 @@ def main():
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(d, out, args.cpu_seconds, as_f64)
+    print(json.dumps(rec), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(args):
+    """Causal prefill of the 4 x 4096-token workload (H=32, d_h=128, r=16):
+    a step is lrkv_prefill with the cache written (append + MFMA attention)."""
+    import torch
+    import rank_compressed_kv_lrkv_amd as L
+    from rank_compressed_kv_lrkv_amd.workloads import PREFILL_WORKLOADS, prefill_inputs
+
+    wl = PREFILL_WORKLOADS[args.workload or "prefill_bf16_L4k"]
+    d = prefill_inputs(wl)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    t = {k: dev(d[k]) for k in ("q", "k_s", "v_s", "z_k", "z_v", "b_k", "b_v")}
+    B, Lq, H, d_h, r = wl.batch, wl.seq_len, wl.heads, wl.head_dim, wl.rank
+    cache = L.LrkvCache.empty(B, H, d_h, r, Lq, dtype=torch.bfloat16)
+    out = torch.empty_like(t["q"])
+
+    def step(with_cache=True):
+        L.lrkv_prefill(t["q"], t["k_s"], t["v_s"], t["z_k"], t["z_v"], t["b_k"], t["b_v"],
+                       cache=cache if with_cache else None, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        step(with_cache=False)             # the attention kernel alone
+        b.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    pairs = B * H * Lq * (Lq + 1) // 2                       # causal (query, key) pairs
+    flops = pairs * 4 * (d_h + r) + B * H * Lq * 4 * d_h * r  # Eq. (6)-(7) contractions + absorption
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "causal prefill over the LRKV cache: TFLOP/s and MFMA utilisation",
+        "value": B * Lq / (step_ms * 1e-3),
+        "unit": "prefill tokens/s (cache written)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) queries, bases and latents; B ~ N(0, 1/r))",
+        "config": {"workload": wl.name, "batch": B, "seq_len": Lq, "heads": H, "head_dim": d_h, "rank": r},
+        "kernels_ms": {"prefill_kernel": kern_ms},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "prefill_kernel",
+                     "algorithmic_flops_per_launch": flops},
+    }
     print(json.dumps(rec), flush=True)
 
 

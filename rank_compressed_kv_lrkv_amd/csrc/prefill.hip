@@ -94,7 +94,7 @@ __device__ __forceinline__ void pf_load(PfStage<PrefillShape<DH, R>>& st, const 
   for (int i = 0; i < P::K_PER; ++i) {
     const int c = tid + i * kPfThreads;
     if (c < P::K_CHUNKS) {
-      const int t = min(kt * kPfTile + c / (DH / 8), L - 1), ch = c % (DH / 8);
+      const int t = min(kt * kPfTile + c % kPfTile, L - 1), ch = c / kPfTile;   // token fastest across lanes
       const size_t row = (size_t(b) * L + t) * DH + ch * 8;
       st.k[i] = *reinterpret_cast<const u32x4*>(p.k_s + row);
       st.v[i] = *reinterpret_cast<const u32x4*>(p.v_s + row);
@@ -105,8 +105,7 @@ __device__ __forceinline__ void pf_load(PfStage<PrefillShape<DH, R>>& st, const 
     for (int i = 0; i < P::Z_PER; ++i) {
       const int c = tid + i * kPfThreads;                 // (token, head in group, 8-dim chunk)
       if (c < P::Z_CHUNKS) {
-        const int per_tok = kPfWaves * R / 8;
-        const int t = min(kt * kPfTile + c / per_tok, L - 1), rem = c % per_tok;
+        const int t = min(kt * kPfTile + c % kPfTile, L - 1), rem = c / kPfTile;     // token fastest
         const int hh = min(hg * kPfWaves + rem / (R / 8), H - 1), ch = rem % (R / 8);
         const size_t off = ((size_t(b) * L + t) * H + hh) * R + ch * 8;
         st.zk[i] = *reinterpret_cast<const u32x4*>(p.z_k + off);
@@ -129,7 +128,7 @@ __device__ __forceinline__ void pf_store(const PfStage<PrefillShape<DH, R>>& st,
   for (int i = 0; i < P::K_PER; ++i) {
     const int c = tid + i * kPfThreads;
     if (c < P::K_CHUNKS) {
-      const int t = c / (DH / 8), ch = c % (DH / 8);
+      const int t = c % kPfTile, ch = c / kPfTile;
       *reinterpret_cast<u32x4*>(sK + t * P::K_STRIDE + ch * 16) = st.k[i];
       const int col = ((t >> 4) << 4) | kslot_pos(t & 15);
       const uint32_t w[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
@@ -144,8 +143,7 @@ __device__ __forceinline__ void pf_store(const PfStage<PrefillShape<DH, R>>& st,
     for (int i = 0; i < P::Z_PER; ++i) {
       const int c = tid + i * kPfThreads;
       if (c < P::Z_CHUNKS) {
-        const int per_tok = kPfWaves * R / 8;
-        const int t = c / per_tok, rem = c % per_tok, w = rem / (R / 8), ch = rem % (R / 8);
+        const int t = c % kPfTile, rem = c / kPfTile, w = rem / (R / 8), ch = rem % (R / 8);
         *reinterpret_cast<u32x4*>(sZK + (w * kPfTile + t) * P::ZK_STRIDE + ch * 16) = st.zk[i];
         const int col = ((t >> 4) << 4) | kslot_pos(t & 15);
         const uint32_t wv[4] = {st.zv[i].x, st.zv[i].y, st.zv[i].z, st.zv[i].w};
