@@ -36,6 +36,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 constexpr int kPfWaves = 4;                 // heads per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfTile = 32;                 // key tokens per tile, query rows per wave
+constexpr float kPfStale = 8.f;             // running-max refresh threshold (log2 units)
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -222,11 +223,12 @@ void prefill_kernel(PrefillKernelParams p) {
     const unsigned char* sVT = sZK + P::S_ZK;
     const unsigned char* sZVT = sVT + P::S_VT;
 
-    // S^T = Kaug . Qaug^T: lane (query n, half) gets tokens 8(r/4)+4half+r%4
-    f32x16_t s = {};
+    // S^T = Kaug . Qaug^T: lane (query n, half) gets tokens 8(r/4)+4half+r%4.
+    // All key operands are read from LDS first, then the MFMAs run back to back.
+    u32x4 ka[P::KCH];
 #pragma unroll
     for (int c = 0; c < DH / 16; ++c)
-      s = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(sK + n * P::K_STRIDE + (16 * c + 8 * half) * 2)), qop[c], s);
+      ka[c] = *reinterpret_cast<const u32x4*>(sK + n * P::K_STRIDE + (16 * c + 8 * half) * 2);
     if constexpr (R > 0) {
 #pragma unroll
       for (int c = 0; c < P::RK / 16; ++c) {
@@ -234,37 +236,67 @@ void prefill_kernel(PrefillKernelParams p) {
         const unsigned char* zr = sZK + (wave * kPfTile + n) * P::ZK_STRIDE + c * 32;
         const uint2 lo = *reinterpret_cast<const uint2*>(zr + half * 8);
         const uint2 hi = *reinterpret_cast<const uint2*>(zr + 16 + half * 8);
-        u32x4 a = {lo.x, lo.y, hi.x, hi.y};
-        if (16 * c + 8 >= R) a = u32x4{lo.x, lo.y, 0u, 0u};  // R = 8: dims 8..15 are padding
-        s = mfma32(as_bf16x8(a), qop[DH / 16 + c], s);
+        ka[DH / 16 + c] = (16 * c + 8 >= R) ? u32x4{lo.x, lo.y, 0u, 0u}     // R = 8: dims 8..15 are padding
+                                            : u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16_t s = {};
+#pragma unroll
+    for (int c = 0; c < P::KCH; ++c) s = mfma32(as_bf16x8(ka[c]), qop[c], s);
+    // value operands for this tile, read while the softmax runs
+    u32x4 va[P::VBLK][2];
+#pragma unroll
+    for (int f = 0; f < DH / 32; ++f)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        va[f][c] = *reinterpret_cast<const u32x4*>(sVT + (32 * f + n) * P::VT_STRIDE + (16 * c + 8 * half) * 2);
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        va[DH / 32][c] = u32x4{0u, 0u, 0u, 0u};
+        if (n < R) va[DH / 32][c] = *reinterpret_cast<const u32x4*>(sZVT + (wave * R + n) * P::VT_STRIDE + (16 * c + 8 * half) * 2);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // online softmax (log2 domain) for query q0+n; causal mask on the diagonal tile
+    // online softmax (log2 domain) for query q0+n.  Only the diagonal tile and
+    // a tile reaching past the sequence end need the mask.  The running max is
+    // refreshed only when a score exceeds it by more than kPfStale (log2
+    // units): weights then stay <= 2^kPfStale, and since the sum and the
+    // output use the same reference the result is unchanged.
     float sv[16];
     float mx = -INFINITY;
+    const bool masked = (kt == qb) || (kt * kPfTile + kPfTile > L);
+    if (masked) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tok = kt * kPfTile + 8 * (r >> 2) + 4 * half + (r & 3);
-      const bool ok = tok <= q0 + n && tok < L;
-      sv[r] = ok ? s[r] * p.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);                     // finite: token kt*32 <= q0 + n always
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
-    float ps = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        const int tok = kt * kPfTile + 8 * (r >> 2) + 4 * half + (r & 3);
+        sv[r] = (tok <= q0 + n && tok < L) ? s[r] : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sv[r] = fast_exp2(sv[r] - m);
-      ps += sv[r];
+      for (int r = 0; r < 16; ++r) {
+        sv[r] = s[r];
+        mx = fmaxf(mx, sv[r]);
+      }
     }
-    lsum = lsum * alpha + ps + __shfl_xor(ps, 32);
-    if (alpha != 1.f) {
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;   // finite: token kt*32 <= q0 + n always
+    if (mx > m + kPfStale) {
+      const float alpha = fast_exp2(m - mx);               // 0 on the first tile (m = -inf)
+      m = mx;
+      lsum *= alpha;
 #pragma unroll
       for (int f = 0; f < P::VBLK; ++f) oacc[f] *= alpha;
     }
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sv[r] = fast_exp2(__builtin_fmaf(sv[r], p.scale_log2, -m));
+      ps += sv[r];
+    }
+    lsum += ps + __shfl_xor(ps, 32);
     bf16x8_t pb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -273,19 +305,9 @@ void prefill_kernel(PrefillKernelParams p) {
 
     // O^T += Vaug^T . P^T
 #pragma unroll
-    for (int f = 0; f < DH / 32; ++f)
+    for (int f = 0; f < P::VBLK; ++f)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        oacc[f] = mfma32(as_bf16x8(*reinterpret_cast<const u32x4*>(sVT + (32 * f + n) * P::VT_STRIDE + (16 * c + 8 * half) * 2)),
-                         pb[c], oacc[f]);
-    if constexpr (R > 0) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        u32x4 a = {0u, 0u, 0u, 0u};
-        if (n < R) a = *reinterpret_cast<const u32x4*>(sZVT + (wave * R + n) * P::VT_STRIDE + (16 * c + 8 * half) * 2);
-        oacc[DH / 32] = mfma32(as_bf16x8(a), pb[c], oacc[DH / 32]);
-      }
-    }
+      for (int c = 0; c < 2; ++c) oacc[f] = mfma32(as_bf16x8(va[f][c]), pb[c], oacc[f]);
 
     if (kt < qb) pf_store<DH, R>(st, smem + ((kt + 1) & 1) * P::STAGE, tid);
     __syncthreads();
