@@ -20,8 +20,10 @@
 //   other 16 are in lane ^ 32);
 //   O^T (features x 32 queries) += Vaug^T . P^T: P^T is reused directly from
 //   the S^T accumulators as the B operand (tokens inside each 16-token chunk
-//   are taken in the order the accumulator layout provides, and the value
-//   tile is stored in LDS transposed with its token columns in that order).
+//   are taken in the order the accumulator layout provides).  Value rows sit
+//   in LDS row-major like the keys; the transposed A operand comes from LDS
+//   transpose reads (ds_read_b64_tr_b16), whose per-lane row addresses put
+//   the tokens in that same order.
 // The absorbed query Q B^K_h and the residual up-projection O_z (B^V_h)^T are
 // MFMA products too.  Softmax runs in fp32 in the log2 domain; P, the absorbed
 // query and O_z enter MFMAs rounded to bf16.
@@ -32,11 +34,13 @@ namespace lrkv {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 constexpr int kPfWaves = 4;                 // heads per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfTile = 32;                 // key tokens per tile, query rows per wave
 constexpr float kPfStale = 8.f;             // running-max refresh threshold (log2 units)
+constexpr int kVmcntZero = 0x0F70;          // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt not waited on
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -44,134 +48,172 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Position of token u (0..15) of a 16-token chunk in the MFMA k-slot order
-// that the 32x32 accumulator layout produces: lanes 0-31 carry tokens
-// {0-3, 8-11}, lanes 32-63 carry {4-7, 12-15}.
-__device__ __forceinline__ int kslot_pos(int u) { return (u & 3) | ((u >> 3) << 2) | (((u >> 2) & 1) << 3); }
+// LDS transpose read of 4 bf16.  Within each group of 16 lanes, lane 4a+c
+// receives element c of the 8-byte rows addressed by lanes 4k+a, k = 0..3
+// (element k of the result from lane 4k+a).  With lane 4k+a addressing token
+// k at features 4a..4a+3, lane 4a+c gets feature 4a+c of tokens 0..3: a
+// column of a row-major tile.
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// bytes [16i, 16i+16) after `lds` (wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+
+// LDS tiles keep rows unpadded; 16-byte chunk ch of row r sits at position
+// ch ^ pf_swz(r).  Over any 8 consecutive rows the swizzle is a bijection, so
+// 8 lanes reading the same chunk of 8 rows hit distinct banks; its bits 1-2
+// follow r & 3, so a transpose read (4 rows x 2 adjacent chunks per 16
+// lanes) also lands on 8 distinct chunk positions.
+__device__ __forceinline__ int pf_swz(int row, int chunks) {
+  return (((row & 3) << 1) | ((row >> 2) & 1)) & (chunks - 1);
+}
 
 template <int DH, int R>
 struct PrefillShape {
   static constexpr int RK = (R + 15) / 16 * 16;          // latent dims padded for the K-dim chunks
   static constexpr int KCH = DH / 16 + RK / 16;           // 16-wide chunks of the augmented key
+  static constexpr int ZCH = RK / 16 > 0 ? RK / 16 : 1;   // latent chunks (array extent)
   static constexpr int VBLK = DH / 32 + (R > 0 ? 1 : 0);  // 32-row blocks of the augmented value
-  static constexpr int K_STRIDE = DH * 2 + 16;            // LDS row of a shared key (padded)
-  static constexpr int ZK_STRIDE = (R > 0 ? R * 2 : 16) + 16;   // LDS row of one head's key latent
-  static constexpr int VT_STRIDE = kPfTile * 2 + 16;      // LDS row of the transposed value tile
-  static constexpr int S_K = kPfTile * K_STRIDE;
-  static constexpr int S_ZK = kPfWaves * kPfTile * ZK_STRIDE;
-  static constexpr int S_VT = DH * VT_STRIDE;
-  static constexpr int S_ZVT = kPfWaves * (R > 0 ? R : 1) * VT_STRIDE;
-  static constexpr int STAGE = S_K + S_ZK + S_VT + S_ZVT;
-  // 16-byte chunks staged per tile
-  static constexpr int K_CHUNKS = kPfTile * DH / 8;
-  static constexpr int Z_CHUNKS = kPfTile * kPfWaves * R / 8;
-  static constexpr int K_PER = (K_CHUNKS + kPfThreads - 1) / kPfThreads;
-  static constexpr int Z_PER = (Z_CHUNKS + kPfThreads - 1) / kPfThreads;
+  // With 0 < R < 32 row R of the latent value block is padding; a row of ones
+  // there makes the value MFMAs accumulate the softmax sum as well.
+  static constexpr bool SUM_ROW = R > 0 && R < 32;
+  static constexpr int SUM_REG = R / 2;                    // accumulator register of row R in lanes 0-31
+  // A side (the key side or the value side of one tile) in LDS: 32 shared
+  // rows of RB bytes, then 32 token rows of ZB bytes holding the latents of
+  // the workgroup's 4 heads, [token][head][rank] as in HBM.
+  static constexpr int RB = DH * 2, CR = RB / 16;
+  static constexpr int ZB = kPfWaves * R * 2, CZ = ZB / 16;
+  static constexpr int SIDE = kPfTile * (RB + ZB);
+  static constexpr int LDS = 4 * SIDE;                     // key side and value side, two of each
+  static constexpr int NR = kPfTile * CR / 64;             // 1 KB DMA transfers per side: shared rows
+  static constexpr int NZ = kPfTile * CZ / 64;             // and latents
   static_assert(DH % 32 == 0 && R <= 32 && R % 8 == 0, "prefill envelope");
+  static_assert(CR >= 4 && (R == 0 || CZ >= 4), "swizzle needs 4 chunks per row");
 };
 
 struct PrefillKernelParams {
   const uint16_t* q; const uint16_t* k_s; const uint16_t* v_s; const uint16_t* z_k; const uint16_t* z_v;
   const uint16_t* b_k; const uint16_t* b_v;
   uint16_t* out;
-  int heads, seq_len, n_qblocks;
+  int heads, seq_len, n_qblocks, n_hgroups, batch;
   float scale_log2;
 };
 
-// Registers holding one key tile on its way from HBM to LDS.
-template <class P>
-struct PfStage {
-  u32x4 k[P::K_PER], v[P::K_PER], zk[P::Z_PER > 0 ? P::Z_PER : 1], zv[P::Z_PER > 0 ? P::Z_PER : 1];
-};
-
-// Load key tile `kt` (tokens 32kt..32kt+31, clamped to the last token) of
-// sequence b for heads [4hg, 4hg+4).
+// Start the transfer of one side of key tile `kt` (tokens 32kt..32kt+31,
+// clamped to the last token) of sequence b into `side`: shared rows from
+// `rows`, latents of heads [4hg, 4hg+4) (clamped to the last head) from
+// `lat`.  Each wave issues its share of the 1 KB transfers.
 template <int DH, int R>
-__device__ __forceinline__ void pf_load(PfStage<PrefillShape<DH, R>>& st, const PrefillKernelParams& p, int b, int hg,
-                                        int kt, int tid) {
+__device__ __forceinline__ void pf_dma(unsigned char* side, const uint16_t* rows, const uint16_t* lat,
+                                       const PrefillKernelParams& p, int b, int hg, int kt, int wave, int lane) {
   using P = PrefillShape<DH, R>;
   const int L = p.seq_len, H = p.heads;
 #pragma unroll
-  for (int i = 0; i < P::K_PER; ++i) {
-    const int c = tid + i * kPfThreads;
-    if (c < P::K_CHUNKS) {
-      const int t = min(kt * kPfTile + c % kPfTile, L - 1), ch = c / kPfTile;   // token fastest across lanes
-      const size_t row = (size_t(b) * L + t) * DH + ch * 8;
-      st.k[i] = *reinterpret_cast<const u32x4*>(p.k_s + row);
-      st.v[i] = *reinterpret_cast<const u32x4*>(p.v_s + row);
+  for (int i = 0; i < (P::NR + kPfWaves - 1) / kPfWaves; ++i) {
+    const int j = wave + i * kPfWaves;
+    if (j < P::NR) {
+      const int q = j * 64 + lane, row = q / P::CR, pos = q % P::CR;
+      const int t = min(kt * kPfTile + row, L - 1);
+      dma16(rows + (size_t(b) * L + t) * DH + (pos ^ pf_swz(row, P::CR)) * 8, side + j * 1024);
     }
   }
   if constexpr (R > 0) {
+    unsigned char* zs = side + kPfTile * P::RB;
 #pragma unroll
-    for (int i = 0; i < P::Z_PER; ++i) {
-      const int c = tid + i * kPfThreads;                 // (token, head in group, 8-dim chunk)
-      if (c < P::Z_CHUNKS) {
-        const int t = min(kt * kPfTile + c % kPfTile, L - 1), rem = c / kPfTile;     // token fastest
-        const int hh = min(hg * kPfWaves + rem / (R / 8), H - 1), ch = rem % (R / 8);
-        const size_t off = ((size_t(b) * L + t) * H + hh) * R + ch * 8;
-        st.zk[i] = *reinterpret_cast<const u32x4*>(p.z_k + off);
-        st.zv[i] = *reinterpret_cast<const u32x4*>(p.z_v + off);
+    for (int i = 0; i < (P::NZ + kPfWaves - 1) / kPfWaves; ++i) {
+      const int j = wave + i * kPfWaves;
+      if (j < P::NZ) {
+        const int q = j * 64 + lane, tok = q / P::CZ, pos = q % P::CZ;
+        const int ch = pos ^ pf_swz(tok, P::CZ);            // chunk of the 4 heads' latents of token tok
+        const int t = min(kt * kPfTile + tok, L - 1);
+        const int hh = min(hg * kPfWaves + ch / (R / 8), H - 1);
+        dma16(lat + ((size_t(b) * L + t) * H + hh) * R + (ch % (R / 8)) * 8, zs + j * 1024);
       }
     }
   }
 }
 
-// Write a staged tile to LDS: keys row-major, values transposed (feature rows,
-// token columns in MFMA k-slot order).
+// S^T tile (32 tokens x 32 queries) of one head from a key side: Kaug .
+// Qaug^T; lane (query n, half) gets tokens 8(r/4)+4half+r%4.  The lane's
+// A-operand k-slots of chunk c are dims 16c+8half..16c+8half+7, one 16-byte
+// chunk of token row n (koff[c] / zoff[c] hold its swizzled offsets).
 template <int DH, int R>
-__device__ __forceinline__ void pf_store(const PfStage<PrefillShape<DH, R>>& st, unsigned char* buf, int tid) {
+__device__ __forceinline__ f32x16_t pf_scores(const unsigned char* side, const bf16x8_t (&qop)[PrefillShape<DH, R>::KCH],
+                                              const int (&koff)[DH / 16], const int (&zoff)[PrefillShape<DH, R>::ZCH],
+                                              int half) {
   using P = PrefillShape<DH, R>;
-  unsigned char* sK = buf;
-  unsigned char* sZK = buf + P::S_K;
-  unsigned char* sVT = sZK + P::S_ZK;
-  unsigned char* sZVT = sVT + P::S_VT;
+  u32x4 ka[P::KCH];
 #pragma unroll
-  for (int i = 0; i < P::K_PER; ++i) {
-    const int c = tid + i * kPfThreads;
-    if (c < P::K_CHUNKS) {
-      const int t = c % kPfTile, ch = c / kPfTile;
-      *reinterpret_cast<u32x4*>(sK + t * P::K_STRIDE + ch * 16) = st.k[i];
-      const int col = ((t >> 4) << 4) | kslot_pos(t & 15);
-      const uint32_t w[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(sVT + (ch * 8 + e) * P::VT_STRIDE + col * 2) =
-            uint16_t((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu));
-    }
-  }
+  for (int c = 0; c < DH / 16; ++c) ka[c] = *reinterpret_cast<const u32x4*>(side + koff[c]);
   if constexpr (R > 0) {
 #pragma unroll
-    for (int i = 0; i < P::Z_PER; ++i) {
-      const int c = tid + i * kPfThreads;
-      if (c < P::Z_CHUNKS) {
-        const int t = c % kPfTile, rem = c / kPfTile, w = rem / (R / 8), ch = rem % (R / 8);
-        *reinterpret_cast<u32x4*>(sZK + (w * kPfTile + t) * P::ZK_STRIDE + ch * 16) = st.zk[i];
-        const int col = ((t >> 4) << 4) | kslot_pos(t & 15);
-        const uint32_t wv[4] = {st.zv[i].x, st.zv[i].y, st.zv[i].z, st.zv[i].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint16_t*>(sZVT + ((w * R) + ch * 8 + e) * P::VT_STRIDE + col * 2) =
-              uint16_t((e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu));
-      }
+    for (int c = 0; c < P::RK / 16; ++c) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(side + zoff[c]);
+      ka[DH / 16 + c] = (R == 8 && half) ? u32x4{0u, 0u, 0u, 0u} : v;   // R = 8: dims 8..15 are padding
     }
   }
+  f32x16_t s = {};
+#pragma unroll
+  for (int c = 0; c < P::KCH; ++c) s = mfma32(as_bf16x8(ka[c]), qop[c], s);
+  return s;
 }
 
 template <int DH, int R>
 __global__ __attribute__((amdgpu_flat_work_group_size(kPfThreads, kPfThreads), amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillKernelParams p) {
   using P = PrefillShape<DH, R>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, half = lane >> 5;
-  const int qb = p.n_qblocks - 1 - int(blockIdx.x);      // heaviest query blocks first
-  const int hg = blockIdx.y, b = blockIdx.z;
+  // 1-D grid, heaviest query blocks first over the whole launch (block qb
+  // scans qb+1 key tiles), batch fastest so that consecutive blocks, which
+  // the dispatcher spreads round-robin over the XCDs, keep one sequence per
+  // XCD when the batch divides 8.
+  const int per_level = p.n_hgroups * p.batch;
+  const int qb = p.n_qblocks - 1 - int(blockIdx.x) / per_level;
+  const int rem = int(blockIdx.x) % per_level;
+  const int b = rem % p.batch, hg = rem / p.batch;
   const int H = p.heads, L = p.seq_len;
   const int h = hg * kPfWaves + wave;
   const bool head_ok = h < H;
   const int hh = head_ok ? h : H - 1;
   const int q0 = qb * kPfTile;
   const int qrow = min(q0 + n, L - 1);
+
+  // Per-lane LDS offsets inside a side (loop-invariant).
+  int koff[DH / 16], zoff[P::ZCH];
+#pragma unroll
+  for (int c = 0; c < DH / 16; ++c) koff[c] = n * P::RB + ((2 * c + half) ^ pf_swz(n, P::CR)) * 16;
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int c = 0; c < P::RK / 16; ++c) {
+      const int ch = wave * (R / 8) + (R == 8 ? 0 : 2 * c + half);
+      zoff[c] = kPfTile * P::RB + n * P::ZB + (ch ^ pf_swz(n, P::CZ)) * 16;
+    }
+  }
+  // Transpose reads of a 16-token value chunk: this lane addresses token
+  // 4*half + k (k = lane bits 2-3) at features 16*(lane bit 4) + 4*(lane
+  // bits 0-1) of each 32-feature block; rows +8 give the second read.
+  const int tr_tok = 4 * half + ((lane >> 2) & 3);
+  int voff[DH / 32];
+#pragma unroll
+  for (int f = 0; f < DH / 32; ++f) {
+    const int ch = 4 * f + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    voff[f] = tr_tok * P::RB + (ch ^ pf_swz(tr_tok, P::CR)) * 16 + 8 * (lane & 1);
+  }
+  int zvoff = 0;
+  if constexpr (R > 0) {
+    int feat = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    feat = feat < R ? feat : 0;                            // latent dims >= R: any valid row, zeroed below
+    const int byte = wave * R * 2 + feat * 2;
+    zvoff = kPfTile * P::RB + tr_tok * P::ZB + ((byte / 16) ^ pf_swz(tr_tok, P::CZ)) * 16 + byte % 16;
+  }
 
   // ---- query rows (B operands, K-dim = features): lane (query n, half) ----
   bf16x8_t qop[P::KCH];
@@ -189,19 +231,23 @@ void prefill_kernel(PrefillKernelParams p) {
       bf16x8_t a;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint16_t v = n < R ? bk[size_t(16 * c + 8 * half + i) * R + n] : uint16_t(0);
-        a[i] = __builtin_bit_cast(__bf16, v);
+        const uint16_t v = bk[size_t(16 * c + 8 * half + i) * R + (n < R ? n : 0)];
+        a[i] = __builtin_bit_cast(__bf16, n < R ? v : uint16_t(0));
       }
       qt = mfma32(a, qop[c], qt);
     }
-    // accumulator rows 8(r/4)+4half+r%4 are the latent dims this lane feeds as
-    // k-slots of the latent chunks (same order as the key latents in LDS)
+    // The accumulator gives lane half the latent dims 16c + {4half..4half+3,
+    // 8+4half..8+4half+3}; the key latents are read as dims 16c+8half..+7, so
+    // the halves trade dims 8-11 (half 0) for 4-7 (half 1).
 #pragma unroll
     for (int c = 0; c < P::RK / 16; ++c) {
-      bf16x8_t v;
+      uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (__bf16)qt[8 * c + i];
-      qop[DH / 16 + c] = v;
+      for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(qt[8 * c + 2 * i], qt[8 * c + 2 * i + 1]);
+      const uint32_t s0 = half ? w[0] : w[2], s1 = half ? w[1] : w[3];
+      const uint32_t r0 = uint32_t(__shfl_xor(int(s0), 32)), r1 = uint32_t(__shfl_xor(int(s1), 32));
+      if (half) { w[0] = r0; w[1] = r1; } else { w[2] = r0; w[3] = r1; }
+      qop[DH / 16 + c] = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
     }
   }
 
@@ -210,55 +256,55 @@ void prefill_kernel(PrefillKernelParams p) {
   for (int f = 0; f < P::VBLK; ++f) oacc[f] = f32x16_t{};
   float m = -INFINITY, lsum = 0.f;
 
-  PfStage<P> st;
-  pf_load<DH, R>(st, p, b, hg, 0, tid);
-  pf_store<DH, R>(st, smem, tid);
+  // Software pipeline over key tiles: the key side runs one tile ahead of the
+  // value side, so that the score MFMAs of tile kt+1 are issued before the
+  // softmax of tile kt and overlap it.  Key side of tile t in kside(t & 1),
+  // value side in vside(t & 1).  Step kt reads kside((kt+1)&1) and
+  // vside(kt&1) and refills kside(kt&1) (tile kt+2) and vside((kt+1)&1)
+  // (tile kt+1), both last read in step kt-1: one barrier per tile.
+  unsigned char* const kside0 = smem;
+  unsigned char* const vside0 = smem + 2 * P::SIDE;
+  pf_dma<DH, R>(kside0, p.k_s, p.z_k, p, b, hg, 0, wave, lane);
+  pf_dma<DH, R>(vside0, p.v_s, p.z_v, p, b, hg, 0, wave, lane);
+  if (qb >= 1) pf_dma<DH, R>(kside0 + P::SIDE, p.k_s, p.z_k, p, b, hg, 1, wave, lane);
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
+  f32x16_t s0 = pf_scores<DH, R>(kside0, qop, koff, zoff, half);
+  __syncthreads();                                         // kside(0) is refilled in step 0
 
-  for (int kt = 0; kt <= qb; ++kt) {
-    if (kt < qb) pf_load<DH, R>(st, p, b, hg, kt + 1, tid);
-    const unsigned char* buf = smem + (kt & 1) * P::STAGE;
-    const unsigned char* sK = buf;
-    const unsigned char* sZK = buf + P::S_K;
-    const unsigned char* sVT = sZK + P::S_ZK;
-    const unsigned char* sZVT = sVT + P::S_VT;
+  // One pipeline step; the two score tiles swap roles every step (the loop
+  // is unrolled by two so that no accumulator is copied).
+  auto step = [&](const int kt, const f32x16_t& s_cur, f32x16_t& s_nxt) __attribute__((always_inline)) {
+    const bool next_k = kt + 2 <= qb, next_v = kt + 1 <= qb;
+    if (next_v) s_nxt = pf_scores<DH, R>(kside0 + ((kt + 1) & 1) * P::SIDE, qop, koff, zoff, half);
 
-    // S^T = Kaug . Qaug^T: lane (query n, half) gets tokens 8(r/4)+4half+r%4.
-    // All key operands are read from LDS first, then the MFMAs run back to back.
-    u32x4 ka[P::KCH];
-#pragma unroll
-    for (int c = 0; c < DH / 16; ++c)
-      ka[c] = *reinterpret_cast<const u32x4*>(sK + n * P::K_STRIDE + (16 * c + 8 * half) * 2);
-    if constexpr (R > 0) {
-#pragma unroll
-      for (int c = 0; c < P::RK / 16; ++c) {
-        // key latent k-slots in accumulator order: lanes 0-31 dims {0-3, 8-11}, lanes 32-63 {4-7, 12-15}
-        const unsigned char* zr = sZK + (wave * kPfTile + n) * P::ZK_STRIDE + c * 32;
-        const uint2 lo = *reinterpret_cast<const uint2*>(zr + half * 8);
-        const uint2 hi = *reinterpret_cast<const uint2*>(zr + 16 + half * 8);
-        ka[DH / 16 + c] = (16 * c + 8 >= R) ? u32x4{lo.x, lo.y, 0u, 0u}     // R = 8: dims 8..15 are padding
-                                            : u32x4{lo.x, lo.y, hi.x, hi.y};
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16_t s = {};
-#pragma unroll
-    for (int c = 0; c < P::KCH; ++c) s = mfma32(as_bf16x8(ka[c]), qop[c], s);
-    // value operands for this tile, read while the softmax runs
+    // value operands of tile kt: lane (feature n, half) gets tokens
+    // {4half..4half+3, 8+4half..8+4half+3} of each 16-token chunk, the k-slot
+    // order of P^T below
+    const unsigned char* vs = vside0 + (kt & 1) * P::SIDE;
     u32x4 va[P::VBLK][2];
 #pragma unroll
     for (int f = 0; f < DH / 32; ++f)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        va[f][c] = *reinterpret_cast<const u32x4*>(sVT + (32 * f + n) * P::VT_STRIDE + (16 * c + 8 * half) * 2);
+      for (int c = 0; c < 2; ++c) {
+        const unsigned char* vp = vs + 16 * c * P::RB + voff[f];
+        const uint2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * P::RB);
+        va[f][c] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
     if constexpr (R > 0) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        va[DH / 32][c] = u32x4{0u, 0u, 0u, 0u};
-        if (n < R) va[DH / 32][c] = *reinterpret_cast<const u32x4*>(sZVT + (wave * R + n) * P::VT_STRIDE + (16 * c + 8 * half) * 2);
+        const unsigned char* zp = vs + 16 * c * P::ZB + zvoff;
+        const uint2 lo = lds_read_tr16(zp), hi = lds_read_tr16(zp + 8 * P::ZB);
+        const uint32_t pad = (P::SUM_ROW && n == R) ? 0x3F803F80u : 0u;   // bf16 1.0 pairs
+        va[DH / 32][c] = n < R ? u32x4{lo.x, lo.y, hi.x, hi.y} : u32x4{pad, pad, pad, pad};
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // Refill the buffers read in the previous step.  Issued after this step's
+    // LDS reads, which therefore never wait on the transfers; they overlap
+    // the softmax and the value MFMAs.
+    if (next_k) pf_dma<DH, R>(kside0 + (kt & 1) * P::SIDE, p.k_s, p.z_k, p, b, hg, kt + 2, wave, lane);
+    if (next_v) pf_dma<DH, R>(vside0 + ((kt + 1) & 1) * P::SIDE, p.v_s, p.z_v, p, b, hg, kt + 1, wave, lane);
 
     // online softmax (log2 domain) for query q0+n.  Only the diagonal tile and
     // a tile reaching past the sequence end need the mask.  The running max is
@@ -272,31 +318,36 @@ void prefill_kernel(PrefillKernelParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = kt * kPfTile + 8 * (r >> 2) + 4 * half + (r & 3);
-        sv[r] = (tok <= q0 + n && tok < L) ? s[r] : -INFINITY;
+        sv[r] = (tok <= q0 + n && tok < L) ? s_cur[r] : -INFINITY;
         mx = fmaxf(mx, sv[r]);
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sv[r] = s[r];
+        sv[r] = s_cur[r];
         mx = fmaxf(mx, sv[r]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;   // finite: token kt*32 <= q0 + n always
-    if (mx > m + kPfStale) {
-      const float alpha = fast_exp2(m - mx);               // 0 on the first tile (m = -inf)
-      m = mx;
+    // Lanes n and n+32 share query n and must share m, so the refresh is
+    // decided for the whole wave; the common case exchanges nothing.
+    if (__builtin_amdgcn_ballot_w64(mx * p.scale_log2 > m + kPfStale)) {
+      const float mn = fmaxf(m, fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2);  // finite: token kt*32 <= q0 + n
+      const float alpha = fast_exp2(m - mn);               // 0 on the first tile (m = -inf)
+      m = mn;
       lsum *= alpha;
 #pragma unroll
       for (int f = 0; f < P::VBLK; ++f) oacc[f] *= alpha;
     }
-    float ps = 0.f;
+    if constexpr (P::SUM_ROW) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sv[r] = fast_exp2(__builtin_fmaf(sv[r], p.scale_log2, -m));
-      ps += sv[r];
+      for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(__builtin_fmaf(sv[r], p.scale_log2, -m));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sv[r] = fast_exp2(__builtin_fmaf(sv[r], p.scale_log2, -m));
+        lsum += sv[r];                                     // this lane's 16 tokens; halves combined at the end
+      }
     }
-    lsum += ps + __shfl_xor(ps, 32);
     bf16x8_t pb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -309,11 +360,26 @@ void prefill_kernel(PrefillKernelParams p) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) oacc[f] = mfma32(as_bf16x8(va[f][c]), pb[c], oacc[f]);
 
-    if (kt < qb) pf_store<DH, R>(st, smem + ((kt + 1) & 1) * P::STAGE, tid);
+    __builtin_amdgcn_s_waitcnt(kVmcntZero);                // this wave's transfers have landed
     __syncthreads();
+  };
+  f32x16_t s1 = {};
+  for (int kt = 0;; kt += 2) {
+    step(kt, s0, s1);
+    if (kt + 1 > qb) break;
+    step(kt + 1, s1, s0);
+    if (kt + 2 > qb) break;
   }
 
   if (!head_ok) return;
+  // softmax sum of query n: from the ones row (lanes 0-31 hold it), else the two halves' partial sums
+  if constexpr (P::SUM_ROW) {
+    const float part = oacc[DH / 32][P::SUM_REG];
+    const float other = __shfl_xor(part, 32);
+    lsum = half ? other : part;
+  } else {
+    lsum += __shfl_xor(lsum, 32);
+  }
   // ---- epilogue: O_s += B^V_h . O_z^T, then divide by the softmax sum ----
   if constexpr (R > 0) {
 #pragma unroll
@@ -360,9 +426,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   kp.heads = a.heads;
   kp.seq_len = a.seq_len;
   kp.n_qblocks = (a.seq_len + kPfTile - 1) / kPfTile;
+  kp.n_hgroups = (a.heads + kPfWaves - 1) / kPfWaves;
+  kp.batch = a.batch;
   kp.scale_log2 = a.scale_log2;
-  const dim3 grid(kp.n_qblocks, (a.heads + kPfWaves - 1) / kPfWaves, a.batch);
-  const size_t lds = 2 * size_t(P::STAGE);
+  const long long blocks = (long long)kp.n_qblocks * kp.n_hgroups * a.batch;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid{static_cast<unsigned>(blocks)};
+  const size_t lds = size_t(P::LDS);
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DH, R>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   if (attr != hipSuccess) return attr;
