@@ -29,7 +29,7 @@ import numpy as np
 HBM_PEAK_GBPS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(ROOT, "profiles")
-DECODE_SRC = os.path.join(ROOT, "rank_compressed_kv_lrkv_amd", "csrc", "decode.hip")
+CSRC = os.path.join(ROOT, "rank_compressed_kv_lrkv_amd", "csrc")
 
 
 def parse():
@@ -54,19 +54,49 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(workload, split):
-    """HBM bytes per scan launch from committed rocprofv3 counter summaries,
-    if they were taken on the current kernel source for this workload."""
-    path = os.path.join(PROFILES, "decode_scan_counters.json")
+def traffic_from_profiles(counters, source, workload, split=None):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 counter
+    summary (profiles/<counters>.json: FETCH_SIZE + WRITE_SIZE per dispatch,
+    each divided by the same counter's reading for a copy of known size), if
+    it was taken on the current kernel source for this workload; else None."""
+    path = os.path.join(PROFILES, counters + ".json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256_16") != source_digest(DECODE_SRC) or rec.get("workload") != workload:
+    if rec.get("source_sha256_16") != source_digest(os.path.join(CSRC, source)) or rec.get("workload") != workload:
         return None
-    if rec.get("split_tokens") != split:
+    if split is not None and rec.get("split_tokens") != split:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def timed(stream, n, fn):
+    """Average milliseconds of `fn` (which enqueues GPU work on `stream`) over
+    n back-to-back calls, from HIP events on that stream."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def copy_reference(args, rec):
+    """Untimed plain device copies of a known size after the measurement: the
+    calibration reference for the FETCH_SIZE/WRITE_SIZE counters."""
+    if args.copy_mb <= 0:
+        return
+    import torch
+    src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    rec["copy_reference_bytes"] = args.copy_mb << 20
 
 
 def thread_count():
@@ -127,27 +157,20 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()       # the library launches on torch's current stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        scan()
-        e1.record(stream)
-        combine()
-        e2.record(stream)
-    torch.cuda.synchronize()
+    step_ms = timed(stream, args.steps, lambda: (scan(), combine()))
     wall = time.perf_counter() - t0
-    scan_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    comb_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
-    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / args.steps
+    # each kernel's average launch duration: back-to-back launches between one
+    # event pair (an event between every launch adds a few us of gap)
+    scan_ms = timed(stream, args.steps, scan)
+    comb_ms = timed(stream, args.steps, combine)
 
     cache_bytes = tokens * 2 * (d_h + H * r) * es
     scan_bytes = cache_bytes + B * H * d_h * es + H * d_h * r * es          # cache + q + B^K
     step_bytes = cache_bytes + 2 * B * H * d_h * es + 2 * H * d_h * r * es  # + out + B^V
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(wl.name, args.split_tokens)
+    traffic = traffic_from_profiles("decode_scan_counters", "decode.hip", wl.name, args.split_tokens)
 
     rec = {
         "metric": "compressed-cache decode: cache tokens/s and achieved HBM GB/s (% of peak)",
@@ -175,13 +198,7 @@ def main():
                      "kernel": "decode_split_kernel", "algorithmic_bytes_per_launch": scan_bytes},
     }
 
-    if args.copy_mb > 0:
-        src = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        rec["copy_reference_bytes"] = args.copy_mb << 20
+    copy_reference(args, rec)
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(d, out, args.cpu_seconds, as_f64)
@@ -217,20 +234,8 @@ def bench_prefill(args):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    step_ms = e0.elapsed_time(e1) / args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in ev:
-        a.record(stream)
-        step(with_cache=False)             # the attention kernel alone
-        b.record(stream)
-    torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = timed(stream, args.steps, step)
+    kern_ms = timed(stream, args.steps, lambda: step(with_cache=False))   # the attention kernel alone
 
     pairs = B * H * Lq * (Lq + 1) // 2                       # causal (query, key) pairs
     flops = pairs * 4 * (d_h + r) + B * H * Lq * 4 * d_h * r  # Eq. (6)-(7) contractions + absorption
@@ -245,9 +250,11 @@ def bench_prefill(args):
         "config": {"workload": wl.name, "batch": B, "seq_len": Lq, "heads": H, "head_dim": d_h, "rank": r},
         "kernels_ms": {"prefill_kernel": kern_ms},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "prefill_kernel",
-                     "algorithmic_flops_per_launch": flops},
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic_from_profiles("prefill_counters", "prefill.hip", wl.name),
+                     "kernel": "prefill_kernel", "algorithmic_flops_per_launch": flops},
     }
+    copy_reference(args, rec)
     print(json.dumps(rec), flush=True)
 
 
