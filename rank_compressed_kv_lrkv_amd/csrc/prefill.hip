@@ -65,12 +65,16 @@ __device__ __forceinline__ void dma16(const void* src, unsigned char* lds) {
 }
 
 // LDS tiles keep rows unpadded; 16-byte chunk ch of row r sits at position
-// ch ^ pf_swz(r).  Over any 8 consecutive rows the swizzle is a bijection, so
-// 8 lanes reading the same chunk of 8 rows hit distinct banks; its bits 1-2
-// follow r & 3, so a transpose read (4 rows x 2 adjacent chunks per 16
-// lanes) also lands on 8 distinct chunk positions.
+// ch ^ pf_swz(r).  gfx950 LDS has 64 banks of 4 bytes and serves 16-byte
+// reads 16 lanes per cycle, 8-byte and transpose reads 32 lanes per cycle.
+// With the swizzle taken as the bit-reversed low 4 bits of the row index
+// (masked to the chunks per row), every read this kernel makes is free of
+// bank conflicts: the 16-byte key and key-latent reads (16 rows, one chunk)
+// and the transpose reads of values and value latents (4 rows x 2-4 adjacent
+// chunks), for rows of 64, 128 and 256 bytes.
 __device__ __forceinline__ int pf_swz(int row, int chunks) {
-  return (((row & 3) << 1) | ((row >> 2) & 1)) & (chunks - 1);
+  const int r = row & 15;
+  return (((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3)) & (chunks - 1);
 }
 
 template <int DH, int R>
@@ -199,20 +203,29 @@ void prefill_kernel(PrefillKernelParams p) {
   }
   // Transpose reads of a 16-token value chunk: this lane addresses token
   // 4*half + k (k = lane bits 2-3) at features 16*(lane bit 4) + 4*(lane
-  // bits 0-1) of each 32-feature block; rows +8 give the second read.
+  // bits 0-1) of each 32-feature block (first read), and token + 8 (second
+  // read; its swizzle differs).  Rows +16 share the swizzle.
   const int tr_tok = 4 * half + ((lane >> 2) & 3);
-  int voff[DH / 32];
+  int voff[DH / 32][2];
 #pragma unroll
   for (int f = 0; f < DH / 32; ++f) {
     const int ch = 4 * f + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    voff[f] = tr_tok * P::RB + (ch ^ pf_swz(tr_tok, P::CR)) * 16 + 8 * (lane & 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = tr_tok + 8 * j;
+      voff[f][j] = row * P::RB + (ch ^ pf_swz(row, P::CR)) * 16 + 8 * (lane & 1);
+    }
   }
-  int zvoff = 0;
+  int zvoff[2] = {0, 0};
   if constexpr (R > 0) {
     int feat = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     feat = feat < R ? feat : 0;                            // latent dims >= R: any valid row, zeroed below
     const int byte = wave * R * 2 + feat * 2;
-    zvoff = kPfTile * P::RB + tr_tok * P::ZB + ((byte / 16) ^ pf_swz(tr_tok, P::CZ)) * 16 + byte % 16;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = tr_tok + 8 * j;
+      zvoff[j] = kPfTile * P::RB + row * P::ZB + ((byte / 16) ^ pf_swz(row, P::CZ)) * 16 + byte % 16;
+    }
   }
 
   // ---- query rows (B operands, K-dim = features): lane (query n, half) ----
@@ -287,15 +300,15 @@ void prefill_kernel(PrefillKernelParams p) {
     for (int f = 0; f < DH / 32; ++f)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const unsigned char* vp = vs + 16 * c * P::RB + voff[f];
-        const uint2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 8 * P::RB);
+        const uint2 lo = lds_read_tr16(vs + 16 * c * P::RB + voff[f][0]);
+        const uint2 hi = lds_read_tr16(vs + 16 * c * P::RB + voff[f][1]);
         va[f][c] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     if constexpr (R > 0) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const unsigned char* zp = vs + 16 * c * P::ZB + zvoff;
-        const uint2 lo = lds_read_tr16(zp), hi = lds_read_tr16(zp + 8 * P::ZB);
+        const uint2 lo = lds_read_tr16(vs + 16 * c * P::ZB + zvoff[0]);
+        const uint2 hi = lds_read_tr16(vs + 16 * c * P::ZB + zvoff[1]);
         const uint32_t pad = (P::SUM_ROW && n == R) ? 0x3F803F80u : 0u;   // bf16 1.0 pairs
         va[DH / 32][c] = n < R ? u32x4{lo.x, lo.y, hi.x, hi.y} : u32x4{pad, pad, pad, pad};
       }
