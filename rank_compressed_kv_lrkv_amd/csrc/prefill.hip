@@ -58,10 +58,17 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane i writes
-// bytes [16i, 16i+16) after `lds` (wave-uniform).
-__device__ __forceinline__ void dma16(const void* src, unsigned char* lds) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+// 16 bytes per lane from global memory straight into LDS through a buffer
+// resource: lane i reads the resource at byte voff + soff (soff uniform) and
+// writes bytes [16i, 16i+16) after `lds` (wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t res, uint32_t voff, uint32_t soff, unsigned char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (__attribute__((address_space(3))) void*)(lds), 16, int(voff),
+                                           int(soff), 0, 0);
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pf_resource(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
 }
 
 // LDS tiles keep rows unpadded; 16-byte chunk ch of row r sits at position
@@ -89,13 +96,17 @@ struct PrefillShape {
   static constexpr int SUM_REG = R / 2;                    // accumulator register of row R in lanes 0-31
   // A side (the key side or the value side of one tile) in LDS: 32 shared
   // rows of RB bytes, then 32 token rows of ZB bytes holding the latents of
-  // the workgroup's 4 heads, [token][head][rank] as in HBM.
+  // the workgroup's 4 heads, [token][head][rank] as in HBM, then 16 constant
+  // bytes (bf16 1, 0, 0, 0) that feed the ones row of the value latents.
   static constexpr int RB = DH * 2, CR = RB / 16;
   static constexpr int ZB = kPfWaves * R * 2, CZ = ZB / 16;
-  static constexpr int SIDE = kPfTile * (RB + ZB);
+  static constexpr int ONES = kPfTile * (RB + ZB);         // offset of the constant inside a side
+  static constexpr int SIDE = ONES + 16;
   static constexpr int LDS = 4 * SIDE;                     // key side and value side, two of each
   static constexpr int NR = kPfTile * CR / 64;             // 1 KB DMA transfers per side: shared rows
   static constexpr int NZ = kPfTile * CZ / 64;             // and latents
+  static constexpr int NRW = (NR + kPfWaves - 1) / kPfWaves;          // per wave
+  static constexpr int NZW = NZ > 0 ? (NZ + kPfWaves - 1) / kPfWaves : 1;
   static_assert(DH % 32 == 0 && R <= 32 && R % 8 == 0, "prefill envelope");
   static_assert(CR >= 4 && (R == 0 || CZ >= 4), "swizzle needs 4 chunks per row");
 };
@@ -108,35 +119,97 @@ struct PrefillKernelParams {
   float scale_log2;
 };
 
-// Start the transfer of one side of key tile `kt` (tokens 32kt..32kt+31,
-// clamped to the last token) of sequence b into `side`: shared rows from
-// `rows`, latents of heads [4hg, 4hg+4) (clamped to the last head) from
-// `lat`.  Each wave issues its share of the 1 KB transfers.
+// This lane's source offsets (bytes from the first row of a tile) for the
+// wave's share of one side's 1 KB transfers; the same for every tile, and for
+// the key side and the value side.  Transfer j carries LDS bytes
+// [1024j, 1024j+1024) of the side: lane i the chunk at position i of its row,
+// i.e. source chunk (position ^ swizzle).
+template <class P>
+struct PfDmaOffsets {
+  uint32_t row[P::NRW], lat[P::NZW];
+};
+
 template <int DH, int R>
-__device__ __forceinline__ void pf_dma(unsigned char* side, const uint16_t* rows, const uint16_t* lat,
-                                       const PrefillKernelParams& p, int b, int hg, int kt, int wave, int lane) {
+__device__ __forceinline__ PfDmaOffsets<PrefillShape<DH, R>> pf_dma_offsets(int H, int hg, int wave, int lane) {
+  using P = PrefillShape<DH, R>;
+  PfDmaOffsets<P> d;
+#pragma unroll
+  for (int i = 0; i < P::NRW; ++i) {
+    const int q = (wave + i * kPfWaves) * 64 + lane, row = q / P::CR, pos = q % P::CR;
+    d.row[i] = uint32_t(row * P::RB + (pos ^ pf_swz(row, P::CR)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < P::NZW; ++i) {
+    d.lat[i] = 0;
+    if constexpr (R > 0) {
+      const int q = (wave + i * kPfWaves) * 64 + lane, tok = q / P::CZ, pos = q % P::CZ;
+      const int ch = pos ^ pf_swz(tok, P::CZ);              // chunk of the 4 heads' latents of token tok
+      const int hh = min(hg * kPfWaves + ch / (R / 8), H - 1);
+      d.lat[i] = uint32_t(((tok * H + hh) * R + (ch % (R / 8)) * 8) * 2);
+    }
+  }
+  return d;
+}
+
+// Buffer resources over sequence b's part of one side's source arrays.
+struct PfSources {
+  __amdgpu_buffer_rsrc_t rows, lat;
+};
+
+template <int DH, int R>
+__device__ __forceinline__ PfSources pf_sources(const uint16_t* rows, const uint16_t* lat, const PrefillKernelParams& p,
+                                                int b) {
+  const size_t L = size_t(p.seq_len);
+  PfSources s;
+  s.rows = pf_resource(rows + size_t(b) * L * DH, uint32_t(L * DH * 2));
+  s.lat = pf_resource(lat + size_t(b) * L * p.heads * R, uint32_t(L * p.heads * (R > 0 ? R : 1) * 2));
+  return s;
+}
+
+// Start the transfer of one side of key tile `kt` (tokens 32kt..32kt+31) into
+// `side`: shared rows and the workgroup's heads' latents.  A whole tile adds
+// a uniform tile offset to each lane's fixed offset; a tile reaching past the
+// last token clamps its rows to token L-1 (their values are masked out of the
+// softmax).  Each wave issues its share of the 1 KB transfers.
+template <int DH, int R>
+__device__ __forceinline__ void pf_dma(unsigned char* side, const PfSources& src, const PfDmaOffsets<PrefillShape<DH, R>>& d,
+                                       const PrefillKernelParams& p, int hg, int kt, int wave, int lane) {
   using P = PrefillShape<DH, R>;
   const int L = p.seq_len, H = p.heads;
+  if (kt * kPfTile + kPfTile <= L) {
 #pragma unroll
-  for (int i = 0; i < (P::NR + kPfWaves - 1) / kPfWaves; ++i) {
+    for (int i = 0; i < P::NRW; ++i) {
+      const int j = wave + i * kPfWaves;
+      if (j < P::NR) dma16(src.rows, d.row[i], uint32_t(kt * kPfTile * P::RB), side + j * 1024);
+    }
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int i = 0; i < P::NZW; ++i) {
+        const int j = wave + i * kPfWaves;
+        if (j < P::NZ) dma16(src.lat, d.lat[i], uint32_t(kt * kPfTile * H * R * 2), side + kPfTile * P::RB + j * 1024);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < P::NRW; ++i) {
     const int j = wave + i * kPfWaves;
     if (j < P::NR) {
       const int q = j * 64 + lane, row = q / P::CR, pos = q % P::CR;
       const int t = min(kt * kPfTile + row, L - 1);
-      dma16(rows + (size_t(b) * L + t) * DH + (pos ^ pf_swz(row, P::CR)) * 8, side + j * 1024);
+      dma16(src.rows, uint32_t(t * P::RB + (pos ^ pf_swz(row, P::CR)) * 16), 0u, side + j * 1024);
     }
   }
   if constexpr (R > 0) {
-    unsigned char* zs = side + kPfTile * P::RB;
 #pragma unroll
-    for (int i = 0; i < (P::NZ + kPfWaves - 1) / kPfWaves; ++i) {
+    for (int i = 0; i < P::NZW; ++i) {
       const int j = wave + i * kPfWaves;
       if (j < P::NZ) {
         const int q = j * 64 + lane, tok = q / P::CZ, pos = q % P::CZ;
         const int ch = pos ^ pf_swz(tok, P::CZ);            // chunk of the 4 heads' latents of token tok
         const int t = min(kt * kPfTile + tok, L - 1);
         const int hh = min(hg * kPfWaves + ch / (R / 8), H - 1);
-        dma16(lat + ((size_t(b) * L + t) * H + hh) * R + (ch % (R / 8)) * 8, zs + j * 1024);
+        dma16(src.lat, uint32_t(((t * H + hh) * R + (ch % (R / 8)) * 8) * 2), 0u, side + kPfTile * P::RB + j * 1024);
       }
     }
   }
@@ -216,17 +289,25 @@ void prefill_kernel(PrefillKernelParams p) {
       voff[f][j] = row * P::RB + (ch ^ pf_swz(row, P::CR)) * 16 + 8 * (lane & 1);
     }
   }
-  int zvoff[2] = {0, 0};
+  // Value latents: lanes addressing dims < R read them; the lanes whose 4
+  // dims start at R read the constant (1, 0, 0, 0), which turns latent row R
+  // into a row of ones (the softmax sum); rows above R are never used, so
+  // their lanes just read some valid latent row.
+  int zvoff[2][2] = {{0, 0}, {0, 0}};
   if constexpr (R > 0) {
-    int feat = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    feat = feat < R ? feat : 0;                            // latent dims >= R: any valid row, zeroed below
-    const int byte = wave * R * 2 + feat * 2;
+    const int feat = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int byte = wave * R * 2 + (feat < R ? feat : 0) * 2;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = tr_tok + 8 * j;
-      zvoff[j] = kPfTile * P::RB + row * P::ZB + ((byte / 16) ^ pf_swz(row, P::CZ)) * 16 + byte % 16;
-    }
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = 16 * c + tr_tok + 8 * j;
+        zvoff[c][j] = (P::SUM_ROW && feat == R)
+                          ? P::ONES
+                          : kPfTile * P::RB + row * P::ZB + ((byte / 16) ^ pf_swz(row, P::CZ)) * 16 + byte % 16;
+      }
   }
+  const PfDmaOffsets<P> dma = pf_dma_offsets<DH, R>(H, hg, wave, lane);
 
   // ---- query rows (B operands, K-dim = features): lane (query n, half) ----
   bf16x8_t qop[P::KCH];
@@ -277,9 +358,11 @@ void prefill_kernel(PrefillKernelParams p) {
   // (tile kt+1), both last read in step kt-1: one barrier per tile.
   unsigned char* const kside0 = smem;
   unsigned char* const vside0 = smem + 2 * P::SIDE;
-  pf_dma<DH, R>(kside0, p.k_s, p.z_k, p, b, hg, 0, wave, lane);
-  pf_dma<DH, R>(vside0, p.v_s, p.z_v, p, b, hg, 0, wave, lane);
-  if (qb >= 1) pf_dma<DH, R>(kside0 + P::SIDE, p.k_s, p.z_k, p, b, hg, 1, wave, lane);
+  if (tid < 2) *reinterpret_cast<uint4*>(vside0 + tid * P::SIDE + P::ONES) = make_uint4(0x3F80u, 0u, 0u, 0u);
+  const PfSources ksrc = pf_sources<DH, R>(p.k_s, p.z_k, p, b), vsrc = pf_sources<DH, R>(p.v_s, p.z_v, p, b);
+  pf_dma<DH, R>(kside0, ksrc, dma, p, hg, 0, wave, lane);
+  pf_dma<DH, R>(vside0, vsrc, dma, p, hg, 0, wave, lane);
+  if (qb >= 1) pf_dma<DH, R>(kside0 + P::SIDE, ksrc, dma, p, hg, 1, wave, lane);
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
   f32x16_t s0 = pf_scores<DH, R>(kside0, qop, koff, zoff, half);
@@ -287,7 +370,7 @@ void prefill_kernel(PrefillKernelParams p) {
 
   // One pipeline step; the two score tiles swap roles every step (the loop
   // is unrolled by two so that no accumulator is copied).
-  auto step = [&](const int kt, const f32x16_t& s_cur, f32x16_t& s_nxt) __attribute__((always_inline)) {
+  auto step = [&](const int kt, f32x16_t& s_cur, f32x16_t& s_nxt) __attribute__((always_inline)) {
     const bool next_k = kt + 2 <= qb, next_v = kt + 1 <= qb;
     if (next_v) s_nxt = pf_scores<DH, R>(kside0 + ((kt + 1) & 1) * P::SIDE, qop, koff, zoff, half);
 
@@ -307,40 +390,38 @@ void prefill_kernel(PrefillKernelParams p) {
     if constexpr (R > 0) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const uint2 lo = lds_read_tr16(vs + 16 * c * P::ZB + zvoff[0]);
-        const uint2 hi = lds_read_tr16(vs + 16 * c * P::ZB + zvoff[1]);
-        const uint32_t pad = (P::SUM_ROW && n == R) ? 0x3F803F80u : 0u;   // bf16 1.0 pairs
-        va[DH / 32][c] = n < R ? u32x4{lo.x, lo.y, hi.x, hi.y} : u32x4{pad, pad, pad, pad};
+        const uint2 lo = lds_read_tr16(vs + zvoff[c][0]), hi = lds_read_tr16(vs + zvoff[c][1]);
+        va[DH / 32][c] = u32x4{lo.x, lo.y, hi.x, hi.y};
       }
     }
     // Refill the buffers read in the previous step.  Issued after this step's
     // LDS reads, which therefore never wait on the transfers; they overlap
     // the softmax and the value MFMAs.
-    if (next_k) pf_dma<DH, R>(kside0 + (kt & 1) * P::SIDE, p.k_s, p.z_k, p, b, hg, kt + 2, wave, lane);
-    if (next_v) pf_dma<DH, R>(vside0 + ((kt + 1) & 1) * P::SIDE, p.v_s, p.z_v, p, b, hg, kt + 1, wave, lane);
+    if (next_k) pf_dma<DH, R>(kside0 + (kt & 1) * P::SIDE, ksrc, dma, p, hg, kt + 2, wave, lane);
+    if (next_v) pf_dma<DH, R>(vside0 + ((kt + 1) & 1) * P::SIDE, vsrc, dma, p, hg, kt + 1, wave, lane);
 
     // online softmax (log2 domain) for query q0+n.  Only the diagonal tile and
     // a tile reaching past the sequence end need the mask.  The running max is
     // refreshed only when a score exceeds it by more than kPfStale (log2
     // units): weights then stay <= 2^kPfStale, and since the sum and the
     // output use the same reference the result is unchanged.
-    float sv[16];
-    float mx = -INFINITY;
-    const bool masked = (kt == qb) || (kt * kPfTile + kPfTile > L);
-    if (masked) {
+    // online softmax (log2 domain) for query q0+n.  Only the diagonal tile and
+    // a tile reaching past the sequence end need the mask, applied in place
+    // to the score registers (dead after this step), so both paths leave the
+    // scores where the common code expects them.  The running max is
+    // refreshed only when a score exceeds it by more than kPfStale (log2
+    // units): weights then stay <= 2^kPfStale, and since the sum and the
+    // output use the same reference the result is unchanged.
+    if ((kt == qb) || (kt * kPfTile + kPfTile > L)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = kt * kPfTile + 8 * (r >> 2) + 4 * half + (r & 3);
-        sv[r] = (tok <= q0 + n && tok < L) ? s_cur[r] : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sv[r] = s_cur[r];
-        mx = fmaxf(mx, sv[r]);
+        if (!(tok <= q0 + n && tok < L)) s_cur[r] = -INFINITY;
       }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[r]);
     // Lanes n and n+32 share query n and must share m, so the refresh is
     // decided for the whole wave; the common case exchanges nothing.
     if (__builtin_amdgcn_ballot_w64(mx * p.scale_log2 > m + kPfStale)) {
@@ -351,15 +432,11 @@ void prefill_kernel(PrefillKernelParams p) {
 #pragma unroll
       for (int f = 0; f < P::VBLK; ++f) oacc[f] *= alpha;
     }
-    if constexpr (P::SUM_ROW) {
+    float sv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] = fast_exp2(__builtin_fmaf(sv[r], p.scale_log2, -m));
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sv[r] = fast_exp2(__builtin_fmaf(sv[r], p.scale_log2, -m));
-        lsum += sv[r];                                     // this lane's 16 tokens; halves combined at the end
-      }
+    for (int r = 0; r < 16; ++r) {
+      sv[r] = fast_exp2(__builtin_fmaf(s_cur[r], p.scale_log2, -m));
+      if constexpr (!P::SUM_ROW) lsum += sv[r];            // this lane's 16 tokens; halves combined at the end
     }
     bf16x8_t pb[2];
 #pragma unroll
