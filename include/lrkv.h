@@ -118,7 +118,10 @@ lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num
  *   scale     softmax scale; <= 0 selects 1/sqrt(head_dim).
  *   split_tokens  tokens per split-K partition (0 = default; otherwise a
  *             positive multiple of 64).  The partial states of all
- *             partitions are merged by a log-sum-exp combine.
+ *             partitions are merged by a log-sum-exp combine.  A partition's
+ *             shared rows and its latents must each span less than 4 GiB
+ *             (split_tokens * max(head_dim, num_heads*rank) * elem_bytes),
+ *             else LRKV_ERR_SHAPE.
  *   workspace device scratch of at least lrkv_decode_workspace_size bytes
  *             for the same arguments; contents on entry are ignored.
  * Every query attends to all of its sequence's cached tokens (the current
@@ -167,6 +170,8 @@ lrkv_status lrkv_decode_combine(int32_t dtype, int32_t batch, int32_t num_heads,
  *   q   [batch][seq_len][num_heads][head_dim];  out same shape.
  *   k_s, v_s [batch][seq_len][head_dim];  z_k, z_v [batch][seq_len][num_heads][rank].
  * Only dtype LRKV_BF16 is supported (bf16 MFMA with fp32 accumulation).
+ * One sequence's rows and latents must each span less than 4 GiB
+ * (seq_len * max(head_dim, num_heads*rank) * 2 bytes), else LRKV_ERR_SHAPE.
  * If the four cache pointers are all non-NULL the tokens are also written,
  * bit-exactly, to cache slots [0, seq_len) of every sequence (seq_len must
  * then be <= capacity); if all four are NULL the cache is not touched. */

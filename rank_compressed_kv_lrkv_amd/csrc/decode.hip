@@ -19,11 +19,17 @@
 //   When H*G < 256 the workgroup runs several independent token streams
 //   ("slots"), each producing its own partial state.
 // Numerics: bf16 products accumulate in fp32 via v_dot2_f32_bf16; the
-// absorbed query B^K_h^T q_h is formed in fp32 and fed as a hi+lo pair of
-// bf16 values (error ~2^-17 relative); softmax runs in the log2 domain with
-// running max m and sum l (fp32 weights); the weights enter the value sums
-// rounded to bf16 (relative error <= 2^-9 each, unbiased).  fp32 storage runs
-// all-fp32 FMAs.
+// absorbed query B^K_h^T q_h is formed in fp32 and rounded once to bf16 for
+// the dot products with the bf16 latents (relative error <= 2^-9 per
+// element, the same as the stored q, k and z themselves); softmax runs in
+// the log2 domain with running max m and sum l (fp32 weights); the weights
+// enter the value sums rounded to bf16 (relative error <= 2^-9 each,
+// unbiased).  fp32 storage runs all-fp32 FMAs.
+//
+// Addressing.  Every global load goes through a buffer resource that starts
+// at the split's first token: a lane adds its fixed byte offset to a uniform
+// offset that advances per tile or per batch, so the loop does no 64-bit
+// address arithmetic.
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -49,7 +55,6 @@ struct DecodeShape {
   static constexpr int RP = R / 2;                     // latent pairs
   static constexpr int ZK_BYTES = R * ES;              // one head's key latent row
   static constexpr int ZV_BYTES = RPL * ES;            // one lane's slice of a value latent row
-  static constexpr bool SPLIT_QT = (ES == 2);          // absorbed query as bf16 hi+lo
   static constexpr int NBT = kDecodeTile / G;          // batches per tile
   static constexpr int KV_CH = kDecodeTile * ROW_CH;   // 16-byte chunks of one K (or V) tile
   static constexpr int K_PER_LANE = (KV_CH + kDecodeThreads - 1) / kDecodeThreads;
@@ -74,6 +79,10 @@ struct DecodeShape {
 
 // Batches of latents in flight ahead of the one being computed.
 constexpr int kZDepth = 1;
+// The running max is refreshed only when a logit exceeds it by more than
+// this (log2 units): weights stay <= 2^kDecStale, and the sum, the value
+// sums and the merge all use the same reference, so the result is unchanged.
+constexpr float kDecStale = 8.f;
 
 struct DecodeKernelParams {
   const void* k_s; const void* v_s; const void* z_k; const void* z_v;
@@ -96,21 +105,22 @@ struct TileRegs {
   u32x4 vb[S::V_PER_LANE];
 };
 
-// Stage the 64-token tile starting at token `base` into registers.  Rows past
-// the split's last token `last` re-read row `last` (valid, finite data whose
-// logit is masked and whose weight is zero), so every load is unconditional.
+// Stage the 64-token tile starting `rel` tokens after the split's first
+// token into registers (kres/vres start at that token).  Rows past the
+// split's last token (`lim` rows after the tile start) re-read that token's
+// row (valid, finite data whose logit is masked and whose weight is zero),
+// so every load is unconditional.
 template <class S>
-__device__ __forceinline__ void tile_load(TileRegs<S>& tr, const unsigned char* kseq, const unsigned char* vseq,
-                                          int base, int last, int tid) {
-  const unsigned char* kbase = kseq + size_t(base) * S::ROW_BYTES;
-  const unsigned char* vbase = vseq + size_t(base) * S::ROW_BYTES;
-  const int lim = last - base;
+__device__ __forceinline__ void tile_load(TileRegs<S>& tr, __amdgpu_buffer_rsrc_t kres, __amdgpu_buffer_rsrc_t vres,
+                                          int rel, int lim, int tid) {
+  const uint32_t soff = uint32_t(rel) * S::ROW_BYTES;
 #pragma unroll
   for (int i = 0; i < S::K_PER_LANE; ++i) {
     const int c = tid + i * kDecodeThreads;
     if (c < S::KV_CH) {
       const int row = min(c / S::ROW_CH, lim), ch = c % S::ROW_CH;
-      tr.k[i] = *reinterpret_cast<const u32x4*>(kbase + row * S::ROW_BYTES + ch * 16);
+      tr.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              kres, row * S::ROW_BYTES + ch * 16, int(soff), 0));
     }
   }
 #pragma unroll
@@ -119,8 +129,10 @@ __device__ __forceinline__ void tile_load(TileRegs<S>& tr, const unsigned char* 
     if (it < S::VPAIR_ITEMS) {
       const int pr = it / S::ROW_CH, ch = it % S::ROW_CH;
       const int r0 = min(2 * pr, lim), r1 = min(2 * pr + 1, lim);
-      tr.va[i] = *reinterpret_cast<const u32x4*>(vbase + r0 * S::ROW_BYTES + ch * 16);
-      tr.vb[i] = *reinterpret_cast<const u32x4*>(vbase + r1 * S::ROW_BYTES + ch * 16);
+      tr.va[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               vres, r0 * S::ROW_BYTES + ch * 16, int(soff), 0));
+      tr.vb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               vres, r1 * S::ROW_BYTES + ch * 16, int(soff), 0));
     }
   }
 }
@@ -174,32 +186,30 @@ struct ZRegs {
   uint32_t zv[8][ZVW];   // [token of the batch][words]  (G <= 8)
 };
 
-// Load the latents of the batch of tokens [tb, tb+G).  A full batch (all G
-// tokens before the split end) uses a (for single-slot waves uniform) base
-// plus precomputed lane offsets; the split's last, partial batch (CLAMP)
-// clamps token indices to the last valid token, whose data is finite and
-// whose weight is zero there.  Every load is unconditional.
+// Load the latents of the batch of tokens [tb, tb+G), tb = tb0 + slot*G,
+// through resources that start at the split's first token t0 (rel0 = tb0 -
+// t0 is uniform).  A full batch (all G tokens before the split end) adds the
+// uniform offset to the lane's fixed offsets (zk_lane: token g of the batch,
+// head h; zv_lane: head h, slice g; both include the slot's first token); the
+// split's last, partial batch (CLAMP) clamps token indices to the last valid
+// token (rel_last), whose data is finite and whose weight is zero there.
 template <class S, int G, bool CLAMP>
-__device__ __forceinline__ void z_load(ZRegs<S>& zr, const unsigned char* zk_seq, const unsigned char* zv_seq,
-                                       int tb, uint32_t zk_lane, uint32_t zv_lane, uint32_t ztok, int last,
-                                       int g) {
+__device__ __forceinline__ void z_load(ZRegs<S>& zr, __amdgpu_buffer_rsrc_t zkres, __amdgpu_buffer_rsrc_t zvres,
+                                       int rel0, int rel_tb, uint32_t zk_lane, uint32_t zv_lane, uint32_t zk_head,
+                                       uint32_t zv_head, uint32_t ztok, int rel_last, int g) {
   if constexpr (S::ZK_BYTES > 0) {
     if constexpr (!CLAMP) {
-      const unsigned char* zkb = zk_seq + size_t(tb) * ztok;
-      const unsigned char* zvb = zv_seq + size_t(tb) * ztok;
-      load_words<S::ZK_BYTES>(zr.zk, zkb + zk_lane);
+      const uint32_t soff = uint32_t(rel0) * ztok;
+      buffer_words<S::ZK_BYTES>(zr.zk, zkres, zk_lane, soff);
 #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const unsigned char* row_j = zvb + j * ztok;
-        load_words<S::ZV_BYTES>(zr.zv[j], row_j + zv_lane);
-      }
+      for (int j = 0; j < G; ++j) buffer_words<S::ZV_BYTES>(zr.zv[j], zvres, zv_lane, soff + uint32_t(j) * ztok);
     } else {
-      const int tok = min(tb + g, last);
-      load_words<S::ZK_BYTES>(zr.zk, zk_seq + size_t(tok) * ztok + (zk_lane - uint32_t(g) * ztok));
+      const int tok = min(rel_tb + g, rel_last);
+      buffer_words<S::ZK_BYTES>(zr.zk, zkres, uint32_t(tok) * ztok + zk_head, 0u);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const int tj = min(tb + j, last);
-        load_words<S::ZV_BYTES>(zr.zv[j], zv_seq + size_t(tj) * ztok + zv_lane);
+        const int tj = min(rel_tb + j, rel_last);
+        buffer_words<S::ZV_BYTES>(zr.zv[j], zvres, uint32_t(tj) * ztok + zv_head, 0u);
       }
     }
   }
@@ -244,19 +254,26 @@ __device__ __forceinline__ void decode_split_body(
   using T = typename S::T;
   using Pair = typename S::Pair;
   const int H = p.heads;
-  const unsigned char* kseq = static_cast<const unsigned char*>(p.k_s) + size_t(b) * p.capacity * S::ROW_BYTES;
-  const unsigned char* vseq = static_cast<const unsigned char*>(p.v_s) + size_t(b) * p.capacity * S::ROW_BYTES;
   const uint32_t ztok = uint32_t(H) * S::ZK_BYTES;           // latent bytes per token
-  const unsigned char* zkseq = static_cast<const unsigned char*>(p.z_k) + size_t(b) * p.capacity * ztok;
-  const unsigned char* zvseq = static_cast<const unsigned char*>(p.z_v) + size_t(b) * p.capacity * ztok;
+  // resources over the split's tokens [t0, t1) (the host keeps them < 4 GiB)
+  const size_t row0 = size_t(b) * p.capacity + size_t(t0);
+  const uint32_t ntok = uint32_t(t1 - t0);
+  const __amdgpu_buffer_rsrc_t kres =
+      buffer_resource(static_cast<const unsigned char*>(p.k_s) + row0 * S::ROW_BYTES, ntok * S::ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t vres =
+      buffer_resource(static_cast<const unsigned char*>(p.v_s) + row0 * S::ROW_BYTES, ntok * S::ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t zkres = buffer_resource(static_cast<const unsigned char*>(p.z_k) + row0 * ztok, ntok * ztok);
+  const __amdgpu_buffer_rsrc_t zvres = buffer_resource(static_cast<const unsigned char*>(p.z_v) + row0 * ztok, ntok * ztok);
 
   const int step = min(p.slots * G, kDecodeTile);
   const int nb = (t1 - t0 + step - 1) / step;                 // rounds
   const bool slot_in_round = slot * G < step;
   const int last = t1 - 1;
   const int ntiles = (t1 - t0 + kDecodeTile - 1) / kDecodeTile;
-  const uint32_t zk_lane = uint32_t(g) * ztok + uint32_t(h) * S::ZK_BYTES;
-  const uint32_t zv_lane = uint32_t(h) * S::ZK_BYTES + uint32_t(g) * S::ZV_BYTES;
+  const uint32_t zk_head = uint32_t(h) * S::ZK_BYTES;
+  const uint32_t zv_head = uint32_t(h) * S::ZK_BYTES + uint32_t(g) * S::ZV_BYTES;
+  const uint32_t zk_lane = uint32_t(slot * G + g) * ztok + zk_head;
+  const uint32_t zv_lane = uint32_t(slot * G) * ztok + zv_head;
 
   // ---- prologue: this lane's slice of q_h, and the absorbed query B^K_h^T q_h ----
   const int hq = active ? h : 0;
@@ -268,7 +285,7 @@ __device__ __forceinline__ void decode_split_body(
 #pragma unroll
     for (int i = 0; i < S::DPL / 2; ++i) qs[i] = pair_at<E>(qw, i);
   }
-  Pair qt_hi[S::RP > 0 ? S::RP : 1], qt_lo[S::RP > 0 ? S::RP : 1];
+  Pair qt[S::RP > 0 ? S::RP : 1];
   if constexpr (R > 0) {
     // lane g sums rows d in its slice of B^K_h, then the group adds up.
     float part[R];
@@ -288,19 +305,20 @@ __device__ __forceinline__ void decode_split_body(
     for (int i = 0; i < S::RP; ++i) {
       const float a = group_sum<G>(part[2 * i]);
       const float c = group_sum<G>(part[2 * i + 1]);
-      qt_hi[i] = E::make_pair(a, c);
-      if constexpr (S::SPLIT_QT) qt_lo[i] = E::make_pair(a - E::lo(qt_hi[i]), c - E::hi(qt_hi[i]));
+      qt[i] = E::make_pair(a, c);
     }
   }
 
   TileRegs<S> tr;
-  tile_load<S>(tr, kseq, vseq, t0, last, tid);
+  tile_load<S>(tr, kres, vres, 0, last - t0, tid);
 
   auto fetch = [&](ZRegs<S>& zr, int n) {
     const int tb = t0 + n * step + slot * G;
     if (!(active && slot_in_round && tb < t1)) return;
-    if (tb + G <= t1) z_load<S, G, false>(zr, zkseq, zvseq, tb, zk_lane, zv_lane, ztok, last, g);
-    else z_load<S, G, true>(zr, zkseq, zvseq, tb, zk_lane, zv_lane, ztok, last, g);
+    if (tb + G <= t1)
+      z_load<S, G, false>(zr, zkres, zvres, n * step, tb - t0, zk_lane, zv_lane, zk_head, zv_head, ztok, last - t0, g);
+    else
+      z_load<S, G, true>(zr, zkres, zvres, n * step, tb - t0, zk_lane, zv_lane, zk_head, zv_head, ztok, last - t0, g);
   };
 
   // One batch: logits of tokens [tb, tb+G), online softmax, aggregation.
@@ -311,7 +329,7 @@ __device__ __forceinline__ void decode_split_body(
       __syncthreads();                                       // previous tile fully consumed
       tile_store<S, E>(tr, s_k, s_v, tid);
       __syncthreads();
-      if (tile + 1 < ntiles) tile_load<S>(tr, kseq, vseq, t0 + (tile + 1) * kDecodeTile, last, tid);
+      if (tile + 1 < ntiles) tile_load<S>(tr, kres, vres, (tile + 1) * kDecodeTile, last - t0 - (tile + 1) * kDecodeTile, tid);
     }
     const int tb = t0 + n * step + slot * G;
     if (!(active && slot_in_round && tb < t1)) return;
@@ -333,17 +351,17 @@ __device__ __forceinline__ void decode_split_body(
     if constexpr (R > 0) {
 #pragma unroll
       for (int i = 0; i < S::RP; ++i) {
-        const Pair zp = pair_at<E>(zc.zk, i);
-        sc = E::dot2(sc, qt_hi[i], zp);
-        if constexpr (S::SPLIT_QT) sc = E::dot2(sc, qt_lo[i], zp);
+        sc = E::dot2(sc, qt[i], pair_at<E>(zc.zk, i));
       }
     }
     const float s = (tb + g < t1) ? sc * p.scale_log2 : -INFINITY;
 
-    // -- online softmax over the batch; rescale only when the running max grows --
-    const float m_new = fmaxf(m, group_max<G>(s));          // finite: token tb is valid
-    if (m_new > m) {
-      const float alpha = fast_exp2(m - m_new);
+    // -- online softmax over the batch; the running max is refreshed only when
+    //    a logit exceeds it by more than kDecStale --
+    const float gmax = group_max<G>(s);                      // finite: token tb is valid
+    if (gmax > m + kDecStale) {
+      const float m_new = gmax;
+      const float alpha = fast_exp2(m - m_new);               // 0 on the first batch (m = -inf)
       l *= alpha;
 #pragma unroll
       for (int i = 0; i < S::DPL; ++i) acc_s[i] *= alpha;

@@ -10,6 +10,8 @@
 #include "../../include/lrkv.h"
 #include "lrkv_internal.h"
 
+#include <algorithm>
+
 namespace {
 
 using lrkv::DecodePlan;
@@ -72,6 +74,11 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
     if (s > cap) s = cap < tile ? tile : cap;
     split = int(s);
   }
+  // The kernels address one split's rows and latents through 32-bit buffer
+  // offsets.
+  const int64_t es = dtype == 1 ? 2 : 4;
+  if (int64_t(split) * std::max<int64_t>(int64_t(head_dim), int64_t(heads) * rank) * es >= (int64_t(1) << 32))
+    return LRKV_ERR_SHAPE;
   pl->split_tokens = split;
   pl->n_splits = int((max_len + split - 1) / split);
   pl->partials = pl->n_splits * pl->slots;
@@ -194,6 +201,9 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
   if (st != LRKV_OK) return st;
   if (!lrkv::prefill_supported(dtype, head_dim, rank, num_heads)) return LRKV_ERR_SHAPE;
   if (seq_len < 0) return LRKV_ERR_SHAPE;
+  // one sequence's rows and latents are addressed through 32-bit buffer offsets
+  if (int64_t(seq_len) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >= (int64_t(1) << 32))
+    return LRKV_ERR_SHAPE;
   const int ncache = (k_shared != nullptr) + (v_shared != nullptr) + (z_k != nullptr) + (z_v != nullptr);
   const bool write_cache = ncache == 4;
   if (ncache != 0 && ncache != 4) return LRKV_ERR_NULL;

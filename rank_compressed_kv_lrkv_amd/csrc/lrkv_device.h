@@ -101,6 +101,40 @@ __device__ __forceinline__ void load_words(uint32_t* w, const void* p) {
   }
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3:
+// no swizzle, no format conversion).  Loads through it take a per-lane byte
+// offset plus a uniform one; offsets at or past `bytes` read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_resource(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
+}
+
+// Load NB bytes (2 or a multiple of 4) at byte voff + soff of a buffer
+// resource into 32-bit words w[0..ceil(NB/4)), using 16-, 8-, 4- and 2-byte
+// accesses; the offset must be aligned to min(NB, 16).
+template <int NB>
+__device__ __forceinline__ void buffer_words(uint32_t* w, __amdgpu_buffer_rsrc_t res, uint32_t voff, uint32_t soff) {
+  if constexpr (NB == 2) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(res, int(voff), int(soff), 0);
+    return;
+  }
+  static_assert(NB == 2 || NB % 4 == 0, "load size");
+  int o = 0;
+#pragma unroll
+  for (; o + 16 <= NB; o += 16) {
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, int(voff + o), int(soff), 0));
+    w[o / 4] = v.x; w[o / 4 + 1] = v.y; w[o / 4 + 2] = v.z; w[o / 4 + 3] = v.w;
+  }
+  if constexpr (NB % 16 >= 8) {
+    constexpr int o8 = NB / 16 * 16;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(res, int(voff + o8), int(soff), 0);
+    w[o8 / 4] = v[0]; w[o8 / 4 + 1] = v[1];
+  }
+  if constexpr (NB % 8 == 4) {
+    constexpr int o4 = NB / 8 * 8;
+    w[o4 / 4] = __builtin_amdgcn_raw_buffer_load_b32(res, int(voff + o4), int(soff), 0);
+  }
+}
+
 // Pair (element i of word array a, element i of word array b), i compile-time.
 template <class E>
 __device__ __forceinline__ typename E::Pair zip_at(const uint32_t* a, const uint32_t* b, int i);

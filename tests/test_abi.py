@@ -80,6 +80,14 @@ def test_workspace_size_rejects(kw, want):
     assert ws_size(**kw)[0] == want
 
 
+def test_workspace_size_split_offset_range():
+    # one split's latents are addressed through 32-bit offsets: 64 heads x rank 64 x 4 bytes
+    # = 16 KiB per token, so 262144-token splits (4 GiB) are rejected and 262080 accepted
+    big = dict(dtype=F32, B=1, H=64, d_h=128, r=64, cap=262144, max_len=262144)
+    assert ws_size(**big, split=262144)[0] == SHAPE
+    assert ws_size(**big, split=262080)[0] == OK
+
+
 def test_workspace_size_null_out():
     assert L.library().lrkv_decode_workspace_size(BF16, 1, 4, 64, 8, 64, 64, 0, None) == NULL
 
