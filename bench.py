@@ -3,7 +3,9 @@
 
 A step is one lrkv_decode call over the whole batch (the split-K scan, then
 the merge and B^V epilogue, enqueued together), on seeded synthetic inputs
-already resident in HBM.  Each kernel's own average duration is timed
+already resident in HBM.  Before the warmup steps the step is repeated,
+untimed, for --settle-s seconds so that the timed steps run at the GPU's
+steady clock.  Each kernel's own average duration is timed
 separately over back-to-back launches of lrkv_decode_partial and
 lrkv_decode_combine.
 The default workload is the 8K-context bf16 decode: 32 sequences x 8192
@@ -39,6 +41,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="before the warmup steps, repeat the step (untimed) for this many seconds: "
+                         "the GPU takes tens of ms of sustained work to reach its steady clock")
     ap.add_argument("--mode", choices=("decode", "prefill"), default="decode",
                     help="decode (the headline line) or the causal-prefill MFMA path")
     ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
@@ -85,6 +90,21 @@ def timed(stream, n, fn):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def settle(fn, seconds):
+    """Repeat `fn` (untimed) until `seconds` of wall clock have passed; returns
+    the number of calls.  Steps timed straight after an idle period run up to
+    ~20% slower until the GPU's clock has ramped, which takes some tens of ms
+    of sustained work."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    return n
 
 
 def copy_reference(args, rec):
@@ -153,6 +173,7 @@ def main():
     call = L.DecodeCall(cache, lens, max_len, q, b_k, b_v, split_tokens=args.split_tokens, out=out, workspace=ws)
     scan, combine = call.partial, call.combine
 
+    settled = settle(call.both, args.settle_s)
     for _ in range(args.warmup):
         call.both()
     torch.cuda.synchronize()
@@ -181,6 +202,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": args.settle_s, "steps": settled},
         "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -232,6 +254,7 @@ def bench_prefill(args):
         L.lrkv_prefill(t["q"], t["k_s"], t["v_s"], t["z_k"], t["z_v"], t["b_k"], t["b_v"],
                        cache=cache if with_cache else None, out=out)
 
+    settled = settle(step, args.settle_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -246,7 +269,8 @@ def bench_prefill(args):
         "metric": "causal prefill over the LRKV cache: TFLOP/s and MFMA utilisation",
         "value": B * Lq / (step_ms * 1e-3),
         "unit": "prefill tokens/s (cache written)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_ms,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle": {"seconds": args.settle_s, "steps": settled}, "ms_per_step": step_ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) queries, bases and latents; B ~ N(0, 1/r))",
         "config": {"workload": wl.name, "batch": B, "seq_len": Lq, "heads": H, "head_dim": d_h, "rank": r},
