@@ -120,7 +120,7 @@ __device__ __forceinline__ void tile_load(TileRegs<S>& tr, __amdgpu_buffer_rsrc_
     if (c < S::KV_CH) {
       const int row = min(c / S::ROW_CH, lim), ch = c % S::ROW_CH;
       tr.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              kres, row * S::ROW_BYTES + ch * 16, int(soff), 0));
+                                              kres, row * S::ROW_BYTES + ch * 16, int(soff), kStream));
     }
   }
 #pragma unroll
@@ -130,9 +130,9 @@ __device__ __forceinline__ void tile_load(TileRegs<S>& tr, __amdgpu_buffer_rsrc_
       const int pr = it / S::ROW_CH, ch = it % S::ROW_CH;
       const int r0 = min(2 * pr, lim), r1 = min(2 * pr + 1, lim);
       tr.va[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               vres, r0 * S::ROW_BYTES + ch * 16, int(soff), 0));
+                                               vres, r0 * S::ROW_BYTES + ch * 16, int(soff), kStream));
       tr.vb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               vres, r1 * S::ROW_BYTES + ch * 16, int(soff), 0));
+                                               vres, r1 * S::ROW_BYTES + ch * 16, int(soff), kStream));
     }
   }
 }
@@ -200,16 +200,16 @@ __device__ __forceinline__ void z_load(ZRegs<S>& zr, __amdgpu_buffer_rsrc_t zkre
   if constexpr (S::ZK_BYTES > 0) {
     if constexpr (!CLAMP) {
       const uint32_t soff = uint32_t(rel0) * ztok;
-      buffer_words<S::ZK_BYTES>(zr.zk, zkres, zk_lane, soff);
+      buffer_words<S::ZK_BYTES, kStream>(zr.zk, zkres, zk_lane, soff);
 #pragma unroll
-      for (int j = 0; j < G; ++j) buffer_words<S::ZV_BYTES>(zr.zv[j], zvres, zv_lane, soff + uint32_t(j) * ztok);
+      for (int j = 0; j < G; ++j) buffer_words<S::ZV_BYTES, kStream>(zr.zv[j], zvres, zv_lane, soff + uint32_t(j) * ztok);
     } else {
       const int tok = min(rel_tb + g, rel_last);
-      buffer_words<S::ZK_BYTES>(zr.zk, zkres, uint32_t(tok) * ztok + zk_head, 0u);
+      buffer_words<S::ZK_BYTES, kStream>(zr.zk, zkres, uint32_t(tok) * ztok + zk_head, 0u);
 #pragma unroll
       for (int j = 0; j < G; ++j) {
         const int tj = min(rel_tb + j, rel_last);
-        buffer_words<S::ZV_BYTES>(zr.zv[j], zvres, uint32_t(tj) * ztok + zv_head, 0u);
+        buffer_words<S::ZV_BYTES, kStream>(zr.zv[j], zvres, uint32_t(tj) * ztok + zv_head, 0u);
       }
     }
   }
@@ -560,7 +560,10 @@ static hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, int
   kp.heads = pl.heads; kp.heads_pow2 = pl.heads_pow2; kp.slots = pl.slots; kp.partials = pl.partials;
   kp.capacity = pl.capacity; kp.max_len = pl.max_len; kp.split_tokens = pl.split_tokens;
   kp.ws_ml = a.ws_ml; kp.ws_acc = a.ws_acc;
-  if ((phase & 1) && pl.n_splits > 0) {
+  if ((phase & 1) && pl.mfma) {
+    const hipError_t e = launch_decode_mfma_scan(pl, a, st);
+    if (e != hipSuccess) return e;
+  } else if ((phase & 1) && pl.n_splits > 0) {
     hipLaunchKernelGGL((decode_split_kernel<E, DH, R, G>), dim3(pl.n_splits, pl.batch), dim3(kDecodeThreads), 0, st, kp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -54,24 +54,29 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
 
   pl->batch = batch; pl->heads = heads; pl->head_dim = head_dim; pl->rank = rank; pl->dtype = dtype;
   pl->capacity = capacity; pl->max_len = int(max_len);
+  pl->mfma = lrkv::decode_mfma_supported(dtype, head_dim, rank, heads);
   pl->group = (rank == 4 || heads > 32) ? 4 : 8;
   int hp = 1;
   while (hp < heads) hp <<= 1;
   pl->heads_pow2 = hp;
-  pl->slots = lrkv::kDecodeThreads / (hp * pl->group);
+  pl->slots = pl->mfma ? lrkv::kMfmaSlots : lrkv::kDecodeThreads / (hp * pl->group);
   if (pl->slots < 1) return LRKV_ERR_SHAPE;
 
   const int tile = lrkv::kDecodeTile;
   int split = split_tokens;
   if (split == 0) {
-    // Aim for about two resident workgroups per compute unit over the whole batch.
-    const int64_t total = int64_t(batch) * max_len;
-    const int64_t target = 2 * int64_t(device_cu_count());
+    // Workgroups over the whole batch: about two per compute unit for the
+    // vector-ALU scan; for the MFMA scan (one resident workgroup per compute
+    // unit) about one, in whole 32-token tiles per wave.
+    const int64_t groups = pl->mfma ? heads / 32 : 1;
+    const int64_t total = int64_t(batch) * max_len * groups;
+    const int64_t target = (pl->mfma ? 1 : 2) * int64_t(device_cu_count());
+    const int64_t unit = pl->mfma ? 2 * tile : tile;
     int64_t s = (total + target - 1) / (target > 0 ? target : 1);
-    s = (s + tile - 1) / tile * tile;
-    if (s < tile) s = tile;
-    const int64_t cap = (max_len + tile - 1) / tile * tile;
-    if (s > cap) s = cap < tile ? tile : cap;
+    s = (s + unit - 1) / unit * unit;
+    if (s < unit) s = unit;
+    const int64_t cap = (max_len + unit - 1) / unit * unit;
+    if (s > cap) s = cap < unit ? unit : cap;
     split = int(s);
   }
   // The kernels address one split's rows and latents through 32-bit buffer

@@ -108,30 +108,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_resource(const void* ba
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
 }
 
+// Cache-policy operand of a buffer load.  kStream sets the gfx950
+// non-temporal bit: the data is read once, so the caches treat its lines as
+// streaming (evicted first, not kept for reuse).  The cache scans use it for
+// every load of cache rows and latents; on the 671 MB decode scan it takes
+// the sustained read rate from about 5.1 to 6.0 TB/s.
+constexpr int kCached = 0;
+constexpr int kStream = 2;
+
 // Load NB bytes (2 or a multiple of 4) at byte voff + soff of a buffer
 // resource into 32-bit words w[0..ceil(NB/4)), using 16-, 8-, 4- and 2-byte
 // accesses; the offset must be aligned to min(NB, 16).
-template <int NB>
+template <int NB, int POLICY = kCached>
 __device__ __forceinline__ void buffer_words(uint32_t* w, __amdgpu_buffer_rsrc_t res, uint32_t voff, uint32_t soff) {
   if constexpr (NB == 2) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b16(res, int(voff), int(soff), 0);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(res, int(voff), int(soff), POLICY);
     return;
   }
   static_assert(NB == 2 || NB % 4 == 0, "load size");
   int o = 0;
 #pragma unroll
   for (; o + 16 <= NB; o += 16) {
-    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, int(voff + o), int(soff), 0));
+    const u32x4 v =
+        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(res, int(voff + o), int(soff), POLICY));
     w[o / 4] = v.x; w[o / 4 + 1] = v.y; w[o / 4 + 2] = v.z; w[o / 4 + 3] = v.w;
   }
   if constexpr (NB % 16 >= 8) {
     constexpr int o8 = NB / 16 * 16;
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(res, int(voff + o8), int(soff), 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(res, int(voff + o8), int(soff), POLICY);
     w[o8 / 4] = v[0]; w[o8 / 4 + 1] = v[1];
   }
   if constexpr (NB % 8 == 4) {
     constexpr int o4 = NB / 8 * 8;
-    w[o4 / 4] = __builtin_amdgcn_raw_buffer_load_b32(res, int(voff + o4), int(soff), 0);
+    w[o4 / 4] = __builtin_amdgcn_raw_buffer_load_b32(res, int(voff + o4), int(soff), POLICY);
   }
 }
 
@@ -224,5 +233,53 @@ __device__ __forceinline__ uint32_t group_bcast(uint32_t v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA, LDS transpose reads and global-to-LDS transfers (gfx950).
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+// D = A.B + C with A 32x16, B 16x32 (bf16), C/D 32x32 fp32.  Lane l holds
+// A row l%32 and B column l%32 at k-slots 8(l/32)..8(l/32)+7, and D column
+// l%32 at rows 8(i/4) + 4(l/32) + i%4 in element i.
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// LDS transpose read of 4 bf16.  Within each group of 16 lanes, lane 4a+c
+// receives element c of the 8-byte rows addressed by lanes 4k+a, k = 0..3
+// (element k of the result from lane 4k+a).  With lane 4k+a addressing token
+// k at features 4a..4a+3, lane 4a+c gets feature 4a+c of tokens 0..3: a
+// column of a row-major tile.
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// 16 bytes per lane from global memory straight into LDS through a buffer
+// resource: lane i reads the resource at byte voff + soff (soff uniform) and
+// writes bytes [16i, 16i+16) after `lds` (wave-uniform).
+template <int POLICY = kCached>
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t res, uint32_t voff, uint32_t soff, unsigned char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (__attribute__((address_space(3))) void*)(lds), 16, int(voff),
+                                           int(soff), 0, POLICY);
+}
+
+// Swizzle of unpadded LDS tiles: 16-byte chunk ch of row r sits at position
+// ch ^ lds_swz(r, chunks).  gfx950 LDS has 64 banks of 4 bytes and serves
+// 16-byte reads 16 lanes per cycle, 8-byte and transpose reads 32 lanes per
+// cycle.  The swizzle is the bit-reversed low 4 bits of the row index, masked
+// to the chunks per row: a bijection on every 8 (or 16) consecutive rows, so
+// 16-byte reads of one chunk from 16 rows are conflict-free, and its bits 1-2
+// follow r&3, so a transpose read's 4 rows x 2 chunks land on 8 distinct
+// positions.
+__device__ __forceinline__ int lds_swz(int row, int chunks) {
+  const int r = row & 15;
+  return (((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3)) & (chunks - 1);
+}
 
 }  // namespace lrkv

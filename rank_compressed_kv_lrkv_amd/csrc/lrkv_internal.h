@@ -20,6 +20,7 @@ struct DecodePlan {
   int heads_pow2;     // heads rounded up to a power of two
   int slots;          // independent token streams per workgroup
   int partials;       // n_splits * slots partial states per (sequence, head)
+  bool mfma;          // scan on the MFMA kernel (one partial state per workgroup: slots = 1)
   size_t ws_ml_bytes, ws_acc_bytes;
 };
 
@@ -35,6 +36,11 @@ struct DecodeArgs {
 
 // Returns false if (dtype, head_dim, rank, heads) is outside the compiled envelope.
 bool decode_supported(int dtype, int head_dim, int rank, int heads);
+// Shapes the MFMA scan takes: bf16, head_dim 64 or 128, rank 0/8/16/32,
+// heads a multiple of 32 up to 64.
+bool decode_mfma_supported(int dtype, int head_dim, int rank, int heads);
+constexpr int kMfmaSlots = 1;        // partial states per MFMA-scan workgroup
+hipError_t launch_decode_mfma_scan(const DecodePlan& plan, const DecodeArgs& args, hipStream_t stream);
 // phase: 1 = split-K scan only, 2 = combine only, 3 = both.
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int phase, hipStream_t stream);
 

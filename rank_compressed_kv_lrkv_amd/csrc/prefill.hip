@@ -32,57 +32,17 @@
 
 namespace lrkv {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-typedef __attribute__((ext_vector_type(4))) short i16x4_t;
-
 constexpr int kPfWaves = 4;                 // heads per workgroup
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfTile = 32;                 // key tokens per tile, query rows per wave
 constexpr float kPfStale = 8.f;             // running-max refresh threshold (log2 units)
 constexpr int kVmcntZero = 0x0F70;          // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt not waited on
 
-__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// LDS transpose read of 4 bf16.  Within each group of 16 lanes, lane 4a+c
-// receives element c of the 8-byte rows addressed by lanes 4k+a, k = 0..3
-// (element k of the result from lane 4k+a).  With lane 4k+a addressing token
-// k at features 4a..4a+3, lane 4a+c gets feature 4a+c of tokens 0..3: a
-// column of a row-major tile.
-__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
-  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
-  return __builtin_bit_cast(uint2, r);
-}
-
-// 16 bytes per lane from global memory straight into LDS through a buffer
-// resource: lane i reads the resource at byte voff + soff (soff uniform) and
-// writes bytes [16i, 16i+16) after `lds` (wave-uniform).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t res, uint32_t voff, uint32_t soff, unsigned char* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (__attribute__((address_space(3))) void*)(lds), 16, int(voff),
-                                           int(soff), 0, 0);
-}
-
-// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t pf_resource(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
-}
-
-// LDS tiles keep rows unpadded; 16-byte chunk ch of row r sits at position
-// ch ^ pf_swz(r).  gfx950 LDS has 64 banks of 4 bytes and serves 16-byte
-// reads 16 lanes per cycle, 8-byte and transpose reads 32 lanes per cycle.
-// With the swizzle taken as the bit-reversed low 4 bits of the row index
-// (masked to the chunks per row), every read this kernel makes is free of
-// bank conflicts: the 16-byte key and key-latent reads (16 rows, one chunk)
-// and the transpose reads of values and value latents (4 rows x 2-4 adjacent
-// chunks), for rows of 64, 128 and 256 bytes.
-__device__ __forceinline__ int pf_swz(int row, int chunks) {
-  const int r = row & 15;
-  return (((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3)) & (chunks - 1);
-}
+// LDS tiles keep rows unpadded, with 16-byte chunk ch of row r at position
+// ch ^ lds_swz(r, chunks per row); with it every read this kernel makes is
+// free of bank conflicts: the 16-byte key and key-latent reads (16 rows, one
+// chunk) and the transpose reads of values and value latents (4 rows x 2-4
+// adjacent chunks), for rows of 64, 128 and 256 bytes.
 
 template <int DH, int R>
 struct PrefillShape {
@@ -136,14 +96,14 @@ __device__ __forceinline__ PfDmaOffsets<PrefillShape<DH, R>> pf_dma_offsets(int 
 #pragma unroll
   for (int i = 0; i < P::NRW; ++i) {
     const int q = (wave + i * kPfWaves) * 64 + lane, row = q / P::CR, pos = q % P::CR;
-    d.row[i] = uint32_t(row * P::RB + (pos ^ pf_swz(row, P::CR)) * 16);
+    d.row[i] = uint32_t(row * P::RB + (pos ^ lds_swz(row, P::CR)) * 16);
   }
 #pragma unroll
   for (int i = 0; i < P::NZW; ++i) {
     d.lat[i] = 0;
     if constexpr (R > 0) {
       const int q = (wave + i * kPfWaves) * 64 + lane, tok = q / P::CZ, pos = q % P::CZ;
-      const int ch = pos ^ pf_swz(tok, P::CZ);              // chunk of the 4 heads' latents of token tok
+      const int ch = pos ^ lds_swz(tok, P::CZ);              // chunk of the 4 heads' latents of token tok
       const int hh = min(hg * kPfWaves + ch / (R / 8), H - 1);
       d.lat[i] = uint32_t(((tok * H + hh) * R + (ch % (R / 8)) * 8) * 2);
     }
@@ -161,8 +121,8 @@ __device__ __forceinline__ PfSources pf_sources(const uint16_t* rows, const uint
                                                 int b) {
   const size_t L = size_t(p.seq_len);
   PfSources s;
-  s.rows = pf_resource(rows + size_t(b) * L * DH, uint32_t(L * DH * 2));
-  s.lat = pf_resource(lat + size_t(b) * L * p.heads * R, uint32_t(L * p.heads * (R > 0 ? R : 1) * 2));
+  s.rows = buffer_resource(rows + size_t(b) * L * DH, uint32_t(L * DH * 2));
+  s.lat = buffer_resource(lat + size_t(b) * L * p.heads * R, uint32_t(L * p.heads * (R > 0 ? R : 1) * 2));
   return s;
 }
 
@@ -197,7 +157,7 @@ __device__ __forceinline__ void pf_dma(unsigned char* side, const PfSources& src
     if (j < P::NR) {
       const int q = j * 64 + lane, row = q / P::CR, pos = q % P::CR;
       const int t = min(kt * kPfTile + row, L - 1);
-      dma16(src.rows, uint32_t(t * P::RB + (pos ^ pf_swz(row, P::CR)) * 16), 0u, side + j * 1024);
+      dma16(src.rows, uint32_t(t * P::RB + (pos ^ lds_swz(row, P::CR)) * 16), 0u, side + j * 1024);
     }
   }
   if constexpr (R > 0) {
@@ -206,7 +166,7 @@ __device__ __forceinline__ void pf_dma(unsigned char* side, const PfSources& src
       const int j = wave + i * kPfWaves;
       if (j < P::NZ) {
         const int q = j * 64 + lane, tok = q / P::CZ, pos = q % P::CZ;
-        const int ch = pos ^ pf_swz(tok, P::CZ);            // chunk of the 4 heads' latents of token tok
+        const int ch = pos ^ lds_swz(tok, P::CZ);            // chunk of the 4 heads' latents of token tok
         const int t = min(kt * kPfTile + tok, L - 1);
         const int hh = min(hg * kPfWaves + ch / (R / 8), H - 1);
         dma16(src.lat, uint32_t(((t * H + hh) * R + (ch % (R / 8)) * 8) * 2), 0u, side + kPfTile * P::RB + j * 1024);
@@ -266,12 +226,12 @@ void prefill_kernel(PrefillKernelParams p) {
   // Per-lane LDS offsets inside a side (loop-invariant).
   int koff[DH / 16], zoff[P::ZCH];
 #pragma unroll
-  for (int c = 0; c < DH / 16; ++c) koff[c] = n * P::RB + ((2 * c + half) ^ pf_swz(n, P::CR)) * 16;
+  for (int c = 0; c < DH / 16; ++c) koff[c] = n * P::RB + ((2 * c + half) ^ lds_swz(n, P::CR)) * 16;
   if constexpr (R > 0) {
 #pragma unroll
     for (int c = 0; c < P::RK / 16; ++c) {
       const int ch = wave * (R / 8) + (R == 8 ? 0 : 2 * c + half);
-      zoff[c] = kPfTile * P::RB + n * P::ZB + (ch ^ pf_swz(n, P::CZ)) * 16;
+      zoff[c] = kPfTile * P::RB + n * P::ZB + (ch ^ lds_swz(n, P::CZ)) * 16;
     }
   }
   // Transpose reads of a 16-token value chunk: this lane addresses token
@@ -286,7 +246,7 @@ void prefill_kernel(PrefillKernelParams p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row = tr_tok + 8 * j;
-      voff[f][j] = row * P::RB + (ch ^ pf_swz(row, P::CR)) * 16 + 8 * (lane & 1);
+      voff[f][j] = row * P::RB + (ch ^ lds_swz(row, P::CR)) * 16 + 8 * (lane & 1);
     }
   }
   // Value latents: lanes addressing dims < R read them; the lanes whose 4
@@ -304,7 +264,7 @@ void prefill_kernel(PrefillKernelParams p) {
         const int row = 16 * c + tr_tok + 8 * j;
         zvoff[c][j] = (P::SUM_ROW && feat == R)
                           ? P::ONES
-                          : kPfTile * P::RB + row * P::ZB + ((byte / 16) ^ pf_swz(row, P::CZ)) * 16 + byte % 16;
+                          : kPfTile * P::RB + row * P::ZB + ((byte / 16) ^ lds_swz(row, P::CZ)) * 16 + byte % 16;
       }
   }
   const PfDmaOffsets<P> dma = pf_dma_offsets<DH, R>(H, hg, wave, lane);

@@ -88,10 +88,11 @@ def test_split_invariance(split):
     check(d, run_decode(d, split_tokens=split), name=f"split {split}")
 
 
-def test_deterministic_bitwise():
-    wl = DECODE_WORKLOADS["small_bf16_T2k"]
-    say("case determinism small_bf16")
-    d = decode_inputs(wl, seed=5)
+@pytest.mark.parametrize("name", ["small_bf16_T2k", "mid_bf16_T8k"])
+def test_deterministic_bitwise(name):
+    wl = DECODE_WORKLOADS[name]
+    say(f"case determinism {name}")
+    d = decode_inputs(wl, seed=5, batch=4, capacity=2048, lens=np.array([2048, 1500, 3, 700], np.int32))
     a = run_decode(d)
     b = run_decode(d)
     assert np.array_equal(a, b)
@@ -112,6 +113,16 @@ EDGE = [
     ("f32_dh128_r16", 4, 128, 16, "f32", [150, 66]),
     ("f32_rank4_g4", 16, 32, 4, "f32", [130, 64]),
     ("f32_rank0", 4, 16, 0, "f32", [64, 2]),
+    # shapes of the MFMA scan (bf16, 32 or 64 heads): every rank it takes,
+    # both head widths, lengths that end inside a tile and inside a wave's
+    # share, empty and one-token sequences
+    ("mfma_r0", 32, 128, 0, "bf16", [300, 33]),
+    ("mfma_dh128_r8", 32, 128, 8, "bf16", [1, 257]),
+    ("mfma_dh64_r8", 32, 64, 8, "bf16", [129, 1]),
+    ("mfma_dh64_r16", 32, 64, 16, "bf16", [31, 0, 64]),
+    ("mfma_dh64_r32", 32, 64, 32, "bf16", [95, 16]),
+    ("mfma_h64_r32", 64, 128, 32, "bf16", [97, 200]),
+    ("mfma_h64_r16", 64, 128, 16, "bf16", [160, 2]),
 ]
 
 
