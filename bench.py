@@ -56,22 +56,37 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# kernel -> the sources its code comes from (the counter summaries record their digest)
+KERNEL_SOURCES = {
+    "decode_mfma_kernel": ("decode_mfma.hip", "lrkv_device.h"),
+    "decode_split_kernel": ("decode.hip", "lrkv_device.h"),
+    "prefill_kernel": ("prefill.hip", "lrkv_device.h"),
+}
 
 
-def traffic_from_profiles(counters, source, workload, split=None):
+def source_digest(names):
+    """sha256 (first 16 hex digits) of the named kernel sources, concatenated in order."""
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(counters, kernel, workload, split=None):
     """HBM bytes per launch of a kernel from a committed rocprofv3 counter
     summary (profiles/<counters>.json: FETCH_SIZE + WRITE_SIZE per dispatch,
     each divided by the same counter's reading for a copy of known size), if
-    it was taken on the current kernel source for this workload; else None."""
+    it was taken on the current sources of that kernel for this workload;
+    else None."""
     path = os.path.join(PROFILES, counters + ".json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256_16") != source_digest(os.path.join(CSRC, source)) or rec.get("workload") != workload:
+    if rec.get("kernel", "").split("<")[0] != kernel or rec.get("workload") != workload:
+        return None
+    if rec.get("source_sha256_16") != source_digest(KERNEL_SOURCES[kernel]):
         return None
     if split is not None and rec.get("split_tokens") != split:
         return None
@@ -193,7 +208,8 @@ def main():
     scan_bytes = cache_bytes + B * H * d_h * es + H * d_h * r * es          # cache + q + B^K
     step_bytes = cache_bytes + 2 * B * H * d_h * es + 2 * H * d_h * r * es  # + out + B^V
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles("decode_scan_counters", "decode.hip", wl.name, args.split_tokens)
+    scan_kernel = L.lrkv_decode_scan_kernel(dt, H, d_h, r)
+    traffic = traffic_from_profiles("decode_scan_counters", scan_kernel, wl.name, args.split_tokens)
 
     rec = {
         "metric": "compressed-cache decode: cache tokens/s and achieved HBM GB/s (% of peak)",
@@ -214,12 +230,12 @@ def main():
                    "cache_MB": cache_bytes / 1e6},
         "hbm_GBps_step": step_bytes / (step_ms * 1e-3) / 1e9,
         "hbm_frac_step": step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "kernels_ms": {"decode_split_kernel": scan_ms, "decode_merge_kernel": comb_ms},
+        "kernels_ms": {scan_kernel: scan_ms, "decode_merge_kernel": comb_ms},
         "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic,
-                     "kernel": "decode_split_kernel", "algorithmic_bytes_per_launch": scan_bytes},
+                     "kernel": scan_kernel, "algorithmic_bytes_per_launch": scan_bytes},
     }
 
     copy_reference(args, rec)
@@ -277,7 +293,7 @@ def bench_prefill(args):
         "kernels_ms": {"prefill_kernel": kern_ms},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic_from_profiles("prefill_counters", "prefill.hip", wl.name),
+                     "traffic": traffic_from_profiles("prefill_counters", "prefill_kernel", wl.name),
                      "kernel": "prefill_kernel", "algorithmic_flops_per_launch": flops},
     }
     copy_reference(args, rec)

@@ -38,8 +38,8 @@
  *     rows whole 16-byte units: head_dim*elem_bytes % 16 == 0 and
  *     rank*elem_bytes % 16 == 0 (rank == 0 is allowed and is MQA).
  *   - Supported envelope: head_dim in {16, 32, 64, 128}; rank in
- *     {0, 4, 8, 16, 32, 64} (bf16 needs rank % 8 == 0); 1 <= num_heads <= 64
- *     (num_heads <= 32 unless rank == 4).  Anything else returns
+ *     {0, 4, 8, 16, 32, 64} (bf16 needs rank % 8 == 0); 1 <= num_heads <= 64.
+ *     Anything else returns
  *     LRKV_ERR_SHAPE before any launch.
  *   - Validation happens on the host before anything is enqueued; a call
  *     that returns an error has launched nothing.  A failed launch returns
@@ -105,6 +105,14 @@ lrkv_status lrkv_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t
 lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num_heads,
                                        int32_t head_dim, int32_t rank, int64_t capacity,
                                        int64_t max_len, int32_t split_tokens, size_t* bytes);
+
+/* Name of the kernel that runs the split-K scan of lrkv_decode for these
+ * sizes: "decode_mfma_kernel" (bf16, head_dim 64 or 128, rank 0/8/16/32,
+ * num_heads a multiple of 32 up to 64: the shared term runs on bf16 MFMA
+ * across 32 heads) or "decode_split_kernel" (every other supported shape:
+ * vector-ALU dot products).  Returns NULL for a shape outside the supported
+ * envelope.  Host-only: launches nothing; the string is static. */
+const char* lrkv_decode_scan_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank);
 
 /* One decode step: for every sequence b and head h,
  *   out[b][h] = softmax_t( scale * (q_bh.k_s[t] + (B^K_h^T q_bh).z^K[t][h]) )

@@ -25,8 +25,8 @@ STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DT
           5: "LRKV_ERR_CAPACITY", 6: "LRKV_ERR_WORKSPACE", 7: "LRKV_ERR_DEVICE"}
 
 EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
-            "lrkv_decode_workspace_size", "lrkv_decode", "lrkv_decode_partial", "lrkv_decode_combine",
-            "lrkv_prefill")
+            "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
+            "lrkv_decode_combine", "lrkv_prefill")
 
 
 class LrkvError(RuntimeError):
@@ -54,6 +54,8 @@ def library() -> ctypes.CDLL:
         lib.lrkv_append.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i32,
                                     _vp, _vp, _vp, _vp, _vp]
         lib.lrkv_append.restype = _i32
+        lib.lrkv_decode_scan_kernel.argtypes = [_i32, _i32, _i32, _i32]
+        lib.lrkv_decode_scan_kernel.restype = ctypes.c_char_p
         lib.lrkv_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _i64, _i32,
                                                    ctypes.POINTER(_sz)]
         lib.lrkv_decode_workspace_size.restype = _i32
@@ -70,6 +72,12 @@ def library() -> ctypes.CDLL:
 
 def lrkv_status_string(status: int) -> str:
     return library().lrkv_status_string(int(status)).decode()
+
+
+def lrkv_decode_scan_kernel(dtype: torch.dtype, num_heads: int, head_dim: int, rank: int) -> Optional[str]:
+    """Name of the kernel lrkv_decode's scan runs on for these sizes (None if unsupported)."""
+    name = library().lrkv_decode_scan_kernel(_dtype_code(dtype), num_heads, head_dim, rank)
+    return None if name is None else name.decode()
 
 
 def lrkv_cache_elems_per_token(num_heads: int, head_dim: int, rank: int) -> int:

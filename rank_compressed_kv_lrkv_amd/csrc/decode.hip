@@ -473,11 +473,14 @@ void decode_split_kernel(DecodeKernelParams p) {
 // Merge the partial states of one (sequence, head) and apply the residual
 // up-projection once: o = (sum_j w_j acc_s_j + B^V_h sum_j w_j acc_z_j) / L,
 // w_j = 2^(m_j - M), L = sum_j w_j l_j (Eq. (7): the latent sums are linear in
-// the weights, so B^V is applied after the merge).  Threads [0, DH) own the
-// shared-value dims, threads [DH, DH+R) the latent dims; the weights are
-// computed once into LDS.
+// the weights, so B^V is applied after the merge).  Thread t < DH + R owns
+// merged dimension t; every thread folds all partial states itself (the
+// (m, l) pairs are the same for every thread and come from cache), eight at
+// a time with all of their loads issued together and an online rescale, so
+// the kernel costs two dependent memory round trips (the length, then
+// everything else) plus one LDS exchange of the latent sums.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeChunk = 256;      // partial states handled per pass
+constexpr int kMergeBatch = 8;        // partial states whose loads are in flight together
 
 template <class E, int DH, int R>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
@@ -485,11 +488,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const void* b_v, void* out, int heads, int partials, int slots, int split_tokens, int max_len) {
   static_assert(DH + R <= kMergeThreads, "one thread per merged dimension");
   using T = typename E::T;
-  __shared__ float s_w[kMergeChunk];
-  __shared__ float s_red[kMergeThreads / 64];
   __shared__ float s_z[R > 0 ? R : 1];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int col = tid < DH + R ? tid : DH + R - 1;           // threads past the last dimension shadow it
   int len = seq_lens[b];
   len = len < 0 ? 0 : (len > max_len ? max_len : len);
   T* o = static_cast<T*>(out) + (size_t(b) * heads + h) * DH;
@@ -497,54 +498,51 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     if (tid < DH) o[tid] = E::from_f32(0.f);
     return;
   }
+  // B^V_h row of this output dimension, loaded alongside the partial states
+  uint32_t bw[R > 0 ? (R * E::kBytes) / 4 : 1];
+  if constexpr (R > 0) {
+    if (tid < DH) load_words<R * E::kBytes>(bw, static_cast<const T*>(b_v) + (size_t(h) * DH + tid) * R);
+  }
   const int n = ((len + split_tokens - 1) / split_tokens) * slots;   // partials written for this sequence
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + size_t(b) * partials * heads + h;
-  const float* acc = ws_acc + (size_t(b) * partials * heads + h) * (DH + R);
+  const float* acc = ws_acc + (size_t(b) * partials * heads + h) * (DH + R) + col;
   const size_t as = size_t(heads) * (DH + R);
 
-  // M = max_j m_j
-  float mx = -INFINITY;
-  for (int j = tid; j < n; j += kMergeThreads) mx = fmaxf(mx, ml[size_t(j) * heads].x);
-  for (int o2 = 32; o2 > 0; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2));
-  if (lane == 0) s_red[wave] = mx;
-  __syncthreads();
-  float M = s_red[0];
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
-  __syncthreads();
-
-  float Lpart = 0.f, a = 0.f;
-  const int col = tid;                                       // merged dimension owned by this thread
-  for (int j0 = 0; j0 < n; j0 += kMergeChunk) {
-    const int cnt = min(kMergeChunk, n - j0);
-    if (tid < cnt) {
-      const float2 v = ml[size_t(j0 + tid) * heads];
-      const float w = fast_exp2(v.x - M);                    // empty partial: m = -inf -> 0
-      s_w[tid] = w;
-      Lpart += w * v.y;
+  float M = -INFINITY, L = 0.f, a = 0.f;
+  for (int j0 = 0; j0 < n; j0 += kMergeBatch) {
+    float2 v[kMergeBatch];
+    float x[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const bool ok = j0 + u < n;
+      v[u] = ok ? ml[size_t(j0 + u) * heads] : make_float2(-INFINITY, 0.f);
+      x[u] = ok ? acc[size_t(j0 + u) * as] : 0.f;
     }
-    __syncthreads();
-    if (col < DH + R) {
-      const float* src = acc + size_t(j0) * as + col;
-#pragma unroll 8
-      for (int j = 0; j < cnt; ++j) a = __builtin_fmaf(s_w[j], src[size_t(j) * as], a);
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) mb = fmaxf(mb, v[u].x);
+    if (mb == -INFINITY) continue;                          // only empty states so far
+    const float r = fast_exp2(M - mb);                      // 0 while M = -inf
+    L *= r;
+    a *= r;
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const float w = fast_exp2(v[u].x - mb);              // empty state: m = -inf -> 0
+      L = __builtin_fmaf(w, v[u].y, L);
+      a = __builtin_fmaf(w, x[u], a);
     }
+    M = mb;
+  }
+  if constexpr (R > 0) {
+    if (tid >= DH && tid < DH + R) s_z[tid - DH] = a;
     __syncthreads();
   }
-  for (int o2 = 32; o2 > 0; o2 >>= 1) Lpart += __shfl_xor(Lpart, o2);
-  if (lane == 0) s_red[wave] = Lpart;
-  if (R > 0 && col >= DH && col < DH + R) s_z[col - DH] = a;
-  __syncthreads();
-  float L = 0.f;
-  for (int w = 0; w < kMergeThreads / 64; ++w) L += s_red[w];
-  if (col < DH) {
+  if (tid < DH) {
     if constexpr (R > 0) {
-      const T* bv = static_cast<const T*>(b_v) + (size_t(h) * DH + col) * R;
-      uint32_t bw[(R * E::kBytes) / 4];
-      load_words<R * E::kBytes>(bw, bv);
 #pragma unroll
       for (int i = 0; i < R; ++i) a = __builtin_fmaf(E::to_f32(elem_at<E>(bw, i)), s_z[i], a);
     }
-    o[col] = E::from_f32(a / L);
+    o[tid] = E::from_f32(a / L);
   }
 }
 

@@ -116,6 +116,12 @@ int64_t lrkv_cache_elems_per_token(int32_t num_heads, int32_t head_dim, int32_t 
   return 2 * (int64_t(head_dim) + int64_t(num_heads) * int64_t(rank));
 }
 
+const char* lrkv_decode_scan_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank) {
+  if (check_sizes(dtype, 1, num_heads, head_dim, rank, 1) != LRKV_OK) return nullptr;
+  if (!lrkv::decode_supported(dtype, head_dim, rank, num_heads)) return nullptr;
+  return lrkv::decode_mfma_supported(dtype, head_dim, rank, num_heads) ? "decode_mfma_kernel" : "decode_split_kernel";
+}
+
 lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
                                        int32_t rank, int64_t capacity, int64_t max_len, int32_t split_tokens,
                                        size_t* bytes) {

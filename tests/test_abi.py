@@ -49,6 +49,20 @@ def test_status_strings_and_elem_count():
     assert L.lrkv_cache_elems_per_token(4, 16, -1) == -1
 
 
+def test_decode_scan_kernel_names():
+    lib = L.library()
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 16) == b"decode_mfma_kernel"
+    assert lib.lrkv_decode_scan_kernel(BF16, 64, 64, 32) == b"decode_mfma_kernel"
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 0) == b"decode_mfma_kernel"
+    assert lib.lrkv_decode_scan_kernel(BF16, 8, 64, 8) == b"decode_split_kernel"     # heads not a multiple of 32
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 32, 16) == b"decode_split_kernel"   # head_dim 32
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 64) == b"decode_split_kernel"  # rank 64
+    assert lib.lrkv_decode_scan_kernel(F32, 32, 128, 16) == b"decode_split_kernel"   # fp32 storage
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 24, 16) is None                     # unsupported head_dim
+    assert lib.lrkv_decode_scan_kernel(7, 32, 128, 16) is None
+    assert L.lrkv_decode_scan_kernel(torch.bfloat16, 32, 128, 16) == "decode_mfma_kernel"
+
+
 def ws_size(dtype=BF16, B=2, H=8, d_h=64, r=8, cap=256, max_len=256, split=0):
     n = ctypes.c_size_t(0)
     st = L.library().lrkv_decode_workspace_size(dtype, B, H, d_h, r, cap, max_len, split, ctypes.byref(n))
