@@ -485,7 +485,8 @@ constexpr int kMergeBatch = 8;        // partial states whose loads are in fligh
 template <class E, int DH, int R>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, const int32_t* __restrict__ seq_lens,
-    const void* b_v, void* out, int heads, int partials, int slots, int split_tokens, int max_len) {
+    const void* b_v, void* out, int heads, int partials, int slots, int split_tokens, int max_len, int batch,
+    const int* __restrict__ ws_meta) {
   static_assert(DH + R <= kMergeThreads, "one thread per merged dimension");
   using T = typename E::T;
   __shared__ float s_z[R > 0 ? R : 1];
@@ -503,9 +504,18 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   if constexpr (R > 0) {
     if (tid < DH) load_words<R * E::kBytes>(bw, static_cast<const T*>(b_v) + (size_t(h) * DH + tid) * R);
   }
-  const int n = ((len + split_tokens - 1) / split_tokens) * slots;   // partials written for this sequence
-  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + size_t(b) * partials * heads + h;
-  const float* acc = ws_acc + (size_t(b) * partials * heads + h) * (DH + R) + col;
+  // the partial states of this sequence: items j0 .. j0 + n - 1
+  int j0, n;
+  if (ws_meta) {                                             // balanced partition, recorded by the scan
+    j0 = ws_meta[b];
+    const int u = ws_meta[batch];
+    n = (len + u - 1) / u;
+  } else {
+    j0 = b * partials;
+    n = ((len + split_tokens - 1) / split_tokens) * slots;
+  }
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml) + size_t(j0) * heads + h;
+  const float* acc = ws_acc + (size_t(j0) * heads + h) * (DH + R) + col;
   const size_t as = size_t(heads) * (DH + R);
 
   float M = -INFINITY, L = 0.f, a = 0.f;
@@ -569,7 +579,7 @@ static hipError_t launch_decode_t(const DecodePlan& pl, const DecodeArgs& a, int
   if (!(phase & 2)) return hipSuccess;
   hipLaunchKernelGGL((decode_merge_kernel<E, DH, R>), dim3(pl.heads, pl.batch), dim3(kMergeThreads), 0, st,
                      a.ws_ml, a.ws_acc, a.seq_lens, a.b_v, a.out, pl.heads, pl.partials, pl.slots,
-                     pl.split_tokens, pl.max_len);
+                     pl.split_tokens, pl.max_len, pl.batch, pl.balanced ? a.ws_meta : nullptr);
   return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@
 // latent value dots rounded to bf16 (relative error <= 2^-9 each), and the
 // running sum l adds the fp32 weights.  Softmax runs in the log2 domain with
 // a lazily refreshed running max.
+#include "decode_balance.h"
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -91,9 +92,11 @@ struct MfParams {
   const int32_t* seq_lens;
   const void* q; const void* b_k;
   float scale_log2;
-  int heads, n_hgroups, partials, max_len, split_tokens;
+  int heads, partials, max_len, split_tokens;
+  int batch, balanced, bal_cap;     // balanced: length-balanced items (grid.x = item), else fixed splits
   int64_t capacity;
   float* ws_ml; float* ws_acc;
+  int* ws_meta;
 };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
@@ -132,19 +135,40 @@ void decode_mfma_kernel(MfParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, hf = lane >> 5;
-  const int split = blockIdx.x;
-  const int hg = int(blockIdx.y) % p.n_hgroups;
-  const int b = int(blockIdx.y) / p.n_hgroups;
+  const int hg = blockIdx.y;
   const int H = p.heads;
   const int h = hg * kMfHeads + j;
 
-  int len = p.seq_lens[b];
-  len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
-  const int t0 = split * p.split_tokens;
-  if (t0 >= len) return;                                    // whole workgroup: uniform exit
-  const int share = p.split_tokens / kMfWaves;
-  const int tw0 = t0 + wave * share;
-  const int ntok = max(0, min(tw0 + share, len) - tw0);     // this wave's tokens [tw0, tw0 + ntok)
+  // This workgroup's work item: a sequence b and its tokens [lo, hi).
+  // Every exit below is uniform over the workgroup.
+  int b, lo, hi, item;
+  if (p.balanced) {
+    item = blockIdx.x;
+    const BalLens L = bal_load(p.seq_lens, p.batch, p.max_len, lane);
+    const int u = bal_item_size(L, p.max_len, p.bal_cap, lane);
+    if (u == 0 || !bal_item(L, u, item, lane, &b, &lo, &hi)) return;
+    // the first item of each sequence records where its items start, and
+    // the item size, for the merge
+    if (lo == 0 && tid == 0) {
+      p.ws_meta[b] = item;
+      p.ws_meta[p.batch] = u;
+    }
+  } else {
+    b = blockIdx.z;
+    item = b * p.partials + int(blockIdx.x);
+    int len = p.seq_lens[b];
+    len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
+    lo = int(blockIdx.x) * p.split_tokens;
+    if (lo >= len) return;
+    hi = min(lo + p.split_tokens, len);
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+  item = __builtin_amdgcn_readfirstlane(item);
+  const int share = ((hi - lo + kMfWaves - 1) / kMfWaves + kMfTile - 1) / kMfTile * kMfTile;
+  const int tw0 = lo + wave * share;
+  const int ntok = max(0, min(tw0 + share, hi) - tw0);      // this wave's tokens [tw0, tw0 + ntok)
   const int ntiles = (ntok + kMfTile - 1) / kMfTile;
 
   // Resources over this wave's tokens (the host keeps them below 4 GiB).
@@ -496,7 +520,7 @@ void decode_mfma_kernel(MfParams p) {
     swap_halves(x0, x1);                                     // the two halves' sums of this head
     lsum = __uint_as_float(x0) + __uint_as_float(x1);
   }
-  const size_t pidx = (size_t(b) * p.partials + size_t(split)) * H + h;
+  const size_t pidx = size_t(item) * H + h;
   if (hf == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * pidx) = make_float2(M, lsum);
   float* dst = p.ws_acc + pidx * (DH + R);
 #pragma unroll
@@ -520,15 +544,16 @@ static hipError_t launch_mfma_t(const DecodePlan& pl, const DecodeArgs& a, hipSt
   kp.k_s = a.k_s; kp.v_s = a.v_s; kp.z_k = a.z_k; kp.z_v = a.z_v;
   kp.seq_lens = a.seq_lens; kp.q = a.q; kp.b_k = a.b_k;
   kp.scale_log2 = a.scale_log2;
-  kp.heads = pl.heads; kp.n_hgroups = pl.heads / kMfHeads; kp.partials = pl.partials;
+  kp.heads = pl.heads; kp.partials = pl.partials;
   kp.max_len = pl.max_len; kp.split_tokens = pl.split_tokens;
+  kp.batch = pl.batch; kp.balanced = pl.balanced; kp.bal_cap = pl.bal_cap;
   kp.capacity = pl.capacity;
-  kp.ws_ml = a.ws_ml; kp.ws_acc = a.ws_acc;
+  kp.ws_ml = a.ws_ml; kp.ws_acc = a.ws_acc; kp.ws_meta = a.ws_meta;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<DH, R>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((decode_mfma_kernel<DH, R>), dim3(pl.n_splits, pl.batch * kp.n_hgroups), dim3(kMfThreads),
-                     size_t(S::LDS), st, kp);
+  const dim3 grid(pl.n_splits, pl.heads / kMfHeads, pl.balanced ? 1 : pl.batch);
+  hipLaunchKernelGGL((decode_mfma_kernel<DH, R>), grid, dim3(kMfThreads), size_t(S::LDS), st, kp);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 
 #include "../../include/lrkv.h"
+#include "decode_balance.h"
 #include "lrkv_internal.h"
 
 #include <algorithm>
@@ -79,17 +80,28 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
     if (s > cap) s = cap < unit ? unit : cap;
     split = int(s);
   }
+  // Default split of the MFMA scan over a batch the device-side partition
+  // takes: items balanced over the actual lengths (up to cap + batch items).
+  pl->balanced = pl->mfma && split_tokens == 0 && batch <= lrkv::kBalMaxBatch && max_len < lrkv::kBalMaxLen;
+  pl->bal_cap = device_cu_count();
   // The kernels address one split's rows and latents through 32-bit buffer
-  // offsets.
+  // offsets (a balanced item is at most max_len tokens).
   const int64_t es = dtype == 1 ? 2 : 4;
-  if (int64_t(split) * std::max<int64_t>(int64_t(head_dim), int64_t(heads) * rank) * es >= (int64_t(1) << 32))
+  const int64_t span = pl->balanced ? std::max<int64_t>(max_len, 1) : split;
+  if (span * std::max<int64_t>(int64_t(head_dim), int64_t(heads) * rank) * es >= (int64_t(1) << 32))
     return LRKV_ERR_SHAPE;
   pl->split_tokens = split;
-  pl->n_splits = int((max_len + split - 1) / split);
-  pl->partials = pl->n_splits * pl->slots;
-  const size_t states = size_t(batch) * size_t(pl->partials) * size_t(heads);
+  if (pl->balanced) {
+    pl->n_splits = max_len > 0 ? pl->bal_cap + batch : 0;
+    pl->partials = pl->n_splits;
+  } else {
+    pl->n_splits = int((max_len + split - 1) / split);
+    pl->partials = pl->n_splits * pl->slots;
+  }
+  const size_t states = (pl->balanced ? size_t(1) : size_t(batch)) * size_t(pl->partials) * size_t(heads);
   pl->ws_ml_bytes = (states * 2 * sizeof(float) + 255) / 256 * 256;
   pl->ws_acc_bytes = (states * size_t(head_dim + rank) * sizeof(float) + 255) / 256 * 256;
+  pl->ws_meta_bytes = pl->balanced ? (size_t(batch + 1) * sizeof(int) + 255) / 256 * 256 : 0;
   return LRKV_OK;
 }
 
@@ -129,7 +141,7 @@ lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num
   DecodePlan pl;
   const lrkv_status st = plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl);
   if (st != LRKV_OK) return st;
-  *bytes = pl.ws_ml_bytes + pl.ws_acc_bytes;
+  *bytes = pl.ws_ml_bytes + pl.ws_acc_bytes + pl.ws_meta_bytes;
   return LRKV_OK;
 }
 
@@ -147,7 +159,7 @@ static lrkv_status decode_phases(int phase, int32_t dtype, int32_t batch, int32_
   if (scan && (!k_shared || !v_shared || !q)) return LRKV_ERR_NULL;
   if (scan && rank > 0 && (!z_k || !z_v || !b_k)) return LRKV_ERR_NULL;
   if (combine && (!out || (rank > 0 && !b_v))) return LRKV_ERR_NULL;
-  const size_t need = pl.ws_ml_bytes + pl.ws_acc_bytes;
+  const size_t need = pl.ws_ml_bytes + pl.ws_acc_bytes + pl.ws_meta_bytes;
   if (!workspace || workspace_bytes < need) return LRKV_ERR_WORKSPACE;
   if (!aligned16(workspace) || !aligned4(seq_lens)) return LRKV_ERR_ALIGN;
   if (scan && (!aligned16(k_shared) || !aligned16(v_shared) || !aligned16(q))) return LRKV_ERR_ALIGN;
@@ -162,6 +174,7 @@ static lrkv_status decode_phases(int phase, int32_t dtype, int32_t batch, int32_
   a.out = out;
   a.ws_ml = static_cast<float*>(workspace);
   a.ws_acc = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + pl.ws_ml_bytes);
+  a.ws_meta = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + pl.ws_ml_bytes + pl.ws_acc_bytes);
   const hipError_t e = lrkv::launch_decode(pl, a, phase, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
 }

@@ -21,7 +21,10 @@ struct DecodePlan {
   int slots;          // independent token streams per workgroup
   int partials;       // n_splits * slots partial states per (sequence, head)
   bool mfma;          // scan on the MFMA kernel (one partial state per workgroup: slots = 1)
-  size_t ws_ml_bytes, ws_acc_bytes;
+  bool balanced;      // length-balanced items computed on the device (MFMA scan, default split):
+                      // n_splits = partials = bal_cap + batch items, state index item * heads + h
+  int bal_cap;        // items the partition aims for (resident scan workgroups)
+  size_t ws_ml_bytes, ws_acc_bytes, ws_meta_bytes;
 };
 
 struct DecodeArgs {
@@ -32,6 +35,7 @@ struct DecodeArgs {
   void* out;
   float* ws_ml;       // [batch][partials][heads] x (m, l)
   float* ws_acc;      // [batch][partials][heads][head_dim + rank]
+  int* ws_meta;       // balanced partition: first item of each sequence [batch], then the item size
 };
 
 // Returns false if (dtype, head_dim, rank, heads) is outside the compiled envelope.

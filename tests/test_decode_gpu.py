@@ -88,6 +88,21 @@ def test_split_invariance(split):
     check(d, run_decode(d, split_tokens=split), name=f"split {split}")
 
 
+@pytest.mark.parametrize("batch,seed", [(70, 31), (130, 32)])
+def test_balanced_partition_many_sequences(batch, seed):
+    """The default partition of the MFMA scan is computed on the device from
+    the lengths (more than one 64-sequence chunk here, with empty, one-token
+    and tile-straddling sequences); the merge must find every sequence's
+    items."""
+    wl = DecodeWorkload("balanced", batch, 32, 64, 8, 300, "bf16", seed)
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 301, size=batch).astype(np.int32)
+    lens[:4] = [0, 1, 300, 129]
+    say(f"case balanced partition batch={batch} lens[:8]={lens[:8].tolist()} total={int(lens.sum())}")
+    d = decode_inputs(wl, lens=lens, capacity=300)
+    check(d, run_decode(d), name=f"balanced B={batch}")
+
+
 @pytest.mark.parametrize("name", ["small_bf16_T2k", "mid_bf16_T8k"])
 def test_deterministic_bitwise(name):
     wl = DECODE_WORKLOADS[name]
