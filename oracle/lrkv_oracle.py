@@ -29,7 +29,8 @@ Readings of points the pages leave open (each is stated where it is used):
     q_h and K_h are d_h wide);
   * decode masking: the query attends to every cached token of its sequence
     (the current token is appended before decoding), so nothing inside the
-    cache is masked; prefill query i sees keys j <= i;
+    cache is masked; prefill query i sees keys j <= i; with start cached
+    tokens in front (a prefill chunk), new token i sees keys j <= start + i;
   * an empty sequence (length 0) yields an all-zero output;
   * no position encoding and no normalisation inside attention.
 
@@ -46,7 +47,7 @@ import numpy as np
 __all__ = [
     "cache_elems_per_token", "cache_ratio_vs_mha", "kv_param_count",
     "head_projections", "cache_from_inputs", "implied_kv", "softmax_attention",
-    "decode", "prefill", "decode_from_weights", "append",
+    "decode", "prefill", "prefill_with_past", "decode_from_weights", "append",
 ]
 
 
@@ -191,6 +192,36 @@ def prefill(q, k_s, v_s, z_k, z_v, b_k, b_v, scale: Optional[float] = None) -> n
     future = np.triu(np.ones((L, L), dtype=bool), k=1)      # j > i
     for b in range(B):
         K, V = implied_kv(k_s[b], v_s[b], z_k[b], z_v[b], b_k, b_v)
+        for h in range(H):
+            S = (q[b, :, h, :] @ K[h].T) * sc
+            S[future] = -np.inf
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            A = E / E.sum(axis=1, keepdims=True)
+            out[b, :, h, :] = A @ V[h]
+    return out
+
+
+def prefill_with_past(q, k_s, v_s, z_k, z_v, b_k, b_v, start, scale: Optional[float] = None) -> np.ndarray:
+    """Causal attention of L new tokens per sequence over everything cached
+    before them and over themselves (a prefill chunk, or a decode step of
+    several tokens).
+
+    q [B, L, H, d_h].  k_s, v_s [B, T, d_h], z_k, z_v [B, T, H, r] hold the
+    cache after the new tokens were written at slots [start[b], start[b] + L).
+    New token i of sequence b sits at position start[b] + i and attends to
+    the cached tokens j <= start[b] + i: the causal mask of slide "Compute
+    logits without expanding historical keys" with start[b] historical keys in
+    front.  Returns [B, L, H, d_h]."""
+    q = np.asarray(q, np.float64)
+    B, L, H, d_h = q.shape
+    sc = _default_scale(d_h, scale)
+    out = np.zeros((B, L, H, d_h), np.float64)
+    for b in range(B):
+        s0 = int(start[b])
+        n = s0 + L
+        K, V = implied_kv(k_s[b, :n], v_s[b, :n], z_k[b, :n], z_v[b, :n], b_k, b_v)
+        pos = s0 + np.arange(L)[:, None]                     # absolute position of each new token
+        future = np.arange(n)[None, :] > pos                 # keys after the query
         for h in range(H):
             S = (q[b, :, h, :] @ K[h].T) * sc
             S[future] = -np.inf

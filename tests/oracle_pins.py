@@ -329,6 +329,66 @@ def pin_prefill_rows_are_decodes(O):
 # ---------------------------------------------------------------------------
 # Append.
 # ---------------------------------------------------------------------------
+def _rand_past(seed, B=3, L=9, T=40, H=3, d_h=8, r=3, zero_b=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, L, H, d_h))
+    k_s, v_s = rng.standard_normal((B, T, d_h)), rng.standard_normal((B, T, d_h))
+    z_k, z_v = rng.standard_normal((B, T, H, r)), rng.standard_normal((B, T, H, r))
+    b_k = rng.standard_normal((H, d_h, r)) / math.sqrt(r)
+    b_v = rng.standard_normal((H, d_h, r)) / math.sqrt(r)
+    if zero_b:
+        b_k[:] = 0.0
+        b_v[:] = 0.0
+    start = np.array([0, 17, T - L][:B], dtype=np.int64)
+    return q, k_s, v_s, z_k, z_v, b_k, b_v, start
+
+
+def pin_prefill_with_past_rows_are_decodes(O):
+    # New token i of a chunk is a decode of its query over the first
+    # start + i + 1 cached tokens (decode itself is pinned to a library
+    # routine and to brute force).
+    q, k_s, v_s, z_k, z_v, b_k, b_v, start = _rand_past(61)
+    got = O.prefill_with_past(q, k_s, v_s, z_k, z_v, b_k, b_v, start)
+    B, L = q.shape[:2]
+    for b in range(B):
+        for i in range(L):
+            want = O.decode(q[b:b + 1, i], k_s[b:b + 1], v_s[b:b + 1], z_k[b:b + 1], z_v[b:b + 1], b_k, b_v,
+                            [int(start[b]) + i + 1])
+            assert rel_err(got[b, i], want[0]) < TIGHT, (b, i)
+
+
+def pin_prefill_with_past_mqa_sdpa(O):
+    # B = 0: every head attends to K_s/V_s under the shifted causal mask;
+    # torch's attention with an explicit boolean mask is the reference.
+    q, k_s, v_s, z_k, z_v, b_k, b_v, start = _rand_past(67, zero_b=True)
+    got = O.prefill_with_past(q, k_s, v_s, z_k, z_v, b_k, b_v, start)
+    B, L, H, d_h = q.shape
+    for b in range(B):
+        n = int(start[b]) + L
+        allowed = np.arange(n)[None, :] <= (int(start[b]) + np.arange(L))[:, None]
+        qh = torch.from_numpy(np.ascontiguousarray(q[b].transpose(1, 0, 2)))
+        Kb = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(k_s[b, :n], (H, n, d_h))))
+        Vb = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(v_s[b, :n], (H, n, d_h))))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qh, Kb, Vb, attn_mask=torch.from_numpy(allowed), scale=1.0 / math.sqrt(d_h)).numpy()
+        assert rel_err(got[b], ref.transpose(1, 0, 2)) < TIGHT, b
+
+
+def pin_chunked_prefill_equals_full(O):
+    # Processing a sequence in chunks, each over everything before it, gives
+    # the rows of one causal prefill over the whole sequence.
+    rng = np.random.default_rng(71)
+    B, T, H, d_h, r = 2, 23, 2, 8, 3
+    q = rng.standard_normal((B, T, H, d_h))
+    k_s, v_s = rng.standard_normal((B, T, d_h)), rng.standard_normal((B, T, d_h))
+    z_k, z_v = rng.standard_normal((B, T, H, r)), rng.standard_normal((B, T, H, r))
+    b_k, b_v = rng.standard_normal((H, d_h, r)) / 2, rng.standard_normal((H, d_h, r)) / 2
+    full = O.prefill(q, k_s, v_s, z_k, z_v, b_k, b_v)
+    for lo, hi in ((0, 8), (8, 9), (9, 23)):
+        part = O.prefill_with_past(q[:, lo:hi], k_s, v_s, z_k, z_v, b_k, b_v, np.full(B, lo))
+        assert rel_err(part, full[:, lo:hi]) < TIGHT, (lo, hi)
+
+
 def pin_append_slots(O):
     rng = np.random.default_rng(3)
     B, T, H, d_h, r, n = 3, 16, 2, 4, 2, 5
@@ -356,5 +416,6 @@ ALL_PINS = [
     pin_decode_mha_special_case, pin_decode_absorbed_equals_reconstructed,
     pin_weight_level_equals_cache_level, pin_decode_closed_forms, pin_decode_invariances,
     pin_prefill_mqa_causal_sdpa, pin_prefill_mha_causal_sdpa, pin_prefill_rows_are_decodes,
+    pin_prefill_with_past_rows_are_decodes, pin_prefill_with_past_mqa_sdpa, pin_chunked_prefill_equals_full,
     pin_append_slots,
 ]

@@ -70,6 +70,26 @@ def _prefill_mask(k):
     return mutant
 
 
+def _past(kind):
+    def mutant(q, k_s, v_s, z_k, z_v, b_k, b_v, start, scale=None):
+        q = np.asarray(q, np.float64)
+        B, L, H, d_h = q.shape
+        out = np.zeros((B, L, H, d_h))
+        for b in range(B):
+            s0 = 0 if kind == "ignored" else int(start[b])
+            n = s0 + L
+            K, V = O.implied_kv(k_s[b, :n], v_s[b, :n], z_k[b, :n], z_v[b, :n], b_k, b_v)
+            pos = s0 + np.arange(L)[:, None]
+            masked = np.arange(n)[None, :] >= pos if kind == "excludes_diagonal" else np.arange(n)[None, :] > pos
+            for h in range(H):
+                S = (q[b, :, h] @ K[h].T) / math.sqrt(d_h)
+                S[masked] = -1e300
+                E = np.exp(S - S.max(axis=1, keepdims=True))
+                out[b, :, h] = (E / E.sum(axis=1, keepdims=True)) @ V[h]
+        return out
+    return mutant
+
+
 def _count_without_heads(mechanism, *, d_h, H=1, r=0, n_kv=1, layers=1):
     if mechanism == "lrkv":
         return 2 * (d_h + r) * layers
@@ -94,6 +114,8 @@ MUTANTS = {
     "causal_mask_excludes_diagonal": ("prefill", _prefill_mask(0)),
     "no_causal_mask": ("prefill", _prefill_mask(None)),
     "causal_mask_one_ahead": ("prefill", _prefill_mask(2)),
+    "past_ignored": ("prefill_with_past", _past("ignored")),
+    "past_mask_excludes_diagonal": ("prefill_with_past", _past("excludes_diagonal")),
 }
 
 
