@@ -140,13 +140,15 @@ __device__ __forceinline__ void pf_dma(unsigned char* side, const PfSources& src
 #pragma unroll
     for (int i = 0; i < P::NRW; ++i) {
       const int j = wave + i * kPfWaves;
-      if (j < P::NR) dma16(src.rows, d.row[i], uint32_t(kt * kPfTile * P::RB), side + j * 1024);
+      // every wave has a transfer at i when the count divides evenly: no branch
+      if (P::NR % kPfWaves == 0 || j < P::NR) dma16(src.rows, d.row[i], uint32_t(kt * kPfTile * P::RB), side + j * 1024);
     }
     if constexpr (R > 0) {
 #pragma unroll
       for (int i = 0; i < P::NZW; ++i) {
         const int j = wave + i * kPfWaves;
-        if (j < P::NZ) dma16(src.lat, d.lat[i], uint32_t(kt * kPfTile * H * R * 2), side + kPfTile * P::RB + j * 1024);
+        if (P::NZ % kPfWaves == 0 || j < P::NZ)
+          dma16(src.lat, d.lat[i], uint32_t(kt * kPfTile * H * R * 2), side + kPfTile * P::RB + j * 1024);
       }
     }
     return;
@@ -178,25 +180,36 @@ __device__ __forceinline__ void pf_dma(unsigned char* side, const PfSources& src
 // S^T tile (32 tokens x 32 queries) of one head from a key side: Kaug .
 // Qaug^T; lane (query n, half) gets tokens 8(r/4)+4half+r%4.  The lane's
 // A-operand k-slots of chunk c are dims 16c+8half..16c+8half+7, one 16-byte
-// chunk of token row n (koff[c] / zoff[c] hold its swizzled offsets).
+// chunk of token row n (koff[c] / zoff[c] hold its swizzled offsets).  The
+// operand reads run kPfAhead chunks ahead of the MFMA chain (scheduling
+// barriers keep that order), so each MFMA waits for a read issued several
+// MFMAs earlier instead of a full LDS round trip.
+constexpr int kPfAhead = 3;
+
 template <int DH, int R>
 __device__ __forceinline__ f32x16_t pf_scores(const unsigned char* side, const bf16x8_t (&qop)[PrefillShape<DH, R>::KCH],
                                               const int (&koff)[DH / 16], const int (&zoff)[PrefillShape<DH, R>::ZCH],
                                               int half) {
   using P = PrefillShape<DH, R>;
   u32x4 ka[P::KCH];
-#pragma unroll
-  for (int c = 0; c < DH / 16; ++c) ka[c] = *reinterpret_cast<const u32x4*>(side + koff[c]);
-  if constexpr (R > 0) {
-#pragma unroll
-    for (int c = 0; c < P::RK / 16; ++c) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(side + zoff[c]);
-      ka[DH / 16 + c] = (R == 8 && half) ? u32x4{0u, 0u, 0u, 0u} : v;   // R = 8: dims 8..15 are padding
+  auto rd = [&](int c) __attribute__((always_inline)) {
+    if (c < DH / 16) {
+      ka[c] = *reinterpret_cast<const u32x4*>(side + koff[c]);
+    } else if constexpr (R > 0) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(side + zoff[c - DH / 16]);
+      ka[c] = (R == 8 && half) ? u32x4{0u, 0u, 0u, 0u} : v;   // R = 8: dims 8..15 are padding
     }
-  }
+  };
+#pragma unroll
+  for (int c = 0; c < kPfAhead && c < P::KCH; ++c) rd(c);
   f32x16_t s = {};
 #pragma unroll
-  for (int c = 0; c < P::KCH; ++c) s = mfma32(as_bf16x8(ka[c]), qop[c], s);
+  for (int c = 0; c < P::KCH; ++c) {
+    if (c + kPfAhead < P::KCH) rd(c + kPfAhead);
+    __builtin_amdgcn_sched_barrier(0);
+    s = mfma32(as_bf16x8(ka[c]), qop[c], s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   return s;
 }
 
