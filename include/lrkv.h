@@ -180,15 +180,44 @@ lrkv_status lrkv_decode_combine(int32_t dtype, int32_t batch, int32_t num_heads,
  * Only dtype LRKV_BF16 is supported (bf16 MFMA with fp32 accumulation).
  * One sequence's rows and latents must each span less than 4 GiB
  * (seq_len * max(head_dim, num_heads*rank) * 2 bytes), else LRKV_ERR_SHAPE.
- * If the four cache pointers are all non-NULL the tokens are also written,
- * bit-exactly, to cache slots [0, seq_len) of every sequence (seq_len must
- * then be <= capacity); if all four are NULL the cache is not touched. */
+ * If the cache pointers are all non-NULL (k_shared, v_shared, and for
+ * rank > 0 also z_k, z_v) the tokens are also written, bit-exactly, to cache
+ * slots [0, seq_len) of every sequence (seq_len must then be <= capacity);
+ * if they are all NULL the cache is not touched. */
 lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
                          int32_t rank, int64_t capacity,
                          void* k_shared, void* v_shared, void* z_k, void* z_v,
                          int32_t seq_len, const void* q,
                          const void* k_s, const void* v_s, const void* z_k_new, const void* z_v_new,
                          const void* b_k, const void* b_v, float scale, void* out, void* stream);
+
+/* A prefill chunk, or a decode step of several tokens, over cached history:
+ * n_new new tokens per sequence attend causally to the tokens already in the
+ * cache and to each other (slide "Compute logits without expanding historical
+ * keys" with historical keys in front of the causal mask).  For sequence b
+ * with s = start_pos[b] tokens already cached:
+ *   1. the new tokens are written, bit-exactly, to cache slots [s, s + n_new);
+ *   2. new token i (position s + i) attends to cache tokens j <= s + i, in the
+ *      absorbed form of Eqs. (6)-(7) on bf16 MFMA with fp32 accumulation.
+ *   start_pos  device int32 [batch]; each value is clamped to [0, max_start].
+ *   max_start  host upper bound on start_pos; max_start + n_new <= capacity
+ *              (else LRKV_ERR_CAPACITY).
+ *   q    [batch][n_new][num_heads][head_dim];  out same shape.
+ *   k_s, v_s [batch][n_new][head_dim];  z_k_new, z_v_new [batch][n_new][num_heads][rank].
+ *   The cache pointers are required (the cache is read and written; z_k and
+ *   z_v may be NULL when rank == 0).
+ * Only dtype LRKV_BF16 and the prefill envelope (head_dim 64 or 128, rank
+ * 0/8/16/32) are supported.  One sequence's history and new tokens must
+ * span less than 4 GiB ((max_start + n_new) * max(head_dim, num_heads*rank)
+ * * 2 bytes), else LRKV_ERR_SHAPE.  With start_pos all zero and an empty
+ * cache this is lrkv_prefill with the cache written. */
+lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                               int32_t rank, int64_t capacity,
+                               void* k_shared, void* v_shared, void* z_k, void* z_v,
+                               const int32_t* start_pos, int32_t max_start, int32_t n_new,
+                               const void* q, const void* k_s, const void* v_s,
+                               const void* z_k_new, const void* z_v_new,
+                               const void* b_k, const void* b_v, float scale, void* out, void* stream);
 
 #ifdef __cplusplus
 }

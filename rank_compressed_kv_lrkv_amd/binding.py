@@ -26,7 +26,7 @@ STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DT
 
 EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
-            "lrkv_decode_combine", "lrkv_prefill")
+            "lrkv_decode_combine", "lrkv_prefill", "lrkv_prefill_chunk")
 
 
 class LrkvError(RuntimeError):
@@ -66,6 +66,9 @@ def library() -> ctypes.CDLL:
         lib.lrkv_prefill.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _i32,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp]
         lib.lrkv_prefill.restype = _i32
+        lib.lrkv_prefill_chunk.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp]
+        lib.lrkv_prefill_chunk.restype = _i32
         _lib = lib
     return _lib
 
@@ -286,6 +289,35 @@ def lrkv_prefill(q, k_s, v_s, z_k, z_v, b_k, b_v, scale: Optional[float] = None,
                                   _ptr(z_v, "z_v", dt), _ptr(b_k, "b_k", dt), _ptr(b_v, "b_v", dt),
                                   0.0 if scale is None else float(scale), _ptr(out, "out", dt), _stream()),
            "lrkv_prefill")
+    return out
+
+
+def lrkv_prefill_chunk(cache: LrkvCache, start_pos: torch.Tensor, max_start: int, q, k_s, v_s, z_k, z_v, b_k, b_v,
+                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """New tokens over cached history: writes them at slots start_pos[b].. of the
+    cache and returns their causal attention over the cache (see lrkv.h)."""
+    dt = q.dtype
+    B, L, H, d_h = q.shape
+    r = z_k.shape[-1]
+    _shape(k_s, "k_s", (B, L, d_h))
+    _shape(v_s, "v_s", (B, L, d_h))
+    _shape(z_k, "z_k", (B, L, H, r))
+    _shape(z_v, "z_v", (B, L, H, r))
+    _shape(b_k, "b_k", (H, d_h, r))
+    _shape(b_v, "b_v", (H, d_h, r))
+    if (cache.batch, cache.heads, cache.head_dim, cache.rank) != (B, H, d_h, r):
+        raise ValueError("cache dimensions differ from the chunk inputs")
+    _shape(start_pos, "start_pos", (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", (B, L, H, d_h))
+    _check(library().lrkv_prefill_chunk(_dtype_code(dt), B, H, d_h, r, cache.capacity, *cache.pointers(),
+                                        _ptr(start_pos, "start_pos", torch.int32), int(max_start), L,
+                                        _ptr(q, "q", dt),
+                                        _ptr(k_s, "k_s", dt), _ptr(v_s, "v_s", dt), _ptr(z_k, "z_k", dt),
+                                        _ptr(z_v, "z_v", dt), _ptr(b_k, "b_k", dt), _ptr(b_v, "b_v", dt),
+                                        0.0 if scale is None else float(scale), _ptr(out, "out", dt), _stream()),
+           "lrkv_prefill_chunk")
     return out
 
 

@@ -10,7 +10,8 @@ __global__ __launch_bounds__(256) void append_kernel(unsigned char* k_s, unsigne
                                                      unsigned char* z_v, const int32_t* __restrict__ pos,
                                                      const unsigned char* __restrict__ nk, const unsigned char* __restrict__ nv,
                                                      const unsigned char* __restrict__ nzk, const unsigned char* __restrict__ nzv,
-                                                     int n_new, int64_t capacity, int shared_row_bytes, int latent_row_bytes) {
+                                                     int n_new, int64_t capacity, int shared_row_bytes, int latent_row_bytes,
+                                                     int pos_max) {
   const int which = blockIdx.z;                      // 0 k_s, 1 v_s, 2 z_k, 3 z_v
   const int b = blockIdx.y;
   const int row_bytes = which < 2 ? shared_row_bytes : latent_row_bytes;
@@ -19,7 +20,9 @@ __global__ __launch_bounds__(256) void append_kernel(unsigned char* k_s, unsigne
   const long idx = long(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= long(n_new) * chunks) return;
   const int i = int(idx / chunks), c = int(idx % chunks);
-  const long slot = long(pos ? pos[b] : 0) + i;
+  int p0 = pos ? pos[b] : 0;
+  p0 = p0 > pos_max ? pos_max : (p0 < 0 && pos_max != INT32_MAX ? 0 : p0);
+  const long slot = long(p0) + i;
   if (slot < 0 || slot >= capacity) return;          // outside the cache: dropped
   unsigned char* dst = which == 0 ? k_s : which == 1 ? v_s : which == 2 ? z_k : z_v;
   const unsigned char* src = which == 0 ? nk : which == 1 ? nv : which == 2 ? nzk : nzv;
@@ -39,7 +42,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
                      static_cast<unsigned char*>(a.v_s), static_cast<unsigned char*>(a.z_k),
                      static_cast<unsigned char*>(a.z_v), a.pos, static_cast<const unsigned char*>(a.new_k_s),
                      static_cast<const unsigned char*>(a.new_v_s), static_cast<const unsigned char*>(a.new_z_k),
-                     static_cast<const unsigned char*>(a.new_z_v), a.n_new, a.capacity, shared_row, latent_row);
+                     static_cast<const unsigned char*>(a.new_z_v), a.n_new, a.capacity, shared_row, latent_row,
+                     a.pos_max);
   return hipGetLastError();
 }
 

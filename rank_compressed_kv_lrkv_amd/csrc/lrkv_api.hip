@@ -210,7 +210,7 @@ lrkv_status lrkv_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t
   lrkv::AppendArgs a;
   a.dtype = dtype; a.batch = batch; a.heads = num_heads; a.head_dim = head_dim; a.rank = rank;
   a.capacity = capacity; a.k_s = k_shared; a.v_s = v_shared; a.z_k = z_k; a.z_v = z_v;
-  a.pos = pos; a.n_new = n_new;
+  a.pos = pos; a.pos_max = INT32_MAX; a.n_new = n_new;
   a.new_k_s = new_k_s; a.new_v_s = new_v_s; a.new_z_k = new_z_k; a.new_z_v = new_z_v;
   const hipError_t e = lrkv::launch_append(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
@@ -228,9 +228,11 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
   // one sequence's rows and latents are addressed through 32-bit buffer offsets
   if (int64_t(seq_len) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >= (int64_t(1) << 32))
     return LRKV_ERR_SHAPE;
-  const int ncache = (k_shared != nullptr) + (v_shared != nullptr) + (z_k != nullptr) + (z_v != nullptr);
-  const bool write_cache = ncache == 4;
-  if (ncache != 0 && ncache != 4) return LRKV_ERR_NULL;
+  // the cache is written when its pointers are given (the latent ones only count for rank > 0)
+  const int want = rank > 0 ? 4 : 2;
+  const int ncache = (k_shared != nullptr) + (v_shared != nullptr) + (rank > 0 ? (z_k != nullptr) + (z_v != nullptr) : 0);
+  const bool write_cache = ncache == want;
+  if (ncache != 0 && ncache != want) return LRKV_ERR_NULL;
   if (write_cache && seq_len > capacity) return LRKV_ERR_CAPACITY;
   if (batch == 0 || seq_len == 0) return LRKV_OK;
   if (!q || !k_s || !v_s || !out) return LRKV_ERR_NULL;
@@ -238,14 +240,15 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
   if (!aligned16(q) || !aligned16(k_s) || !aligned16(v_s) || !aligned16(out)) return LRKV_ERR_ALIGN;
   if (rank > 0 && (!aligned16(z_k_new) || !aligned16(z_v_new) || !aligned16(b_k) || !aligned16(b_v)))
     return LRKV_ERR_ALIGN;
-  if (write_cache && (!aligned16(k_shared) || !aligned16(v_shared) || !aligned16(z_k) || !aligned16(z_v)))
+  if (write_cache && (!aligned16(k_shared) || !aligned16(v_shared) ||
+                      (rank > 0 && (!aligned16(z_k) || !aligned16(z_v)))))
     return LRKV_ERR_ALIGN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (write_cache) {
     lrkv::AppendArgs a;
     a.dtype = dtype; a.batch = batch; a.heads = num_heads; a.head_dim = head_dim; a.rank = rank;
     a.capacity = capacity; a.k_s = k_shared; a.v_s = v_shared; a.z_k = z_k; a.z_v = z_v;
-    a.pos = nullptr; a.n_new = seq_len;
+    a.pos = nullptr; a.pos_max = INT32_MAX; a.n_new = seq_len;
     a.new_k_s = k_s; a.new_v_s = v_s; a.new_z_k = z_k_new; a.new_z_v = z_v_new;
     if (lrkv::launch_append(a, s) != hipSuccess) return LRKV_ERR_DEVICE;
   }
@@ -255,6 +258,47 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
   p.q = q; p.k_s = k_s; p.v_s = v_s; p.z_k = z_k_new; p.z_v = z_v_new; p.b_k = b_k; p.b_v = b_v;
   p.scale_log2 = sc * 1.4426950408889634f;
   p.out = out;
+  p.kv_stride = seq_len; p.start = nullptr; p.max_start = 0;
+  return lrkv::launch_prefill(p, s) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+}
+
+lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
+                               int64_t capacity, void* k_shared, void* v_shared, void* z_k, void* z_v,
+                               const int32_t* start_pos, int32_t max_start, int32_t n_new, const void* q,
+                               const void* k_s, const void* v_s, const void* z_k_new, const void* z_v_new,
+                               const void* b_k, const void* b_v, float scale, void* out, void* stream) {
+  const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, capacity);
+  if (st != LRKV_OK) return st;
+  if (!lrkv::prefill_supported(dtype, head_dim, rank, num_heads)) return LRKV_ERR_SHAPE;
+  if (n_new < 0 || max_start < 0) return LRKV_ERR_SHAPE;
+  if (int64_t(max_start) + n_new > capacity) return LRKV_ERR_CAPACITY;
+  // one sequence's keys (history and new tokens) are addressed through 32-bit buffer offsets
+  if ((int64_t(max_start) + n_new) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >=
+      (int64_t(1) << 32))
+    return LRKV_ERR_SHAPE;
+  if (batch == 0 || n_new == 0) return LRKV_OK;
+  if (!k_shared || !v_shared || !start_pos || !q || !k_s || !v_s || !out) return LRKV_ERR_NULL;
+  if (rank > 0 && (!z_k || !z_v || !z_k_new || !z_v_new || !b_k || !b_v)) return LRKV_ERR_NULL;
+  if (!aligned16(k_shared) || !aligned16(v_shared) || !aligned4(start_pos) || !aligned16(q) || !aligned16(k_s) ||
+      !aligned16(v_s) || !aligned16(out))
+    return LRKV_ERR_ALIGN;
+  if (rank > 0 && (!aligned16(z_k) || !aligned16(z_v) || !aligned16(z_k_new) || !aligned16(z_v_new) ||
+                   !aligned16(b_k) || !aligned16(b_v)))
+    return LRKV_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  lrkv::AppendArgs a;
+  a.dtype = dtype; a.batch = batch; a.heads = num_heads; a.head_dim = head_dim; a.rank = rank;
+  a.capacity = capacity; a.k_s = k_shared; a.v_s = v_shared; a.z_k = z_k; a.z_v = z_v;
+  a.pos = start_pos; a.pos_max = max_start; a.n_new = n_new;
+  a.new_k_s = k_s; a.new_v_s = v_s; a.new_z_k = z_k_new; a.new_z_v = z_v_new;
+  if (lrkv::launch_append(a, s) != hipSuccess) return LRKV_ERR_DEVICE;
+  const float sc = (scale > 0.f && std::isfinite(scale)) ? scale : 1.0f / std::sqrt(float(head_dim));
+  lrkv::PrefillArgs p;
+  p.batch = batch; p.heads = num_heads; p.head_dim = head_dim; p.rank = rank; p.seq_len = n_new;
+  p.q = q; p.k_s = k_shared; p.v_s = v_shared; p.z_k = z_k; p.z_v = z_v; p.b_k = b_k; p.b_v = b_v;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.out = out;
+  p.kv_stride = int(capacity); p.start = start_pos; p.max_start = max_start;
   return lrkv::launch_prefill(p, s) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
 }
 

@@ -53,6 +53,7 @@ struct AppendArgs {
   int64_t capacity;
   void* k_s; void* v_s; void* z_k; void* z_v;
   const int32_t* pos;      // device [batch], or NULL: slot 0 for every sequence
+  int pos_max;             // positions are clamped to [0, pos_max] (INT32_MAX: no clamp)
   int n_new;
   const void* new_k_s; const void* new_v_s; const void* new_z_k; const void* new_z_v;
 };
@@ -64,6 +65,9 @@ struct PrefillArgs {
   const void* b_k; const void* b_v;
   float scale_log2;
   void* out;
+  int kv_stride;           // tokens per sequence in k_s/v_s/z_k/z_v (seq_len, or the cache capacity)
+  const int32_t* start;    // device [batch] history lengths, or NULL (no history)
+  int max_start;           // start is clamped to [0, max_start]
 };
 bool prefill_supported(int dtype, int head_dim, int rank, int heads);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

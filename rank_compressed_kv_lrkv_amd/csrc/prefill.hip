@@ -1,9 +1,11 @@
 // LRKV causal prefill on bf16 MFMA (gfx950 v_mfma_f32_32x32x16_bf16).
 //
 // Method (Low-Rank Key Value Attention, slide discussion of arXiv:2601.11471v3):
-// with L fresh tokens, every query row i of head h attends to keys j <= i
+// with L new tokens, every query row i of head h attends to keys j <= i
 // (slide "Compute logits without expanding historical keys", Eq. (6), causal
-// mask) through the absorbed forms
+// mask); with start tokens of history already cached, new token i sits at
+// position start + i and attends to the cached keys j <= start + i.  Both go
+// through the absorbed forms
 //   S = scale * [Q_h | Q_h B^K_h] . [K_s | R^K_h]^T           (inner dim d_h + r)
 //   [O_s | O_z] = softmax(S) . [V_s | R^V_h]
 //   O = O_s + O_z (B^V_h)^T, normalised by the softmax sum   (Eq. (7)).
@@ -76,6 +78,13 @@ struct PrefillKernelParams {
   const uint16_t* b_k; const uint16_t* b_v;
   uint16_t* out;
   int heads, seq_len, n_qblocks, n_hgroups, batch;
+  // Keys and values: rows kv_stride tokens apart per sequence.  Without
+  // history (start == NULL) they are the fresh tokens (kv_stride = seq_len);
+  // with history they are the cache, where new token i of sequence b sits at
+  // slot start[b] + i (start clamped to [0, max_start]).
+  int kv_stride;
+  const int32_t* start;
+  int max_start;
   float scale_log2;
 };
 
@@ -118,11 +127,11 @@ struct PfSources {
 
 template <int DH, int R>
 __device__ __forceinline__ PfSources pf_sources(const uint16_t* rows, const uint16_t* lat, const PrefillKernelParams& p,
-                                                int b) {
-  const size_t L = size_t(p.seq_len);
+                                                int b, int nkeys) {
+  const size_t stride = size_t(p.kv_stride), n = size_t(nkeys);
   PfSources s;
-  s.rows = buffer_resource(rows + size_t(b) * L * DH, uint32_t(L * DH * 2));
-  s.lat = buffer_resource(lat + size_t(b) * L * p.heads * R, uint32_t(L * p.heads * (R > 0 ? R : 1) * 2));
+  s.rows = buffer_resource(rows + size_t(b) * stride * DH, uint32_t(n * DH * 2));
+  s.lat = buffer_resource(lat + size_t(b) * stride * p.heads * R, uint32_t(n * p.heads * (R > 0 ? R : 1) * 2));
   return s;
 }
 
@@ -133,9 +142,9 @@ __device__ __forceinline__ PfSources pf_sources(const uint16_t* rows, const uint
 // softmax).  Each wave issues its share of the 1 KB transfers.
 template <int DH, int R>
 __device__ __forceinline__ void pf_dma(unsigned char* side, const PfSources& src, const PfDmaOffsets<PrefillShape<DH, R>>& d,
-                                       const PrefillKernelParams& p, int hg, int kt, int wave, int lane) {
+                                       const PrefillKernelParams& p, int hg, int kt, int wave, int lane, int L) {
   using P = PrefillShape<DH, R>;
-  const int L = p.seq_len, H = p.heads;
+  const int H = p.heads;
   if (kt * kPfTile + kPfTile <= L) {
 #pragma unroll
     for (int i = 0; i < P::NRW; ++i) {
@@ -235,6 +244,13 @@ void prefill_kernel(PrefillKernelParams p) {
   const int hh = head_ok ? h : H - 1;
   const int q0 = qb * kPfTile;
   const int qrow = min(q0 + n, L - 1);
+  // History: the block's queries sit at positions start + q0 .. and see the
+  // keys up to their own position; nkeys keys in all.
+  int start = p.start ? p.start[b] : 0;
+  start = start < 0 ? 0 : (start > p.max_start ? p.max_start : start);
+  const int qpos0 = start + q0;
+  const int nkeys = start + L;
+  const int kt_last = min(qpos0 + kPfTile - 1, nkeys - 1) / kPfTile;   // last key tile of this block
 
   // Per-lane LDS offsets inside a side (loop-invariant).
   int koff[DH / 16], zoff[P::ZCH];
@@ -332,10 +348,11 @@ void prefill_kernel(PrefillKernelParams p) {
   unsigned char* const kside0 = smem;
   unsigned char* const vside0 = smem + 2 * P::SIDE;
   if (tid < 2) *reinterpret_cast<uint4*>(vside0 + tid * P::SIDE + P::ONES) = make_uint4(0x3F80u, 0u, 0u, 0u);
-  const PfSources ksrc = pf_sources<DH, R>(p.k_s, p.z_k, p, b), vsrc = pf_sources<DH, R>(p.v_s, p.z_v, p, b);
-  pf_dma<DH, R>(kside0, ksrc, dma, p, hg, 0, wave, lane);
-  pf_dma<DH, R>(vside0, vsrc, dma, p, hg, 0, wave, lane);
-  if (qb >= 1) pf_dma<DH, R>(kside0 + P::SIDE, ksrc, dma, p, hg, 1, wave, lane);
+  const PfSources ksrc = pf_sources<DH, R>(p.k_s, p.z_k, p, b, nkeys);
+  const PfSources vsrc = pf_sources<DH, R>(p.v_s, p.z_v, p, b, nkeys);
+  pf_dma<DH, R>(kside0, ksrc, dma, p, hg, 0, wave, lane, nkeys);
+  pf_dma<DH, R>(vside0, vsrc, dma, p, hg, 0, wave, lane, nkeys);
+  if (kt_last >= 1) pf_dma<DH, R>(kside0 + P::SIDE, ksrc, dma, p, hg, 1, wave, lane, nkeys);
   __builtin_amdgcn_s_waitcnt(kVmcntZero);
   __syncthreads();
   f32x16_t s0 = pf_scores<DH, R>(kside0, qop, koff, zoff, half);
@@ -344,7 +361,7 @@ void prefill_kernel(PrefillKernelParams p) {
   // One pipeline step; the two score tiles swap roles every step (the loop
   // is unrolled by two so that no accumulator is copied).
   auto step = [&](const int kt, f32x16_t& s_cur, f32x16_t& s_nxt) __attribute__((always_inline)) {
-    const bool next_k = kt + 2 <= qb, next_v = kt + 1 <= qb;
+    const bool next_k = kt + 2 <= kt_last, next_v = kt + 1 <= kt_last;
     if (next_v) s_nxt = pf_scores<DH, R>(kside0 + ((kt + 1) & 1) * P::SIDE, qop, koff, zoff, half);
 
     // value operands of tile kt: lane (feature n, half) gets tokens
@@ -370,26 +387,22 @@ void prefill_kernel(PrefillKernelParams p) {
     // Refill the buffers read in the previous step.  Issued after this step's
     // LDS reads, which therefore never wait on the transfers; they overlap
     // the softmax and the value MFMAs.
-    if (next_k) pf_dma<DH, R>(kside0 + (kt & 1) * P::SIDE, ksrc, dma, p, hg, kt + 2, wave, lane);
-    if (next_v) pf_dma<DH, R>(vside0 + ((kt + 1) & 1) * P::SIDE, vsrc, dma, p, hg, kt + 1, wave, lane);
+    if (next_k) pf_dma<DH, R>(kside0 + (kt & 1) * P::SIDE, ksrc, dma, p, hg, kt + 2, wave, lane, nkeys);
+    if (next_v) pf_dma<DH, R>(vside0 + ((kt + 1) & 1) * P::SIDE, vsrc, dma, p, hg, kt + 1, wave, lane, nkeys);
 
-    // online softmax (log2 domain) for query q0+n.  Only the diagonal tile and
-    // a tile reaching past the sequence end need the mask.  The running max is
-    // refreshed only when a score exceeds it by more than kPfStale (log2
-    // units): weights then stay <= 2^kPfStale, and since the sum and the
-    // output use the same reference the result is unchanged.
-    // online softmax (log2 domain) for query q0+n.  Only the diagonal tile and
-    // a tile reaching past the sequence end need the mask, applied in place
-    // to the score registers (dead after this step), so both paths leave the
-    // scores where the common code expects them.  The running max is
-    // refreshed only when a score exceeds it by more than kPfStale (log2
-    // units): weights then stay <= 2^kPfStale, and since the sum and the
-    // output use the same reference the result is unchanged.
-    if ((kt == qb) || (kt * kPfTile + kPfTile > L)) {
+    // online softmax (log2 domain) for the query at position qpos0 + n.
+    // Only tiles reaching past the block's first query position (the
+    // diagonal) or past the last key need the mask, applied in place to the
+    // score registers (dead after this step), so both paths leave the scores
+    // where the common code expects them.  The running max is refreshed only
+    // when a score exceeds it by more than kPfStale (log2 units): weights
+    // then stay <= 2^kPfStale, and since the sum and the output use the same
+    // reference the result is unchanged.
+    if (kt * kPfTile + kPfTile - 1 > qpos0 || kt * kPfTile + kPfTile > nkeys) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = kt * kPfTile + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (!(tok <= q0 + n && tok < L)) s_cur[r] = -INFINITY;
+        if (!(tok <= qpos0 + n && tok < nkeys)) s_cur[r] = -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -398,7 +411,7 @@ void prefill_kernel(PrefillKernelParams p) {
     // Lanes n and n+32 share query n and must share m, so the refresh is
     // decided for the whole wave; the common case exchanges nothing.
     if (__builtin_amdgcn_ballot_w64(mx * p.scale_log2 > m + kPfStale)) {
-      const float mn = fmaxf(m, fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2);  // finite: token kt*32 <= q0 + n
+      const float mn = fmaxf(m, fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2);  // finite: key 0 <= qpos0 + n
       const float alpha = fast_exp2(m - mn);               // 0 on the first tile (m = -inf)
       m = mn;
       lsum *= alpha;
@@ -429,9 +442,9 @@ void prefill_kernel(PrefillKernelParams p) {
   f32x16_t s1 = {};
   for (int kt = 0;; kt += 2) {
     step(kt, s0, s1);
-    if (kt + 1 > qb) break;
+    if (kt + 1 > kt_last) break;
     step(kt + 1, s1, s0);
-    if (kt + 2 > qb) break;
+    if (kt + 2 > kt_last) break;
   }
 
   if (!head_ok) return;
@@ -492,6 +505,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   kp.n_hgroups = (a.heads + kPfWaves - 1) / kPfWaves;
   kp.batch = a.batch;
   kp.scale_log2 = a.scale_log2;
+  kp.kv_stride = a.kv_stride;
+  kp.start = a.start;
+  kp.max_start = a.max_start;
   const long long blocks = (long long)kp.n_qblocks * kp.n_hgroups * a.batch;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid{static_cast<unsigned>(blocks)};

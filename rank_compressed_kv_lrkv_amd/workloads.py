@@ -167,3 +167,38 @@ def append_inputs(B: int, n: int, H: int, d_h: int, r: int, dtype: str, seed: in
     z_v = rng.standard_normal((B, n, H, r), dtype=np.float32)
     return dict(k_s=_store(k_s, dtype), v_s=_store(v_s, dtype), z_k=_store(z_k, dtype),
                 z_v=_store(z_v, dtype), dtype=dtype)
+
+
+SENTINEL = 30.0      # cache slots outside a sequence's history: never to be read as keys
+
+
+def chunk_inputs(*, batch: int, heads: int, head_dim: int, rank: int, capacity: int, starts, n_new: int,
+                 seed: int, dtype: str = "bf16") -> dict:
+    """A cache with starts[b] tokens of history per sequence (N(0,1) rows and
+    latents; every other slot holds SENTINEL) and n_new new tokens per
+    sequence drawn like a prefill workload (q, rows, latents N(0,1),
+    B ~ N(0, 1/r)).  Returns the history cache under ``cache_*`` and the new
+    tokens, queries and weights under the prefill names."""
+    starts = np.asarray(starts, dtype=np.int32)
+    assert starts.shape == (batch,) and int(starts.max(initial=0)) + n_new <= capacity
+    rng = np.random.default_rng(seed)
+    B, H, d_h, r, T = batch, heads, head_dim, rank, capacity
+    cache = {
+        "cache_k_s": np.full((B, T, d_h), SENTINEL, np.float32),
+        "cache_v_s": np.full((B, T, d_h), SENTINEL, np.float32),
+        "cache_z_k": np.full((B, T, H, r), SENTINEL, np.float32),
+        "cache_z_v": np.full((B, T, H, r), SENTINEL, np.float32),
+    }
+    for b in range(B):
+        s0 = int(starts[b])
+        cache["cache_k_s"][b, :s0] = rng.standard_normal((s0, d_h), dtype=np.float32)
+        cache["cache_v_s"][b, :s0] = rng.standard_normal((s0, d_h), dtype=np.float32)
+        cache["cache_z_k"][b, :s0] = rng.standard_normal((s0, H, r), dtype=np.float32)
+        cache["cache_z_v"][b, :s0] = rng.standard_normal((s0, H, r), dtype=np.float32)
+    new = prefill_inputs(PrefillWorkload("chunk", B, n_new, H, d_h, r, dtype, int(rng.integers(1 << 30))))
+    out = {k: _store(v, dtype) for k, v in cache.items()}
+    out.update(new)
+    out["starts"] = starts
+    out["capacity"] = T
+    return out
+

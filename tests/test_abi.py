@@ -181,3 +181,31 @@ def prefill_call(**over):
 ])
 def test_prefill_rejects_before_launch(kw, want):
     assert prefill_call(**kw) == want
+
+
+def chunk_call(**over):
+    a = dict(dtype=BF16, B=2, H=8, d_h=64, r=8, cap=256, k=FAKE, v=FAKE, zk=FAKE, zv=FAKE, start=FAKE, max_start=100,
+             n=64, q=FAKE, ks=FAKE, vs=FAKE, zkn=FAKE, zvn=FAKE, bk=FAKE, bv=FAKE, scale=0.0, out=FAKE)
+    a.update(over)
+    return L.library().lrkv_prefill_chunk(a["dtype"], a["B"], a["H"], a["d_h"], a["r"], a["cap"], a["k"], a["v"],
+                                          a["zk"], a["zv"], a["start"], a["max_start"], a["n"], a["q"], a["ks"],
+                                          a["vs"], a["zkn"], a["zvn"], a["bk"], a["bv"], a["scale"], a["out"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=F32, r=4), SHAPE),               # bf16 only
+    (dict(d_h=32), SHAPE),                       # outside the prefill envelope
+    (dict(max_start=-1), SHAPE), (dict(n=-1), SHAPE),
+    (dict(max_start=200, n=64), CAP),            # history bound + new tokens past the capacity
+    (dict(k=None), NULL), (dict(start=None), NULL), (dict(q=None), NULL), (dict(bk=None), NULL),
+    (dict(start=FAKE + 2), ALIGN), (dict(zv=MIS), ALIGN), (dict(ks=MIS), ALIGN),
+])
+def test_prefill_chunk_rejects_before_launch(kw, want):
+    assert chunk_call(**kw) == want
+
+
+@no_gpu
+def test_prefill_chunk_empty_is_noop():
+    assert chunk_call(n=0, k=None, q=None, out=None) == OK
+
