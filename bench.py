@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="before the warmup steps, repeat the step (untimed) for this many seconds: "
                          "the GPU takes tens of ms of sustained work to reach its steady clock")
-    ap.add_argument("--mode", choices=("decode", "prefill"), default="decode",
-                    help="decode (the headline line) or the causal-prefill MFMA path")
+    ap.add_argument("--mode", choices=("decode", "prefill", "chunk", "rank-sweep"), default="decode",
+                    help="decode (the headline line); the causal-prefill MFMA path; a prefill chunk over a "
+                         "4096-token history; or decode at ranks 0/8/16/32 on the headline shape")
     ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
@@ -163,6 +164,10 @@ def main():
     L.library()     # fails loudly if the HIP library is missing
     if args.mode == "prefill":
         return bench_prefill(args)
+    if args.mode == "chunk":
+        return bench_chunk(args)
+    if args.mode == "rank-sweep":
+        return bench_rank_sweep(args)
     wl = DECODE_WORKLOADS[args.workload or "mid_bf16_T8k"]
     t_gen = time.perf_counter()
     d = decode_inputs(wl)
@@ -298,6 +303,94 @@ def bench_prefill(args):
     }
     copy_reference(args, rec)
     print(json.dumps(rec), flush=True)
+
+
+def bench_chunk(args):
+    """A prefill chunk over cached history: 4 sequences with 4096 cached
+    tokens each take 512 new tokens (H=32, d_h=128, r=16); a step is one
+    lrkv_prefill_chunk call (cache write + attention over 4096 + i + 1 keys)."""
+    import torch
+    import rank_compressed_kv_lrkv_amd as L
+    from rank_compressed_kv_lrkv_amd.workloads import chunk_inputs
+
+    B, H, d_h, r, hist, n = 4, 32, 128, 16, 4096, 512
+    d = chunk_inputs(batch=B, heads=H, head_dim=d_h, rank=r, capacity=hist + n, starts=[hist] * B, n_new=n,
+                     seed=20261207)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    cache = L.LrkvCache(*(dev(d["cache_" + k]) for k in ("k_s", "v_s", "z_k", "z_v")))
+    t = {k: dev(d[k]) for k in ("q", "k_s", "v_s", "z_k", "z_v", "b_k", "b_v")}
+    start = torch.full((B,), hist, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(t["q"])
+
+    def step():
+        L.lrkv_prefill_chunk(cache, start, hist, t["q"], t["k_s"], t["v_s"], t["z_k"], t["z_v"], t["b_k"], t["b_v"],
+                             out=out)
+
+    settled = settle(step, args.settle_s)
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    step_ms = timed(stream, args.steps, step)
+    pairs = B * H * (n * hist + n * (n + 1) // 2)             # (query, key) pairs under the shifted causal mask
+    flops = pairs * 4 * (d_h + r) + B * H * n * 4 * d_h * r
+    tflops = flops / (step_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "prefill chunk over a cached history: new tokens/s and TFLOP/s",
+        "value": B * n / (step_ms * 1e-3), "unit": "new tokens/s (cache written)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle": {"seconds": args.settle_s, "steps": settled}, "ms_per_step": step_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) history, queries, rows and latents; B ~ N(0, 1/r))",
+        "config": {"workload": "chunk_bf16_hist4k_new512", "batch": B, "history": hist, "new_tokens": n,
+                   "heads": H, "head_dim": d_h, "rank": r},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "append_kernel + prefill_kernel", "algorithmic_flops_per_launch": flops},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_rank_sweep(args):
+    """Decode on the headline shape (32 sequences x 8192 tokens, H=32, d_h=128)
+    at ranks 0 (the MQA cache), 8, 16 and 32: cache elements per token
+    2(d_h + H r) and the measured step, to show how the cache ratio turns
+    into time.  One JSON line per rank."""
+    import torch
+    import rank_compressed_kv_lrkv_amd as L
+    from rank_compressed_kv_lrkv_amd.workloads import DecodeWorkload, decode_inputs
+
+    for r in (0, 8, 16, 32):
+        wl = DecodeWorkload(f"mid_bf16_T8k_r{r}", 32, 32, 128, r, 8192, "bf16", 20261204)
+        d = decode_inputs(wl)
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+        cache = L.LrkvCache(dev(d["k_s"]), dev(d["v_s"]), dev(d["z_k"]), dev(d["z_v"]))
+        q, b_k, b_v = dev(d["q"]), dev(d["b_k"]), dev(d["b_v"])
+        lens = torch.from_numpy(np.asarray(d["seq_lens"], np.int32)).cuda()
+        call = L.DecodeCall(cache, lens, 8192, q, b_k, b_v)
+        settle(call.both, args.settle_s)
+        for _ in range(args.warmup):
+            call.both()
+        stream = torch.cuda.current_stream()
+        step_ms = timed(stream, args.steps, call.both)
+        scan_ms = timed(stream, args.steps, call.partial)
+        elems = L.lrkv_cache_elems_per_token(32, 128, r)
+        cache_bytes = 32 * 8192 * elems * 2
+        print(json.dumps({
+            "metric": "decode step vs rank", "workload": wl.name, "rank": r, "cache_elems_per_token": elems,
+            "cache_ratio_vs_mha": elems / (2 * 32 * 128), "cache_MB": cache_bytes / 1e6,
+            "scan_kernel": L.lrkv_decode_scan_kernel(torch.bfloat16, 32, 128, r),
+            "ms_per_step": step_ms, "scan_ms": scan_ms,
+            "cache_tokens_per_s": 32 * 8192 / (step_ms * 1e-3),
+            "scan_hbm_frac": cache_bytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        }), flush=True)
+        del cache, q, b_k, b_v, call
+        torch.cuda.empty_cache()
 
 
 def cpu_baseline(d, out_dev, budget_s, as_f64):
