@@ -18,8 +18,8 @@
 // the split-K merge.
 //
 // Work decomposition.  A workgroup is 4 wave64 over one sequence, one group
-// of 32 heads and one split of the context; each wave scans its own quarter
-// of the split in 32-token tiles, and at the end the four waves' states are
+// of 32 heads and one split of the context; the split's 32-token tiles are
+// dealt to the four waves round-robin, and at the end the four waves' states are
 // folded in LDS into the workgroup's partial state (m, l, sum p v_s,
 // sum p z^V) for the split-K merge.  Lane l owns head l%32 of the group and,
 // in every tile, the 16 tokens 8(i/4) + 4(l/32) + i%4 (i = 0..15) of the
@@ -166,33 +166,36 @@ void decode_mfma_kernel(MfParams p) {
   lo = __builtin_amdgcn_readfirstlane(lo);
   hi = __builtin_amdgcn_readfirstlane(hi);
   item = __builtin_amdgcn_readfirstlane(item);
-  const int share = ((hi - lo + kMfWaves - 1) / kMfWaves + kMfTile - 1) / kMfTile * kMfTile;
-  const int tw0 = lo + wave * share;
-  const int ntok = max(0, min(tw0 + share, hi) - tw0);      // this wave's tokens [tw0, tw0 + ntok)
-  const int ntiles = (ntok + kMfTile - 1) / kMfTile;
+  // The item's 32-token tiles are dealt to the four waves round-robin (wave
+  // w takes tiles w, w+4, ...), so that the workgroup streams one contiguous
+  // run of the cache.
+  const int nwg = hi - lo;                                  // the item's tokens [lo, hi)
+  const int ntile_wg = (nwg + kMfTile - 1) / kMfTile;
+  const int ntiles = ntile_wg > wave ? (ntile_wg - wave + kMfWaves - 1) / kMfWaves : 0;   // this wave's
+  auto gtile = [&](int kt) { return wave + kMfWaves * kt; };   // item tile of this wave's kt-th tile
 
-  // Resources over this wave's tokens (the host keeps them below 4 GiB).
-  const size_t row0 = size_t(b) * size_t(p.capacity) + size_t(tw0);
+  // Resources over the item's tokens (the host keeps them below 4 GiB).
+  const size_t row0 = size_t(b) * size_t(p.capacity) + size_t(lo);
   const uint32_t ztok = uint32_t(H) * S::ZB;                // latent bytes per token
   const __amdgpu_buffer_rsrc_t kres =
-      buffer_resource(static_cast<const unsigned char*>(p.k_s) + row0 * S::RB, uint32_t(ntok) * S::RB);
+      buffer_resource(static_cast<const unsigned char*>(p.k_s) + row0 * S::RB, uint32_t(nwg) * S::RB);
   const __amdgpu_buffer_rsrc_t vres =
-      buffer_resource(static_cast<const unsigned char*>(p.v_s) + row0 * S::RB, uint32_t(ntok) * S::RB);
+      buffer_resource(static_cast<const unsigned char*>(p.v_s) + row0 * S::RB, uint32_t(nwg) * S::RB);
   const __amdgpu_buffer_rsrc_t zkres =
-      buffer_resource(static_cast<const unsigned char*>(p.z_k) + row0 * ztok, uint32_t(ntok) * ztok);
+      buffer_resource(static_cast<const unsigned char*>(p.z_k) + row0 * ztok, uint32_t(nwg) * ztok);
   const __amdgpu_buffer_rsrc_t zvres =
-      buffer_resource(static_cast<const unsigned char*>(p.z_v) + row0 * ztok, uint32_t(ntok) * ztok);
+      buffer_resource(static_cast<const unsigned char*>(p.z_v) + row0 * ztok, uint32_t(nwg) * ztok);
 
   unsigned char* const ktile = smem + wave * 2 * S::VT;    // this wave's key tile
   unsigned char* const vtile = ktile + S::VT;               // and value tile
 
-  // Shared-row tile transfer: transfer x carries LDS bytes [1024x, 1024x +
-  // 1024) of a tile, lane i the chunk at position pos of row rw, i.e. source
-  // chunk pos ^ lds_swz(rw).  Rows at or past the wave's last token clamp to
-  // it (a partial last tile; the tile after the last one, which is
+  // Shared-row tile transfer (tile = item tile index): transfer x carries
+  // LDS bytes [1024x, 1024x + 1024) of a tile, lane i the chunk at position
+  // pos of row rw, i.e. source chunk pos ^ lds_swz(rw).  Rows at or past the
+  // item's last token clamp to it (a partial last tile; a tile past the end,
   // transferred but never read, re-reads that row).
   auto row_dma = [&](__amdgpu_buffer_rsrc_t res, int tile, unsigned char* dst) {
-    const int last = ntok - 1 - tile * kMfTile;             // >= -32
+    const int last = nwg - 1 - tile * kMfTile;
     const int base = tile * kMfTile;
 #pragma unroll
     for (int x = 0; x < S::NT; ++x) {
@@ -231,7 +234,7 @@ void decode_mfma_kernel(MfParams p) {
   // for an earlier batch never drains a later one: (1) the query operand and
   // the inputs of the absorbed query; (2) the first transfers (key tile 0,
   // value tile 0, latent groups 0..D-1), unconditional like every load here
-  // (a wave without tokens reads nothing: its resources are empty); (3) the
+  // (a wave without tiles reads zeros, or the item's last row); (3) the
   // absorbed query q~_h = B^K_h^T q_h for the group's 32 heads (Eq. (6)),
   // 8 lanes per head, formed while (2) is in flight and shared through LDS. ----
   bf16x8_t qop[S::KC];                                       // B operand: q_h dims 16c + 8hf .. +7
@@ -252,10 +255,10 @@ void decode_mfma_kernel(MfParams p) {
     for (int dd = 0; dd < DPL; ++dd) load_words<R * 2>(bkw[dd], bk + size_t(dd) * R);
   }
   __builtin_amdgcn_sched_barrier(0);
-  row_dma(kres, 0, ktile);
-  row_dma(vres, 0, vtile);
+  row_dma(kres, gtile(0), ktile);
+  row_dma(vres, gtile(0), vtile);
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    (z_load(std::integral_constant<int, I>{}, I, 0), ...);
+    (z_load(std::integral_constant<int, I>{}, I, gtile(0)), ...);
   }(std::make_integer_sequence<int, S::D>{});
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (R > 0) {
@@ -336,7 +339,7 @@ void decode_mfma_kernel(MfParams p) {
     }
     __builtin_amdgcn_s_waitcnt(kLgkmZero);                    // key reads done before the refill
     __builtin_amdgcn_sched_barrier(0);
-    row_dma(kres, kt + 1, ktile);
+    row_dma(kres, gtile(kt + 1), ktile);
     __builtin_amdgcn_sched_barrier(0);
 
     // -- latent scores: s += q~_h . z^K_{t,h}; ring positions 0..NG-1.  Each
@@ -357,7 +360,7 @@ void decode_mfma_kernel(MfParams p) {
             s[a * S::KG + t] += sum_halves(pa, pb);
           }
           __builtin_amdgcn_sched_barrier(0);
-          z_load(std::integral_constant<int, slot>{}, a + S::D, kt);   // a + D < 2NG: same tile
+          z_load(std::integral_constant<int, slot>{}, a + S::D, gtile(kt));   // a + D < 2NG: same tile
           __builtin_amdgcn_sched_barrier(0);
         }(), ...);
       }(std::make_integer_sequence<int, S::NG>{});
@@ -366,10 +369,10 @@ void decode_mfma_kernel(MfParams p) {
     // -- online softmax (log2 domain).  Only a partial last tile is masked.
     //    Lanes l and l^32 hold the same head and must share m, so the refresh
     //    is decided for the whole wave; the common case exchanges nothing. --
-    if ((kt + 1) * kMfTile > ntok) {
+    if ((gtile(kt) + 1) * kMfTile > nwg) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (kt * kMfTile + acc_row(i, hf) >= ntok) s[i] = -INFINITY;
+        if (gtile(kt) * kMfTile + acc_row(i, hf) >= nwg) s[i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -415,7 +418,7 @@ void decode_mfma_kernel(MfParams p) {
     }
     __builtin_amdgcn_s_waitcnt(kLgkmZero);                    // value reads done before the refill
     __builtin_amdgcn_sched_barrier(0);
-    row_dma(vres, kt + 1, vtile);
+    row_dma(vres, gtile(kt + 1), vtile);
     __builtin_amdgcn_sched_barrier(0);
 
     // -- latent values: acc_z += sum_t p_t z^V_{t,h} over all 32 tokens of the
@@ -449,9 +452,9 @@ void decode_mfma_kernel(MfParams p) {
           __builtin_amdgcn_sched_barrier(0);
           constexpr int nxt = pos + S::D;                      // next position for this slot
           if constexpr (nxt < 2 * S::NG) {
-            z_load(std::integral_constant<int, slot>{}, nxt, kt);
+            z_load(std::integral_constant<int, slot>{}, nxt, gtile(kt));
           } else {
-            z_load(std::integral_constant<int, slot>{}, nxt - 2 * S::NG, kt + 1);
+            z_load(std::integral_constant<int, slot>{}, nxt - 2 * S::NG, gtile(kt + 1));
           }
           __builtin_amdgcn_sched_barrier(0);
         }(), ...);

@@ -92,7 +92,10 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
     return LRKV_ERR_SHAPE;
   pl->split_tokens = split;
   if (pl->balanced) {
-    pl->n_splits = max_len > 0 ? pl->bal_cap + batch : 0;
+    // the partition makes at most max(cap, non-empty sequences) items: no
+    // workgroup beyond those (one more round of empty workgroups would trail
+    // the scan)
+    pl->n_splits = max_len > 0 ? std::max(pl->bal_cap, int(batch)) : 0;
     pl->partials = pl->n_splits;
   } else {
     pl->n_splits = int((max_len + split - 1) / split);

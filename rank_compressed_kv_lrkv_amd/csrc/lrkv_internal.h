@@ -22,7 +22,7 @@ struct DecodePlan {
   int partials;       // n_splits * slots partial states per (sequence, head)
   bool mfma;          // scan on the MFMA kernel (one partial state per workgroup: slots = 1)
   bool balanced;      // length-balanced items computed on the device (MFMA scan, default split):
-                      // n_splits = partials = bal_cap + batch items, state index item * heads + h
+                      // n_splits = partials = max(bal_cap, batch) items, state index item * heads + h
   int bal_cap;        // items the partition aims for (resident scan workgroups)
   size_t ws_ml_bytes, ws_acc_bytes, ws_meta_bytes;
 };
