@@ -47,7 +47,7 @@ import numpy as np
 __all__ = [
     "cache_elems_per_token", "cache_ratio_vs_mha", "kv_param_count",
     "head_projections", "cache_from_inputs", "implied_kv", "softmax_attention",
-    "decode", "prefill", "prefill_with_past", "decode_from_weights", "append",
+    "decode", "prefill", "prefill_with_past", "decode_from_weights", "append", "projected_rows",
 ]
 
 
@@ -117,6 +117,24 @@ def cache_from_inputs(X: np.ndarray, W_shared: np.ndarray, U: np.ndarray):
     shared = X @ np.asarray(W_shared, np.float64)
     latents = np.stack([X @ np.asarray(U[h], np.float64) for h in range(U.shape[0])], axis=1)
     return shared, latents
+
+
+def projected_rows(X, Wk_shared, Wv_shared, Uk, Uv) -> dict:
+    """Cache rows of new tokens computed from their inputs X [B, n, d]: for
+    every sequence, the shared key and value features and the per-head key and
+    value latents of cache_from_inputs (Eqs. (4)-(5)), with the key weights
+    W^K_shared, U^K_h and the value weights W^V_shared, U^V_h.  Returns the
+    dict append() takes: k_s, v_s [B, n, d_h]; z_k, z_v [B, n, H, r]."""
+    X = np.asarray(X, np.float64)
+    rows = {"k_s": [], "v_s": [], "z_k": [], "z_v": []}
+    for b in range(X.shape[0]):
+        k_s, z_k = cache_from_inputs(X[b], Wk_shared, Uk)
+        v_s, z_v = cache_from_inputs(X[b], Wv_shared, Uv)
+        rows["k_s"].append(k_s)
+        rows["v_s"].append(v_s)
+        rows["z_k"].append(z_k)
+        rows["z_v"].append(z_v)
+    return {key: np.stack(val) for key, val in rows.items()}
 
 
 # ---------------------------------------------------------------------------

@@ -410,6 +410,61 @@ def pin_append_slots(O):
     assert per_tok == O.cache_elems_per_token("lrkv", H=H, d_h=d_h, r=r)
 
 
+def _rand_projection(seed, d=5, H=2, d_h=4, r=2):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((d, d_h)), rng.standard_normal((d, d_h)),
+            rng.standard_normal((H, d, r)), rng.standard_normal((H, d, r)))
+
+
+def pin_projected_rows_brute_force(O):
+    # Every cached element of a new token is one exactly rounded dot product of
+    # its input row with one weight column (slide "Cache shared features and
+    # compact per-head latents", Eqs. (4)-(5)), in the cache's [B, n, H, r] order.
+    rng = np.random.default_rng(11)
+    B, n, d, H, d_h, r = 2, 3, 5, 2, 4, 3
+    Wk, Wv, Uk, Uv = _rand_projection(12, d, H, d_h, r)
+    X = rng.standard_normal((B, n, d))
+    got = O.projected_rows(X, Wk, Wv, Uk, Uv)
+    for b in range(B):
+        for i in range(n):
+            x = X[b, i]
+            for c in range(d_h):
+                assert abs(got["k_s"][b, i, c] - math.fsum(x[k] * Wk[k, c] for k in range(d))) < 1e-13
+                assert abs(got["v_s"][b, i, c] - math.fsum(x[k] * Wv[k, c] for k in range(d))) < 1e-13
+            for h in range(H):
+                for j in range(r):
+                    assert abs(got["z_k"][b, i, h, j] - math.fsum(x[k] * Uk[h, k, j] for k in range(d))) < 1e-13
+                    assert abs(got["z_v"][b, i, h, j] - math.fsum(x[k] * Uv[h, k, j] for k in range(d))) < 1e-13
+
+
+def pin_projected_rows_identity_inputs(O):
+    # Unit input rows pick out weight rows: X = I_d gives back W_shared and,
+    # for head h, U_h (as [d, H, r] in the cache's latent order).
+    d, H, d_h, r = 6, 3, 4, 2
+    Wk, Wv, Uk, Uv = _rand_projection(13, d, H, d_h, r)
+    got = O.projected_rows(np.eye(d)[None], Wk, Wv, Uk, Uv)
+    assert np.array_equal(got["k_s"][0], Wk) and np.array_equal(got["v_s"][0], Wv)
+    assert np.array_equal(got["z_k"][0], np.transpose(Uk, (1, 0, 2)))
+    assert np.array_equal(got["z_v"][0], np.transpose(Uv, (1, 0, 2)))
+
+
+def pin_projected_rows_decode_like_weights(O):
+    # Rows projected from inputs, decoded from the cache, equal attention with
+    # the explicit per-head projections W_h = W_shared + U_h B_h^T (Eqs. (2)-(5)).
+    rng = np.random.default_rng(14)
+    d, H, d_h, r, L = 7, 2, 4, 3, 9
+    Wk, Wv, Uk, Uv = _rand_projection(15, d, H, d_h, r)
+    Bk, Bv = rng.standard_normal((H, d_h, r)), rng.standard_normal((H, d_h, r))
+    X = rng.standard_normal((1, L, d))
+    q = rng.standard_normal((H, d_h))
+    rows = O.projected_rows(X, Wk, Wv, Uk, Uv)
+    got = O.decode(q[None], rows["k_s"], rows["v_s"], rows["z_k"], rows["z_v"], Bk, Bv, [L])[0]
+    WK = np.stack([Wk + Uk[h] @ Bk[h].T for h in range(H)])
+    WV = np.stack([Wv + Uv[h] @ Bv[h].T for h in range(H)])
+    ref = np.stack([_sdpa(q[h][None], X[0] @ WK[h], X[0] @ WV[h], 1.0 / math.sqrt(d_h))[0] for h in range(H)])
+    assert rel_err(got, ref) < 1e-12
+
+
 ALL_PINS = [
     pin_cache_counts_printed, pin_cache_ratios_printed, pin_cache_ratio_boxed_form,
     pin_table12_megabytes, pin_kv_param_count_matches_arrays, pin_decode_mqa_reduction,
@@ -417,5 +472,6 @@ ALL_PINS = [
     pin_weight_level_equals_cache_level, pin_decode_closed_forms, pin_decode_invariances,
     pin_prefill_mqa_causal_sdpa, pin_prefill_mha_causal_sdpa, pin_prefill_rows_are_decodes,
     pin_prefill_with_past_rows_are_decodes, pin_prefill_with_past_mqa_sdpa, pin_chunked_prefill_equals_full,
-    pin_append_slots,
+    pin_append_slots, pin_projected_rows_brute_force, pin_projected_rows_identity_inputs,
+    pin_projected_rows_decode_like_weights,
 ]

@@ -19,6 +19,7 @@ _orig_implied = O.implied_kv
 _orig_softmax = O.softmax_attention
 _orig_decode = O.decode
 _orig_prefill = O.prefill
+_orig_projected = O.projected_rows
 
 
 def _implied(fk=None, fv=None):
@@ -98,6 +99,15 @@ def _count_without_heads(mechanism, *, d_h, H=1, r=0, n_kv=1, layers=1):
 
 _orig_count = O.cache_elems_per_token
 
+
+def _projected(kind):
+    def mutant(X, Wk_shared, Wv_shared, Uk, Uv):
+        if kind == "kv_swapped":
+            return _orig_projected(X, Wv_shared, Wk_shared, Uk, Uv)
+        Uk_shift = np.roll(np.asarray(Uk), 1, axis=0)           # head h takes U of head h - 1
+        return _orig_projected(X, Wk_shared, Wv_shared, Uk_shift, Uv)
+    return mutant
+
 MUTANTS = {
     "lrkv_count_without_heads": ("cache_elems_per_token", _count_without_heads),
     "drop_key_latent": ("implied_kv", _implied(fk=lambda k, z, bk, bv, h: k)),
@@ -116,6 +126,8 @@ MUTANTS = {
     "causal_mask_one_ahead": ("prefill", _prefill_mask(2)),
     "past_ignored": ("prefill_with_past", _past("ignored")),
     "past_mask_excludes_diagonal": ("prefill_with_past", _past("excludes_diagonal")),
+    "projection_kv_swapped": ("projected_rows", _projected("kv_swapped")),
+    "projection_latent_of_previous_head": ("projected_rows", _projected("head_shift")),
 }
 
 
