@@ -44,9 +44,10 @@ def parse():
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="before the warmup steps, repeat the step (untimed) for this many seconds: "
                          "the GPU takes tens of ms of sustained work to reach its steady clock")
-    ap.add_argument("--mode", choices=("decode", "prefill", "chunk", "rank-sweep"), default="decode",
+    ap.add_argument("--mode", choices=("decode", "prefill", "chunk", "rank-sweep", "project"), default="decode",
                     help="decode (the headline line); the causal-prefill MFMA path; a prefill chunk over a "
-                         "4096-token history; or decode at ranks 0/8/16/32 on the headline shape")
+                         "4096-token history; decode at ranks 0/8/16/32 on the headline shape; or the fused "
+                         "projection + append of 4 x 4096 tokens from d = 4096")
     ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
@@ -62,6 +63,7 @@ KERNEL_SOURCES = {
     "decode_mfma_kernel": ("decode_mfma.hip", "lrkv_device.h"),
     "decode_split_kernel": ("decode.hip", "lrkv_device.h"),
     "prefill_kernel": ("prefill.hip", "lrkv_device.h"),
+    "project_append_kernel": ("project.hip", "lrkv_device.h"),
 }
 
 
@@ -168,6 +170,8 @@ def main():
         return bench_chunk(args)
     if args.mode == "rank-sweep":
         return bench_rank_sweep(args)
+    if args.mode == "project":
+        return bench_project(args)
     wl = DECODE_WORKLOADS[args.workload or "mid_bf16_T8k"]
     t_gen = time.perf_counter()
     d = decode_inputs(wl)
@@ -350,6 +354,71 @@ def bench_chunk(args):
                      "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
                      "kernel": "append_kernel + prefill_kernel", "algorithmic_flops_per_launch": flops},
     }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_project(args):
+    """Fused projection + append: the cache rows of 4 sequences x 4096 new
+    tokens computed from hidden states of width d = H d_h = 4096 (H=32,
+    d_h=128, r=16: 1280 outputs per token) and written into the cache; a step
+    is one lrkv_project_append call (one bf16 MFMA GEMM with the cache
+    scatter in its epilogue).  The same call for one token per sequence over
+    32 sequences (a decode step's projection) is timed beside it."""
+    import torch
+    import rank_compressed_kv_lrkv_amd as L
+    from rank_compressed_kv_lrkv_amd.workloads import projection_inputs
+
+    B, n, d, H, d_h, r = 4, 4096, 4096, 32, 128, 16
+    inp = projection_inputs(batch=B, n_new=n, d_model=d, heads=H, head_dim=d_h, rank=r, dtype="bf16",
+                            seed=20261208)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    w = L.lrkv_pack_projection(dev(inp["wk"]), dev(inp["wv"]), dev(inp["uk"]), dev(inp["uv"]))
+    x = dev(inp["x"])
+    cache = L.LrkvCache.empty(B, H, d_h, r, n, dtype=torch.bfloat16, zero=False)
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+
+    def step():
+        L.lrkv_project_append(cache, pos, x, w)
+
+    settled = settle(step, args.settle_s)
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    step_ms = timed(stream, args.steps, step)
+    N = 2 * (d_h + H * r)
+    flops = 2 * B * n * N * d
+    tflops = flops / (step_ms * 1e-3) / 1e12
+    # decode-step shape: 32 sequences, one token each, same weights
+    Bd = 32
+    xd = torch.randn(Bd, 1, d, device="cuda").to(torch.bfloat16)
+    cache_d = L.LrkvCache.empty(Bd, H, d_h, r, 64, dtype=torch.bfloat16, zero=False)
+    pos_d = torch.full((Bd,), 5, dtype=torch.int32, device="cuda")
+    dec = lambda: L.lrkv_project_append(cache_d, pos_d, xd, w)
+    for _ in range(args.warmup):
+        dec()
+    dec_ms = timed(stream, args.steps, dec)
+    dec_bytes = N * d * 2 + Bd * d * 2 + Bd * N * 2
+    rec = {
+        "metric": "fused projection + append: new tokens/s and TFLOP/s",
+        "value": B * n / (step_ms * 1e-3), "unit": "new tokens/s (cache written)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle": {"seconds": args.settle_s, "steps": settled}, "ms_per_step": step_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded hidden states N(0,1), projection weights N(0, 1/d))",
+        "config": {"workload": "project_bf16_B4_L4096_d4096", "batch": B, "new_tokens": n, "d_model": d,
+                   "heads": H, "head_dim": d_h, "rank": r, "outputs_per_token": N},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic_from_profiles("project_counters", "project_append_kernel",
+                                                      "project_bf16_B4_L4096_d4096"),
+                     "kernel": "project_append_kernel", "algorithmic_flops_per_launch": flops},
+        "decode_shape": {"batch": Bd, "new_tokens": 1, "ms": dec_ms, "algorithmic_bytes": dec_bytes,
+                         "GB_per_s": dec_bytes / (dec_ms * 1e-3) / 1e9},
+    }
+    copy_reference(args, rec)
     print(json.dumps(rec), flush=True)
 
 

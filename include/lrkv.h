@@ -219,6 +219,43 @@ lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, 
                                const void* z_k_new, const void* z_v_new,
                                const void* b_k, const void* b_v, float scale, void* out, void* stream);
 
+/* Packs the key/value projection weights into the output-major matrix that
+ * lrkv_project_append reads (slide "LRKV constrains differences between
+ * heads", Eqs. (2)-(3): each head's projection is W_shared + U_h B_h^T, and
+ * the cache keeps only the products with W_shared and U_h).
+ *   wk_shared, wv_shared  [d_model][head_dim];  u_k, u_v [num_heads][d_model][rank].
+ *   w_packed  [2(head_dim + num_heads*rank)][d_model], caller-allocated:
+ *     row n < head_dim is column n of wk_shared, the next head_dim rows the
+ *     columns of wv_shared, row 2 head_dim + h*rank + j column j of u_k[h],
+ *     and the last num_heads*rank rows the same for u_v.
+ * Elements are copied bit-exactly.  Weights change rarely, so this runs once
+ * per weight update, not per step.  Pointers need only element alignment;
+ * u_k and u_v may be NULL when rank == 0. */
+lrkv_status lrkv_pack_projection(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank,
+                                 int32_t d_model, const void* wk_shared, const void* wv_shared,
+                                 const void* u_k, const void* u_v, void* w_packed, void* stream);
+
+/* Fused projection + append: the cache rows of n_new new tokens computed from
+ * their hidden states and written straight into the cache (slide "Cache
+ * shared features and compact per-head latents", Eqs. (4)-(5)): for token i
+ * of sequence b with hidden state x = x[b][i] (width d_model),
+ *   k_s = x W^K_shared,  v_s = x W^V_shared,  z^K_h = x U^K_h,  z^V_h = x U^V_h,
+ * as one product x . w_packed^T (w_packed from lrkv_pack_projection), fp32
+ * accumulation, each result rounded once to dtype and stored at cache slot
+ * pos[b] + i of its array.  Slots outside [0, capacity) are dropped, as in
+ * lrkv_append.
+ *   x    [batch][n_new][d_model];  pos device int32 [batch].
+ * bf16 with head_dim, num_heads*rank and d_model multiples of 32 runs on bf16
+ * MFMA; other shapes and fp32 on vector-ALU fused multiply-adds.  x, w_packed
+ * and the cache pointers must be 16-byte aligned; z_k and z_v may be NULL
+ * when rank == 0.  batch*n_new must be below 2^31 and d_model at most 65536,
+ * else LRKV_ERR_SHAPE. */
+lrkv_status lrkv_project_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                int32_t rank, int64_t capacity,
+                                void* k_shared, void* v_shared, void* z_k, void* z_v,
+                                const int32_t* pos, int32_t n_new, int32_t d_model,
+                                const void* x, const void* w_packed, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

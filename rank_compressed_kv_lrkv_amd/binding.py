@@ -26,7 +26,8 @@ STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DT
 
 EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
-            "lrkv_decode_combine", "lrkv_prefill", "lrkv_prefill_chunk")
+            "lrkv_decode_combine", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
+            "lrkv_project_append")
 
 
 class LrkvError(RuntimeError):
@@ -69,6 +70,11 @@ def library() -> ctypes.CDLL:
         lib.lrkv_prefill_chunk.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                            _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp]
         lib.lrkv_prefill_chunk.restype = _i32
+        lib.lrkv_pack_projection.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
+        lib.lrkv_pack_projection.restype = _i32
+        lib.lrkv_project_append.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                            _vp, _vp, _vp]
+        lib.lrkv_project_append.restype = _i32
         _lib = lib
     return _lib
 
@@ -319,6 +325,40 @@ def lrkv_prefill_chunk(cache: LrkvCache, start_pos: torch.Tensor, max_start: int
                                         0.0 if scale is None else float(scale), _ptr(out, "out", dt), _stream()),
            "lrkv_prefill_chunk")
     return out
+
+
+def lrkv_pack_projection(wk_shared, wv_shared, u_k, u_v, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed projection weight [2(d_h + H r)][d] from W^K_shared, W^V_shared
+    [d][d_h] and U^K, U^V [H][d][r] (see lrkv.h)."""
+    dt = wk_shared.dtype
+    d, d_h = wk_shared.shape
+    H, _, r = u_k.shape
+    _shape(wv_shared, "wv_shared", (d, d_h))
+    _shape(u_k, "u_k", (H, d, r))
+    _shape(u_v, "u_v", (H, d, r))
+    if out is None:
+        out = torch.empty(2 * (d_h + H * r), d, dtype=dt, device=wk_shared.device)
+    _shape(out, "out", (2 * (d_h + H * r), d))
+    _check(library().lrkv_pack_projection(_dtype_code(dt), H, d_h, r, d, _ptr(wk_shared, "wk_shared", dt),
+                                          _ptr(wv_shared, "wv_shared", dt), _ptr(u_k, "u_k", dt),
+                                          _ptr(u_v, "u_v", dt), _ptr(out, "out", dt), _stream()),
+           "lrkv_pack_projection")
+    return out
+
+
+def lrkv_project_append(cache: LrkvCache, pos: torch.Tensor, x: torch.Tensor, w_packed: torch.Tensor) -> None:
+    """Fused projection + append: the cache rows of x [B][n_new][d] computed
+    with the packed weight and written at slots pos[b].. (see lrkv.h)."""
+    dt = cache.dtype
+    B, n_new, d = x.shape
+    if B != cache.batch:
+        raise ValueError("x and cache differ in batch")
+    _shape(w_packed, "w_packed", (2 * (cache.head_dim + cache.heads * cache.rank), d))
+    _shape(pos, "pos", (B,))
+    _check(library().lrkv_project_append(_dtype_code(dt), cache.batch, cache.heads, cache.head_dim, cache.rank,
+                                         cache.capacity, *cache.pointers(), _ptr(pos, "pos", torch.int32), n_new,
+                                         d, _ptr(x, "x", dt), _ptr(w_packed, "w_packed", dt), _stream()),
+           "lrkv_project_append")
 
 
 def default_scale(head_dim: int) -> float:

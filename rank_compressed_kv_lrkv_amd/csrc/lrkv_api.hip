@@ -305,4 +305,47 @@ lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, 
   return lrkv::launch_prefill(p, s) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
 }
 
+lrkv_status lrkv_pack_projection(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank,
+                                 int32_t d_model, const void* wk_shared, const void* wv_shared,
+                                 const void* u_k, const void* u_v, void* w_packed, void* stream) {
+  if (dtype != LRKV_F32 && dtype != LRKV_BF16) return LRKV_ERR_DTYPE;
+  if (num_heads < 1 || head_dim < 1 || rank < 0 || d_model < 0) return LRKV_ERR_SHAPE;
+  if ((int64_t(head_dim) + int64_t(num_heads) * rank) * 2 * std::max(d_model, 1) * elem_bytes(dtype) >=
+      (int64_t(1) << 40))
+    return LRKV_ERR_SHAPE;
+  if (d_model == 0) return LRKV_OK;
+  if (!wk_shared || !wv_shared || !w_packed) return LRKV_ERR_NULL;
+  if (rank > 0 && (!u_k || !u_v)) return LRKV_ERR_NULL;
+  const uintptr_t mask = uintptr_t(elem_bytes(dtype) - 1);
+  for (const void* ptr : {wk_shared, wv_shared, u_k, u_v, static_cast<const void*>(w_packed)})
+    if (reinterpret_cast<uintptr_t>(ptr) & mask) return LRKV_ERR_ALIGN;
+  lrkv::PackArgs a;
+  a.dtype = dtype; a.heads = num_heads; a.head_dim = head_dim; a.rank = rank; a.d_model = d_model;
+  a.wk_shared = wk_shared; a.wv_shared = wv_shared; a.u_k = u_k; a.u_v = u_v; a.w_packed = w_packed;
+  return lrkv::launch_pack_projection(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+}
+
+lrkv_status lrkv_project_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                int32_t rank, int64_t capacity, void* k_shared, void* v_shared, void* z_k,
+                                void* z_v, const int32_t* pos, int32_t n_new, int32_t d_model, const void* x,
+                                const void* w_packed, void* stream) {
+  const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, capacity);
+  if (st != LRKV_OK) return st;
+  if (n_new < 0 || d_model < 1 || d_model > 65536) return LRKV_ERR_SHAPE;
+  if (int64_t(batch) * n_new >= INT32_MAX) return LRKV_ERR_SHAPE;
+  if ((int64_t(head_dim) + int64_t(num_heads) * rank) * 2 >= INT32_MAX) return LRKV_ERR_SHAPE;
+  if (batch == 0 || n_new == 0) return LRKV_OK;
+  if (!k_shared || !v_shared || !pos || !x || !w_packed) return LRKV_ERR_NULL;
+  if (rank > 0 && (!z_k || !z_v)) return LRKV_ERR_NULL;
+  if (!aligned16(k_shared) || !aligned16(v_shared) || !aligned4(pos) || !aligned16(x) || !aligned16(w_packed))
+    return LRKV_ERR_ALIGN;
+  if (rank > 0 && (!aligned16(z_k) || !aligned16(z_v))) return LRKV_ERR_ALIGN;
+  lrkv::ProjectArgs a;
+  a.dtype = dtype; a.batch = batch; a.heads = num_heads; a.head_dim = head_dim; a.rank = rank;
+  a.d_model = d_model; a.n_new = n_new; a.capacity = capacity;
+  a.k_s = k_shared; a.v_s = v_shared; a.z_k = z_k; a.z_v = z_v; a.pos = pos; a.x = x; a.w = w_packed;
+  return lrkv::launch_project_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LRKV_OK
+                                                                                        : LRKV_ERR_DEVICE;
+}
+
 }  // extern "C"

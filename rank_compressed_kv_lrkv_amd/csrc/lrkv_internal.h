@@ -72,4 +72,25 @@ struct PrefillArgs {
 bool prefill_supported(int dtype, int head_dim, int rank, int heads);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+struct ProjectArgs {
+  int dtype, batch, heads, head_dim, rank, d_model, n_new;
+  int64_t capacity;
+  void* k_s; void* v_s; void* z_k; void* z_v;
+  const int32_t* pos;      // device [batch]
+  const void* x;           // [batch][n_new][d_model]
+  const void* w;           // packed projection [2(head_dim + heads*rank)][d_model]
+};
+// Shapes the MFMA projection takes: bf16, head_dim and heads*rank multiples
+// of 32, d_model a multiple of 32 (others run on the vector-ALU kernel).
+bool project_mfma_supported(int dtype, int head_dim, int rank, int heads, int d_model);
+hipError_t launch_project_append(const ProjectArgs& a, hipStream_t stream);
+
+struct PackArgs {
+  int dtype, heads, head_dim, rank, d_model;
+  const void* wk_shared; const void* wv_shared;   // [d_model][head_dim]
+  const void* u_k; const void* u_v;               // [heads][d_model][rank]
+  void* w_packed;                                 // [2(head_dim + heads*rank)][d_model]
+};
+hipError_t launch_pack_projection(const PackArgs& a, hipStream_t stream);
+
 }  // namespace lrkv

@@ -17,6 +17,7 @@ Draw order (fixed, part of the workload definition):
   decode : lengths (ragged workloads only), q, then per sequence b in order
            K_s[b,:len], V_s[b,:len], Z^K[b,:len], Z^V[b,:len]; then B^K, B^V.
   prefill: Q, K_s, V_s, Z^K, Z^V, B^K, B^V.
+  projection: X, W^K_shared, W^V_shared, U^K, U^V.
 Cache slots at or beyond a sequence's length are zero.
 """
 from __future__ import annotations
@@ -29,7 +30,7 @@ import numpy as np
 __all__ = [
     "DecodeWorkload", "PrefillWorkload", "DECODE_WORKLOADS", "PREFILL_WORKLOADS",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "decode_inputs", "prefill_inputs",
-    "append_inputs", "as_f64",
+    "append_inputs", "as_f64", "projection_inputs",
 ]
 
 
@@ -202,3 +203,21 @@ def chunk_inputs(*, batch: int, heads: int, head_dim: int, rank: int, capacity: 
     out["capacity"] = T
     return out
 
+
+
+def projection_inputs(*, batch: int, n_new: int, d_model: int, heads: int, head_dim: int, rank: int,
+                      dtype: str, seed: int) -> dict:
+    """Inputs of the fused projection + append: hidden states X [B, n, d] ~ N(0, 1)
+    and the key/value projection weights W^K_shared, W^V_shared [d, d_h] and
+    U^K, U^V [H, d, r] ~ N(0, 1/d), so every projected feature has unit
+    variance, like the cache rows of the decode workloads."""
+    rng = np.random.default_rng(seed)
+    B, n, d, H, d_h, r = batch, n_new, d_model, heads, head_dim, rank
+    w_std = np.float32(1.0 / np.sqrt(d))
+    x = rng.standard_normal((B, n, d), dtype=np.float32)
+    wk = rng.standard_normal((d, d_h), dtype=np.float32) * w_std
+    wv = rng.standard_normal((d, d_h), dtype=np.float32) * w_std
+    uk = rng.standard_normal((H, d, r), dtype=np.float32) * w_std
+    uv = rng.standard_normal((H, d, r), dtype=np.float32) * w_std
+    return dict(x=_store(x, dtype), wk=_store(wk, dtype), wv=_store(wv, dtype), uk=_store(uk, dtype),
+                uv=_store(uv, dtype), dtype=dtype, heads=H, head_dim=d_h, rank=r, d_model=d)

@@ -209,3 +209,50 @@ def test_prefill_chunk_rejects_before_launch(kw, want):
 def test_prefill_chunk_empty_is_noop():
     assert chunk_call(n=0, k=None, q=None, out=None) == OK
 
+
+
+def project_call(**over):
+    a = dict(dtype=BF16, B=2, H=8, d_h=64, r=8, cap=256, k=FAKE, v=FAKE, zk=FAKE, zv=FAKE, pos=FAKE, n=16, d=512,
+             x=FAKE, w=FAKE)
+    a.update(over)
+    return L.library().lrkv_project_append(a["dtype"], a["B"], a["H"], a["d_h"], a["r"], a["cap"], a["k"], a["v"],
+                                           a["zk"], a["zv"], a["pos"], a["n"], a["d"], a["x"], a["w"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=7), DTYPE), (dict(n=-1), SHAPE), (dict(d=0), SHAPE), (dict(d=65537), SHAPE),
+    (dict(d_h=20), SHAPE), (dict(cap=0), SHAPE),
+    (dict(x=None), NULL), (dict(w=None), NULL), (dict(pos=None), NULL), (dict(zv=None), NULL),
+    (dict(x=MIS), ALIGN), (dict(w=MIS), ALIGN), (dict(pos=FAKE + 2), ALIGN), (dict(zk=MIS), ALIGN),
+])
+def test_project_append_rejects_before_launch(kw, want):
+    assert project_call(**kw) == want
+
+
+@no_gpu
+def test_project_append_empty_is_noop():
+    assert project_call(n=0, x=None, k=None, pos=None) == OK
+    assert project_call(B=0, x=None, w=None) == OK
+
+
+def pack_call(**over):
+    a = dict(dtype=BF16, H=8, d_h=64, r=8, d=512, wk=FAKE, wv=FAKE, uk=FAKE, uv=FAKE, out=FAKE)
+    a.update(over)
+    return L.library().lrkv_pack_projection(a["dtype"], a["H"], a["d_h"], a["r"], a["d"], a["wk"], a["wv"],
+                                            a["uk"], a["uv"], a["out"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=2), DTYPE), (dict(H=0), SHAPE), (dict(r=-1), SHAPE), (dict(d=-1), SHAPE),
+    (dict(wk=None), NULL), (dict(out=None), NULL), (dict(uk=None), NULL),
+    (dict(wv=FAKE + 1), ALIGN), (dict(dtype=F32, out=FAKE + 2), ALIGN),
+])
+def test_pack_projection_rejects_before_launch(kw, want):
+    assert pack_call(**kw) == want
+
+
+@no_gpu
+def test_pack_projection_empty_is_noop():
+    assert pack_call(d=0, wk=None, out=None) == OK

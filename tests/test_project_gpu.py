@@ -1,0 +1,181 @@
+"""lrkv_pack_projection and lrkv_project_append (HIP, through the C ABI)
+against the float64 oracle: the cache rows of new tokens computed from their
+inputs (Eqs. (4)-(5)) land in their slots within the dtype's tolerance; every
+other slot keeps its bits; rows outside the cache are dropped."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import rank_compressed_kv_lrkv_amd as L
+from rank_compressed_kv_lrkv_amd.workloads import SENTINEL, _store, as_f64, projection_inputs
+from tests.gpu_util import TOL, TORCH_DT, err_ratio, from_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("k_s", "v_s", "z_k", "z_v")
+
+
+def bits(t):
+    return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu().numpy()
+
+
+def canary_cache(B, T, H, d_h, r, dt):
+    tdt = TORCH_DT[dt]
+    full = lambda *shape: torch.full(shape, SENTINEL, dtype=tdt, device="cuda")
+    return L.LrkvCache(full(B, T, d_h), full(B, T, d_h), full(B, T, H, r), full(B, T, H, r))
+
+
+def packed_weight(inp):
+    dt = inp["dtype"]
+    return L.lrkv_pack_projection(*(to_dev(inp[k], dt) for k in ("wk", "wv", "uk", "uv")))
+
+
+def oracle_rows(inp):
+    dt = inp["dtype"]
+    return O.projected_rows(*(as_f64(inp[k], dt) for k in ("x", "wk", "wv", "uk", "uv")))
+
+
+def check_cache(cache, rows, pos, dt, T):
+    """Written slots against the oracle rows; every other slot bit-identical to the canary."""
+    canary = bits(torch.full((1,), SENTINEL, dtype=TORCH_DT[dt]))[0]
+    worst = 0.0
+    for key in KEYS:
+        got_t = getattr(cache, key)
+        got = from_dev(got_t)
+        got_bits = bits(got_t)
+        want = rows[key]
+        B, n = want.shape[0], want.shape[1]
+        written = np.zeros(got.shape[:2], bool)
+        for b in range(B):
+            for i in range(n):
+                slot = int(pos[b]) + i
+                if 0 <= slot < T:
+                    written[b, slot] = True
+        assert np.all(got_bits[~written] == canary), f"{key}: a slot outside the new rows changed"
+        if not written.any():
+            continue
+        gs, ws = [], []
+        for b in range(B):
+            for i in range(n):
+                slot = int(pos[b]) + i
+                if 0 <= slot < T:
+                    gs.append(got[b, slot])
+                    ws.append(want[b, i])
+        if want[0, 0].size == 0:
+            continue
+        g, w = np.stack(gs), np.stack(ws)
+        e = err_ratio(g, w)
+        worst = max(worst, e)
+        assert e <= TOL[dt], f"{key}: max|err|/max|want| = {e:.3e}"
+        if dt == "bf16":
+            # one rounding of each fp32 sum to bf16 (relative 2^-8 at most) plus fp32 accumulation
+            bound = np.abs(w) * 2.0 ** -8 + 1e-3 * np.max(np.abs(w))
+            assert np.all(np.abs(g - w) <= bound), f"{key}: beyond one bf16 rounding"
+    return worst
+
+
+def run_case(dt, B, n, d, H, d_h, r, T, pos, seed):
+    say(f"case project {dt} B={B} n={n} d={d} H={H} d_h={d_h} r={r} T={T} pos={list(pos)}")
+    inp = projection_inputs(batch=B, n_new=n, d_model=d, heads=H, head_dim=d_h, rank=r, dtype=dt, seed=seed)
+    w = packed_weight(inp)
+    cache = canary_cache(B, T, H, d_h, r, dt)
+    L.lrkv_project_append(cache, torch.tensor(np.asarray(pos, np.int32)).cuda(), to_dev(inp["x"], dt), w)
+    torch.cuda.synchronize()
+    return check_cache(cache, oracle_rows(inp), pos, dt, T)
+
+
+@pytest.mark.parametrize("dt,B,n,d,H,d_h,r", [
+    ("bf16", 3, 37, 160, 4, 64, 8),       # MFMA: 111 rows (ragged row tile), 192 outputs (half a column block)
+    ("bf16", 2, 130, 4096, 32, 128, 16),  # the bf16 model shape: 260 rows, 1280 outputs, d = 4096
+    ("bf16", 2, 50, 256, 8, 128, 32),     # rank 32
+    ("bf16", 3, 21, 128, 8, 64, 0),       # rank 0 (MQA rows only)
+    ("bf16", 2, 33, 72, 3, 40, 8),        # vector-ALU path (widths not multiples of 32)
+    ("f32", 1, 64, 64, 4, 16, 4),         # the tiny fp32 shape, d = H d_h = 64
+    ("f32", 2, 45, 200, 4, 32, 8),        # fp32, ragged contraction
+])
+def test_project_append_parity(dt, B, n, d, H, d_h, r):
+    T = n + 11
+    pos = [(5 * b) % 12 for b in range(B)]
+    run_case(dt, B, n, d, H, d_h, r, T, pos, seed=1000 + d + n)
+
+
+def test_project_append_decode_shape():
+    # one new token per sequence over the bf16 model shape (a decode step's projection)
+    run_case("bf16", 32, 1, 4096, 32, 128, 16, 40, [(7 * b) % 40 for b in range(32)], seed=77)
+
+
+def test_project_append_drops_rows_outside_cache():
+    T = 20
+    run_case("bf16", 3, 9, 96, 4, 32, 8, T, [T - 4, -5, 3], seed=5)
+    run_case("f32", 2, 6, 32, 2, 16, 4, T, [T - 2, -3], seed=6)
+
+
+def test_project_append_empty_is_noop():
+    say("case project empty")
+    dt, B, H, d_h, r, T, d = "bf16", 2, 4, 32, 8, 8, 64
+    cache = canary_cache(B, T, H, d_h, r, dt)
+    before = [bits(getattr(cache, k)).copy() for k in KEYS]
+    w = torch.zeros(2 * (d_h + H * r), d, dtype=torch.bfloat16, device="cuda")
+    L.lrkv_project_append(cache, torch.zeros(B, dtype=torch.int32, device="cuda"),
+                          torch.zeros(B, 0, d, dtype=torch.bfloat16, device="cuda"), w)
+    torch.cuda.synchronize()
+    assert all(np.array_equal(bits(getattr(cache, k)), b0) for k, b0 in zip(KEYS, before))
+
+
+@pytest.mark.parametrize("dt,H,d_h,r,d", [("bf16", 32, 128, 16, 4096), ("f32", 3, 8, 5, 37), ("bf16", 4, 64, 0, 96)])
+def test_pack_projection_layout(dt, H, d_h, r, d):
+    say(f"case pack {dt} H={H} d_h={d_h} r={r} d={d}")
+    inp = projection_inputs(batch=1, n_new=1, d_model=d, heads=H, head_dim=d_h, rank=r, dtype=dt, seed=9)
+    got = bits(packed_weight(inp))
+    sdt = np.int16 if dt == "bf16" else np.int32
+    view = lambda a: np.ascontiguousarray(a).view(sdt)
+    want = np.concatenate([view(inp["wk"]).T, view(inp["wv"]).T,
+                           np.transpose(view(inp["uk"]), (0, 2, 1)).reshape(H * r, d),
+                           np.transpose(view(inp["uv"]), (0, 2, 1)).reshape(H * r, d)], axis=0)
+    assert np.array_equal(got, want)
+
+
+def test_project_then_decode_matches_weight_level_oracle():
+    # inputs -> cache (fused projection) -> decode, against attention with the explicit
+    # per-head projections W_h = W_shared + U_h B_h^T (slide "LRKV constrains
+    # differences between heads", Eqs. (2)-(3))
+    dt, B, n, d, H, d_h, r = "bf16", 2, 96, 256, 32, 128, 16
+    say("case project then decode")
+    inp = projection_inputs(batch=B, n_new=n, d_model=d, heads=H, head_dim=d_h, rank=r, dtype=dt, seed=31)
+    rng = np.random.default_rng(32)
+    q = _store(rng.standard_normal((B, H, d_h), dtype=np.float32), dt)
+    bk = _store(rng.standard_normal((H, d_h, r), dtype=np.float32) / np.float32(np.sqrt(r)), dt)
+    bv = _store(rng.standard_normal((H, d_h, r), dtype=np.float32) / np.float32(np.sqrt(r)), dt)
+    cache = L.LrkvCache.empty(B, H, d_h, r, n, dtype=torch.bfloat16)
+    L.lrkv_project_append(cache, torch.zeros(B, dtype=torch.int32, device="cuda"), to_dev(inp["x"], dt),
+                          packed_weight(inp))
+    lens = torch.full((B,), n, dtype=torch.int32, device="cuda")
+    got = from_dev(L.lrkv_decode(cache, lens, n, to_dev(q, dt), to_dev(bk, dt), to_dev(bv, dt)))
+    f = lambda a: as_f64(a, dt)
+    want = np.stack([O.decode_from_weights(f(inp["x"])[b], f(q)[b], f(inp["wk"]), f(inp["wv"]), f(inp["uk"]),
+                                           f(inp["uv"]), f(bk), f(bv)) for b in range(B)])
+    # the cache rows are rounded to bf16 before the decode reads them: the bf16 bar
+    assert err_ratio(got, want) <= TOL[dt]
+
+
+def test_project_append_full_size_sampled():
+    # The benchmarked launch: 4 sequences x 4096 tokens, d = 4096, H = 32, d_h = 128,
+    # r = 16.  Sampled tokens (first, last, every tile edge region) against the oracle.
+    dt, B, n, d, H, d_h, r = "bf16", 4, 4096, 4096, 32, 128, 16
+    say("case project full size sampled")
+    inp = projection_inputs(batch=B, n_new=n, d_model=d, heads=H, head_dim=d_h, rank=r, dtype=dt, seed=4242)
+    w = packed_weight(inp)
+    cache = L.LrkvCache.empty(B, H, d_h, r, n, dtype=torch.bfloat16, zero=False)
+    L.lrkv_project_append(cache, torch.zeros(B, dtype=torch.int32, device="cuda"), to_dev(inp["x"], dt), w)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    toks = sorted(set([0, 127, 128, 255, n - 1] + list(rng.integers(0, n, 11))))
+    f = lambda a: as_f64(a, dt)
+    for b in (0, B - 1):
+        rows = O.projected_rows(f(inp["x"][b:b + 1, toks]), f(inp["wk"]), f(inp["wv"]), f(inp["uk"]), f(inp["uv"]))
+        for key in KEYS:
+            got = from_dev(getattr(cache, key)[b, toks])
+            want = rows[key][0]
+            assert err_ratio(got, want) <= TOL[dt], (b, key)
+            assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-3 * np.max(np.abs(want))), (b, key)
