@@ -63,7 +63,7 @@ KERNEL_SOURCES = {
     "decode_mfma_kernel": ("decode_mfma.hip", "lrkv_device.h"),
     "decode_split_kernel": ("decode.hip", "lrkv_device.h"),
     "prefill_kernel": ("prefill.hip", "lrkv_device.h"),
-    "project_append_kernel": ("project.hip", "lrkv_device.h"),
+    "project_gemm_kernel": ("project.hip", "lrkv_device.h"),
 }
 
 
@@ -390,6 +390,7 @@ def bench_project(args):
     step_ms = timed(stream, args.steps, step)
     N = 2 * (d_h + H * r)
     flops = 2 * B * n * N * d
+    kernel = L.lrkv_project_kernel(torch.bfloat16, B, n, H, d_h, r, d)
     tflops = flops / (step_ms * 1e-3) / 1e12
     # decode-step shape: 32 sequences, one token each, same weights
     Bd = 32
@@ -412,10 +413,10 @@ def bench_project(args):
                    "heads": H, "head_dim": d_h, "rank": r, "outputs_per_token": N},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic_from_profiles("project_counters", "project_append_kernel",
-                                                      "project_bf16_B4_L4096_d4096"),
-                     "kernel": "project_append_kernel", "algorithmic_flops_per_launch": flops},
+                     "traffic": traffic_from_profiles("project_counters", kernel, "project_bf16_B4_L4096_d4096"),
+                     "kernel": kernel, "algorithmic_flops_per_launch": flops},
         "decode_shape": {"batch": Bd, "new_tokens": 1, "ms": dec_ms, "algorithmic_bytes": dec_bytes,
+                         "kernel": L.lrkv_project_kernel(torch.bfloat16, Bd, 1, H, d_h, r, d),
                          "GB_per_s": dec_bytes / (dec_ms * 1e-3) / 1e9},
     }
     copy_reference(args, rec)

@@ -250,6 +250,17 @@ lrkv_status lrkv_pack_projection(int32_t dtype, int32_t num_heads, int32_t head_
  * and the cache pointers must be 16-byte aligned; z_k and z_v may be NULL
  * when rank == 0.  batch*n_new must be below 2^31 and d_model at most 65536,
  * else LRKV_ERR_SHAPE. */
+/* Name of the kernel lrkv_project_append runs for these sizes on the current
+ * device: "project_gemm_kernel" (bf16 MFMA, 256-row tiles, when they are at
+ * least as many as the device's compute units), "project_skinny_kernel"
+ * (bf16 MFMA, at most 64 rows: the weight read spread over columns and the
+ * contraction), "project_append_kernel" (bf16 MFMA, 128 x 128 tiles, the
+ * rows in between) or "project_append_valu_kernel" (fp32, and bf16 widths
+ * that are not multiples of 32).  NULL for invalid sizes.  Host-only:
+ * launches nothing; the string is static. */
+const char* lrkv_project_kernel(int32_t dtype, int32_t batch, int32_t n_new, int32_t num_heads, int32_t head_dim,
+                                int32_t rank, int32_t d_model);
+
 lrkv_status lrkv_project_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
                                 int32_t rank, int64_t capacity,
                                 void* k_shared, void* v_shared, void* z_k, void* z_v,

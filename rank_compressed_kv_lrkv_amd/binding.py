@@ -27,7 +27,7 @@ STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DT
 EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
             "lrkv_decode_combine", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
-            "lrkv_project_append")
+            "lrkv_project_kernel", "lrkv_project_append")
 
 
 class LrkvError(RuntimeError):
@@ -75,6 +75,8 @@ def library() -> ctypes.CDLL:
         lib.lrkv_project_append.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                             _vp, _vp, _vp]
         lib.lrkv_project_append.restype = _i32
+        lib.lrkv_project_kernel.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
+        lib.lrkv_project_kernel.restype = ctypes.c_char_p
         _lib = lib
     return _lib
 
@@ -344,6 +346,13 @@ def lrkv_pack_projection(wk_shared, wv_shared, u_k, u_v, out: Optional[torch.Ten
                                           _ptr(u_v, "u_v", dt), _ptr(out, "out", dt), _stream()),
            "lrkv_pack_projection")
     return out
+
+
+def lrkv_project_kernel(dtype: torch.dtype, batch: int, n_new: int, heads: int, head_dim: int, rank: int,
+                        d_model: int) -> Optional[str]:
+    """Name of the kernel lrkv_project_append runs for these sizes (None if invalid)."""
+    name = library().lrkv_project_kernel(_dtype_code(dtype), batch, n_new, heads, head_dim, rank, d_model)
+    return None if name is None else name.decode()
 
 
 def lrkv_project_append(cache: LrkvCache, pos: torch.Tensor, x: torch.Tensor, w_packed: torch.Tensor) -> None:

@@ -325,6 +325,13 @@ lrkv_status lrkv_pack_projection(int32_t dtype, int32_t num_heads, int32_t head_
   return lrkv::launch_pack_projection(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
 }
 
+const char* lrkv_project_kernel(int32_t dtype, int32_t batch, int32_t n_new, int32_t num_heads, int32_t head_dim,
+                                int32_t rank, int32_t d_model) {
+  if (check_sizes(dtype, batch, num_heads, head_dim, rank, 1) != LRKV_OK) return nullptr;
+  if (batch < 1 || n_new < 1 || d_model < 1 || d_model > 65536 || int64_t(batch) * n_new >= INT32_MAX) return nullptr;
+  return lrkv::project_kernel_name(dtype, batch, n_new, num_heads, head_dim, rank, d_model);
+}
+
 lrkv_status lrkv_project_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
                                 int32_t rank, int64_t capacity, void* k_shared, void* v_shared, void* z_k,
                                 void* z_v, const int32_t* pos, int32_t n_new, int32_t d_model, const void* x,

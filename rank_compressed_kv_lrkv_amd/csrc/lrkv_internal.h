@@ -84,6 +84,8 @@ struct ProjectArgs {
 // of 32, d_model a multiple of 32 (others run on the vector-ALU kernel).
 bool project_mfma_supported(int dtype, int head_dim, int rank, int heads, int d_model);
 hipError_t launch_project_append(const ProjectArgs& a, hipStream_t stream);
+// Name of the kernel launch_project_append runs for these sizes on the current device.
+const char* project_kernel_name(int dtype, int batch, int n_new, int heads, int head_dim, int rank, int d_model);
 
 struct PackArgs {
   int dtype, heads, head_dim, rank, d_model;

@@ -36,6 +36,10 @@ constexpr int kPjRowBytes = kPjBK * 2;                   // one row of a step sl
 constexpr int kPjSlice = kPjBM * kPjRowBytes;            // 8 KB per operand and step
 constexpr int kPjChunks = kPjRowBytes / 16;              // 16-byte chunks per slice row
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): wait until at most n (< 64) vector-memory loads are outstanding.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 struct ProjectParams {
   const uint16_t* x; const uint16_t* w;
   uint16_t* k_s; uint16_t* v_s; uint16_t* z_k; uint16_t* z_v;
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(kPjThreads) void project_append_kernel(ProjectParam
   load_step(0, 0);
   for (int ks = 0; ks < nsteps; ++ks) {
     const int buf = ks & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);                     // this wave's transfers of step ks have landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));               // this wave's transfers of step ks have landed
     __syncthreads();                                        // everyone's have; buffer buf^1 is free
     if (ks + 1 < nsteps) load_step(ks + 1, buf ^ 1);
 #pragma unroll
@@ -144,6 +148,275 @@ __global__ __launch_bounds__(kPjThreads) void project_append_kernel(ProjectParam
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         if (col_ok[j]) base[j][row * width[j] + col0[j] + n_lane] = f32_to_bf16(acc[i][j][e]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Large-tile projection for many tokens: a workgroup of 8 waves computes a
+// 256 x (64 TJ) block of C, each wave a 64 x (32 TJ) part (2 x TJ tiles of
+// v_mfma_f32_32x32x16_bf16: 2 + TJ operand reads from LDS per 2 TJ MFMAs).
+// The contraction runs kPgBK at a time (one 128-byte line of every row)
+// through a ring of kPgStages LDS stages; waves 0-3 copy the X slice of a
+// stage, waves 4-7 the W slice, one stage ahead of the MFMAs.  One
+// workgroup per compute unit (144 KB of LDS for TJ = 5), two waves per SIMD.
+//
+// Tile order is XCD-aware: workgroups are dispatched round-robin over the 8
+// XCDs (L2 domains), so workgroup L runs on XCD L % 8; it takes tile
+// (L % 8) * T/8 + L / 8 of the T tiles numbered row block by row block, so
+// the column blocks of one row block run on one XCD at the same time and
+// read its X rows (the large operand: 2 MB per row block at d = 4096) from
+// that XCD's L2 once, while every XCD reads all of W (10.5 MB).
+// ---------------------------------------------------------------------------
+constexpr int kPgStages = 2;
+constexpr int kPgThreads = 512;
+constexpr int kPgBK = 64;                                  // contraction per stage
+constexpr int kPgRowBytes = kPgBK * 2;                     // bytes of one row in a stage
+constexpr int kPgChunks = kPgRowBytes / 16;                // 16-byte chunks per stage row
+constexpr int kPgXferRows = 1024 / kPgRowBytes;            // rows one 1 KB transfer carries
+
+template <int TJ>
+struct PgShape {
+  static constexpr int BM = 256, BN = 64 * TJ;
+  static constexpr int A_BYTES = BM * kPgRowBytes, B_BYTES = BN * kPgRowBytes;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS = kPgStages * STAGE;
+  static constexpr int A_XF = BM / kPgXferRows / 4;   // 1 KB transfers per stage of each X-copying wave
+  static constexpr int B_XF = BN / kPgXferRows / 4;   // ... of each W-copying wave
+  static constexpr int XF = A_XF > B_XF ? A_XF : B_XF;
+};
+
+// Store one 32 x 32 accumulator tile's bf16 results at their cache slots:
+// element e of lane (n_lane, hf) is row rows[e] (cache row index, or -1 when
+// dropped), column col0 + n_lane of the array at base with row width `width`.
+__device__ __forceinline__ void store_tile(uint16_t* base, int width, int col0, const long* rows, int n_lane,
+                                           const f32x16_t& acc) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (rows[e] >= 0) base[size_t(rows[e]) * width + col0 + n_lane] = f32_to_bf16(acc[e]);
+}
+
+// The array, first column and row width of the 32-column tile starting at output n0.
+__device__ __forceinline__ uint16_t* column_target(const ProjectParams& p, int n0, int* col0, int* width) {
+  if (n0 < p.head_dim) { *col0 = n0; *width = p.head_dim; return p.k_s; }
+  if (n0 < 2 * p.head_dim) { *col0 = n0 - p.head_dim; *width = p.head_dim; return p.v_s; }
+  if (n0 < 2 * p.head_dim + p.hr) { *col0 = n0 - 2 * p.head_dim; *width = p.hr; return p.z_k; }
+  *col0 = n0 - 2 * p.head_dim - p.hr; *width = p.hr; return p.z_v;
+}
+
+// Cache row (sequence-major slot index) of output row m, or -1 if m is past
+// the tokens or its slot is outside the cache.
+__device__ __forceinline__ long cache_row(const ProjectParams& p, int m) {
+  if (m >= p.M) return -1;
+  const int b = m / p.n_new, tok = m - b * p.n_new;
+  const long slot = long(p.pos ? p.pos[b] : 0) + tok;
+  return (slot < 0 || slot >= p.capacity) ? -1 : long(b) * p.capacity + slot;
+}
+
+// Workgroup barrier without the memory fence of __syncthreads, which would
+// also wait for every global -> LDS transfer still in flight, the stages
+// ahead included.  The stage about to be read is complete once each wave's
+// explicit vmcnt wait before the barrier has passed; every LDS read of the
+// previous stage has returned, since its MFMAs were issued before the barrier;
+// the empty asm statements keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int TJ>
+__global__ __attribute__((amdgpu_flat_work_group_size(kPgThreads, kPgThreads), amdgpu_waves_per_eu(2)))
+void project_gemm_kernel(ProjectParams p) {
+  using S = PgShape<TJ>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;                 // the wave's 64 x 32TJ part
+  const int n_lane = lane & 31, hf = lane >> 5;
+
+  // XCD-aware tile order (runs of whole row blocks per XCD)
+  const int nr = (p.M + S::BM - 1) / S::BM, nc = (p.N + S::BN - 1) / S::BN, T = nr * nc;
+  const int L = blockIdx.x;
+  const int t = (T % 8 == 0) ? (L % 8) * (T / 8) + L / 8 : L;
+  const int m0 = (t / nc) * S::BM, nb0 = (t % nc) * S::BN;
+
+  // copy role: waves 0-3 the X rows m0.., waves 4-7 the W rows nb0..
+  const bool x_role = wave < 4;
+  const int w4 = wave & 3;
+  const int rows_valid = x_role ? min(S::BM, p.M - m0) : min(S::BN, p.N - nb0);
+  const uint16_t* src = x_role ? p.x + size_t(m0) * p.K : p.w + size_t(nb0) * p.K;
+  const __amdgpu_buffer_rsrc_t res = buffer_resource(src, uint32_t(rows_valid) * p.K * 2);
+  const int nxf = x_role ? S::A_XF : S::B_XF;
+  const int region = x_role ? 0 : S::A_BYTES;
+  uint32_t off[S::XF];
+#pragma unroll
+  for (int u = 0; u < S::XF; ++u) {
+    const int row = (w4 * nxf + u) * kPgXferRows + lane / kPgChunks;
+    const int ch = (lane % kPgChunks) ^ lds_swz(row, kPgChunks);
+    off[u] = uint32_t(min(row, rows_valid - 1)) * p.K * 2 + ch * 16;
+  }
+  auto issue = [&](int ks, int stage) {
+    unsigned char* dst = smem + stage * S::STAGE + region + w4 * nxf * 1024;
+    const uint32_t k_off = uint32_t(ks) * kPgRowBytes;
+#pragma unroll
+    for (int u = 0; u < S::XF; ++u)
+      if (u < nxf) dma16(res, off[u] + k_off, 0u, dst + u * 1024);
+  };
+
+  // operand reads: lane (row n_lane of a 32-row tile, half hf) takes chunk 2c + hf
+  constexpr int KC = kPgBK / 16;                           // MFMA contraction chunks per stage
+  int a_rd[2][KC], b_rd[TJ][KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ra = wm * 64 + i * 32 + n_lane;
+      a_rd[i][c] = ra * kPgRowBytes + ((2 * c + hf) ^ lds_swz(ra, kPgChunks)) * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int rb = wn * 32 * TJ + j * 32 + n_lane;
+      b_rd[j][c] = S::A_BYTES + rb * kPgRowBytes + ((2 * c + hf) ^ lds_swz(rb, kPgChunks)) * 16;
+    }
+  }
+
+  f32x16_t acc[2][TJ];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
+
+  const int nsteps = p.K / kPgBK;
+#pragma unroll
+  for (int s = 0; s < kPgStages - 1; ++s)
+    if (s < nsteps) issue(s, s);
+  for (int ks = 0; ks < nsteps; ++ks) {
+    // stage ks has landed once at most (kPgStages - 2) later stages of this
+    // wave's transfers are outstanding (all of them near the end)
+    if (ks + kPgStages - 2 < nsteps) {
+      if (x_role) __builtin_amdgcn_s_waitcnt(vmcnt_imm((kPgStages - 2) * S::A_XF));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm((kPgStages - 2) * S::B_XF));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    stage_barrier();                                       // every wave's part landed; stage (ks-1) is free
+    if (ks + kPgStages - 1 < nsteps) issue(ks + kPgStages - 1, (ks + kPgStages - 1) % kPgStages);
+    const unsigned char* st = smem + (ks % kPgStages) * S::STAGE;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 av[2], bv[TJ];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) av[i] = *reinterpret_cast<const u32x4*>(st + a_rd[i][c]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) bv[j] = *reinterpret_cast<const u32x4*>(st + b_rd[j][c]);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) acc[i][j] = mfma32(as_bf16x8(av[i]), as_bf16x8(bv[j]), acc[i][j]);
+    }
+  }
+
+  // ---- epilogue: element e of tile (i, j) is row 8(e/4) + 4hf + e%4, column n_lane ----
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    long rows[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) rows[e] = cache_row(p, m0 + wm * 64 + i * 32 + 8 * (e / 4) + 4 * hf + (e % 4));
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int n0 = nb0 + wn * 32 * TJ + j * 32;
+      if (n0 >= p.N) continue;
+      int col0, width;
+      uint16_t* base = column_target(p, n0, &col0, &width);
+      store_tile(base, width, col0, rows, n_lane, acc[i][j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Projection of a few tokens (at most 64 rows, e.g. one token per sequence in
+// a decode step): the weight read dominates, so the work is spread over the
+// output columns and the contraction.  A workgroup of 16 waves takes 32
+// output columns and every row; wave w takes the 16-wide contraction chunks
+// w, w + 16, ... (in runs of kPsGroup consecutive chunks).  Operands go straight from global memory to registers (lane
+// (n_lane, hf) loads 16 bytes of W row n0 + n_lane and of X rows
+// 32 i + n_lane, at contraction offset 16 c + 8 hf), PsUnroll<MT> chunks in
+// flight per wave; the 16 partial tiles are summed in LDS at the end.
+// ---------------------------------------------------------------------------
+constexpr int kPsThreads = 1024, kPsWaves = 16, kPsHalf = kPsWaves / 2;
+constexpr int kPsGroup = 1;            // consecutive 16-wide chunks a wave takes together
+template <int MT> constexpr int PsUnroll = MT == 1 ? 8 : 4;
+
+template <int MT>   // 32-row tiles covering the rows
+__global__ __launch_bounds__(kPsThreads) void project_skinny_kernel(ProjectParams p) {
+  constexpr int U = PsUnroll<MT>;
+  static_assert(U % kPsGroup == 0, "whole runs of chunks per iteration");
+  __shared__ float s_red[kPsHalf * MT * 16 * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_lane = lane & 31, hf = lane >> 5;
+  const int n0 = blockIdx.x * 32;
+  const uint32_t row_bytes = uint32_t(p.K) * 2;
+  const __amdgpu_buffer_rsrc_t wres = buffer_resource(p.w + size_t(n0) * p.K, uint32_t(min(32, p.N - n0)) * row_bytes);
+  const __amdgpu_buffer_rsrc_t xres = buffer_resource(p.x, uint32_t(p.M) * row_bytes);   // rows >= M read zero
+  const uint32_t w_off = uint32_t(min(n_lane, p.N - n0 - 1)) * row_bytes + hf * 16;
+  uint32_t x_off[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) x_off[i] = uint32_t(i * 32 + n_lane) * row_bytes + hf * 16;
+
+  f32x16_t acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x16_t{};
+  const int kchunks = p.K / 16;
+  for (int g0 = wave; g0 * kPsGroup < kchunks; g0 += kPsWaves * (U / kPsGroup)) {
+    u32x4 bw[U], ax[U][MT];
+    auto chunk = [&](int u) { return (g0 + kPsWaves * (u / kPsGroup)) * kPsGroup + u % kPsGroup; };
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t koff = uint32_t(min(chunk(u), kchunks - 1)) * 32;
+      bw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, int(w_off + koff), 0, kStream));
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        ax[u][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, int(x_off[i] + koff), 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (chunk(u) < kchunks)                             // uniform: chunks past the end add nothing
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i] = mfma32(as_bf16x8(ax[u][i]), as_bf16x8(bw[u]), acc[i]);
+  }
+
+  // sum the 16 partial tiles: the upper 8 waves hand theirs to the lower 8,
+  // which then share out the final sums
+  auto red = [&](int w, int i, int e) -> float& { return s_red[((w * MT + i) * 16 + e) * 64 + lane]; };
+  if (wave >= kPsHalf) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red(wave - kPsHalf, i, e) = acc[i][e];
+  }
+  __syncthreads();
+  if (wave < kPsHalf) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red(wave, i, e) += acc[i][e];
+  }
+  __syncthreads();
+  if (wave >= kPsHalf) return;
+  int col0, width;
+  uint16_t* base = column_target(p, n0, &col0, &width);
+  // wave w sums and stores elements 2w and 2w + 1 of every row tile
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = 2 * wave + k;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kPsHalf; ++w) v += red(w, i, e);
+      const long row = cache_row(p, i * 32 + 8 * (e / 4) + 4 * hf + (e % 4));
+      if (row >= 0) base[size_t(row) * width + col0 + n_lane] = f32_to_bf16(v);
     }
 }
 
@@ -262,6 +535,34 @@ bool project_mfma_supported(int dtype, int head_dim, int rank, int heads, int d_
   return dtype == 1 && head_dim % 32 == 0 && (heads * rank) % 32 == 0 && d_model % kPjBK == 0 && d_model > 0;
 }
 
+// Compute units of the current device.
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+template <int TJ>
+hipError_t launch_gemm(const ProjectParams& p, dim3 grid, hipStream_t st) {
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&project_gemm_kernel<TJ>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, PgShape<TJ>::LDS);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((project_gemm_kernel<TJ>), grid, dim3(kPgThreads), size_t(PgShape<TJ>::LDS), st, p);
+  return hipGetLastError();
+}
+
+const char* project_kernel_name(int dtype, int batch, int n_new, int heads, int head_dim, int rank, int d_model) {
+  if (!project_mfma_supported(dtype, head_dim, rank, heads, d_model)) return "project_append_valu_kernel";
+  const long M = long(batch) * n_new, N = 2L * (head_dim + long(heads) * rank);
+  const int tj = N % 320 == 0 ? 5 : 4;
+  if (d_model % kPgBK == 0 && (M + 255) / 256 * ((N + 64 * tj - 1) / (64 * tj)) >= device_cus())
+    return "project_gemm_kernel";
+  if (M <= 64) return "project_skinny_kernel";
+  return "project_append_kernel";
+}
+
 hipError_t launch_project_append(const ProjectArgs& a, hipStream_t st) {
   ProjectParams p;
   p.x = static_cast<const uint16_t*>(a.x);
@@ -278,6 +579,21 @@ hipError_t launch_project_append(const ProjectArgs& a, hipStream_t st) {
   p.capacity = a.capacity;
   if (p.M <= 0) return hipSuccess;
   if (project_mfma_supported(a.dtype, a.head_dim, a.rank, a.heads, a.d_model)) {
+    const int tj = p.N % 320 == 0 ? 5 : 4;
+    const long big_tiles = long((p.M + 255) / 256) * ((p.N + 64 * tj - 1) / (64 * tj));
+    if (p.K % kPgBK == 0 && big_tiles >= device_cus()) {
+      // enough large tiles to fill the chip: the 256-row, 8-wave kernel
+      const dim3 grid{unsigned(big_tiles)};
+      if (tj == 5) return launch_gemm<5>(p, grid, st);
+      return launch_gemm<4>(p, grid, st);
+    }
+    if (p.M <= 64) {
+      // a few tokens: spread the weight read over columns and contraction
+      const dim3 grid{unsigned(p.N / 32)};
+      if (p.M <= 32) hipLaunchKernelGGL(project_skinny_kernel<1>, grid, dim3(kPsThreads), 0, st, p);
+      else hipLaunchKernelGGL(project_skinny_kernel<2>, grid, dim3(kPsThreads), 0, st, p);
+      return hipGetLastError();
+    }
     const dim3 grid((p.N + kPjBN - 1) / kPjBN, (p.M + kPjBM - 1) / kPjBM);
     hipLaunchKernelGGL(project_append_kernel, grid, dim3(kPjThreads), 0, st, p);
   } else {

@@ -256,3 +256,20 @@ def test_pack_projection_rejects_before_launch(kw, want):
 @no_gpu
 def test_pack_projection_empty_is_noop():
     assert pack_call(d=0, wk=None, out=None) == OK
+
+
+def test_project_kernel_names():
+    # host-only: the choice depends on the sizes (and on the compute-unit count
+    # for the large-tile kernel; 256 on MI355X, also the value assumed without a GPU)
+    k = lambda *a: L.lrkv_project_kernel(*a)
+    bf, f32 = torch.bfloat16, torch.float32
+    assert k(f32, 4, 4096, 32, 128, 16, 4096) == "project_append_valu_kernel"
+    assert k(bf, 2, 33, 3, 40, 8, 72) == "project_append_valu_kernel"
+    assert k(bf, 32, 1, 32, 128, 16, 4096) == "project_skinny_kernel"
+    assert k(bf, 8, 8, 32, 128, 16, 4096) == "project_skinny_kernel"
+    assert k(bf, 2, 130, 32, 128, 16, 4096) == "project_append_kernel"
+    assert k(bf, 4, 4096, 32, 128, 16, 4064) == "project_append_kernel"      # d not a multiple of 64
+    if not torch.cuda.is_available() or torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert k(bf, 4, 4096, 32, 128, 16, 4096) == "project_gemm_kernel"
+    assert k(bf, 0, 4, 32, 128, 16, 4096) is None
+    assert k(bf, 4, 4, 32, 128, 16, 0) is None

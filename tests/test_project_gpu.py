@@ -75,8 +75,11 @@ def check_cache(cache, rows, pos, dt, T):
     return worst
 
 
-def run_case(dt, B, n, d, H, d_h, r, T, pos, seed):
-    say(f"case project {dt} B={B} n={n} d={d} H={H} d_h={d_h} r={r} T={T} pos={list(pos)}")
+def run_case(dt, B, n, d, H, d_h, r, T, pos, seed, kernel=None):
+    name = L.lrkv_project_kernel(TORCH_DT[dt], B, n, H, d_h, r, d)
+    say(f"case project {dt} B={B} n={n} d={d} H={H} d_h={d_h} r={r} T={T} pos={list(pos)[:4]} kernel={name}")
+    if kernel is not None:
+        assert name == kernel
     inp = projection_inputs(batch=B, n_new=n, d_model=d, heads=H, head_dim=d_h, rank=r, dtype=dt, seed=seed)
     w = packed_weight(inp)
     cache = canary_cache(B, T, H, d_h, r, dt)
@@ -86,10 +89,10 @@ def run_case(dt, B, n, d, H, d_h, r, T, pos, seed):
 
 
 @pytest.mark.parametrize("dt,B,n,d,H,d_h,r", [
-    ("bf16", 3, 37, 160, 4, 64, 8),       # MFMA: 111 rows (ragged row tile), 192 outputs (half a column block)
+    ("bf16", 3, 37, 160, 4, 64, 8),       # MFMA 128 x 128: 111 rows (ragged row tile), 192 outputs
     ("bf16", 2, 130, 4096, 32, 128, 16),  # the bf16 model shape: 260 rows, 1280 outputs, d = 4096
     ("bf16", 2, 50, 256, 8, 128, 32),     # rank 32
-    ("bf16", 3, 21, 128, 8, 64, 0),       # rank 0 (MQA rows only)
+    ("bf16", 3, 31, 128, 8, 64, 0),       # rank 0 (MQA rows only)
     ("bf16", 2, 33, 72, 3, 40, 8),        # vector-ALU path (widths not multiples of 32)
     ("f32", 1, 64, 64, 4, 16, 4),         # the tiny fp32 shape, d = H d_h = 64
     ("f32", 2, 45, 200, 4, 32, 8),        # fp32, ragged contraction
@@ -97,12 +100,35 @@ def run_case(dt, B, n, d, H, d_h, r, T, pos, seed):
 def test_project_append_parity(dt, B, n, d, H, d_h, r):
     T = n + 11
     pos = [(5 * b) % 12 for b in range(B)]
-    run_case(dt, B, n, d, H, d_h, r, T, pos, seed=1000 + d + n)
+    name = "project_append_valu_kernel" if dt == "f32" or d_h % 32 or (H * r) % 32 else "project_append_kernel"
+    run_case(dt, B, n, d, H, d_h, r, T, pos, seed=1000 + d + n, kernel=name)
 
 
 def test_project_append_decode_shape():
     # one new token per sequence over the bf16 model shape (a decode step's projection)
-    run_case("bf16", 32, 1, 4096, 32, 128, 16, 40, [(7 * b) % 40 for b in range(32)], seed=77)
+    run_case("bf16", 32, 1, 4096, 32, 128, 16, 40, [(7 * b) % 40 for b in range(32)], seed=77,
+             kernel="project_skinny_kernel")
+
+
+@pytest.mark.parametrize("B,n,d", [(1, 1, 4096), (1, 17, 544), (8, 4, 256), (3, 11, 4096), (8, 8, 1024)])
+def test_project_append_few_tokens(B, n, d):
+    # at most 64 rows: one or two 32-row tiles, contraction split over the waves
+    # (d = 544: 34 chunks of 16, not a multiple of the 16 waves x 8 in flight)
+    run_case("bf16", B, n, d, 32, 128, 16, n + 5, [(3 * b) % 5 for b in range(B)], seed=300 + B * n + d,
+             kernel="project_skinny_kernel")
+
+
+@pytest.mark.parametrize("B,n,d,r", [
+    (4, 4096, 64, 16),      # 64 x 4 tiles of 256 x 320 in XCD order, a single contraction stage
+    (1, 16461, 128, 16),    # 65 x 4 tiles (not a multiple of 8: launch order), ragged last row tile
+    (2, 11008, 128, 8),     # r = 8: N = 768, 256-wide column tiles, 86 x 3 tiles
+    (4, 4096, 704, 16),     # eleven contraction stages: the ring wraps
+])
+def test_project_append_large_tiles(B, n, d, r):
+    if torch.cuda.get_device_properties(0).multi_processor_count > 256:
+        pytest.skip("sizes chosen for at most 256 compute units")
+    run_case("bf16", B, n, d, 32, 128, r, n + 3, [b % 3 for b in range(B)], seed=500 + n + d,
+             kernel="project_gemm_kernel")
 
 
 def test_project_append_drops_rows_outside_cache():
