@@ -243,16 +243,29 @@ void decode_mfma_kernel(MfParams p) {
 #pragma unroll
     for (int c = 0; c < S::KC; ++c) qop[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 16 * c));
   }
-  constexpr int DPL = DH / 8;
+  // Absorbed-query inputs, 8 lanes per head (hq = tid / 8, g = tid % 8).
+  // B^K_h is DH rows of CPR 16-byte chunks (4 KB at DH = 128, R = 16); load k
+  // of lane g takes chunk 8k + g, so the 8 lanes of a head read 128
+  // contiguous bytes per instruction (one cache line, 8 lines per wave
+  // instruction).  Chunk 8k + g holds B^K_h[d][i0 .. i0 + 7] with
+  // d = (8k + g) / CPR and i0 = 8 ((8k + g) % CPR) = 8 (g % CPR).  The
+  // lane also holds the whole row q_h (QW chunks, the same addresses for the
+  // 8 lanes of a head) and picks q_h[d] out of chunk k / CPR.
+  constexpr int CPR = R >= 8 ? R / 8 : 1;                   // 16-byte chunks per row of B^K_h
+  constexpr int NBK = R > 0 ? DH * CPR / 8 : 1;             // B^K chunks per lane
+  constexpr int QW = DH / 8;                                 // 16-byte chunks of a query row
   const int hq = tid / 8, g = tid % 8;
-  uint32_t qw[DPL / 2];
-  uint32_t bkw[DPL][R > 0 ? R / 2 : 1];
+  u32x4 qrow[R > 0 ? QW : 1];
+  u32x4 bkv[NBK];
   if constexpr (R > 0) {
-    const uint16_t* qsl = static_cast<const uint16_t*>(p.q) + (size_t(b) * H + hg * kMfHeads + hq) * DH + g * DPL;
-    const uint16_t* bk = static_cast<const uint16_t*>(p.b_k) + (size_t(hg * kMfHeads + hq) * DH + g * DPL) * R;
-    load_words<DPL * 2>(qw, qsl);
+    const u32x4* qsl = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.q) +
+                                                        (size_t(b) * H + hg * kMfHeads + hq) * DH);
+    const u32x4* bk = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.b_k) +
+                                                       size_t(hg * kMfHeads + hq) * DH * R);
 #pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) load_words<R * 2>(bkw[dd], bk + size_t(dd) * R);
+    for (int c = 0; c < QW; ++c) qrow[c] = qsl[c];
+#pragma unroll
+    for (int k = 0; k < NBK; ++k) bkv[k] = bk[8 * k + g];
   }
   __builtin_amdgcn_sched_barrier(0);
   row_dma(kres, gtile(0), ktile);
@@ -262,19 +275,36 @@ void decode_mfma_kernel(MfParams p) {
   }(std::make_integer_sequence<int, S::D>{});
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (R > 0) {
-    float part[R];
+    // part[e] = sum over this lane's d of q_h[d] B^K_h[d][i0 + e]; q_h[d] is
+    // element ek + gq of chunk k / CPR, with ek = 8 (k % CPR) / CPR from the
+    // load index and gq = g / CPR from the lane (selected, not indexed)
+    const int gq = g / CPR;
+    float part[8];
 #pragma unroll
-    for (int i = 0; i < R; ++i) part[i] = 0.f;
+    for (int e = 0; e < 8; ++e) part[e] = 0.f;
 #pragma unroll
-    for (int dd = 0; dd < DPL; ++dd) {
-      const float qd = bf16_to_f32(elem_at<BF16>(qw, dd));
+    for (int k = 0; k < NBK; ++k) {
+      const u32x4 qc = qrow[k / CPR];
+      const int el = 8 * (k % CPR) / CPR + gq;               // element of the chunk, 0..7
+      const uint32_t w01 = (el & 2) ? qc.y : qc.x, w23 = (el & 2) ? qc.w : qc.z;
+      const uint32_t w = (el & 4) ? w23 : w01;
+      const float qd = __uint_as_float((el & 1) ? (w & 0xffff0000u) : (w << 16));
+      const uint32_t bw[4] = {bkv[k].x, bkv[k].y, bkv[k].z, bkv[k].w};
 #pragma unroll
-      for (int i = 0; i < R; ++i) part[i] = __builtin_fmaf(qd, bf16_to_f32(elem_at<BF16>(bkw[dd], i)), part[i]);
+      for (int e = 0; e < 8; ++e) part[e] = __builtin_fmaf(qd, bf16_to_f32(elem_at<BF16>(bw, e)), part[e]);
     }
+    // sum over the lanes of the head with the same g % CPR (xor of the bits above CPR)
+    auto xor_add = [&]<int M>(std::integral_constant<int, M>) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const float v = group_sum<8>(part[i]);
-      if (g == (i % 8)) s_qt[hq * R + i] = v;
+      for (int e = 0; e < 8; ++e)
+        part[e] += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(part[e]), 0x1F | (M << 10)));
+    };
+    if constexpr (CPR <= 1) xor_add(std::integral_constant<int, 1>{});
+    if constexpr (CPR <= 2) xor_add(std::integral_constant<int, 2>{});
+    if constexpr (CPR <= 4) xor_add(std::integral_constant<int, 4>{});
+    if (gq == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_qt[hq * R + 8 * (g % CPR) + e] = part[e];
     }
   }
   __syncthreads();
