@@ -507,9 +507,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   // the partial states of this sequence: items j0 .. j0 + n - 1
   int j0, n;
   if (ws_meta) {                                             // balanced partition, recorded by the scan
-    j0 = ws_meta[b];
-    const int u = ws_meta[batch];
-    n = (len + u - 1) / u;
+    // clamped to the workspace, so that a workspace the scan did not fill
+    // (a contract violation) gives wrong values, never an access outside it
+    j0 = min(max(ws_meta[b], 0), partials - 1);
+    const int u = max(ws_meta[batch], 1);
+    n = min((len + u - 1) / u, partials - j0);
   } else {
     j0 = b * partials;
     n = ((len + split_tokens - 1) / split_tokens) * slots;
