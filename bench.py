@@ -46,8 +46,8 @@ def parse():
                          "the GPU takes tens of ms of sustained work to reach its steady clock")
     ap.add_argument("--mode", choices=("decode", "prefill", "chunk", "rank-sweep", "project"), default="decode",
                     help="decode (the headline line); the causal-prefill MFMA path; a prefill chunk over a "
-                         "4096-token history; decode at ranks 0/8/16/32 on the headline shape; or the fused "
-                         "projection + append of 4 x 4096 tokens from d = 4096")
+                         "4096-token history; decode at ranks 0/8/16/32 and plain MHA on the headline shape; or "
+                         "the fused projection + append of 4 x 4096 tokens from d = 4096")
     ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
@@ -427,7 +427,8 @@ def bench_rank_sweep(args):
     """Decode on the headline shape (32 sequences x 8192 tokens, H=32, d_h=128)
     at ranks 0 (the MQA cache), 8, 16 and 32: cache elements per token
     2(d_h + H r) and the measured step, to show how the cache ratio turns
-    into time.  One JSON line per rank."""
+    into time; then the plain MHA decode (2 H d_h elements per token) at the
+    same shape.  One JSON line per point."""
     import torch
     import rank_compressed_kv_lrkv_amd as L
     from rank_compressed_kv_lrkv_amd.workloads import DecodeWorkload, decode_inputs
@@ -461,6 +462,31 @@ def bench_rank_sweep(args):
         }), flush=True)
         del cache, q, b_k, b_v, call
         torch.cuda.empty_cache()
+
+    # the plain MHA cache at the same shape: every head's own K and V rows
+    B, T, H, d_h = 32, 8192, 32, 128
+    gen = torch.Generator(device="cuda").manual_seed(20261209)
+    k = torch.randn(B, T, H, d_h, device="cuda", generator=gen).to(torch.bfloat16)
+    v = torch.randn(B, T, H, d_h, device="cuda", generator=gen).to(torch.bfloat16)
+    q = torch.randn(B, H, d_h, device="cuda", generator=gen).to(torch.bfloat16)
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    ws = torch.empty(max(L.lrkv_mha_decode_workspace_size(torch.bfloat16, B, H, d_h, T, T), 16), dtype=torch.uint8,
+                     device="cuda")
+    step = lambda: L.lrkv_mha_decode(k, v, lens, T, q, out=out, workspace=ws)
+    settle(step, args.settle_s)
+    for _ in range(args.warmup):
+        step()
+    step_ms = timed(torch.cuda.current_stream(), args.steps, step)
+    elems = 2 * H * d_h
+    cache_bytes = B * T * elems * 2
+    print(json.dumps({
+        "metric": "decode step vs rank", "workload": "mha_bf16_T8k", "rank": None, "mechanism": "mha",
+        "cache_elems_per_token": elems, "cache_ratio_vs_mha": 1.0, "cache_MB": cache_bytes / 1e6,
+        "scan_kernel": "mha_split_kernel", "ms_per_step": step_ms,
+        "cache_tokens_per_s": B * T / (step_ms * 1e-3),
+        "step_hbm_frac": cache_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+    }), flush=True)
 
 
 def cpu_baseline(d, out_dev, budget_s, as_f64):

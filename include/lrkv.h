@@ -267,6 +267,30 @@ lrkv_status lrkv_project_append(int32_t dtype, int32_t batch, int32_t num_heads,
                                 const int32_t* pos, int32_t n_new, int32_t d_model,
                                 const void* x, const void* w_packed, void* stream);
 
+/* Plain multi-head attention decode over a full per-head K/V cache, the
+ * baseline LRKV's cache is compared with at a matched shape (slide "Can
+ * heads share storage while keeping distinct K/V features?": MHA caches
+ * 2 num_heads head_dim elements per token per layer).  For every sequence b
+ * and head h:
+ *   out[b][h] = softmax_t(scale * q_bh . k[b][t][h]) applied to v[b][t][h],
+ *               t < seq_lens[b].
+ *   k, v      [batch][capacity][num_heads][head_dim];  q, out [batch][num_heads][head_dim].
+ *   seq_lens, max_len, scale: as for lrkv_decode (lengths clamped to
+ *             [0, max_len], a sequence of length 0 gets zeros).
+ *   split_tokens  tokens per split (0 = default, else a positive multiple of
+ *             64); one split's rows must span less than 4 GiB.
+ *   workspace at least lrkv_mha_decode_workspace_size bytes; contents on
+ *             entry are ignored.
+ * head_dim must be 64 or 128.  Partial states per (split, head) are merged
+ * by the same log-sum-exp combine as lrkv_decode. */
+lrkv_status lrkv_mha_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                           int64_t capacity, int64_t max_len, int32_t split_tokens,
+                                           size_t* bytes);
+lrkv_status lrkv_mha_decode(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int64_t capacity,
+                            const void* k, const void* v, const int32_t* seq_lens, int64_t max_len,
+                            const void* q, float scale, int32_t split_tokens, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DT
 EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
             "lrkv_decode_combine", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
-            "lrkv_project_kernel", "lrkv_project_append")
+            "lrkv_project_kernel", "lrkv_project_append", "lrkv_mha_decode_workspace_size", "lrkv_mha_decode")
 
 
 class LrkvError(RuntimeError):
@@ -77,6 +77,11 @@ def library() -> ctypes.CDLL:
         lib.lrkv_project_append.restype = _i32
         lib.lrkv_project_kernel.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
         lib.lrkv_project_kernel.restype = ctypes.c_char_p
+        lib.lrkv_mha_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i64, _i64, _i32, ctypes.POINTER(_sz)]
+        lib.lrkv_mha_decode_workspace_size.restype = _i32
+        lib.lrkv_mha_decode.argtypes = [_i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _i64, _vp, _f32, _i32, _vp, _vp,
+                                        _sz, _vp]
+        lib.lrkv_mha_decode.restype = _i32
         _lib = lib
     return _lib
 
@@ -368,6 +373,38 @@ def lrkv_project_append(cache: LrkvCache, pos: torch.Tensor, x: torch.Tensor, w_
                                          cache.capacity, *cache.pointers(), _ptr(pos, "pos", torch.int32), n_new,
                                          d, _ptr(x, "x", dt), _ptr(w_packed, "w_packed", dt), _stream()),
            "lrkv_project_append")
+
+
+def lrkv_mha_decode_workspace_size(dtype: torch.dtype, batch: int, heads: int, head_dim: int, capacity: int,
+                                   max_len: int, split_tokens: int = 0) -> int:
+    n = _sz(0)
+    _check(library().lrkv_mha_decode_workspace_size(_dtype_code(dtype), batch, heads, head_dim, capacity, max_len,
+                                                    split_tokens, ctypes.byref(n)),
+           "lrkv_mha_decode_workspace_size")
+    return int(n.value)
+
+
+def lrkv_mha_decode(k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor, max_len: int, q: torch.Tensor,
+                    scale: Optional[float] = None, split_tokens: int = 0, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Plain MHA decode over a per-head cache k, v [B][T][H][d_h] (see lrkv.h)."""
+    dt = q.dtype
+    B, T, H, d_h = k.shape
+    _shape(v, "v", (B, T, H, d_h))
+    _shape(q, "q", (B, H, d_h))
+    _shape(seq_lens, "seq_lens", (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", (B, H, d_h))
+    if workspace is None:
+        nbytes = lrkv_mha_decode_workspace_size(dt, B, H, d_h, T, max_len, split_tokens)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(library().lrkv_mha_decode(_dtype_code(dt), B, H, d_h, T, _ptr(k, "k", dt), _ptr(v, "v", dt),
+                                     _ptr(seq_lens, "seq_lens", torch.int32), int(max_len), _ptr(q, "q", dt),
+                                     0.0 if scale is None else float(scale), split_tokens, _ptr(out, "out", dt),
+                                     _ptr(workspace, "workspace"), workspace.numel(), _stream()),
+           "lrkv_mha_decode")
+    return out
 
 
 def default_scale(head_dim: int) -> float:

@@ -632,4 +632,25 @@ hipError_t launch_decode(const DecodePlan& pl, const DecodeArgs& a, int phase, h
   return pl.dtype == 1 ? dispatch_dim<BF16>(pl, a, phase, st) : dispatch_dim<F32>(pl, a, phase, st);
 }
 
+hipError_t launch_plain_merge(int dtype, int head_dim, const float* ws_ml, const float* ws_acc,
+                              const int32_t* seq_lens, void* out, int heads, int partials, int split_tokens,
+                              int max_len, int batch, hipStream_t st) {
+  const dim3 grid(heads, batch);
+  if (dtype == 1 && head_dim == 64)
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, 64, 0>), grid, dim3(kMergeThreads), 0, st, ws_ml, ws_acc, seq_lens,
+                       nullptr, out, heads, partials, 1, split_tokens, max_len, batch, nullptr);
+  else if (dtype == 1 && head_dim == 128)
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, 128, 0>), grid, dim3(kMergeThreads), 0, st, ws_ml, ws_acc,
+                       seq_lens, nullptr, out, heads, partials, 1, split_tokens, max_len, batch, nullptr);
+  else if (dtype == 0 && head_dim == 64)
+    hipLaunchKernelGGL((decode_merge_kernel<F32, 64, 0>), grid, dim3(kMergeThreads), 0, st, ws_ml, ws_acc, seq_lens,
+                       nullptr, out, heads, partials, 1, split_tokens, max_len, batch, nullptr);
+  else if (dtype == 0 && head_dim == 128)
+    hipLaunchKernelGGL((decode_merge_kernel<F32, 128, 0>), grid, dim3(kMergeThreads), 0, st, ws_ml, ws_acc,
+                       seq_lens, nullptr, out, heads, partials, 1, split_tokens, max_len, batch, nullptr);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 }  // namespace lrkv

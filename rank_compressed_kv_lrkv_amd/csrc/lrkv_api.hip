@@ -355,4 +355,77 @@ lrkv_status lrkv_project_append(int32_t dtype, int32_t batch, int32_t num_heads,
                                                                                         : LRKV_ERR_DEVICE;
 }
 
+// Plain MHA decode (the matched-shape baseline): fixed splits of the context,
+// about two workgroups per compute unit by default.
+static lrkv_status plan_mha(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int64_t capacity,
+                            int64_t max_len, int32_t split_tokens, int* split_out, int* n_splits, size_t* ws_ml,
+                            size_t* ws_acc) {
+  if (dtype != LRKV_F32 && dtype != LRKV_BF16) return LRKV_ERR_DTYPE;
+  if (batch < 0 || num_heads < 1 || capacity < 1 || capacity > INT32_MAX || max_len < 0 || split_tokens < 0)
+    return LRKV_ERR_SHAPE;
+  if (!lrkv::mha_supported(dtype, head_dim)) return LRKV_ERR_SHAPE;
+  if (max_len > capacity) return LRKV_ERR_CAPACITY;
+  if (split_tokens % 64 != 0) return LRKV_ERR_SHAPE;
+  int64_t split = split_tokens;
+  if (split == 0) {
+    const int64_t groups = (num_heads + 31) / 32;
+    const int64_t target = 2 * int64_t(device_cu_count());
+    split = (int64_t(batch) * max_len * groups + target - 1) / target;
+    split = std::max<int64_t>(64, (split + 63) / 64 * 64);
+    split = std::min<int64_t>(split, std::max<int64_t>(64, (max_len + 63) / 64 * 64));
+  }
+  // one split's rows (and the loads of a step past its end) are addressed
+  // through 32-bit buffer offsets
+  if ((split + 64) * num_heads * head_dim * elem_bytes(dtype) >= (int64_t(1) << 32)) return LRKV_ERR_SHAPE;
+  const int64_t ns = max_len > 0 ? (max_len + split - 1) / split : 0;
+  *split_out = int(split);
+  *n_splits = int(ns);
+  *ws_ml = (size_t(batch) * ns * num_heads * 2 * sizeof(float) + 255) / 256 * 256;   // keeps the sums 16-byte aligned
+  *ws_acc = size_t(batch) * ns * num_heads * head_dim * sizeof(float);
+  return LRKV_OK;
+}
+
+lrkv_status lrkv_mha_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                           int64_t capacity, int64_t max_len, int32_t split_tokens, size_t* bytes) {
+  if (!bytes) return LRKV_ERR_NULL;
+  int split, ns;
+  size_t ml, acc;
+  const lrkv_status st = plan_mha(dtype, batch, num_heads, head_dim, capacity, max_len, split_tokens, &split, &ns,
+                                  &ml, &acc);
+  if (st != LRKV_OK) return st;
+  *bytes = ml + acc;
+  return LRKV_OK;
+}
+
+lrkv_status lrkv_mha_decode(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int64_t capacity,
+                            const void* k, const void* v, const int32_t* seq_lens, int64_t max_len, const void* q,
+                            float scale, int32_t split_tokens, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  int split, ns;
+  size_t ml, acc;
+  const lrkv_status st = plan_mha(dtype, batch, num_heads, head_dim, capacity, max_len, split_tokens, &split, &ns,
+                                  &ml, &acc);
+  if (st != LRKV_OK) return st;
+  if (batch == 0) return LRKV_OK;
+  if (!k || !v || !seq_lens || !q || !out) return LRKV_ERR_NULL;
+  if (ns > 0 && (!workspace || workspace_bytes < ml + acc)) return LRKV_ERR_WORKSPACE;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(out) || !aligned4(seq_lens) ||
+      (ns > 0 && !aligned16(workspace)))
+    return LRKV_ERR_ALIGN;
+  const float sc = (scale > 0.f && std::isfinite(scale)) ? scale : 1.0f / std::sqrt(float(head_dim));
+  lrkv::MhaArgs a;
+  a.dtype = dtype; a.batch = batch; a.heads = num_heads; a.head_dim = head_dim; a.max_len = int(max_len);
+  a.split_tokens = split; a.n_splits = ns; a.phase = 3; a.capacity = capacity;
+  a.k = k; a.v = v; a.seq_lens = seq_lens; a.q = q; a.scale_log2 = sc * 1.4426950408889634f; a.out = out;
+  a.ws_ml = static_cast<float*>(workspace);
+  a.ws_acc = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + ml);
+  if (ns == 0) {
+    // every length is 0: the output is all zeros, produced by the merge alone
+    a.n_splits = 1;
+    a.phase = 2;
+    a.ws_ml = a.ws_acc = nullptr;
+  }
+  return lrkv::launch_mha_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+}
+
 }  // extern "C"

@@ -95,4 +95,23 @@ struct PackArgs {
 };
 hipError_t launch_pack_projection(const PackArgs& a, hipStream_t stream);
 
+// The log-sum-exp merge of rank-0 partial states laid out [batch][partials][heads]
+// (fixed splits), for caches without latents.
+hipError_t launch_plain_merge(int dtype, int head_dim, const float* ws_ml, const float* ws_acc,
+                              const int32_t* seq_lens, void* out, int heads, int partials, int split_tokens,
+                              int max_len, int batch, hipStream_t stream);
+
+struct MhaArgs {
+  int dtype, batch, heads, head_dim, max_len, split_tokens, n_splits, phase;   // phase: 1 scan, 2 merge, 3 both
+  int64_t capacity;
+  const void* k; const void* v;      // [batch][capacity][heads][head_dim]
+  const int32_t* seq_lens;
+  const void* q;                     // [batch][heads][head_dim]
+  float scale_log2;
+  void* out;
+  float* ws_ml; float* ws_acc;       // [batch][n_splits][heads] x (m, l); [batch][n_splits][heads][head_dim]
+};
+bool mha_supported(int dtype, int head_dim);
+hipError_t launch_mha_decode(const MhaArgs& a, hipStream_t stream);
+
 }  // namespace lrkv

@@ -30,7 +30,7 @@ import numpy as np
 __all__ = [
     "DecodeWorkload", "PrefillWorkload", "DECODE_WORKLOADS", "PREFILL_WORKLOADS",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "decode_inputs", "prefill_inputs",
-    "append_inputs", "as_f64", "projection_inputs",
+    "append_inputs", "as_f64", "projection_inputs", "mha_inputs",
 ]
 
 
@@ -221,3 +221,21 @@ def projection_inputs(*, batch: int, n_new: int, d_model: int, heads: int, head_
     uv = rng.standard_normal((H, d, r), dtype=np.float32) * w_std
     return dict(x=_store(x, dtype), wk=_store(wk, dtype), wv=_store(wv, dtype), uk=_store(uk, dtype),
                 uv=_store(uv, dtype), dtype=dtype, heads=H, head_dim=d_h, rank=r, d_model=d)
+
+
+def mha_inputs(*, batch: int, capacity: int, heads: int, head_dim: int, lens, dtype: str, seed: int) -> dict:
+    """A plain per-head K/V cache for the MHA baseline: q [B, H, d_h], k and v
+    [B, T, H, d_h], all N(0, 1) up to each sequence's length, zero beyond."""
+    rng = np.random.default_rng(seed)
+    B, T, H, d_h = batch, capacity, heads, head_dim
+    seq_lens = np.asarray(lens, dtype=np.int32)
+    assert seq_lens.shape == (B,) and int(seq_lens.max(initial=0)) <= T
+    sdt = np.uint16 if dtype == "bf16" else np.float32
+    q = _store(rng.standard_normal((B, H, d_h), dtype=np.float32), dtype)
+    k = np.zeros((B, T, H, d_h), sdt)
+    v = np.zeros((B, T, H, d_h), sdt)
+    for b in range(B):
+        n = int(seq_lens[b])
+        k[b, :n] = _store(rng.standard_normal((n, H, d_h), dtype=np.float32), dtype)
+        v[b, :n] = _store(rng.standard_normal((n, H, d_h), dtype=np.float32), dtype)
+    return dict(q=q, k=k, v=v, seq_lens=seq_lens, dtype=dtype)

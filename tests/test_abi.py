@@ -273,3 +273,31 @@ def test_project_kernel_names():
         assert k(bf, 4, 4096, 32, 128, 16, 4096) == "project_gemm_kernel"
     assert k(bf, 0, 4, 32, 128, 16, 4096) is None
     assert k(bf, 4, 4, 32, 128, 16, 0) is None
+
+
+def test_mha_workspace_size_formula():
+    # [batch][splits][heads] x (m, l) plus [batch][splits][heads][head_dim], fp32
+    n = ctypes.c_size_t(0)
+    assert L.library().lrkv_mha_decode_workspace_size(BF16, 2, 8, 64, 4096, 1000, 256, ctypes.byref(n)) == OK
+    assert n.value == 2 * 4 * 8 * (2 + 64) * 4
+    assert L.library().lrkv_mha_decode_workspace_size(BF16, 2, 8, 64, 4096, 0, 256, ctypes.byref(n)) == OK
+    assert n.value == 0
+
+
+def mha_call(**over):
+    a = dict(dtype=BF16, B=2, H=8, d_h=128, cap=256, k=FAKE, v=FAKE, lens=FAKE, max_len=200, q=FAKE, scale=0.0,
+             split=64, out=FAKE, ws=FAKE, ws_bytes=1 << 20)
+    a.update(over)
+    return L.library().lrkv_mha_decode(a["dtype"], a["B"], a["H"], a["d_h"], a["cap"], a["k"], a["v"], a["lens"],
+                                       a["max_len"], a["q"], a["scale"], a["split"], a["out"], a["ws"],
+                                       a["ws_bytes"], None)
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=4), DTYPE), (dict(d_h=96), SHAPE), (dict(H=0), SHAPE), (dict(split=100), SHAPE),
+    (dict(max_len=300), CAP), (dict(k=None), NULL), (dict(lens=None), NULL), (dict(out=None), NULL),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS), (dict(q=MIS), ALIGN), (dict(lens=FAKE + 2), ALIGN),
+])
+def test_mha_decode_rejects_before_launch(kw, want):
+    assert mha_call(**kw) == want
