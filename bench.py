@@ -381,7 +381,7 @@ def bench_project(args):
     pos = torch.zeros(B, dtype=torch.int32, device="cuda")
 
     def step():
-        L.lrkv_project_append(cache, pos, x, w)
+        L.lrkv_project_append(cache, pos, x, w, workspace=None)
 
     settled = settle(step, args.settle_s)
     for _ in range(args.warmup):
@@ -397,7 +397,9 @@ def bench_project(args):
     xd = torch.randn(Bd, 1, d, device="cuda").to(torch.bfloat16)
     cache_d = L.LrkvCache.empty(Bd, H, d_h, r, 64, dtype=torch.bfloat16, zero=False)
     pos_d = torch.full((Bd,), 5, dtype=torch.int32, device="cuda")
-    dec = lambda: L.lrkv_project_append(cache_d, pos_d, xd, w)
+    ws_d = torch.empty(max(L.lrkv_project_workspace_size(torch.bfloat16, Bd, 1, H, d_h, r, d), 16),
+                       dtype=torch.uint8, device="cuda")
+    dec = lambda: L.lrkv_project_append(cache_d, pos_d, xd, w, workspace=ws_d)
     for _ in range(args.warmup):
         dec()
     dec_ms = timed(stream, args.steps, dec)
@@ -416,7 +418,7 @@ def bench_project(args):
                      "traffic": traffic_from_profiles("project_counters", kernel, "project_bf16_B4_L4096_d4096"),
                      "kernel": kernel, "algorithmic_flops_per_launch": flops},
         "decode_shape": {"batch": Bd, "new_tokens": 1, "ms": dec_ms, "algorithmic_bytes": dec_bytes,
-                         "kernel": L.lrkv_project_kernel(torch.bfloat16, Bd, 1, H, d_h, r, d),
+                         "kernel": L.lrkv_project_kernel(torch.bfloat16, Bd, 1, H, d_h, r, d, True),
                          "GB_per_s": dec_bytes / (dec_ms * 1e-3) / 1e9},
     }
     copy_reference(args, rec)

@@ -235,6 +235,26 @@ lrkv_status lrkv_pack_projection(int32_t dtype, int32_t num_heads, int32_t head_
                                  int32_t d_model, const void* wk_shared, const void* wv_shared,
                                  const void* u_k, const void* u_v, void* w_packed, void* stream);
 
+/* Name of the kernel lrkv_project_append runs for these sizes on the current
+ * device, with (with_workspace != 0) or without a workspace:
+ * "project_gemm_kernel" (bf16 MFMA, 256-row tiles, when they are at least as
+ * many as the device's compute units), "project_splitk_kernel" (bf16 MFMA,
+ * at most 64 rows, with a workspace: the contraction split across
+ * workgroups, then a reduction kernel), "project_skinny_kernel" (the same
+ * rows without a workspace: one workgroup per 32 output columns),
+ * "project_append_kernel" (bf16 MFMA, 128 x 128 tiles, the rows in between)
+ * or "project_append_valu_kernel" (fp32, and bf16 widths that are not
+ * multiples of 32).  NULL for invalid sizes.  Host-only: launches nothing;
+ * the string is static. */
+const char* lrkv_project_kernel(int32_t dtype, int32_t batch, int32_t n_new, int32_t num_heads, int32_t head_dim,
+                                int32_t rank, int32_t d_model, int32_t with_workspace);
+
+/* Bytes of device workspace with which lrkv_project_append splits the
+ * contraction of these sizes across workgroups (fp32 partial sums); 0 where
+ * the sizes have no use for one.  Written to *bytes. */
+lrkv_status lrkv_project_workspace_size(int32_t dtype, int32_t batch, int32_t n_new, int32_t num_heads,
+                                        int32_t head_dim, int32_t rank, int32_t d_model, size_t* bytes);
+
 /* Fused projection + append: the cache rows of n_new new tokens computed from
  * their hidden states and written straight into the cache (slide "Cache
  * shared features and compact per-head latents", Eqs. (4)-(5)): for token i
@@ -245,27 +265,21 @@ lrkv_status lrkv_pack_projection(int32_t dtype, int32_t num_heads, int32_t head_
  * pos[b] + i of its array.  Slots outside [0, capacity) are dropped, as in
  * lrkv_append.
  *   x    [batch][n_new][d_model];  pos device int32 [batch].
+ *   workspace  optional (NULL, or at least lrkv_project_workspace_size
+ *        bytes, 16-byte aligned; contents on entry ignored): for a few tokens
+ *        it lets the contraction spread over more workgroups.  A smaller one
+ *        is not used.
  * bf16 with head_dim, num_heads*rank and d_model multiples of 32 runs on bf16
  * MFMA; other shapes and fp32 on vector-ALU fused multiply-adds.  x, w_packed
  * and the cache pointers must be 16-byte aligned; z_k and z_v may be NULL
  * when rank == 0.  batch*n_new must be below 2^31 and d_model at most 65536,
  * else LRKV_ERR_SHAPE. */
-/* Name of the kernel lrkv_project_append runs for these sizes on the current
- * device: "project_gemm_kernel" (bf16 MFMA, 256-row tiles, when they are at
- * least as many as the device's compute units), "project_skinny_kernel"
- * (bf16 MFMA, at most 64 rows: the weight read spread over columns and the
- * contraction), "project_append_kernel" (bf16 MFMA, 128 x 128 tiles, the
- * rows in between) or "project_append_valu_kernel" (fp32, and bf16 widths
- * that are not multiples of 32).  NULL for invalid sizes.  Host-only:
- * launches nothing; the string is static. */
-const char* lrkv_project_kernel(int32_t dtype, int32_t batch, int32_t n_new, int32_t num_heads, int32_t head_dim,
-                                int32_t rank, int32_t d_model);
-
 lrkv_status lrkv_project_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
                                 int32_t rank, int64_t capacity,
                                 void* k_shared, void* v_shared, void* z_k, void* z_v,
                                 const int32_t* pos, int32_t n_new, int32_t d_model,
-                                const void* x, const void* w_packed, void* stream);
+                                const void* x, const void* w_packed, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Plain multi-head attention decode over a full per-head K/V cache, the
  * baseline LRKV's cache is compared with at a matched shape (slide "Can

@@ -9,5 +9,5 @@ from .binding import (  # noqa: F401
     lrkv_append, lrkv_cache_elems_per_token, lrkv_decode, lrkv_decode_scan_kernel, lrkv_decode_workspace_size,
     lrkv_mha_decode, lrkv_mha_decode_workspace_size,
     lrkv_pack_projection, lrkv_prefill, lrkv_prefill_chunk, lrkv_project_append, lrkv_project_kernel,
-    lrkv_status_string,
+    lrkv_project_workspace_size, lrkv_status_string,
 )

@@ -27,7 +27,7 @@ STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DT
 EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
             "lrkv_decode_combine", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
-            "lrkv_project_kernel", "lrkv_project_append", "lrkv_mha_decode_workspace_size", "lrkv_mha_decode")
+            "lrkv_project_kernel", "lrkv_project_workspace_size", "lrkv_project_append", "lrkv_mha_decode_workspace_size", "lrkv_mha_decode")
 
 
 class LrkvError(RuntimeError):
@@ -73,9 +73,11 @@ def library() -> ctypes.CDLL:
         lib.lrkv_pack_projection.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
         lib.lrkv_pack_projection.restype = _i32
         lib.lrkv_project_append.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
-                                            _vp, _vp, _vp]
+                                            _vp, _vp, _vp, _sz, _vp]
         lib.lrkv_project_append.restype = _i32
-        lib.lrkv_project_kernel.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
+        lib.lrkv_project_kernel.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
+        lib.lrkv_project_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+        lib.lrkv_project_workspace_size.restype = _i32
         lib.lrkv_project_kernel.restype = ctypes.c_char_p
         lib.lrkv_mha_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i64, _i64, _i32, ctypes.POINTER(_sz)]
         lib.lrkv_mha_decode_workspace_size.restype = _i32
@@ -354,24 +356,43 @@ def lrkv_pack_projection(wk_shared, wv_shared, u_k, u_v, out: Optional[torch.Ten
 
 
 def lrkv_project_kernel(dtype: torch.dtype, batch: int, n_new: int, heads: int, head_dim: int, rank: int,
-                        d_model: int) -> Optional[str]:
+                        d_model: int, with_workspace: bool = True) -> Optional[str]:
     """Name of the kernel lrkv_project_append runs for these sizes (None if invalid)."""
-    name = library().lrkv_project_kernel(_dtype_code(dtype), batch, n_new, heads, head_dim, rank, d_model)
+    name = library().lrkv_project_kernel(_dtype_code(dtype), batch, n_new, heads, head_dim, rank, d_model,
+                                         int(bool(with_workspace)))
     return None if name is None else name.decode()
 
 
-def lrkv_project_append(cache: LrkvCache, pos: torch.Tensor, x: torch.Tensor, w_packed: torch.Tensor) -> None:
+def lrkv_project_workspace_size(dtype: torch.dtype, batch: int, n_new: int, heads: int, head_dim: int, rank: int,
+                                d_model: int) -> int:
+    n = _sz(0)
+    _check(library().lrkv_project_workspace_size(_dtype_code(dtype), batch, n_new, heads, head_dim, rank, d_model,
+                                                 ctypes.byref(n)),
+           "lrkv_project_workspace_size")
+    return int(n.value)
+
+
+def lrkv_project_append(cache: LrkvCache, pos: torch.Tensor, x: torch.Tensor, w_packed: torch.Tensor,
+                        workspace="auto") -> None:
     """Fused projection + append: the cache rows of x [B][n_new][d] computed
-    with the packed weight and written at slots pos[b].. (see lrkv.h)."""
+    with the packed weight and written at slots pos[b].. (see lrkv.h).
+    workspace: "auto" allocates the one the sizes can use, None passes none,
+    or a uint8 device tensor."""
     dt = cache.dtype
     B, n_new, d = x.shape
     if B != cache.batch:
         raise ValueError("x and cache differ in batch")
     _shape(w_packed, "w_packed", (2 * (cache.head_dim + cache.heads * cache.rank), d))
     _shape(pos, "pos", (B,))
+    if isinstance(workspace, str):
+        nbytes = lrkv_project_workspace_size(dt, B, n_new, cache.heads, cache.head_dim, cache.rank, d) if n_new else 0
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device) if nbytes else None
+    ws_ptr = _ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
     _check(library().lrkv_project_append(_dtype_code(dt), cache.batch, cache.heads, cache.head_dim, cache.rank,
                                          cache.capacity, *cache.pointers(), _ptr(pos, "pos", torch.int32), n_new,
-                                         d, _ptr(x, "x", dt), _ptr(w_packed, "w_packed", dt), _stream()),
+                                         d, _ptr(x, "x", dt), _ptr(w_packed, "w_packed", dt), ws_ptr, ws_bytes,
+                                         _stream()),
            "lrkv_project_append")
 
 

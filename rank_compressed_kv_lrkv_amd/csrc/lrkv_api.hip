@@ -326,16 +326,26 @@ lrkv_status lrkv_pack_projection(int32_t dtype, int32_t num_heads, int32_t head_
 }
 
 const char* lrkv_project_kernel(int32_t dtype, int32_t batch, int32_t n_new, int32_t num_heads, int32_t head_dim,
-                                int32_t rank, int32_t d_model) {
+                                int32_t rank, int32_t d_model, int32_t with_workspace) {
   if (check_sizes(dtype, batch, num_heads, head_dim, rank, 1) != LRKV_OK) return nullptr;
   if (batch < 1 || n_new < 1 || d_model < 1 || d_model > 65536 || int64_t(batch) * n_new >= INT32_MAX) return nullptr;
-  return lrkv::project_kernel_name(dtype, batch, n_new, num_heads, head_dim, rank, d_model);
+  return lrkv::project_kernel_name(dtype, batch, n_new, num_heads, head_dim, rank, d_model, with_workspace != 0);
+}
+
+lrkv_status lrkv_project_workspace_size(int32_t dtype, int32_t batch, int32_t n_new, int32_t num_heads,
+                                        int32_t head_dim, int32_t rank, int32_t d_model, size_t* bytes) {
+  if (!bytes) return LRKV_ERR_NULL;
+  const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, 1);
+  if (st != LRKV_OK) return st;
+  if (n_new < 0 || d_model < 1 || d_model > 65536 || int64_t(batch) * n_new >= INT32_MAX) return LRKV_ERR_SHAPE;
+  *bytes = lrkv::project_workspace_bytes(dtype, batch, n_new, num_heads, head_dim, rank, d_model);
+  return LRKV_OK;
 }
 
 lrkv_status lrkv_project_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
                                 int32_t rank, int64_t capacity, void* k_shared, void* v_shared, void* z_k,
                                 void* z_v, const int32_t* pos, int32_t n_new, int32_t d_model, const void* x,
-                                const void* w_packed, void* stream) {
+                                const void* w_packed, void* workspace, size_t workspace_bytes, void* stream) {
   const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, capacity);
   if (st != LRKV_OK) return st;
   if (n_new < 0 || d_model < 1 || d_model > 65536) return LRKV_ERR_SHAPE;
@@ -347,10 +357,13 @@ lrkv_status lrkv_project_append(int32_t dtype, int32_t batch, int32_t num_heads,
   if (!aligned16(k_shared) || !aligned16(v_shared) || !aligned4(pos) || !aligned16(x) || !aligned16(w_packed))
     return LRKV_ERR_ALIGN;
   if (rank > 0 && (!aligned16(z_k) || !aligned16(z_v))) return LRKV_ERR_ALIGN;
+  if (workspace && !aligned16(workspace)) return LRKV_ERR_ALIGN;
   lrkv::ProjectArgs a;
   a.dtype = dtype; a.batch = batch; a.heads = num_heads; a.head_dim = head_dim; a.rank = rank;
   a.d_model = d_model; a.n_new = n_new; a.capacity = capacity;
   a.k_s = k_shared; a.v_s = v_shared; a.z_k = z_k; a.z_v = z_v; a.pos = pos; a.x = x; a.w = w_packed;
+  a.ws = static_cast<float*>(workspace);
+  a.ws_bytes = workspace ? workspace_bytes : 0;
   return lrkv::launch_project_append(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LRKV_OK
                                                                                         : LRKV_ERR_DEVICE;
 }

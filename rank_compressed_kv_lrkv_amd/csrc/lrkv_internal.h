@@ -79,13 +79,20 @@ struct ProjectArgs {
   const int32_t* pos;      // device [batch]
   const void* x;           // [batch][n_new][d_model]
   const void* w;           // packed projection [2(head_dim + heads*rank)][d_model]
+  float* ws;               // optional workspace for the split-contraction path (NULL: not used)
+  size_t ws_bytes;
 };
 // Shapes the MFMA projection takes: bf16, head_dim and heads*rank multiples
 // of 32, d_model a multiple of 32 (others run on the vector-ALU kernel).
 bool project_mfma_supported(int dtype, int head_dim, int rank, int heads, int d_model);
 hipError_t launch_project_append(const ProjectArgs& a, hipStream_t stream);
-// Name of the kernel launch_project_append runs for these sizes on the current device.
-const char* project_kernel_name(int dtype, int batch, int n_new, int heads, int head_dim, int rank, int d_model);
+// Name of the kernel launch_project_append runs for these sizes on the current
+// device, with or without a workspace of project_workspace_bytes.
+const char* project_kernel_name(int dtype, int batch, int n_new, int heads, int head_dim, int rank, int d_model,
+                                bool with_workspace);
+// Workspace bytes that let these sizes split the contraction across workgroups (0: no use for one).
+size_t project_workspace_bytes(int dtype, int batch, int n_new, int heads, int head_dim, int rank, int d_model);
+size_t project_ws_bytes(long M, long N, int d_model);
 
 struct PackArgs {
   int dtype, heads, head_dim, rank, d_model;

@@ -421,6 +421,101 @@ __global__ __launch_bounds__(kPsThreads) void project_skinny_kernel(ProjectParam
 }
 
 // ---------------------------------------------------------------------------
+// The same few-token projection with the contraction also split across
+// workgroups, when the caller passes a workspace: the weight read (the whole
+// cost) then spreads over (N / 32) x S workgroups instead of N / 32.
+// Workgroup (column block, slice s) sums its slice of 16-wide chunks over
+// its 4 waves and writes the fp32 partial C_s [M][N] to the workspace; a
+// second kernel adds the S partials of each output, rounds once and stores
+// at the cache slot.
+// ---------------------------------------------------------------------------
+constexpr int kPkThreads = 256, kPkWaves = 4, kPkUnroll = 4, kPkMaxSlices = 16;
+
+int project_slices(int d_model) {
+  const int chunks = d_model / 16;
+  return max(1, min(kPkMaxSlices, chunks / kPkWaves));   // at least one chunk per wave and slice
+}
+
+template <int MT>
+__global__ __launch_bounds__(kPkThreads) void project_splitk_kernel(ProjectParams p, float* ws, int slices) {
+  __shared__ float s_red[kPkWaves * MT * 16 * 64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_lane = lane & 31, hf = lane >> 5;
+  const int n0 = blockIdx.x * 32, sl = blockIdx.y;
+  const int kchunks = p.K / 16;
+  const int c_lo = sl * kchunks / slices, c_hi = (sl + 1) * kchunks / slices;
+  const uint32_t row_bytes = uint32_t(p.K) * 2;
+  const __amdgpu_buffer_rsrc_t wres = buffer_resource(p.w + size_t(n0) * p.K, uint32_t(min(32, p.N - n0)) * row_bytes);
+  const __amdgpu_buffer_rsrc_t xres = buffer_resource(p.x, uint32_t(p.M) * row_bytes);   // rows >= M read zero
+  const uint32_t w_off = uint32_t(min(n_lane, p.N - n0 - 1)) * row_bytes + hf * 16;
+  uint32_t x_off[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) x_off[i] = uint32_t(i * 32 + n_lane) * row_bytes + hf * 16;
+
+  f32x16_t acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = f32x16_t{};
+  for (int c0 = c_lo + wave; c0 < c_hi; c0 += kPkWaves * kPkUnroll) {
+    u32x4 bw[kPkUnroll], ax[kPkUnroll][MT];
+#pragma unroll
+    for (int u = 0; u < kPkUnroll; ++u) {
+      const uint32_t koff = uint32_t(min(c0 + kPkWaves * u, c_hi - 1)) * 32;
+      bw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, int(w_off + koff), 0, kStream));
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        ax[u][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, int(x_off[i] + koff), 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < kPkUnroll; ++u)
+      if (c0 + kPkWaves * u < c_hi)                        // uniform
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i] = mfma32(as_bf16x8(ax[u][i]), as_bf16x8(bw[u]), acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s_red[((wave * MT + i) * 16 + e) * 64 + lane] = acc[i][e];
+  __syncthreads();
+  // wave w adds up elements 4w .. 4w + 3 of every row tile and writes them
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 4 * wave + k;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kPkWaves; ++w) v += s_red[((w * MT + i) * 16 + e) * 64 + lane];
+      const int m = i * 32 + 8 * (e / 4) + 4 * hf + (e % 4);
+      if (m < p.M) ws[(size_t(sl) * p.M + m) * p.N + n0 + n_lane] = v;
+    }
+}
+
+// Thread t adds up outputs 4t .. 4t + 3 (N is a multiple of 32, so they share
+// a row and an array) over the slices, all slices' loads issued together.
+__global__ __launch_bounds__(256) void project_reduce_kernel(ProjectParams p, const float* ws, int slices) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (4 * t >= p.M * p.N) return;
+  const int m = (4 * t) / p.N, n = 4 * t - m * p.N;
+  float4 part[kPkMaxSlices];
+#pragma unroll
+  for (int s = 0; s < kPkMaxSlices; ++s)
+    part[s] = s < slices ? *reinterpret_cast<const float4*>(ws + (size_t(s) * p.M + m) * p.N + n)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 v = part[0];
+#pragma unroll
+  for (int s = 1; s < kPkMaxSlices; ++s) {
+    v.x += part[s].x; v.y += part[s].y; v.z += part[s].z; v.w += part[s].w;
+  }
+  const long row = cache_row(p, m);
+  if (row < 0) return;
+  int col0, width;
+  uint16_t* base = column_target(p, n & ~31, &col0, &width);
+  uint16_t* dst = base + size_t(row) * width + col0 + (n & 31);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
+// ---------------------------------------------------------------------------
 // Vector-ALU projection for the shapes the MFMA kernel does not take (fp32,
 // or bf16 with array widths that are not multiples of 32): a 64 x 64 block of
 // C per workgroup, 4 x 4 outputs per lane, the contraction staged through LDS
@@ -553,13 +648,26 @@ hipError_t launch_gemm(const ProjectParams& p, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
-const char* project_kernel_name(int dtype, int batch, int n_new, int heads, int head_dim, int rank, int d_model) {
+size_t project_ws_bytes(long M, long N, int d_model) {
+  return size_t(project_slices(d_model)) * size_t(M) * size_t(N) * sizeof(float);
+}
+
+size_t project_workspace_bytes(int dtype, int batch, int n_new, int heads, int head_dim, int rank, int d_model) {
+  const long M = long(batch) * n_new, N = 2L * (head_dim + long(heads) * rank);
+  if (!project_mfma_supported(dtype, head_dim, rank, heads, d_model) || M > 64 || M <= 0) return 0;
+  const int tj = N % 320 == 0 ? 5 : 4;
+  if (d_model % kPgBK == 0 && (M + 255) / 256 * ((N + 64 * tj - 1) / (64 * tj)) >= device_cus()) return 0;
+  return project_ws_bytes(M, N, d_model);
+}
+
+const char* project_kernel_name(int dtype, int batch, int n_new, int heads, int head_dim, int rank, int d_model,
+                                bool with_workspace) {
   if (!project_mfma_supported(dtype, head_dim, rank, heads, d_model)) return "project_append_valu_kernel";
   const long M = long(batch) * n_new, N = 2L * (head_dim + long(heads) * rank);
   const int tj = N % 320 == 0 ? 5 : 4;
   if (d_model % kPgBK == 0 && (M + 255) / 256 * ((N + 64 * tj - 1) / (64 * tj)) >= device_cus())
     return "project_gemm_kernel";
-  if (M <= 64) return "project_skinny_kernel";
+  if (M <= 64) return with_workspace ? "project_splitk_kernel" : "project_skinny_kernel";
   return "project_append_kernel";
 }
 
@@ -586,6 +694,18 @@ hipError_t launch_project_append(const ProjectArgs& a, hipStream_t st) {
       const dim3 grid{unsigned(big_tiles)};
       if (tj == 5) return launch_gemm<5>(p, grid, st);
       return launch_gemm<4>(p, grid, st);
+    }
+    if (p.M <= 64 && a.ws != nullptr && a.ws_bytes >= project_ws_bytes(p.M, p.N, p.K)) {
+      // a few tokens, with a workspace: the contraction split across workgroups too
+      const int slices = project_slices(p.K);
+      const dim3 grid(unsigned(p.N / 32), unsigned(slices));
+      if (p.M <= 32) hipLaunchKernelGGL(project_splitk_kernel<1>, grid, dim3(kPkThreads), 0, st, p, a.ws, slices);
+      else hipLaunchKernelGGL(project_splitk_kernel<2>, grid, dim3(kPkThreads), 0, st, p, a.ws, slices);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(project_reduce_kernel, dim3(unsigned((p.M * p.N / 4 + 255) / 256)), dim3(256), 0, st, p,
+                         static_cast<const float*>(a.ws), slices);
+      return hipGetLastError();
     }
     if (p.M <= 64) {
       // a few tokens: spread the weight read over columns and contraction

@@ -213,10 +213,11 @@ def test_prefill_chunk_empty_is_noop():
 
 def project_call(**over):
     a = dict(dtype=BF16, B=2, H=8, d_h=64, r=8, cap=256, k=FAKE, v=FAKE, zk=FAKE, zv=FAKE, pos=FAKE, n=16, d=512,
-             x=FAKE, w=FAKE)
+             x=FAKE, w=FAKE, ws=None, ws_bytes=0)
     a.update(over)
     return L.library().lrkv_project_append(a["dtype"], a["B"], a["H"], a["d_h"], a["r"], a["cap"], a["k"], a["v"],
-                                           a["zk"], a["zv"], a["pos"], a["n"], a["d"], a["x"], a["w"], None)
+                                           a["zk"], a["zv"], a["pos"], a["n"], a["d"], a["x"], a["w"], a["ws"],
+                                           a["ws_bytes"], None)
 
 
 @no_gpu
@@ -225,6 +226,7 @@ def project_call(**over):
     (dict(d_h=20), SHAPE), (dict(cap=0), SHAPE),
     (dict(x=None), NULL), (dict(w=None), NULL), (dict(pos=None), NULL), (dict(zv=None), NULL),
     (dict(x=MIS), ALIGN), (dict(w=MIS), ALIGN), (dict(pos=FAKE + 2), ALIGN), (dict(zk=MIS), ALIGN),
+    (dict(ws=MIS, ws_bytes=1 << 20), ALIGN),
 ])
 def test_project_append_rejects_before_launch(kw, want):
     assert project_call(**kw) == want
@@ -259,20 +261,33 @@ def test_pack_projection_empty_is_noop():
 
 
 def test_project_kernel_names():
-    # host-only: the choice depends on the sizes (and on the compute-unit count
-    # for the large-tile kernel; 256 on MI355X, also the value assumed without a GPU)
+    # host-only: the choice depends on the sizes, on whether a workspace is
+    # given, and on the compute-unit count for the large-tile kernel (256 on
+    # MI355X, also the value assumed without a GPU)
     k = lambda *a: L.lrkv_project_kernel(*a)
     bf, f32 = torch.bfloat16, torch.float32
     assert k(f32, 4, 4096, 32, 128, 16, 4096) == "project_append_valu_kernel"
     assert k(bf, 2, 33, 3, 40, 8, 72) == "project_append_valu_kernel"
-    assert k(bf, 32, 1, 32, 128, 16, 4096) == "project_skinny_kernel"
-    assert k(bf, 8, 8, 32, 128, 16, 4096) == "project_skinny_kernel"
+    assert k(bf, 32, 1, 32, 128, 16, 4096) == "project_splitk_kernel"
+    assert k(bf, 32, 1, 32, 128, 16, 4096, False) == "project_skinny_kernel"
+    assert k(bf, 8, 8, 32, 128, 16, 4096, False) == "project_skinny_kernel"
     assert k(bf, 2, 130, 32, 128, 16, 4096) == "project_append_kernel"
     assert k(bf, 4, 4096, 32, 128, 16, 4064) == "project_append_kernel"      # d not a multiple of 64
     if not torch.cuda.is_available() or torch.cuda.get_device_properties(0).multi_processor_count == 256:
         assert k(bf, 4, 4096, 32, 128, 16, 4096) == "project_gemm_kernel"
     assert k(bf, 0, 4, 32, 128, 16, 4096) is None
     assert k(bf, 4, 4, 32, 128, 16, 0) is None
+
+
+def test_project_workspace_size():
+    # a few tokens: 16 slices of the contraction (at least one 16-wide chunk
+    # per wave), one fp32 partial per slice, token and output; else none
+    ws = lambda *a: L.lrkv_project_workspace_size(*a)
+    bf = torch.bfloat16
+    assert ws(bf, 32, 1, 32, 128, 16, 4096) == 16 * 32 * 1280 * 4
+    assert ws(bf, 8, 8, 8, 64, 8, 128) == 2 * 64 * 256 * 4          # 8 chunks: 2 slices
+    assert ws(bf, 2, 130, 32, 128, 16, 4096) == 0
+    assert ws(torch.float32, 1, 4, 4, 16, 4, 64) == 0
 
 
 def test_mha_workspace_size_formula():

@@ -75,15 +75,16 @@ def check_cache(cache, rows, pos, dt, T):
     return worst
 
 
-def run_case(dt, B, n, d, H, d_h, r, T, pos, seed, kernel=None):
-    name = L.lrkv_project_kernel(TORCH_DT[dt], B, n, H, d_h, r, d)
+def run_case(dt, B, n, d, H, d_h, r, T, pos, seed, kernel=None, workspace=True):
+    name = L.lrkv_project_kernel(TORCH_DT[dt], B, n, H, d_h, r, d, workspace)
     say(f"case project {dt} B={B} n={n} d={d} H={H} d_h={d_h} r={r} T={T} pos={list(pos)[:4]} kernel={name}")
     if kernel is not None:
         assert name == kernel
     inp = projection_inputs(batch=B, n_new=n, d_model=d, heads=H, head_dim=d_h, rank=r, dtype=dt, seed=seed)
     w = packed_weight(inp)
     cache = canary_cache(B, T, H, d_h, r, dt)
-    L.lrkv_project_append(cache, torch.tensor(np.asarray(pos, np.int32)).cuda(), to_dev(inp["x"], dt), w)
+    L.lrkv_project_append(cache, torch.tensor(np.asarray(pos, np.int32)).cuda(), to_dev(inp["x"], dt), w,
+                          workspace="auto" if workspace else None)
     torch.cuda.synchronize()
     return check_cache(cache, oracle_rows(inp), pos, dt, T)
 
@@ -104,18 +105,23 @@ def test_project_append_parity(dt, B, n, d, H, d_h, r):
     run_case(dt, B, n, d, H, d_h, r, T, pos, seed=1000 + d + n, kernel=name)
 
 
-def test_project_append_decode_shape():
+@pytest.mark.parametrize("workspace", [True, False])
+def test_project_append_decode_shape(workspace):
     # one new token per sequence over the bf16 model shape (a decode step's projection)
     run_case("bf16", 32, 1, 4096, 32, 128, 16, 40, [(7 * b) % 40 for b in range(32)], seed=77,
-             kernel="project_skinny_kernel")
+             kernel="project_splitk_kernel" if workspace else "project_skinny_kernel", workspace=workspace)
 
 
-@pytest.mark.parametrize("B,n,d", [(1, 1, 4096), (1, 17, 544), (8, 4, 256), (3, 11, 4096), (8, 8, 1024)])
-def test_project_append_few_tokens(B, n, d):
-    # at most 64 rows: one or two 32-row tiles, contraction split over the waves
-    # (d = 544: 34 chunks of 16, not a multiple of the 16 waves x 8 in flight)
+@pytest.mark.parametrize("workspace", [True, False])
+@pytest.mark.parametrize("B,n,d", [(1, 1, 4096), (1, 17, 544), (8, 4, 256), (3, 11, 4096), (8, 8, 1024),
+                                   (2, 5, 96)])
+def test_project_append_few_tokens(B, n, d, workspace):
+    # at most 64 rows: one or two 32-row tiles; without a workspace the contraction
+    # is split over one workgroup's waves (d = 544: 34 chunks of 16, not a multiple
+    # of the 16 waves x 8 in flight), with one also across workgroups (slices of
+    # uneven length; d = 96: 6 chunks, one slice)
     run_case("bf16", B, n, d, 32, 128, 16, n + 5, [(3 * b) % 5 for b in range(B)], seed=300 + B * n + d,
-             kernel="project_skinny_kernel")
+             kernel="project_splitk_kernel" if workspace else "project_skinny_kernel", workspace=workspace)
 
 
 @pytest.mark.parametrize("B,n,d,r", [
