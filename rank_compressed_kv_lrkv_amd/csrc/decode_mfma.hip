@@ -277,21 +277,30 @@ void decode_mfma_kernel(MfParams p) {
   if constexpr (R > 0) {
     // part[e] = sum over this lane's d of q_h[d] B^K_h[d][i0 + e]; q_h[d] is
     // element ek + gq of chunk k / CPR, with ek = 8 (k % CPR) / CPR from the
-    // load index and gq = g / CPR from the lane (selected, not indexed)
+    // load index and gq = g / CPR from the lane (selected, not indexed);
+    // NBK is even (DH >= 64), so loads pair up for dot2
     const int gq = g / CPR;
     float part[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[e] = 0.f;
-#pragma unroll
-    for (int k = 0; k < NBK; ++k) {
+    auto q_bits = [&](int k) -> uint32_t {                   // bf16 bits of q_h[d] for load k
       const u32x4 qc = qrow[k / CPR];
       const int el = 8 * (k % CPR) / CPR + gq;               // element of the chunk, 0..7
       const uint32_t w01 = (el & 2) ? qc.y : qc.x, w23 = (el & 2) ? qc.w : qc.z;
       const uint32_t w = (el & 4) ? w23 : w01;
-      const float qd = __uint_as_float((el & 1) ? (w & 0xffff0000u) : (w << 16));
-      const uint32_t bw[4] = {bkv[k].x, bkv[k].y, bkv[k].z, bkv[k].w};
+      return (el & 1) ? (w >> 16) : (w & 0xffffu);
+    };
+    // loads k and k + 1 in one bf16 dot2 per output: (q[d_k], q[d_k+1]) . (B_k[e], B_k+1[e])
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[e] = __builtin_fmaf(qd, bf16_to_f32(elem_at<BF16>(bw, e)), part[e]);
+    for (int k = 0; k < NBK; k += 2) {
+      const uint32_t qp = q_bits(k) | (q_bits(k + 1) << 16);
+      const uint32_t b0[4] = {bkv[k].x, bkv[k].y, bkv[k].z, bkv[k].w};
+      const uint32_t b1[4] = {bkv[k + 1].x, bkv[k + 1].y, bkv[k + 1].z, bkv[k + 1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bp = __builtin_amdgcn_perm(b1[e / 2], b0[e / 2], (e & 1) ? 0x07060302u : 0x05040100u);
+        part[e] = BF16::dot2(part[e], qp, bp);
+      }
     }
     // sum over the lanes of the head with the same g % CPR (xor of the bits above CPR)
     auto xor_add = [&]<int M>(std::integral_constant<int, M>) {
