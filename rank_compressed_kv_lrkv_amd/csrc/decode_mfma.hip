@@ -80,7 +80,7 @@ struct MfShape {
   static constexpr int GL = KG * 2 * LPT;      // loads per latent group
   static constexpr int D = 4;                  // latent groups in flight
   static constexpr int TILES = kMfWaves * 2 * VT + kMfHeads * (R > 0 ? R : 1) * 4;   // tiles, absorbed query
-  static constexpr int FOLD = (3 * 64 * (16 * VB + (R > 0 ? R / 2 : 0) + 4) + kMfWaves * kMfHeads) * 4;
+  static constexpr int FOLD = (kMfWaves * 64 * (16 * VB + (R > 0 ? R / 2 : 0) + 4) + kMfWaves * kMfHeads) * 4;
   static constexpr int LDS = TILES > FOLD ? TILES : FOLD;
   static_assert(DH % 32 == 0 && VT % 1024 == 0, "tiles made of 1 KB transfers");
   static_assert(R % 8 == 0 && R <= 32, "latent rows of whole 16-byte units");
@@ -506,8 +506,8 @@ void decode_mfma_kernel(MfParams p) {
   //      scaled by 2^(m - M) and added (Eq. (7) is linear in the weights).
   //      The tile memory is reused once every transfer into it has landed. ----
   constexpr int P = 16 * S::VB + (R > 0 ? R / 2 : 0) + 4;   // floats per lane (stride conflict-free for 16-byte access)
-  float* const s_red = reinterpret_cast<float*>(smem);      // [wave 1..3][lane][P]
-  float* const s_m = s_red + 3 * 64 * P;                    // [wave][head]
+  float* const s_red = reinterpret_cast<float*>(smem);      // [wave][lane][P]
+  float* const s_m = s_red + kMfWaves * 64 * P;             // [wave][head]
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
   if (hf == 0) s_m[wave * kMfHeads + j] = m;
@@ -516,66 +516,63 @@ void decode_mfma_kernel(MfParams p) {
 #pragma unroll
   for (int w = 1; w < kMfWaves; ++w) M = fmaxf(M, s_m[w * kMfHeads + j]);   // finite: wave 0 has tokens
   const float sc = m == -INFINITY ? 0.f : fast_exp2(m - M);
-  lsum *= sc;
-#pragma unroll
-  for (int f = 0; f < S::VB; ++f) oacc[f] *= sc;
-#pragma unroll
-  for (int i = 0; i < (R > 0 ? R / 2 : 1); ++i) acc_z[i] *= sc;
-  if (wave > 0) {
-    float* dst = s_red + ((wave - 1) * 64 + lane) * P;
+  {
+    float* dst = s_red + (wave * 64 + lane) * P;
 #pragma unroll
     for (int f = 0; f < S::VB; ++f)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4)
-        *reinterpret_cast<float4*>(dst + 16 * f + 4 * r4) =
-            make_float4(oacc[f][4 * r4], oacc[f][4 * r4 + 1], oacc[f][4 * r4 + 2], oacc[f][4 * r4 + 3]);
+        *reinterpret_cast<float4*>(dst + 16 * f + 4 * r4) = make_float4(
+            oacc[f][4 * r4] * sc, oacc[f][4 * r4 + 1] * sc, oacc[f][4 * r4 + 2] * sc, oacc[f][4 * r4 + 3] * sc);
     if constexpr (R > 0) {
 #pragma unroll
       for (int i = 0; i < R / 2; i += 4)
-        *reinterpret_cast<float4*>(dst + 16 * S::VB + i) = make_float4(acc_z[i], acc_z[i + 1], acc_z[i + 2], acc_z[i + 3]);
+        *reinterpret_cast<float4*>(dst + 16 * S::VB + i) =
+            make_float4(acc_z[i] * sc, acc_z[i + 1] * sc, acc_z[i + 2] * sc, acc_z[i + 3] * sc);
     }
-    dst[P - 4] = lsum;
+    dst[P - 4] = lsum * sc;
   }
   __syncthreads();
-  if (wave > 0) return;
+  // Block x of the state (value block f = x for x < VB; the latent sums and
+  // the softmax sum for x = VB) is added up over the waves and written by
+  // wave x % 4, so the four waves share the final reads and stores.
+  const size_t pidx = size_t(item) * H + h;
+  float* const out_acc = p.ws_acc + pidx * (DH + R);
+  const float* const src0 = s_red + lane * P;               // this lane's slot of wave 0
 #pragma unroll
-  for (int w = 0; w < kMfWaves - 1; ++w) {
-    const float* src = s_red + (w * 64 + lane) * P;
+  for (int f = 0; f < S::VB; ++f) {
+    if (f % kMfWaves != wave) continue;                     // uniform
 #pragma unroll
-    for (int f = 0; f < S::VB; ++f)
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 a = *reinterpret_cast<const float4*>(src0 + 16 * f + 4 * r4);
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + 16 * f + 4 * r4);
-        oacc[f][4 * r4] += v.x; oacc[f][4 * r4 + 1] += v.y; oacc[f][4 * r4 + 2] += v.z; oacc[f][4 * r4 + 3] += v.w;
+      for (int w = 1; w < kMfWaves; ++w) {
+        const float4 v = *reinterpret_cast<const float4*>(src0 + w * 64 * P + 16 * f + 4 * r4);
+        a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
       }
+      *reinterpret_cast<float4*>(out_acc + 32 * f + 8 * r4 + 4 * hf) = a;
+    }
+  }
+  if (S::VB % kMfWaves == wave) {
     if constexpr (R > 0) {
 #pragma unroll
       for (int i = 0; i < R / 2; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + 16 * S::VB + i);
-        acc_z[i] += v.x; acc_z[i + 1] += v.y; acc_z[i + 2] += v.z; acc_z[i + 3] += v.w;
+        float4 a = *reinterpret_cast<const float4*>(src0 + 16 * S::VB + i);
+#pragma unroll
+        for (int w = 1; w < kMfWaves; ++w) {
+          const float4 v = *reinterpret_cast<const float4*>(src0 + w * 64 * P + 16 * S::VB + i);
+          a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+        }
+        *reinterpret_cast<float4*>(out_acc + DH + hf * (R / 2) + i) = a;
       }
     }
-    lsum += src[P - 4];
-  }
-  {
-    uint32_t x0 = __float_as_uint(lsum), x1 = x0;
+    float ls = src0[P - 4];
+#pragma unroll
+    for (int w = 1; w < kMfWaves; ++w) ls += src0[w * 64 * P + P - 4];
+    uint32_t x0 = __float_as_uint(ls), x1 = x0;
     swap_halves(x0, x1);                                     // the two halves' sums of this head
-    lsum = __uint_as_float(x0) + __uint_as_float(x1);
-  }
-  const size_t pidx = size_t(item) * H + h;
-  if (hf == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * pidx) = make_float2(M, lsum);
-  float* dst = p.ws_acc + pidx * (DH + R);
-#pragma unroll
-  for (int f = 0; f < S::VB; ++f)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *reinterpret_cast<float4*>(dst + 32 * f + 8 * r4 + 4 * hf) =
-          make_float4(oacc[f][4 * r4], oacc[f][4 * r4 + 1], oacc[f][4 * r4 + 2], oacc[f][4 * r4 + 3]);
-  if constexpr (R > 0) {
-#pragma unroll
-    for (int i = 0; i < R / 2; i += 4)
-      *reinterpret_cast<float4*>(dst + DH + hf * (R / 2) + i) =
-          make_float4(acc_z[i], acc_z[i + 1], acc_z[i + 2], acc_z[i + 3]);
+    ls = __uint_as_float(x0) + __uint_as_float(x1);
+    if (hf == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * pidx) = make_float2(M, ls);
   }
 }
 
