@@ -8,8 +8,9 @@
 // The work is one matrix-vector product per head and token, so the scan is
 // HBM-bound on the vector ALUs: a workgroup (4 waves) takes one sequence, one
 // split of its tokens and 32 heads; 8 lanes share a head, each owning d_h/8
-// dimensions.  Per token the 8 heads of a wave are 8 contiguous rows, so a
-// wave's loads for one token cover 8 d_h elements of every row in one run.
+// dimensions in 16-byte pieces: piece c of lane g is bytes
+// [128 c + 16 g, 128 c + 16 g + 16) of the head's row, so each load
+// instruction of a wave reads one whole 128-byte line of each of its 8 heads.
 // MhaUnroll tokens are loaded together (non-temporal, through buffer
 // resources, so tokens past the split read zeros), then scored with a DPP
 // sum over the 8 lanes, folded into a running max / sum / output in the log2
@@ -54,11 +55,17 @@ __global__ __launch_bounds__(kMhaThreads) void mha_split_kernel(MhaParams p) {
   if (t0 >= len) return;                               // uniform over the workgroup
   const int n = min(p.split_tokens, len - t0);
 
-  // query slice, pre-scaled into the log2 domain
+  constexpr int NPC = SB / 16;                         // 16-byte pieces per lane
+  constexpr int EPC = 16 / E::kBytes;                  // elements per piece
+  // query slice, pre-scaled into the log2 domain: element e of the lane is
+  // dimension (128 (e / EPC) + 16 g) / kBytes + e % EPC
   float qf[DPL];
   {
+    const unsigned char* qrow = reinterpret_cast<const unsigned char*>(static_cast<const T*>(p.q) +
+                                                                        (size_t(b) * H + hc) * DH);
     uint32_t w[SB / 4];
-    load_words<SB>(w, static_cast<const T*>(p.q) + (size_t(b) * H + hc) * DH + g * DPL);
+#pragma unroll
+    for (int c = 0; c < NPC; ++c) load_words<16>(w + 4 * c, qrow + 128 * c + 16 * g);
 #pragma unroll
     for (int e = 0; e < DPL; ++e) qf[e] = E::to_f32(elem_at<E>(w, e)) * p.scale_log2;
   }
@@ -67,7 +74,7 @@ __global__ __launch_bounds__(kMhaThreads) void mha_split_kernel(MhaParams p) {
   const size_t row0 = (size_t(b) * size_t(p.capacity) + size_t(t0)) * size_t(H) * DH;
   const __amdgpu_buffer_rsrc_t kres = buffer_resource(static_cast<const T*>(p.k) + row0, uint32_t(n) * tok_bytes);
   const __amdgpu_buffer_rsrc_t vres = buffer_resource(static_cast<const T*>(p.v) + row0, uint32_t(n) * tok_bytes);
-  const uint32_t lane_off = (uint32_t(hc) * DH + uint32_t(g) * DPL) * E::kBytes;
+  const uint32_t lane_off = uint32_t(hc) * DH * E::kBytes + uint32_t(g) * 16;
 
   float m = -INFINITY, l = 0.f, o[DPL];
 #pragma unroll
@@ -77,8 +84,11 @@ __global__ __launch_bounds__(kMhaThreads) void mha_split_kernel(MhaParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t off = uint32_t(t + u) * tok_bytes + lane_off;
-      buffer_words<SB, kStream>(kw[u], kres, off, 0u);
-      buffer_words<SB, kStream>(vw[u], vres, off, 0u);
+#pragma unroll
+      for (int c = 0; c < NPC; ++c) {
+        buffer_words<16, kStream>(kw[u] + 4 * c, kres, off + 128 * c, 0u);
+        buffer_words<16, kStream>(vw[u] + 4 * c, vres, off + 128 * c, 0u);
+      }
     }
     float s[U];
     float mx = m;
@@ -107,9 +117,15 @@ __global__ __launch_bounds__(kMhaThreads) void mha_split_kernel(MhaParams p) {
   if (!active) return;
   const size_t pidx = (size_t(b) * p.partials + split) * H + hh;
   if (g == 0) *reinterpret_cast<float2*>(p.ws_ml + 2 * pidx) = make_float2(m, l);
-  float* dst = p.ws_acc + pidx * DH + g * DPL;
+  float* const acc = p.ws_acc + pidx * DH;
 #pragma unroll
-  for (int e = 0; e < DPL; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+  for (int c = 0; c < NPC; ++c) {
+    float* dst = acc + (128 * c + 16 * g) / E::kBytes;
+#pragma unroll
+    for (int e = 0; e < EPC; e += 4)
+      *reinterpret_cast<float4*>(dst + e) =
+          make_float4(o[EPC * c + e], o[EPC * c + e + 1], o[EPC * c + e + 2], o[EPC * c + e + 3]);
+  }
 }
 
 template <class E, int DH>
