@@ -27,7 +27,8 @@ STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DT
 EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
             "lrkv_decode_combine", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
-            "lrkv_project_kernel", "lrkv_project_workspace_size", "lrkv_project_append", "lrkv_mha_decode_workspace_size", "lrkv_mha_decode")
+            "lrkv_project_kernel", "lrkv_project_workspace_size", "lrkv_project_append",
+            "lrkv_mha_decode_workspace_size", "lrkv_mha_decode")
 
 
 class LrkvError(RuntimeError):
