@@ -588,8 +588,7 @@ static hipError_t launch_mfma_t(const DecodePlan& pl, const DecodeArgs& a, hipSt
   kp.batch = pl.batch; kp.balanced = pl.balanced; kp.bal_cap = pl.bal_cap;
   kp.capacity = pl.capacity;
   kp.ws_ml = a.ws_ml; kp.ws_acc = a.ws_acc; kp.ws_meta = a.ws_meta;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mfma_kernel<DH, R>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+  const hipError_t attr = allow_dynamic_lds<&decode_mfma_kernel<DH, R>>(S::LDS);
   if (attr != hipSuccess) return attr;
   const dim3 grid(pl.n_splits, pl.heads / kMfHeads, pl.balanced ? 1 : pl.batch);
   hipLaunchKernelGGL((decode_mfma_kernel<DH, R>), grid, dim3(kMfThreads), size_t(S::LDS), st, kp);

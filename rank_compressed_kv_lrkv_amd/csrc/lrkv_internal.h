@@ -5,7 +5,24 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace lrkv {
+
+// Raise a kernel's dynamic-LDS limit to `bytes`, once per device (the
+// attribute belongs to the kernel on the device current at the call).
+template <auto Kernel>
+hipError_t allow_dynamic_lds(int bytes) {
+  static std::atomic<uint64_t> done{0};        // bit d: set on device d
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 constexpr int kDecodeThreads = 256;  // one workgroup = 4 wave64
 constexpr int kDecodeTile = 64;      // cache tokens staged in LDS per step

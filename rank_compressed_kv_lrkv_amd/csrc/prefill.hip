@@ -512,8 +512,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid{static_cast<unsigned>(blocks)};
   const size_t lds = size_t(P::LDS);
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DH, R>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  const hipError_t attr = allow_dynamic_lds<&prefill_kernel<DH, R>>(int(lds));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((prefill_kernel<DH, R>), grid, dim3(kPfThreads), lds, st, kp);
   return hipGetLastError();

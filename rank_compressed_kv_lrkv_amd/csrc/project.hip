@@ -641,8 +641,7 @@ int device_cus() {
 
 template <int TJ>
 hipError_t launch_gemm(const ProjectParams& p, dim3 grid, hipStream_t st) {
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&project_gemm_kernel<TJ>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, PgShape<TJ>::LDS);
+  const hipError_t attr = allow_dynamic_lds<&project_gemm_kernel<TJ>>(PgShape<TJ>::LDS);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((project_gemm_kernel<TJ>), grid, dim3(kPgThreads), size_t(PgShape<TJ>::LDS), st, p);
   return hipGetLastError();
