@@ -224,7 +224,11 @@ void decode_mfma_kernel(MfParams p) {
 #pragma unroll
         for (int sd = 0; sd < 2; ++sd) {
           const uint32_t tok = uint32_t(tile) * kMfTile + uint32_t(acc_row(i, sd));
-          buffer_words<S::HB, kStream>(ring[slot][t][sd], res, tok * ztok + lane_off, 0u);
+          // r = 32: a half row is two 16-byte loads, and each load instruction
+          // covers every other 16 bytes of its 2 KB; with the cached policy the
+          // second half of each line is then served by the L1, where the
+          // streaming policy fetched it again
+          buffer_words<S::HB, (R == 32 ? kCached : kStream)>(ring[slot][t][sd], res, tok * ztok + lane_off, 0u);
         }
       }
     }
