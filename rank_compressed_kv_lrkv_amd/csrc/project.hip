@@ -341,7 +341,10 @@ void project_gemm_kernel(ProjectParams p) {
 // w, w + 16, ... (in runs of kPsGroup consecutive chunks).  Operands go straight from global memory to registers (lane
 // (n_lane, hf) loads 16 bytes of W row n0 + n_lane and of X rows
 // 32 i + n_lane, at contraction offset 16 c + 8 hf), PsUnroll<MT> chunks in
-// flight per wave; the 16 partial tiles are summed in LDS at the end.
+// flight per wave; the 16 partial tiles are summed in LDS at the end.  Each
+// load instruction takes 32 bytes of each of 32 rows, so a 128-byte line is
+// touched by four instructions: the loads keep the cached policy, and the L1
+// serves the later touches.
 // ---------------------------------------------------------------------------
 constexpr int kPsThreads = 1024, kPsWaves = 16, kPsHalf = kPsWaves / 2;
 constexpr int kPsGroup = 1;            // consecutive 16-wide chunks a wave takes together
@@ -374,7 +377,7 @@ __global__ __launch_bounds__(kPsThreads) void project_skinny_kernel(ProjectParam
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t koff = uint32_t(min(chunk(u), kchunks - 1)) * 32;
-      bw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, int(w_off + koff), 0, kStream));
+      bw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, int(w_off + koff), 0, kCached));
 #pragma unroll
       for (int i = 0; i < MT; ++i)
         ax[u][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, int(x_off[i] + koff), 0, 0));
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(kPkThreads) void project_splitk_kernel(ProjectParam
 #pragma unroll
     for (int u = 0; u < kPkUnroll; ++u) {
       const uint32_t koff = uint32_t(min(c0 + kPkWaves * u, c_hi - 1)) * 32;
-      bw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, int(w_off + koff), 0, kStream));
+      bw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, int(w_off + koff), 0, kCached));
 #pragma unroll
       for (int i = 0; i < MT; ++i)
         ax[u][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, int(x_off[i] + koff), 0, 0));
