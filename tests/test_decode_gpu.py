@@ -156,3 +156,27 @@ def test_lengths_clamped_to_max_len():
     got = run_decode(d, max_len=256)            # the kernel sees at most 256 tokens per sequence
     d2 = dict(d, seq_lens=np.array([256, 256], np.int32))
     check(d2, got, name="clamped")
+
+
+@pytest.mark.parametrize("name,split", [("mid_bf16_T8k", 0), ("mid_bf16_T8k", 256), ("small_bf16_T2k", 0)])
+def test_partial_then_combine_equals_decode(name, split):
+    # lrkv_decode_partial followed by lrkv_decode_combine on the same workspace
+    # is the same computation as lrkv_decode: bitwise the same output
+    import rank_compressed_kv_lrkv_amd as L
+    from tests.gpu_util import device_cache, to_dev
+    wl = DECODE_WORKLOADS[name]
+    say(f"case partial + combine {name} split={split}")
+    d = decode_inputs(wl, seed=9, batch=5, capacity=1200, lens=np.array([1200, 1, 640, 0, 999], np.int32))
+    dt = d["dtype"]
+    cache = device_cache(d)
+    lens = torch.from_numpy(np.asarray(d["seq_lens"], np.int32)).cuda()
+    q, b_k, b_v = to_dev(d["q"], dt), to_dev(d["b_k"], dt), to_dev(d["b_v"], dt)
+    ws = L.decode_workspace(cache, 1200, split)
+    both = L.lrkv_decode(cache, lens, 1200, q, b_k, b_v, split_tokens=split, workspace=ws)
+    out = torch.full_like(both, 7.0)
+    L.lrkv_decode(cache, lens, 1200, q, b_k, b_v, split_tokens=split, out=out, workspace=ws, phase="partial")
+    L.lrkv_decode(cache, lens, 1200, q, b_k, b_v, split_tokens=split, out=out, workspace=ws, phase="combine")
+    torch.cuda.synchronize()
+    a, b = both.float().cpu().numpy(), out.float().cpu().numpy()
+    assert np.array_equal(a, b)
+    check(d, a.astype(np.float64), name=f"{name} split={split}")
