@@ -80,3 +80,17 @@ def test_mha_decode_headline_shape_sampled():
         qq = q[b, h].float().cpu().numpy().astype(np.float64)
         want = O.softmax_attention(qq, kk, vv, 1.0 / np.sqrt(d_h))
         assert err_ratio(got[b, h], want) <= TOL["bf16"], (b, h)
+
+
+def test_mha_decode_lengths_clamped_to_max_len():
+    # lengths above max_len (and negative ones) are clamped to [0, max_len]
+    say("case mha max_len clamp")
+    T = 400
+    d = mha_inputs(batch=3, capacity=T, heads=8, head_dim=128, lens=[400, 250, 100], dtype="bf16", seed=12)
+    lens = torch.tensor([400, 250, -5], dtype=torch.int32, device="cuda")
+    dt = d["dtype"]
+    got = from_dev(L.lrkv_mha_decode(to_dev(d["k"], dt), to_dev(d["v"], dt), lens, 300, to_dev(d["q"], dt)))
+    clamped = dict(d, seq_lens=np.array([300, 250, 0], np.int32))
+    want = oracle_mha(clamped)
+    assert err_ratio(got, want) <= TOL[dt]
+    assert np.all(got[2] == 0)
