@@ -75,7 +75,10 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
     const int64_t unit = pl->mfma ? 2 * tile : tile;
     int64_t s = (total + target - 1) / (target > 0 ? target : 1);
     s = (s + unit - 1) / unit * unit;
-    if (s < unit) s = unit;
+    // at least two tiles per split: a small cache split one tile at a time
+    // leaves the merge more partial states than the scan saves time (the
+    // 8 x 2048-token bf16 batch: 20.3 us per step at 64 tokens, 15.5 at 128)
+    if (s < 2 * tile) s = 2 * tile;
     const int64_t cap = (max_len + unit - 1) / unit * unit;
     if (s > cap) s = cap < unit ? unit : cap;
     split = int(s);
