@@ -60,7 +60,7 @@ def parse():
 
 # kernel -> the sources its code comes from (the counter summaries record their digest)
 KERNEL_SOURCES = {
-    "decode_mfma_kernel": ("decode_mfma.hip", "lrkv_device.h"),
+    "decode_mfma_kernel": ("decode_mfma.hip", "decode_balance.h", "lrkv_device.h"),
     "decode_split_kernel": ("decode.hip", "lrkv_device.h"),
     "prefill_kernel": ("prefill.hip", "lrkv_device.h"),
     "project_gemm_kernel": ("project.hip", "lrkv_device.h"),
