@@ -338,10 +338,11 @@ void project_gemm_kernel(ProjectParams p) {
 // a decode step): the weight read dominates, so the work is spread over the
 // output columns and the contraction.  A workgroup of 16 waves takes 32
 // output columns and every row; wave w takes the 16-wide contraction chunks
-// w, w + 16, ... (in runs of kPsGroup consecutive chunks).  Operands go straight from global memory to registers (lane
-// (n_lane, hf) loads 16 bytes of W row n0 + n_lane and of X rows
-// 32 i + n_lane, at contraction offset 16 c + 8 hf), PsUnroll<MT> chunks in
-// flight per wave; the 16 partial tiles are summed in LDS at the end.  Each
+// w, w + 16, ... (in runs of kPsGroup consecutive chunks).  Operands go
+// straight from global memory to registers (lane (n_lane, hf) loads 16 bytes
+// of W row n0 + n_lane and of X rows 32 i + n_lane, at contraction offset
+// 16 c + 8 hf), PsUnroll<MT> chunks in flight per wave; the 16 partial tiles
+// are summed in LDS at the end.  Each
 // load instruction takes 32 bytes of each of 32 rows, so a 128-byte line is
 // touched by four instructions: the loads keep the cached policy, and the L1
 // serves the later touches.
