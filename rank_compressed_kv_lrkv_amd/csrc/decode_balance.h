@@ -138,4 +138,33 @@ __device__ __forceinline__ bool bal_item(const BalLens& L, int u, int i, int lan
   return false;
 }
 
+// The same partition in closed form when every length is the same L > 0
+// (the common uniform batch): with k = limit / batch items allowed per
+// sequence, the smallest admissible u is ceil(L / k) rounded up to the item
+// step (and at least kBalMinItem), and item i is sequence i / ceil(L / u),
+// piece i % ceil(L / u).  Returns false, touching nothing, if the lengths
+// differ or are 0 (the general path applies).
+__device__ __forceinline__ bool bal_uniform(const BalLens& L, int batch, int cap, int i, int lane, int* u_out,
+                                            int* b_out, int* lo, int* hi, bool* valid) {
+  const int l0 = __builtin_amdgcn_readfirstlane(L.v[0]);      // sequence 0
+  int diff = 0;
+#pragma unroll
+  for (int k = 0; k < kBalLanes; ++k)
+    if (k < L.chunks) diff += (lane + 64 * k < batch && L.v[k] != l0);
+  if (l0 <= 0 || bal_wave_sum(diff, lane) != 0) return false;
+  const int per_max = max(cap, batch) / batch;                 // items one sequence may have
+  int u = (l0 + per_max - 1) / per_max;
+  u = max(kBalMinItem, (u + kBalStep - 1) / kBalStep * kBalStep);
+  const int per = (l0 + u - 1) / u;                            // items per sequence
+  *u_out = u;
+  *valid = i < batch * per;
+  if (*valid) {
+    *b_out = i / per;
+    const int s = i - *b_out * per;
+    *lo = s * u;
+    *hi = min(l0, (s + 1) * u);
+  }
+  return true;
+}
+
 }  // namespace lrkv

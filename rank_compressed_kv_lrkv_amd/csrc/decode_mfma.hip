@@ -145,8 +145,13 @@ void decode_mfma_kernel(MfParams p) {
   if (p.balanced) {
     item = blockIdx.x;
     const BalLens L = bal_load(p.seq_lens, p.batch, p.max_len, lane);
-    const int u = bal_item_size(L, p.max_len, p.bal_cap, lane);
-    if (u == 0 || !bal_item(L, u, item, lane, &b, &lo, &hi)) return;
+    int u;
+    bool valid;
+    if (!bal_uniform(L, p.batch, p.bal_cap, item, lane, &u, &b, &lo, &hi, &valid)) {
+      u = bal_item_size(L, p.max_len, p.bal_cap, lane);
+      valid = u != 0 && bal_item(L, u, item, lane, &b, &lo, &hi);
+    }
+    if (!valid) return;
     // the first item of each sequence records where its items start, and
     // the item size, for the merge
     if (lo == 0 && tid == 0) {

@@ -180,3 +180,13 @@ def test_partial_then_combine_equals_decode(name, split):
     a, b = both.float().cpu().numpy(), out.float().cpu().numpy()
     assert np.array_equal(a, b)
     check(d, a.astype(np.float64), name=f"{name} split={split}")
+
+
+@pytest.mark.parametrize("batch,length", [(5, 700), (3, 1), (40, 130), (7, 2048)])
+def test_balanced_partition_uniform_lengths(batch, length):
+    # every length equal: the partition in closed form (the same items as the general search)
+    wl = DECODE_WORKLOADS["mid_bf16_T8k"]
+    say(f"case balanced uniform batch={batch} length={length}")
+    d = decode_inputs(wl, seed=40 + batch, batch=batch, capacity=length,
+                      lens=np.full(batch, length, np.int32))
+    check(d, run_decode(d), name=f"uniform B={batch} L={length}")
