@@ -44,10 +44,12 @@ def parse():
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="before the warmup steps, repeat the step (untimed) for this many seconds: "
                          "the GPU takes tens of ms of sustained work to reach its steady clock")
-    ap.add_argument("--mode", choices=("decode", "prefill", "chunk", "rank-sweep", "project"), default="decode",
+    ap.add_argument("--mode", choices=("decode", "prefill", "chunk", "rank-sweep", "project", "vendor"),
+                    default="decode",
                     help="decode (the headline line); the causal-prefill MFMA path; a prefill chunk over a "
-                         "4096-token history; decode at ranks 0/8/16/32 and plain MHA on the headline shape; or "
-                         "the fused projection + append of 4 x 4096 tokens from d = 4096")
+                         "4096-token history; decode at ranks 0/8/16/32 and plain MHA on the headline shape; "
+                         "the fused projection + append of 4 x 4096 tokens from d = 4096; or the vendor "
+                         "libraries (hipBLASLt GEMM, PyTorch flash attention) timed beside the two MFMA kernels")
     ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
@@ -172,6 +174,8 @@ def main():
         return bench_rank_sweep(args)
     if args.mode == "project":
         return bench_project(args)
+    if args.mode == "vendor":
+        return bench_vendor(args)
     wl = DECODE_WORKLOADS[args.workload or "mid_bf16_T8k"]
     t_gen = time.perf_counter()
     d = decode_inputs(wl)
@@ -422,6 +426,90 @@ def bench_project(args):
                          "GB_per_s": dec_bytes / (dec_ms * 1e-3) / 1e9},
     }
     copy_reference(args, rec)
+    print(json.dumps(rec), flush=True)
+
+
+def bench_vendor(args):
+    """Vendor libraries at the shapes of the two MFMA kernels, timed beside
+    them in one process (context, not the LRKV computation):
+    - hipBLASLt (torch.matmul, bf16) on the projection GEMM, 16384 x 4096 x
+      1280, against lrkv_project_append of the same size (random packed W);
+    - PyTorch's flash-attention backend (forced: no fallback to the math
+      path) on dense causal MHA of the prefill workload's shape (B=4, H=32,
+      L=4096, d=128), against lrkv_prefill's attention kernel (no cache
+      write) on LRKV inputs of that shape with r = 16.
+    Inputs are torch.randn on the device; each call is settled, warmed up
+    and timed like the other modes."""
+    import torch
+    import torch.nn.functional as F
+    import rank_compressed_kv_lrkv_amd as L
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261209)
+
+    def randn(*shape, scale=1.0):
+        return (torch.randn(*shape, device="cuda", generator=gen) * scale).to(torch.bfloat16)
+
+    def run(fn):
+        settle(fn, args.settle_s)
+        for _ in range(args.warmup):
+            fn()
+        return timed(stream, args.steps, fn)
+
+    B, n, d, H, d_h, r = 4, 4096, 4096, 32, 128, 16
+    N, M = 2 * (d_h + H * r), B * n
+    gemm_flops = 2 * M * N * d
+    x = randn(B, n, d)
+    w = randn(N, d, scale=d ** -0.5)                          # the packed layout [N][d]
+    wt = w.t().contiguous()
+    out = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    x2 = x.view(M, d)
+    blas_ms = run(lambda: torch.matmul(x2, wt, out=out))
+    cache = L.LrkvCache.empty(B, H, d_h, r, n, dtype=torch.bfloat16, zero=False)
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+    proj_ms = run(lambda: L.lrkv_project_append(cache, pos, x, w, workspace=None))
+    del x, x2, w, wt, out, cache
+
+    Lq = n
+    pairs = B * H * Lq * (Lq + 1) // 2
+    mha_flops = pairs * 4 * d_h
+    lrkv_flops = pairs * 4 * (d_h + r) + B * H * Lq * 4 * d_h * r
+    q_l = randn(B, Lq, H, d_h)
+    t = {"k_s": randn(B, Lq, d_h), "v_s": randn(B, Lq, d_h), "z_k": randn(B, Lq, H, r), "z_v": randn(B, Lq, H, r),
+         "b_k": randn(H, d_h, r, scale=r ** -0.5), "b_v": randn(H, d_h, r, scale=r ** -0.5)}
+    o_l = torch.empty_like(q_l)
+    lrkv_ms = run(lambda: L.lrkv_prefill(q_l, t["k_s"], t["v_s"], t["z_k"], t["z_v"], t["b_k"], t["b_v"], out=o_l))
+    del q_l, t, o_l
+    q, k, v = randn(B, H, Lq, d_h), randn(B, H, Lq, d_h), randn(B, H, Lq, d_h)
+    flash = {"backend": "torch SDPA, FLASH_ATTENTION only", "shape": [B, H, Lq, d_h], "causal": True}
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            fa_ms = run(lambda: F.scaled_dot_product_attention(q, k, v, is_causal=True))
+        fa_tf = mha_flops / (fa_ms * 1e-3) / 1e12
+        flash.update({"ms": fa_ms, "TFLOP/s": fa_tf, "frac": fa_tf / MFMA_BF16_PEAK_TFLOPS})
+    except RuntimeError as e:
+        flash["unavailable"] = str(e)[:200]
+
+    def entry(ms, flops, **kw):
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"ms": ms, "TFLOP/s": tf, "frac": tf / MFMA_BF16_PEAK_TFLOPS, **kw}
+
+    rec = {
+        "metric": "vendor libraries beside the LRKV MFMA kernels (context)",
+        "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "dtype": "bf16", "steps": args.steps, "warmup": args.warmup,
+        "projection_gemm": {
+            "shape_MxKxN": [M, d, N],
+            "hipblaslt_torch_matmul": entry(blas_ms, gemm_flops),
+            "lrkv_project_append": entry(proj_ms, gemm_flops,
+                                         kernel=L.lrkv_project_kernel(torch.bfloat16, B, n, H, d_h, r, d)),
+        },
+        "causal_prefill": {
+            "mha_flash_attention": flash,
+            "lrkv_prefill_kernel": entry(lrkv_ms, lrkv_flops, rank=r),
+        },
+    }
     print(json.dumps(rec), flush=True)
 
 
