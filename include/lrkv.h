@@ -24,7 +24,10 @@
  *     library allocates no device memory, keeps no per-call state, never
  *     synchronises, and enqueues all work on `stream` (a hipStream_t passed
  *     as void*; NULL is the default stream).  Results are ready when the
- *     stream has drained.
+ *     stream has drained.  Since the calls only launch kernels (no
+ *     allocation, memset, copy or synchronisation), a caller may capture
+ *     them on a stream into a HIP graph and replay it; every replay reads the
+ *     buffers' contents at replay time.
  *   - `dtype` (lrkv_dtype) is the storage type of q, the cache, B^K, B^V,
  *     the new rows and the output, one type per call.  Arithmetic is fp32
  *     (bf16 products accumulate in fp32).
