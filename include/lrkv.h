@@ -21,8 +21,9 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library allocates no device memory, keeps no per-call state, never
- *     synchronises, and enqueues all work on `stream` (a hipStream_t passed
+ *     library allocates no device memory (the one fixed scratch array of
+ *     lrkv_decode_noalloc is part of its code object), keeps no per-call
+ *     state, never synchronises, and enqueues all work on `stream` (a hipStream_t passed
  *     as void*; NULL is the default stream).  Results are ready when the
  *     stream has drained.  Since the calls only launch kernels (no
  *     allocation, memset, copy or synchronisation), a caller may capture
@@ -67,7 +68,8 @@ typedef enum lrkv_status {
   LRKV_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned */
   LRKV_ERR_CAPACITY = 5,   /* max_len or seq_len exceeds capacity */
   LRKV_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than lrkv_decode_workspace_size */
-  LRKV_ERR_DEVICE = 7      /* a HIP runtime call or kernel launch failed */
+  LRKV_ERR_DEVICE = 7,     /* a HIP runtime call or kernel launch failed */
+  LRKV_ERR_SCRATCH = 8     /* lrkv_decode_noalloc: the call needs more than its fixed scratch */
 } lrkv_status;
 
 typedef enum lrkv_dtype {
@@ -173,6 +175,28 @@ lrkv_status lrkv_decode_combine(int32_t dtype, int32_t batch, int32_t num_heads,
                                 const void* q, const void* b_k, const void* b_v, float scale,
                                 int32_t split_tokens, void* out,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* lrkv_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and result as lrkv_decode, without the workspace.  The
+ * split-K partial states go to a scratch array the library holds in device
+ * memory, 16 MiB per device (allocated with the code object, held until the
+ * process ends).  This call allocates nothing and calls no allocating
+ * routine.  A call whose lrkv_decode_workspace_size exceeds 16 MiB returns
+ * LRKV_ERR_SCRATCH before any launch (the default split of every shape with
+ * batch*num_heads*(head_dim+rank) <= 4M fp32 per resident workgroup fits;
+ * the 32 x 8192-token headline shape needs 4.6 MiB).  All calls on one
+ * device share that device's scratch, so calls that overlap in time on one
+ * device (two streams, or two host threads) race and give wrong results;
+ * calls ordered on one stream are safe.  The first call on a device looks up
+ * the scratch address once (no allocation; LRKV_ERR_DEVICE if it fails). */
+lrkv_status lrkv_decode_noalloc(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                int32_t rank, int64_t capacity,
+                                const void* k_shared, const void* v_shared,
+                                const void* z_k, const void* z_v,
+                                const int32_t* seq_lens, int64_t max_len,
+                                const void* q, const void* b_k, const void* b_v, float scale,
+                                int32_t split_tokens, void* out, void* stream);
 
 /* Causal prefill of seq_len fresh tokens per sequence (slides "Compute
  * logits without expanding historical keys" and "Aggregate values before

@@ -22,11 +22,11 @@ LIB_PATH = os.path.join(_HERE, "lib", "liblrkv.so")
 LRKV_F32 = 0
 LRKV_BF16 = 1
 STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DTYPE", 4: "LRKV_ERR_ALIGN",
-          5: "LRKV_ERR_CAPACITY", 6: "LRKV_ERR_WORKSPACE", 7: "LRKV_ERR_DEVICE"}
+          5: "LRKV_ERR_CAPACITY", 6: "LRKV_ERR_WORKSPACE", 7: "LRKV_ERR_DEVICE", 8: "LRKV_ERR_SCRATCH"}
 
 EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
-            "lrkv_decode_combine", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
+            "lrkv_decode_combine", "lrkv_decode_noalloc", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
             "lrkv_project_kernel", "lrkv_project_workspace_size", "lrkv_project_append",
             "lrkv_mha_decode_workspace_size", "lrkv_mha_decode")
 
@@ -65,6 +65,9 @@ def library() -> ctypes.CDLL:
             fn.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64,
                            _vp, _vp, _vp, _f32, _i32, _vp, _vp, _sz, _vp]
             fn.restype = _i32
+        lib.lrkv_decode_noalloc.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64,
+                                            _vp, _vp, _vp, _f32, _i32, _vp, _vp]
+        lib.lrkv_decode_noalloc.restype = _i32
         lib.lrkv_prefill.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _i32,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp]
         lib.lrkv_prefill.restype = _i32
@@ -240,6 +243,29 @@ def lrkv_decode(cache: LrkvCache, seq_lens: torch.Tensor, max_len: int, q: torch
                                  _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                  _stream()),
            "lrkv_decode")
+    return out
+
+
+def lrkv_decode_noalloc(cache: LrkvCache, seq_lens: torch.Tensor, max_len: int, q: torch.Tensor, b_k: torch.Tensor,
+                        b_v: torch.Tensor, scale: Optional[float] = None, split_tokens: int = 0,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lrkv_decode without a workspace: the partial states go to the library's
+    fixed per-device scratch (see lrkv.h).  Pass `out` to allocate nothing."""
+    dt = cache.dtype
+    B, H, d_h, r = cache.batch, cache.heads, cache.head_dim, cache.rank
+    _shape(q, "q", (B, H, d_h))
+    _shape(b_k, "b_k", (H, d_h, r))
+    _shape(b_v, "b_v", (H, d_h, r))
+    _shape(seq_lens, "seq_lens", (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", (B, H, d_h))
+    _check(library().lrkv_decode_noalloc(_dtype_code(dt), B, H, d_h, r, cache.capacity, *cache.pointers(),
+                                         _ptr(seq_lens, "seq_lens", torch.int32), max_len, _ptr(q, "q", dt),
+                                         _ptr(b_k, "b_k", dt), _ptr(b_v, "b_v", dt),
+                                         0.0 if scale is None else float(scale), split_tokens,
+                                         _ptr(out, "out", dt), _stream()),
+           "lrkv_decode_noalloc")
     return out
 
 

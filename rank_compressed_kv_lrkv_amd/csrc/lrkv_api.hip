@@ -111,6 +111,34 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
   return LRKV_OK;
 }
 
+// Device scratch of lrkv_decode_noalloc: the split-K partial states of a
+// decode, for callers that cannot allocate.  One copy per device, alive until
+// the process ends; every lrkv_decode_noalloc call on a device writes its
+// copy, so calls that overlap on one device race.  Nothing in it has to
+// start at zero: the scan writes every state the merge reads.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device with that device current.  In host code the array's name is
+// only a stand-in for the symbol, never a device address.
+hipError_t scratch_address(void** out) {
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u)) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,6 +153,7 @@ const char* lrkv_status_string(int32_t s) {
     case LRKV_ERR_CAPACITY: return "length exceeds cache capacity";
     case LRKV_ERR_WORKSPACE: return "workspace missing or too small";
     case LRKV_ERR_DEVICE: return "HIP runtime or launch failure";
+    case LRKV_ERR_SCRATCH: return "request exceeds the library's fixed device scratch";
     default: return "unknown status";
   }
 }
@@ -195,6 +224,22 @@ static lrkv_status decode_phases(int phase, int32_t dtype, int32_t batch, int32_
       b_v, scale, split_tokens, out, workspace, workspace_bytes, stream
 
 lrkv_status lrkv_decode(LRKV_DECODE_ARGS) { return decode_phases(3, LRKV_DECODE_PASS); }
+
+lrkv_status lrkv_decode_noalloc(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
+                                int64_t capacity, const void* k_shared, const void* v_shared, const void* z_k,
+                                const void* z_v, const int32_t* seq_lens, int64_t max_len, const void* q,
+                                const void* b_k, const void* b_v, float scale, int32_t split_tokens, void* out,
+                                void* stream) {
+  DecodePlan pl;
+  const lrkv_status st = plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl);
+  if (st != LRKV_OK) return st;
+  if (pl.ws_ml_bytes + pl.ws_acc_bytes + pl.ws_meta_bytes > kScratchBytes) return LRKV_ERR_SCRATCH;
+  if (batch == 0) return LRKV_OK;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return LRKV_ERR_DEVICE;
+  return decode_phases(3, dtype, batch, num_heads, head_dim, rank, capacity, k_shared, v_shared, z_k, z_v, seq_lens,
+                       max_len, q, b_k, b_v, scale, split_tokens, out, ws, kScratchBytes, stream);
+}
 lrkv_status lrkv_decode_partial(LRKV_DECODE_ARGS) { return decode_phases(1, LRKV_DECODE_PASS); }
 lrkv_status lrkv_decode_combine(LRKV_DECODE_ARGS) { return decode_phases(2, LRKV_DECODE_PASS); }
 

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_elem_count():
     assert L.lrkv_status_string(0) == "ok"
-    for s in range(1, 8):
+    for s in range(1, 9):
         assert L.lrkv_status_string(s) not in ("ok", "unknown status")
     assert L.lrkv_status_string(99) == "unknown status"
     assert L.lrkv_cache_elems_per_token(32, 128, 16) == 2 * (128 + 32 * 16)
