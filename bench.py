@@ -1,23 +1,29 @@
 #!/usr/bin/env python3
-"""Throughput of LRKV compressed-cache decode on one MI355X.
+"""Throughput of LRKV compressed-cache decode (and prefill) on one MI355X.
 
 A step is one lrkv_decode call over the whole batch (the split-K scan, then
 the merge and B^V epilogue, enqueued together), on seeded synthetic inputs
 already resident in HBM.  Before the warmup steps the step is repeated,
 untimed, for --settle-s seconds so that the timed steps run at the GPU's
-steady clock.  Each kernel's own average duration is timed
-separately over back-to-back launches of lrkv_decode_partial and
-lrkv_decode_combine.
-The default workload is the 8K-context bf16 decode: 32 sequences x 8192
-cached tokens, H=32 heads, d_h=128, r=16 (cache 671 MB, larger than the
-256 MB Infinity Cache, so every step streams it from HBM).
+steady clock.  Every time reported is the median of --trials trials, each
+the average over --steps back-to-back launches between two HIP events on
+the launch stream; each kernel's own duration is timed the same way over
+launches of lrkv_decode_partial and lrkv_decode_combine alone.
 
-Prints one JSON line.  `value` is cache tokens per second for the whole
-step; `roofline` prices the dominant kernel (the scan) against the HBM
-peak using the algorithmic bytes of one launch and its average duration
-from HIP events recorded around it on the launch stream; `cpu_baseline`
-times the float64 oracle on a bounded sample of the same workload on the
-host cores and reports its agreement with the GPU on that sample.
+`value` is the 8K-context bf16 decode: 32 sequences x 8192 cached tokens,
+H=32 heads, d_h=128, r=16 (cache 671 MB, larger than the 256 MB Infinity
+Cache, so every step streams it from HBM).  The default run also measures,
+under `configs`, the other synthetic workloads: the tiny fp32 decode (a
+latency), the small bf16 decode (L2-resident latency, and throughput over
+rotated copies whose working set exceeds twice L2 plus the Infinity
+Cache), the ragged 1K-64K-token decode (checked in full against the
+oracle) and the causal prefill (TFLOP/s against the bf16 MFMA peak, sampled
+rows checked against the oracle), each with the oracle timed beside it.
+
+Prints one JSON line.  `roofline` prices the dominant kernel (the scan)
+against the HBM peak using the algorithmic bytes of one launch and its
+duration; `cpu_baseline` times the float64 oracle on the host cores (all of
+them, and one thread for the small configs) as a reported baseline.
 """
 from __future__ import annotations
 
@@ -52,8 +58,13 @@ def parse():
                          "libraries (hipBLASLt GEMM, PyTorch flash attention) timed beside the two MFMA kernels")
     ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
+    ap.add_argument("--engine", type=int, default=0, choices=(0, 1, 2),
+                    help="decode scan: 0 the default for the shape, 1 the vector-ALU scan, 2 the MFMA scan")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trials", type=int, default=5, help="timed trials per figure (the median is reported)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="decode mode: measure the selected workload only (no `configs` section)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, run `steps` plain device copies of this many MB (untimed), "
                          "a known-size reference for the HBM byte counters")
@@ -110,6 +121,12 @@ def timed(stream, n, fn):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def timed_median(stream, n, fn, trials):
+    """Median (and spread) of `trials` runs of timed(stream, n, fn)."""
+    runs = sorted(timed(stream, n, fn) for _ in range(max(1, trials)))
+    return float(np.median(runs)), runs
 
 
 def settle(fn, seconds):
@@ -177,104 +194,293 @@ def main():
     if args.mode == "vendor":
         return bench_vendor(args)
     wl = DECODE_WORKLOADS[args.workload or "mid_bf16_T8k"]
-    t_gen = time.perf_counter()
     d = decode_inputs(wl)
-    t_gen = time.perf_counter() - t_gen
-    dt = torch.bfloat16 if d["dtype"] == "bf16" else torch.float32
-
-    def dev(a):
-        if d["dtype"] == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
-
-    cache = L.LrkvCache(dev(d["k_s"]), dev(d["v_s"]), dev(d["z_k"]), dev(d["z_v"]))
-    q, b_k, b_v = dev(d["q"]), dev(d["b_k"]), dev(d["b_v"])
-    lens_np = np.asarray(d["seq_lens"], np.int32)
-    lens = torch.from_numpy(lens_np).cuda()
-    max_len = int(d["capacity"])
-    out = torch.empty_like(q)
-    ws = L.decode_workspace(cache, max_len, args.split_tokens)
-    B, H, d_h, r = wl.batch, wl.heads, wl.head_dim, wl.rank
-    es = 2 if d["dtype"] == "bf16" else 4
-    tokens = int(np.minimum(lens_np, max_len).sum())
-
-    call = L.DecodeCall(cache, lens, max_len, q, b_k, b_v, split_tokens=args.split_tokens, out=out, workspace=ws)
-    scan, combine = call.partial, call.combine
-
-    settled = settle(call.both, args.settle_s)
-    for _ in range(args.warmup):
-        call.both()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()       # the library launches on torch's current stream
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    # a step is one lrkv_decode call (scan + merge enqueued together)
-    step_ms = timed(stream, args.steps, call.both)
-    wall = time.perf_counter() - t0
-    # each kernel's average launch duration: back-to-back launches between one
-    # event pair (an event between every launch adds a few us of gap)
-    scan_ms = timed(stream, args.steps, scan)
-    comb_ms = timed(stream, args.steps, combine)
-
-    cache_bytes = tokens * 2 * (d_h + H * r) * es
-    scan_bytes = cache_bytes + B * H * d_h * es + H * d_h * r * es          # cache + q + B^K
-    step_bytes = cache_bytes + 2 * B * H * d_h * es + 2 * H * d_h * r * es  # + out + B^V
-    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
-    scan_kernel = L.lrkv_decode_scan_kernel(dt, H, d_h, r)
-    traffic = traffic_from_profiles("decode_scan_counters", scan_kernel, wl.name, args.split_tokens)
-
+    m = measure_decode(args, wl, d, engine=args.engine)
     rec = {
         "metric": "compressed-cache decode: cache tokens/s and achieved HBM GB/s (% of peak)",
-        "value": tokens / (step_ms * 1e-3),
+        "value": m["tokens_per_s"],
         "unit": "cache tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "settle": {"seconds": args.settle_s, "steps": settled},
-        "ms_per_step": step_ms,
+        "trials": args.trials,
+        "settle": {"seconds": args.settle_s, "steps": m["settled"]},
+        "ms_per_step": m["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if d["dtype"] == "bf16" else "f32",
+        "dtype": m["dtype"],
         "data": "synthetic (seeded N(0,1) queries, bases and latents; B ~ N(0, 1/r))",
+        "config": m["config"],
+        "hbm_GBps_step": m["hbm_GBps_step"],
+        "hbm_frac_step": m["hbm_frac_step"],
+        "kernels_ms": m["kernels_ms"],
+        "step_ms_trials": m["step_ms_trials"],
+        "wall_s_timed": m["wall_s_timed"],
+        "roofline": m["roofline"],
+    }
+    copy_reference(args, rec)
+    progress(f"{wl.name} measured")
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(d, m["out"], args.cpu_seconds, as_f64)
+        rec["cpu_baseline"].update(cpu_identity())
+        progress("cpu baseline done")
+    del m
+    if not args.headline_only and args.workload is None and args.engine == 0:
+        rec["configs"] = other_configs(args)
+    print(json.dumps(rec), flush=True)
+
+
+def _dev(a, dtype):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def measure_decode(args, wl, d, rotate_mb: float = 0.0, engine: int = 0):
+    """Decode steps of one workload: step, scan and merge times (medians of
+    the trials), bytes and the roofline of the scan.  With rotate_mb > 0 the
+    steps cycle over enough copies of the cache (and queries) that their
+    working set exceeds rotate_mb, so no step finds its cache in L2 or the
+    Infinity Cache."""
+    import torch
+    import rank_compressed_kv_lrkv_amd as L
+
+    dt = torch.bfloat16 if d["dtype"] == "bf16" else torch.float32
+    B, H, d_h, r = wl.batch, wl.heads, wl.head_dim, wl.rank
+    es = 2 if d["dtype"] == "bf16" else 4
+    lens_np = np.asarray(d["seq_lens"], np.int32)
+    max_len = int(d["capacity"])
+    tokens = int(np.minimum(lens_np, max_len).sum())
+    cache_bytes = tokens * 2 * (d_h + H * r) * es
+    copies = 1
+    if rotate_mb > 0:
+        per_copy = (d["k_s"].nbytes + d["v_s"].nbytes + d["z_k"].nbytes + d["z_v"].nbytes) / 1e6
+        copies = int(np.ceil(rotate_mb / per_copy)) + 1
+    lens = torch.from_numpy(lens_np).cuda()
+    out = torch.empty((B, H, d_h), dtype=dt, device="cuda")
+    calls = []
+    keep = []
+    for c in range(copies):
+        cache = L.LrkvCache(_dev(d["k_s"], d["dtype"]), _dev(d["v_s"], d["dtype"]), _dev(d["z_k"], d["dtype"]),
+                            _dev(d["z_v"], d["dtype"]))
+        q, b_k, b_v = _dev(d["q"], d["dtype"]), _dev(d["b_k"], d["dtype"]), _dev(d["b_v"], d["dtype"])
+        ws = L.decode_workspace(cache, max_len, args.split_tokens, engine)
+        calls.append(L.DecodeCall(cache, lens, max_len, q, b_k, b_v, split_tokens=args.split_tokens, out=out,
+                                  workspace=ws, engine=engine))
+        keep.append((cache, q, b_k, b_v, ws))
+    state = {"i": 0}
+
+    def rotating(kind):
+        def fn():
+            call = calls[state["i"]]
+            state["i"] = (state["i"] + 1) % copies
+            getattr(call, kind)()
+        return fn
+
+    both, scan, combine = rotating("both"), rotating("partial"), rotating("combine")
+    settled = settle(both, args.settle_s)
+    for _ in range(args.warmup):
+        both()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()       # the library launches on torch's current stream
+    t0 = time.perf_counter()
+    # a step is one lrkv_decode call (scan + merge enqueued together)
+    step_ms, step_runs = timed_median(stream, args.steps, both, args.trials)
+    wall = time.perf_counter() - t0
+    # each kernel's duration: back-to-back launches between one event pair
+    scan_ms, _ = timed_median(stream, args.steps, scan, args.trials)
+    comb_ms, _ = timed_median(stream, args.steps, combine, args.trials)
+    calls[0].both()
+    torch.cuda.synchronize()
+
+    scan_bytes = cache_bytes + B * H * d_h * es + H * d_h * r * es          # cache + q + B^K
+    step_bytes = cache_bytes + 2 * B * H * d_h * es + 2 * H * d_h * r * es  # + out + B^V
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    scan_kernel = {1: "decode_split_kernel", 2: "decode_mfma_kernel"}.get(engine) or \
+        L.lrkv_decode_scan_kernel(dt, H, d_h, r)
+    traffic = traffic_from_profiles("decode_scan_counters", scan_kernel, wl.name, args.split_tokens)
+    return {
+        "tokens": tokens, "tokens_per_s": tokens / (step_ms * 1e-3), "step_ms": step_ms,
+        "step_ms_trials": step_runs, "wall_s_timed": wall, "settled": settled,
+        "dtype": "bf16" if d["dtype"] == "bf16" else "f32",
         "config": {"workload": wl.name, "batch": B, "heads": H, "head_dim": d_h, "rank": r,
                    "context": max_len, "cache_tokens": tokens, "split_tokens": args.split_tokens or "default",
                    "cache_MB": cache_bytes / 1e6},
         "hbm_GBps_step": step_bytes / (step_ms * 1e-3) / 1e9,
         "hbm_frac_step": step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "kernels_ms": {scan_kernel: scan_ms, "decode_merge_kernel": comb_ms},
-        "wall_s_timed": wall,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": scan_kernel, "algorithmic_bytes_per_launch": scan_bytes},
+        "copies": copies, "out": out,
     }
 
-    copy_reference(args, rec)
 
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(d, out, args.cpu_seconds, as_f64)
-    print(json.dumps(rec), flush=True)
+def progress(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def other_configs(args):
+    """The synthetic configurations besides the headline: each measured on
+    the GPU and checked against the oracle, with the oracle's own rate on
+    this host beside it."""
+    import torch
+    from rank_compressed_kv_lrkv_amd.workloads import DECODE_WORKLOADS, as_f64, decode_inputs
+
+    res = {}
+    # Causal prefill (MFMA) first: it runs at the part's power limit, and is
+    # measured before the long host-side oracle checks and HBM-bound decodes.
+    res["prefill_bf16_L4k"] = prefill_record(args)
+    torch.cuda.empty_cache()
+    progress("prefill_bf16_L4k done")
+    # Tiny fp32 decode: latency-bound (19 KB of cache).
+    wl = DECODE_WORKLOADS["tiny_f32_T64"]
+    d = decode_inputs(wl)
+    m = measure_decode(args, wl, d)
+    o = oracle_decode_check(d, m["out"], as_f64, budget_s=5.0)
+    res[wl.name] = {"kind": "latency", "step_us": m["step_ms"] * 1e3, "kernels_us":
+                    {k: v * 1e3 for k, v in m["kernels_ms"].items()}, "cache_tokens": m["tokens"],
+                    "gpu_vs_oracle_max_err_over_inf_norm": o["err"], "oracle": o["rate"]}
+    progress("tiny_f32_T64 done")
+    # Small bf16 decode: the 8.4 MB cache stays in L2 when one copy is reused
+    # (a latency); over rotated copies (working set above 2 x (L2 + MALL))
+    # each step reads its cache from HBM.
+    wl = DECODE_WORKLOADS["small_bf16_T2k"]
+    d = decode_inputs(wl)
+    m = measure_decode(args, wl, d)
+    o = oracle_decode_check(d, m["out"], as_f64, budget_s=5.0)
+    mr = measure_decode(args, wl, d, rotate_mb=2 * (32 + 256))
+    res[wl.name] = {
+        "kind": "latency (L2-resident) and rotated-buffer throughput",
+        "l2_resident": {"step_us": m["step_ms"] * 1e3,
+                        "kernels_us": {k: v * 1e3 for k, v in m["kernels_ms"].items()}},
+        "rotated": {"copies": mr["copies"], "step_us": mr["step_ms"] * 1e3, "cache_tokens_per_s": mr["tokens_per_s"],
+                    "hbm_GBps_step": mr["hbm_GBps_step"], "hbm_frac_step": mr["hbm_frac_step"],
+                    "kernels_us": {k: v * 1e3 for k, v in mr["kernels_ms"].items()},
+                    "scan_frac": mr["roofline"]["frac"]},
+        "gpu_vs_oracle_max_err_over_inf_norm": o["err"], "oracle": o["rate"]}
+    del m, mr
+    torch.cuda.empty_cache()
+    progress("small_bf16_T2k done")
+    # The headline decode on the vector-ALU scan (no MFMA in decode), for
+    # comparison with the default MFMA scan.
+    wl = DECODE_WORKLOADS["mid_bf16_T8k"]
+    d = decode_inputs(wl)
+    m = measure_decode(args, wl, d, engine=1)
+    o = oracle_decode_check(d, m["out"], as_f64, budget_s=3.0)
+    progress("mid_bf16_T8k on the vector-ALU scan measured")
+    res["mid_bf16_T8k_vector_alu_scan"] = {
+        "kind": "throughput (the headline shape on decode_split_kernel)", "cache_tokens_per_s": m["tokens_per_s"],
+        "step_ms": m["step_ms"], "kernels_ms": m["kernels_ms"], "hbm_GBps_step": m["hbm_GBps_step"],
+        "hbm_frac_step": m["hbm_frac_step"], "roofline": m["roofline"],
+        "gpu_vs_oracle_max_err_over_inf_norm": o["err"], "checked": o["checked"]}
+    del m, d
+    torch.cuda.empty_cache()
+    # Ragged long-context decode: 16 sequences of 1K-64K tokens, r = 32.
+    wl = DECODE_WORKLOADS["ragged_bf16_T1k_64k"]
+    d = decode_inputs(wl)
+    m = measure_decode(args, wl, d)
+    o = oracle_decode_check(d, m["out"], as_f64, budget_s=1e9)    # every (sequence, head) pair
+    res[wl.name] = {"kind": "throughput", "cache_tokens": m["tokens"], "cache_tokens_per_s": m["tokens_per_s"],
+                    "step_ms": m["step_ms"], "kernels_ms": m["kernels_ms"], "hbm_GBps_step": m["hbm_GBps_step"],
+                    "hbm_frac_step": m["hbm_frac_step"], "roofline": m["roofline"],
+                    "gpu_vs_oracle_max_err_over_inf_norm": o["err"], "checked": o["checked"], "oracle": o["rate"]}
+    del m, d
+    torch.cuda.empty_cache()
+    progress("ragged_bf16_T1k_64k done")
+    return res
+
+
+def oracle_decode_check(d, out_dev, as_f64, budget_s):
+    """The oracle, one whole sequence (all heads) at a time until budget_s of
+    wall clock is spent, against the GPU output; its rate on this host."""
+    sys.path.insert(0, ROOT)
+    import oracle as O
+    got = out_dev.float().cpu().numpy().astype(np.float64)
+    dt = d["dtype"]
+    f = lambda k: as_f64(d[k], dt)
+    bk, bv, q = f("b_k"), f("b_v"), f("q")
+    lens = np.asarray(d["seq_lens"])
+    toks, secs, err, done = 0, 0.0, 0.0, 0
+    for b in range(len(lens)):
+        L_ = int(lens[b])
+        args = (q[b:b + 1], as_f64(d["k_s"][b:b + 1, :L_], dt), as_f64(d["v_s"][b:b + 1, :L_], dt),
+                as_f64(d["z_k"][b:b + 1, :L_], dt), as_f64(d["z_v"][b:b + 1, :L_], dt), bk, bv, lens[b:b + 1])
+        t = time.perf_counter()
+        want = O.decode(*args)
+        secs += time.perf_counter() - t
+        toks += L_
+        done += 1
+        err = max(err, float(np.max(np.abs(got[b] - want[0])) / max(np.max(np.abs(want[0])), 1e-30)))
+        if secs >= budget_s:
+            break
+    return {"err": err, "checked": f"{done} of {len(lens)} sequences, all heads",
+            "rate": {"value": toks / secs, "unit": "cache tokens/s", "cores": thread_count(), "kind": "oracle",
+                     "sample": f"{done} of {len(lens)} sequences, all heads ({toks} cache tokens), float64 numpy, "
+                               f"{secs:.2f} s"}}
+
+
+def cpu_identity():
+    """The host CPU model and the single-thread oracle rate on the small decode configs."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    single = {}
+    try:
+        from threadpoolctl import threadpool_limits
+        from rank_compressed_kv_lrkv_amd.workloads import DECODE_WORKLOADS, as_f64, decode_inputs
+        sys.path.insert(0, ROOT)
+        import oracle as O
+        with threadpool_limits(limits=1):
+            for name, budget in (("tiny_f32_T64", 1.0), ("small_bf16_T2k", 3.0), ("mid_bf16_T8k", 5.0)):
+                d = decode_inputs(DECODE_WORKLOADS[name])
+                dt = d["dtype"]
+                f = lambda k: as_f64(d[k], dt)
+                lens = np.asarray(d["seq_lens"])
+                toks, secs, done = 0, 0.0, 0
+                for b in range(len(lens)):
+                    L_ = int(lens[b])
+                    a = (f("q")[b:b + 1], as_f64(d["k_s"][b:b + 1, :L_], dt), as_f64(d["v_s"][b:b + 1, :L_], dt),
+                         as_f64(d["z_k"][b:b + 1, :L_], dt), as_f64(d["z_v"][b:b + 1, :L_], dt), f("b_k"),
+                         f("b_v"), lens[b:b + 1])
+                    t = time.perf_counter()
+                    O.decode(*a)
+                    secs += time.perf_counter() - t
+                    toks += L_
+                    done += 1
+                    if secs >= budget:
+                        break
+                single[name] = {"cache_tokens_per_s": toks / secs, "sample": f"{done} of {len(lens)} sequences",
+                                "seconds": secs}
+    except Exception as e:      # the baseline is a report; never fail the bench for it
+        single["error"] = str(e)[:200]
+    return {"cpu_model": model, "logical_cpus_visible": len(os.sched_getaffinity(0)),
+            "single_thread": single}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def bench_prefill(args):
+def prefill_record(args):
     """Causal prefill of the 4 x 4096-token workload (H=32, d_h=128, r=16):
-    a step is lrkv_prefill with the cache written (append + MFMA attention)."""
+    the attention kernel alone (its TFLOP/s priced against the bf16 MFMA
+    peak) and lrkv_prefill with the cache written (the step); sampled query
+    rows checked against the oracle, and the oracle's rate on this host."""
     import torch
     import rank_compressed_kv_lrkv_amd as L
-    from rank_compressed_kv_lrkv_amd.workloads import PREFILL_WORKLOADS, prefill_inputs
+    from rank_compressed_kv_lrkv_amd.workloads import PREFILL_WORKLOADS, as_f64, prefill_inputs
 
-    wl = PREFILL_WORKLOADS[args.workload or "prefill_bf16_L4k"]
+    wl = PREFILL_WORKLOADS[args.workload if args.mode == "prefill" and args.workload else "prefill_bf16_L4k"]
     d = prefill_inputs(wl)
-
-    def dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-
-    t = {k: dev(d[k]) for k in ("q", "k_s", "v_s", "z_k", "z_v", "b_k", "b_v")}
+    t = {k: _dev(d[k], "bf16") for k in ("q", "k_s", "v_s", "z_k", "z_v", "b_k", "b_v")}
     B, Lq, H, d_h, r = wl.batch, wl.seq_len, wl.heads, wl.head_dim, wl.rank
     cache = L.LrkvCache.empty(B, H, d_h, r, Lq, dtype=torch.bfloat16)
     out = torch.empty_like(t["q"])
@@ -288,26 +494,81 @@ def bench_prefill(args):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    step_ms = timed(stream, args.steps, step)
-    kern_ms = timed(stream, args.steps, lambda: step(with_cache=False))   # the attention kernel alone
+    steps = max(1, min(args.steps, 20))
+    step_ms, _ = timed_median(stream, steps, step, args.trials)
+    kern_ms, kern_runs = timed_median(stream, steps, lambda: step(with_cache=False), args.trials)
+    torch.cuda.synchronize()
 
     pairs = B * H * Lq * (Lq + 1) // 2                       # causal (query, key) pairs
     flops = pairs * 4 * (d_h + r) + B * H * Lq * 4 * d_h * r  # Eq. (6)-(7) contractions + absorption
     tflops = flops / (kern_ms * 1e-3) / 1e12
     rec = {
-        "metric": "causal prefill over the LRKV cache: TFLOP/s and MFMA utilisation",
-        "value": B * Lq / (step_ms * 1e-3),
-        "unit": "prefill tokens/s (cache written)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "settle": {"seconds": args.settle_s, "steps": settled}, "ms_per_step": step_ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) queries, bases and latents; B ~ N(0, 1/r))",
+        "value": B * Lq / (step_ms * 1e-3), "unit": "prefill tokens/s (cache written)",
+        "settle": {"seconds": args.settle_s, "steps": settled}, "ms_per_step": step_ms, "steps": steps,
         "config": {"workload": wl.name, "batch": B, "seq_len": Lq, "heads": H, "head_dim": d_h, "rank": r},
-        "kernels_ms": {"prefill_kernel": kern_ms},
+        "kernels_ms": {"prefill_kernel": kern_ms}, "prefill_kernel_ms_trials": kern_runs,
+        "causal_pairs_per_s": pairs / (kern_ms * 1e-3),
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": traffic_from_profiles("prefill_counters", "prefill_kernel", wl.name),
                      "kernel": "prefill_kernel", "algorithmic_flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        rec.update(oracle_prefill_check(d, out, as_f64))
+    return rec
+
+
+def oracle_prefill_check(d, out_dev, as_f64, budget_s=8.0):
+    """Sampled rows of the prefill output against the oracle (query row i of
+    head h over keys 0..i, one by one), and the oracle's rate in causal
+    (query, key) pairs per second on this host (whole rows, all heads, until
+    budget_s is spent)."""
+    sys.path.insert(0, ROOT)
+    import oracle as O
+    got = out_dev.float().cpu().numpy().astype(np.float64)
+    f = lambda k: as_f64(d[k], "bf16")
+    q, b_k, b_v = f("q"), f("b_k"), f("b_v")
+    B, Lq, H, _ = q.shape
+    err, checked = 0.0, 0
+    for b, h in ((0, 0), (B - 1, H - 1), (B // 2, H // 2 + 1)):
+        for i in (0, 1, 31, 32, 33, Lq // 4, Lq // 2 - 1, Lq - 1):
+            n = i + 1
+            want = O.decode(q[b:b + 1, i][:, [h]], as_f64(d["k_s"][b:b + 1, :n], "bf16"),
+                            as_f64(d["v_s"][b:b + 1, :n], "bf16"), as_f64(d["z_k"][b:b + 1, :n][:, :, [h]], "bf16"),
+                            as_f64(d["z_v"][b:b + 1, :n][:, :, [h]], "bf16"), b_k[[h]], b_v[[h]], [n])[0, 0]
+            err = max(err, float(np.max(np.abs(got[b, i, h] - want)) / np.max(np.abs(want))))
+            checked += 1
+    # oracle rate: the plain prefill of the first n rows of sequence 0, all
+    # heads, for n = 256, 512, ... while the next size (about 4x the cost of
+    # the last) still fits the budget
+    t0 = time.perf_counter()
+    secs, rows, pairs, last, n = 0.0, 0, 0, 0.0, 256
+    while n <= Lq and secs + 4.5 * last < budget_s:
+        t = time.perf_counter()
+        O.prefill(q[:1, :n], f("k_s")[:1, :n], f("v_s")[:1, :n], f("z_k")[:1, :n], f("z_v")[:1, :n], b_k, b_v)
+        last = time.perf_counter() - t
+        secs += last
+        pairs += H * n * (n + 1) // 2
+        rows = n
+        n *= 2
+    return {"gpu_vs_oracle_max_err_over_inf_norm": err, "checked": f"{checked} (sequence, head, query row) samples",
+            "oracle": {"value": pairs / secs, "unit": "causal pairs/s", "cores": thread_count(), "kind": "oracle",
+                       "sample": f"plain causal prefill of the first 256..{rows} tokens of sequence 0, all {H} heads, "
+                                 f"float64 numpy, {secs:.1f} s"},
+            "oracle_wall_s": time.perf_counter() - t0}
+
+
+def bench_prefill(args):
+    """--mode prefill: the prefill workload as the headline line."""
+    r = prefill_record(args)
+    rec = {
+        "metric": "causal prefill over the LRKV cache: TFLOP/s and MFMA utilisation",
+        "value": r.pop("value"), "unit": r.pop("unit"),
+        "n_gpus": 1, "steps": r.pop("steps"), "warmup": args.warmup, "trials": args.trials,
+        "settle": r.pop("settle"), "ms_per_step": r.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) queries, bases and latents; B ~ N(0, 1/r))",
+        **r,
     }
     copy_reference(args, rec)
     print(json.dumps(rec), flush=True)

@@ -198,6 +198,31 @@ lrkv_status lrkv_decode_noalloc(int32_t dtype, int32_t batch, int32_t num_heads,
                                 const void* q, const void* b_k, const void* b_v, float scale,
                                 int32_t split_tokens, void* out, void* stream);
 
+/* lrkv_decode with an explicit choice of scan kernel, and of the phases to
+ * run (for comparing the two scans on one shape, and timing them apart).
+ *   engine  0: the default for the shape (as lrkv_decode_scan_kernel names);
+ *           1: the vector-ALU scan, decode_split_kernel (every supported
+ *              shape), with its fixed splits;
+ *           2: the MFMA scan, decode_mfma_kernel (only its shapes; others
+ *              return LRKV_ERR_SHAPE).
+ *   phases  1: the split-K scan (as lrkv_decode_partial), 2: the merge (as
+ *           lrkv_decode_combine), 3: both (as lrkv_decode).
+ * The remaining arguments are lrkv_decode's.  The workspace must be at least
+ * lrkv_decode_workspace_size_ex(engine, ...) bytes for the same sizes and
+ * split; the two phases of one decode must use the same engine. */
+lrkv_status lrkv_decode_workspace_size_ex(int32_t engine, int32_t dtype, int32_t batch, int32_t num_heads,
+                                          int32_t head_dim, int32_t rank, int64_t capacity,
+                                          int64_t max_len, int32_t split_tokens, size_t* bytes);
+lrkv_status lrkv_decode_ex(int32_t engine, int32_t phases,
+                           int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                           int32_t rank, int64_t capacity,
+                           const void* k_shared, const void* v_shared,
+                           const void* z_k, const void* z_v,
+                           const int32_t* seq_lens, int64_t max_len,
+                           const void* q, const void* b_k, const void* b_v, float scale,
+                           int32_t split_tokens, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Causal prefill of seq_len fresh tokens per sequence (slides "Compute
  * logits without expanding historical keys" and "Aggregate values before
  * the residual up-projection" with seq_len queries; query i sees keys

@@ -26,7 +26,7 @@ STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DT
 
 EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
-            "lrkv_decode_combine", "lrkv_decode_noalloc", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
+            "lrkv_decode_combine", "lrkv_decode_noalloc", "lrkv_decode_workspace_size_ex", "lrkv_decode_ex", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
             "lrkv_project_kernel", "lrkv_project_workspace_size", "lrkv_project_append",
             "lrkv_mha_decode_workspace_size", "lrkv_mha_decode")
 
@@ -65,6 +65,12 @@ def library() -> ctypes.CDLL:
             fn.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64,
                            _vp, _vp, _vp, _f32, _i32, _vp, _vp, _sz, _vp]
             fn.restype = _i32
+        lib.lrkv_decode_workspace_size_ex.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i64, _i64, _i32,
+                                                      ctypes.POINTER(_sz)]
+        lib.lrkv_decode_workspace_size_ex.restype = _i32
+        lib.lrkv_decode_ex.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64,
+                                       _vp, _vp, _vp, _f32, _i32, _vp, _vp, _sz, _vp]
+        lib.lrkv_decode_ex.restype = _i32
         lib.lrkv_decode_noalloc.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64,
                                             _vp, _vp, _vp, _f32, _i32, _vp, _vp]
         lib.lrkv_decode_noalloc.restype = _i32
@@ -212,17 +218,27 @@ def lrkv_decode_workspace_size(dtype: torch.dtype, batch: int, heads: int, head_
     return int(n.value)
 
 
-def decode_workspace(cache: LrkvCache, max_len: int, split_tokens: int = 0) -> torch.Tensor:
-    nbytes = lrkv_decode_workspace_size(cache.dtype, cache.batch, cache.heads, cache.head_dim, cache.rank,
-                                        cache.capacity, max_len, split_tokens)
+def lrkv_decode_workspace_size_ex(engine: int, dtype: torch.dtype, batch: int, heads: int, head_dim: int, rank: int,
+                                  capacity: int, max_len: int, split_tokens: int = 0) -> int:
+    n = _sz(0)
+    _check(library().lrkv_decode_workspace_size_ex(int(engine), _dtype_code(dtype), batch, heads, head_dim, rank,
+                                                   capacity, max_len, split_tokens, ctypes.byref(n)),
+           "lrkv_decode_workspace_size_ex")
+    return int(n.value)
+
+
+def decode_workspace(cache: LrkvCache, max_len: int, split_tokens: int = 0, engine: int = 0) -> torch.Tensor:
+    nbytes = lrkv_decode_workspace_size_ex(engine, cache.dtype, cache.batch, cache.heads, cache.head_dim,
+                                           cache.rank, cache.capacity, max_len, split_tokens)
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=cache.k_s.device)
 
 
 def lrkv_decode(cache: LrkvCache, seq_lens: torch.Tensor, max_len: int, q: torch.Tensor, b_k: torch.Tensor,
                 b_v: torch.Tensor, scale: Optional[float] = None, split_tokens: int = 0,
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                phase: str = "both") -> torch.Tensor:
-    """phase: "both" (lrkv_decode), "partial" (lrkv_decode_partial) or "combine" (lrkv_decode_combine)."""
+                phase: str = "both", engine: int = 0) -> torch.Tensor:
+    """phase: "both" (lrkv_decode), "partial" (lrkv_decode_partial) or "combine" (lrkv_decode_combine);
+    engine != 0 goes through lrkv_decode_ex (1: vector-ALU scan, 2: MFMA scan)."""
     dt = cache.dtype
     B, H, d_h, r = cache.batch, cache.heads, cache.head_dim, cache.rank
     _shape(q, "q", (B, H, d_h))
@@ -233,9 +249,13 @@ def lrkv_decode(cache: LrkvCache, seq_lens: torch.Tensor, max_len: int, q: torch
         out = torch.empty_like(q)
     _shape(out, "out", (B, H, d_h))
     if workspace is None:
-        workspace = decode_workspace(cache, max_len, split_tokens)
-    fn = {"both": library().lrkv_decode, "partial": library().lrkv_decode_partial,
-          "combine": library().lrkv_decode_combine}[phase]
+        workspace = decode_workspace(cache, max_len, split_tokens, engine)
+    if engine:
+        phases = {"both": 3, "partial": 1, "combine": 2}[phase]
+        fn = lambda *a: library().lrkv_decode_ex(int(engine), phases, *a)
+    else:
+        fn = {"both": library().lrkv_decode, "partial": library().lrkv_decode_partial,
+              "combine": library().lrkv_decode_combine}[phase]
     _check(fn(_dtype_code(dt), cache.batch, cache.heads, cache.head_dim, cache.rank,
                                  cache.capacity, *cache.pointers(), _ptr(seq_lens, "seq_lens", torch.int32),
                                  max_len, _ptr(q, "q", dt), _ptr(b_k, "b_k", dt), _ptr(b_v, "b_v", dt),
@@ -277,12 +297,13 @@ class DecodeCall:
     argument checking from loops that repeat the same decode."""
 
     def __init__(self, cache: LrkvCache, seq_lens, max_len, q, b_k, b_v, scale=None, split_tokens=0,
-                 out=None, workspace=None):
+                 out=None, workspace=None, engine=0):
         self.out = out if out is not None else torch.empty_like(q)
-        self.workspace = workspace if workspace is not None else decode_workspace(cache, max_len, split_tokens)
+        self.workspace = (workspace if workspace is not None
+                          else decode_workspace(cache, max_len, split_tokens, engine))
         # validate once through the regular path (a real call), then freeze the argument tuple
         lrkv_decode(cache, seq_lens, max_len, q, b_k, b_v, scale, split_tokens, self.out, self.workspace,
-                    phase="partial")
+                    phase="partial", engine=engine)
         dt = cache.dtype
         self._keep = (cache, seq_lens, q, b_k, b_v)
         self._args = (_dtype_code(dt), cache.batch, cache.heads, cache.head_dim, cache.rank, cache.capacity,
@@ -291,7 +312,11 @@ class DecodeCall:
                       split_tokens, _ptr(self.out, "out", dt), _ptr(self.workspace, "workspace"),
                       self.workspace.numel())
         lib = library()
-        self._fns = (lib.lrkv_decode, lib.lrkv_decode_partial, lib.lrkv_decode_combine)
+        if engine:
+            ex = lib.lrkv_decode_ex
+            self._fns = tuple((lambda ph: (lambda *a: ex(int(engine), ph, *a)))(ph) for ph in (3, 1, 2))
+        else:
+            self._fns = (lib.lrkv_decode, lib.lrkv_decode_partial, lib.lrkv_decode_combine)
 
     def _call(self, i):
         st = self._fns[i](*self._args, torch.cuda.current_stream().cuda_stream)

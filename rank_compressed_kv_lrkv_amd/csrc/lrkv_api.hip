@@ -44,18 +44,22 @@ lrkv_status check_sizes(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
   return LRKV_OK;
 }
 
+// engine: 0 = the default for the shape, 1 = the vector-ALU scan
+// (decode_split_kernel), 2 = the MFMA scan (decode_mfma_kernel).
 lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t head_dim, int32_t rank,
-                        int64_t capacity, int64_t max_len, int32_t split_tokens, DecodePlan* pl) {
+                        int64_t capacity, int64_t max_len, int32_t split_tokens, DecodePlan* pl, int32_t engine = 0) {
   lrkv_status st = check_sizes(dtype, batch, heads, head_dim, rank, capacity);
   if (st != LRKV_OK) return st;
+  if (engine < 0 || engine > 2) return LRKV_ERR_SHAPE;
   if (!lrkv::decode_supported(dtype, head_dim, rank, heads)) return LRKV_ERR_SHAPE;
+  if (engine == 2 && !lrkv::decode_mfma_supported(dtype, head_dim, rank, heads)) return LRKV_ERR_SHAPE;
   if (max_len < 0 || split_tokens < 0) return LRKV_ERR_SHAPE;
   if (max_len > capacity) return LRKV_ERR_CAPACITY;
   if (split_tokens != 0 && split_tokens % lrkv::kDecodeTile != 0) return LRKV_ERR_SHAPE;
 
   pl->batch = batch; pl->heads = heads; pl->head_dim = head_dim; pl->rank = rank; pl->dtype = dtype;
   pl->capacity = capacity; pl->max_len = int(max_len);
-  pl->mfma = lrkv::decode_mfma_supported(dtype, head_dim, rank, heads);
+  pl->mfma = engine != 1 && lrkv::decode_mfma_supported(dtype, head_dim, rank, heads);
   pl->group = (rank == 4 || heads > 32) ? 4 : 8;
   int hp = 1;
   while (hp < heads) hp <<= 1;
@@ -180,13 +184,28 @@ lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num
   return LRKV_OK;
 }
 
+lrkv_status lrkv_decode_workspace_size_ex(int32_t engine, int32_t dtype, int32_t batch, int32_t num_heads,
+                                          int32_t head_dim, int32_t rank, int64_t capacity, int64_t max_len,
+                                          int32_t split_tokens, size_t* bytes) {
+  if (!bytes) return LRKV_ERR_NULL;
+  DecodePlan pl;
+  const lrkv_status st =
+      plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl, engine);
+  if (st != LRKV_OK) return st;
+  *bytes = pl.ws_ml_bytes + pl.ws_acc_bytes + pl.ws_meta_bytes;
+  return LRKV_OK;
+}
+
 static lrkv_status decode_phases(int phase, int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
                                  int32_t rank, int64_t capacity, const void* k_shared, const void* v_shared,
                                  const void* z_k, const void* z_v, const int32_t* seq_lens, int64_t max_len,
                                  const void* q, const void* b_k, const void* b_v, float scale, int32_t split_tokens,
-                                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                                 void* out, void* workspace, size_t workspace_bytes, void* stream,
+                                 int32_t engine = 0) {
+  if (phase < 1 || phase > 3) return LRKV_ERR_SHAPE;
   DecodePlan pl;
-  const lrkv_status st = plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl);
+  const lrkv_status st =
+      plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl, engine);
   if (st != LRKV_OK) return st;
   if (batch == 0) return LRKV_OK;
   const bool scan = phase & 1, combine = phase & 2;
@@ -224,6 +243,9 @@ static lrkv_status decode_phases(int phase, int32_t dtype, int32_t batch, int32_
       b_v, scale, split_tokens, out, workspace, workspace_bytes, stream
 
 lrkv_status lrkv_decode(LRKV_DECODE_ARGS) { return decode_phases(3, LRKV_DECODE_PASS); }
+lrkv_status lrkv_decode_ex(int32_t engine, int32_t phases, LRKV_DECODE_ARGS) {
+  return decode_phases(phases, LRKV_DECODE_PASS, engine);
+}
 
 lrkv_status lrkv_decode_noalloc(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
                                 int64_t capacity, const void* k_shared, const void* v_shared, const void* z_k,

@@ -316,3 +316,24 @@ def mha_call(**over):
 ])
 def test_mha_decode_rejects_before_launch(kw, want):
     assert mha_call(**kw) == want
+
+
+@no_gpu
+def test_decode_ex_validation():
+    lib = L.library()
+    n = ctypes.c_size_t(0)
+    # engine 2 (MFMA scan) only on its shapes; engine 1 everywhere the vector scan runs
+    assert lib.lrkv_decode_workspace_size_ex(2, BF16, 2, 8, 64, 8, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_decode_workspace_size_ex(1, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == OK
+    assert lib.lrkv_decode_workspace_size_ex(3, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_decode_workspace_size_ex(-1, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    # the default engine matches lrkv_decode_workspace_size
+    m = ctypes.c_size_t(0)
+    assert lib.lrkv_decode_workspace_size_ex(0, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == OK
+    assert lib.lrkv_decode_workspace_size(BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(m)) == OK
+    assert n.value == m.value
+    p = 16
+    for phases in (0, 4, -1):
+        st = lib.lrkv_decode_ex(1, phases, BF16, 2, 32, 128, 16, 256, p, p, p, p, p, 256, p, p, p,
+                                ctypes.c_float(0.0), 0, p, p, 1 << 30, None)
+        assert st == SHAPE, (phases, st)

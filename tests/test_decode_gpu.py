@@ -190,3 +190,40 @@ def test_balanced_partition_uniform_lengths(batch, length):
     d = decode_inputs(wl, seed=40 + batch, batch=batch, capacity=length,
                       lens=np.full(batch, length, np.int32))
     check(d, run_decode(d), name=f"uniform B={batch} L={length}")
+
+
+def test_vector_alu_scan_on_headline_shape():
+    # lrkv_decode_ex(engine=1) runs the vector-ALU scan on a shape whose
+    # default is the MFMA scan; both are held to the oracle
+    import torch
+    import rank_compressed_kv_lrkv_amd as L
+    from tests.gpu_util import device_cache, from_dev, to_dev
+    wl = DECODE_WORKLOADS["mid_bf16_T8k"]
+    lens = np.array([1000, 999, 513, 1, 64, 65], np.int32)
+    say(f"case {wl.name} engine=1 batch=6 capacity=1000 lens={lens.tolist()}")
+    d = decode_inputs(wl, batch=6, capacity=1000, lens=lens, seed=17)
+    cache = device_cache(d)
+    lt = torch.from_numpy(lens).cuda()
+    args = (cache, lt, 1000, to_dev(d["q"], "bf16"), to_dev(d["b_k"], "bf16"), to_dev(d["b_v"], "bf16"))
+    for engine in (1, 2):
+        out = L.lrkv_decode(*args, engine=engine)
+        torch.cuda.synchronize()
+        check(d, from_dev(out), name=f"engine {engine}")
+
+
+def test_vector_alu_scan_full_headline_sampled():
+    import torch
+    import rank_compressed_kv_lrkv_amd as L
+    from tests.gpu_util import device_cache, from_dev, to_dev
+    wl = DECODE_WORKLOADS["mid_bf16_T8k"]
+    say(f"case {wl} engine=1 (full size, sampled)")
+    d = decode_inputs(wl)
+    cache = device_cache(d)
+    lt = torch.from_numpy(np.asarray(d["seq_lens"], np.int32)).cuda()
+    out = L.lrkv_decode(cache, lt, wl.capacity, to_dev(d["q"], "bf16"), to_dev(d["b_k"], "bf16"),
+                        to_dev(d["b_v"], "bf16"), engine=1)
+    torch.cuda.synchronize()
+    got = from_dev(out)
+    assert np.all(np.isfinite(got))
+    for b, h in ((0, 0), (31, 31), (17, 9)):
+        check(d, got, [b], [h], name=f"vector scan full b={b} h={h}")
