@@ -48,6 +48,7 @@ __all__ = [
     "cache_elems_per_token", "cache_ratio_vs_mha", "kv_param_count",
     "head_projections", "cache_from_inputs", "implied_kv", "softmax_attention",
     "decode", "prefill", "prefill_with_past", "decode_from_weights", "append", "projected_rows",
+    "prefill_forward_lse", "prefill_backward",
 ]
 
 
@@ -278,3 +279,88 @@ def append(cache: dict, pos, new: dict) -> dict:
             p = int(pos[b])
             outc[key][b, p:p + n] = src[b]
     return outc
+
+
+# ---------------------------------------------------------------------------
+# Training-side workload.
+# Slide "Training learns the base and residuals together" (paper Sec. 3):
+# W_shared, U_h and B_h are trained jointly, and training evaluates the full
+# per-head K/V.  The forward pass of a layer's attention is the causal
+# prefill above; its backward pass is the gradient of a scalar loss with
+# respect to every input of that prefill.  Written here the plain way: the
+# per-head keys and values are reconstructed explicitly (the "expanded"
+# evaluation of the same model), ordinary softmax attention is
+# differentiated per head, and the chain rule runs through
+#   K_h = K_s + Z^K_h (B^K_h)^T,   V_h = V_s + Z^V_h (B^V_h)^T
+# (slide "Cache shared features and compact per-head latents").
+# ---------------------------------------------------------------------------
+def prefill_forward_lse(q, k_s, v_s, z_k, z_v, b_k, b_v, scale: Optional[float] = None):
+    """The causal prefill of ``prefill`` and, for every query row i of every
+    head, the natural log-sum-exp of its scaled causal logits,
+    lse[b, i, h] = log sum_{j <= i} exp(scale * q_{b,i,h} . k_{h,j}).
+    Returns (out [B, L, H, d_h], lse [B, L, H])."""
+    q = np.asarray(q, np.float64)
+    B, L, H, d_h = q.shape
+    sc = _default_scale(d_h, scale)
+    out = np.zeros((B, L, H, d_h), np.float64)
+    lse = np.zeros((B, L, H), np.float64)
+    future = np.triu(np.ones((L, L), dtype=bool), k=1)
+    for b in range(B):
+        K, V = implied_kv(k_s[b], v_s[b], z_k[b], z_v[b], b_k, b_v)
+        for h in range(H):
+            S = (q[b, :, h, :] @ K[h].T) * sc
+            S[future] = -np.inf
+            mx = S.max(axis=1, keepdims=True)
+            E = np.exp(S - mx)
+            tot = E.sum(axis=1, keepdims=True)
+            out[b, :, h, :] = (E / tot) @ V[h]
+            lse[b, :, h] = (mx + np.log(tot))[:, 0]
+    return out, lse
+
+
+def prefill_backward(q, k_s, v_s, z_k, z_v, b_k, b_v, d_out, scale: Optional[float] = None) -> dict:
+    """Gradients of the scalar sum(d_out * prefill(q, k_s, v_s, z_k, z_v,
+    b_k, b_v)) with respect to each input (a vector-Jacobian product).
+
+    Per sequence b and head h, with K_h, V_h reconstructed and the causal
+    softmax A = softmax(scale * Q_h K_h^T) (future keys masked):
+      dV_h = A^T dO_h,      dA = dO_h V_h^T,
+      dS   = A o (dA - rowsum(A o dA))        (derivative of the softmax),
+      dQ_h = scale * dS K_h,   dK_h = scale * dS^T Q_h;
+    then through K_h = K_s + Z^K_h (B^K_h)^T (and V likewise):
+      dK_s = sum_h dK_h,   dZ^K_h = dK_h B^K_h,   dB^K_h = sum_b dK_h^T Z^K_h.
+    Returns float64 arrays named after the inputs: dq [B, L, H, d_h],
+    dk_s, dv_s [B, L, d_h], dz_k, dz_v [B, L, H, r], db_k, db_v [H, d_h, r]."""
+    q = np.asarray(q, np.float64)
+    d_out = np.asarray(d_out, np.float64)
+    z_k = np.asarray(z_k, np.float64)
+    z_v = np.asarray(z_v, np.float64)
+    b_k = np.asarray(b_k, np.float64)
+    b_v = np.asarray(b_v, np.float64)
+    B, L, H, d_h = q.shape
+    r = b_k.shape[2]
+    sc = _default_scale(d_h, scale)
+    g = {"dq": np.zeros_like(q), "dk_s": np.zeros((B, L, d_h)), "dv_s": np.zeros((B, L, d_h)),
+         "dz_k": np.zeros((B, L, H, r)), "dz_v": np.zeros((B, L, H, r)),
+         "db_k": np.zeros((H, d_h, r)), "db_v": np.zeros((H, d_h, r))}
+    future = np.triu(np.ones((L, L), dtype=bool), k=1)
+    for b in range(B):
+        K, V = implied_kv(k_s[b], v_s[b], z_k[b], z_v[b], b_k, b_v)
+        for h in range(H):
+            Qh, dO = q[b, :, h, :], d_out[b, :, h, :]
+            S = (Qh @ K[h].T) * sc
+            S[future] = -np.inf
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            A = E / E.sum(axis=1, keepdims=True)
+            dV = A.T @ dO
+            dA = dO @ V[h].T
+            dS = A * (dA - (A * dA).sum(axis=1, keepdims=True))
+            g["dq"][b, :, h, :] = sc * (dS @ K[h])
+            dK = sc * (dS.T @ Qh)
+            g["dk_s"][b] += dK
+            g["dv_s"][b] += dV
+            g["dz_k"][b, :, h, :] = dK @ b_k[h]
+            g["dz_v"][b, :, h, :] = dV @ b_v[h]
+            g["db_k"][h] += dK.T @ z_k[b, :, h, :]
+            g["db_v"][h] += dV.T @ z_v[b, :, h, :]
+    return g

@@ -465,6 +465,117 @@ def pin_projected_rows_decode_like_weights(O):
     assert rel_err(got, ref) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# Training-side forward (log-sum-exp) and backward (slide "Training learns
+# the base and residuals together").
+# ---------------------------------------------------------------------------
+_GRAD_NAMES = ("dq", "dk_s", "dv_s", "dz_k", "dz_v", "db_k", "db_v")
+
+
+def pin_forward_lse_brute_force(O):
+    # lse[b, i, h] = log sum_{j <= i} exp(scale q.k_{h,j}), with every logit
+    # built by scalar loops (math.fsum) straight from the cache definition
+    # k_{h,j} = k_{s,j} + B^K_h z^K_{j,h}, and the log-sum-exp from scipy
+    from scipy.special import logsumexp
+    q, k_s, v_s, z_k, z_v, b_k, b_v = _rand_prefill(53, B=1, L=5, H=2, d_h=3, r=2)
+    out, lse = O.prefill_forward_lse(q, k_s, v_s, z_k, z_v, b_k, b_v)
+    assert rel_err(out, O.prefill(q, k_s, v_s, z_k, z_v, b_k, b_v)) < TIGHT
+    B, L, H, d_h = q.shape
+    r = b_k.shape[2]
+    sc = 1.0 / math.sqrt(d_h)
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                logits = []
+                for j in range(i + 1):
+                    kj = [k_s[b, j, e] + math.fsum(b_k[h, e, c] * z_k[b, j, h, c] for c in range(r))
+                          for e in range(d_h)]
+                    logits.append(sc * math.fsum(q[b, i, h, e] * kj[e] for e in range(d_h)))
+                assert abs(lse[b, i, h] - logsumexp(logits)) < 1e-12 * max(1.0, abs(lse[b, i, h]))
+
+
+def _loss(O, args, d_out):
+    return float(np.sum(d_out * O.prefill(*args)))
+
+
+def pin_backward_finite_differences(O):
+    # Every gradient element against a central difference of the (pinned)
+    # forward oracle: sum(d_out * prefill(x)) at x +- eps e_k.
+    rng = np.random.default_rng(59)
+    args = list(_rand_prefill(59, B=2, L=4, H=2, d_h=3, r=2))
+    d_out = rng.standard_normal(args[0].shape)
+    g = O.prefill_backward(*args, d_out)
+    eps = 1e-6
+    for idx, name in enumerate(_GRAD_NAMES):
+        x = args[idx]
+        fd = np.zeros_like(x)
+        for k in np.ndindex(x.shape):
+            old = x[k]
+            x[k] = old + eps
+            up = _loss(O, args, d_out)
+            x[k] = old - eps
+            dn = _loss(O, args, d_out)
+            x[k] = old
+            fd[k] = (up - dn) / (2 * eps)
+        err = float(np.max(np.abs(g[name] - fd)) / max(np.max(np.abs(fd)), 1e-30))
+        assert err < 1e-6, (name, err)
+
+
+def pin_backward_torch_autograd(O):
+    # The same gradients by torch autograd (float64, CPU) through the library
+    # attention routine on K_h = K_s + Z^K_h B^K_h^T and V_h likewise.
+    rng = np.random.default_rng(61)
+    args = _rand_prefill(61, B=2, L=9, H=3, d_h=4, r=3)
+    d_out = rng.standard_normal(args[0].shape)
+    g = O.prefill_backward(*args, d_out)
+    t = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in args]
+    q, k_s, v_s, z_k, z_v, b_k, b_v = t
+    K = k_s[:, None] + torch.einsum("blhr,hdr->bhld", z_k, b_k)       # [B, H, L, d_h]
+    V = v_s[:, None] + torch.einsum("blhr,hdr->bhld", z_v, b_v)
+    out = torch.nn.functional.scaled_dot_product_attention(q.permute(0, 2, 1, 3), K, V, is_causal=True,
+                                                           scale=1.0 / math.sqrt(q.shape[-1]))
+    (out.permute(0, 2, 1, 3) * torch.from_numpy(d_out)).sum().backward()
+    for name, x in zip(_GRAD_NAMES, t):
+        assert rel_err(g[name], x.grad.numpy()) < TIGHT, name
+
+
+def pin_backward_mqa_sdpa(O):
+    # B^K = B^V = 0: LRKV is MQA, and the shared rows get the heads' summed
+    # key/value gradients of the library routine; the latents get none.
+    rng = np.random.default_rng(67)
+    q, k_s, v_s, z_k, z_v, b_k, b_v = _rand_prefill(67, B=1, L=7, H=3, d_h=4, r=2, zero_b=True)
+    d_out = rng.standard_normal(q.shape)
+    g = O.prefill_backward(q, k_s, v_s, z_k, z_v, b_k, b_v, d_out)
+    B, L, H, d_h = q.shape
+    tq = torch.tensor(np.transpose(q, (0, 2, 1, 3)).copy(), requires_grad=True)
+    tk = torch.tensor(np.broadcast_to(k_s[:, None], (B, H, L, d_h)).copy(), requires_grad=True)
+    tv = torch.tensor(np.broadcast_to(v_s[:, None], (B, H, L, d_h)).copy(), requires_grad=True)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=1.0 / math.sqrt(d_h))
+    (out * torch.from_numpy(np.transpose(d_out, (0, 2, 1, 3)).copy())).sum().backward()
+    assert rel_err(g["dq"], np.transpose(tq.grad.numpy(), (0, 2, 1, 3))) < TIGHT
+    assert rel_err(g["dk_s"], tk.grad.numpy().sum(axis=1)) < TIGHT
+    assert rel_err(g["dv_s"], tv.grad.numpy().sum(axis=1)) < TIGHT
+    assert np.all(g["dz_k"] == 0) and np.all(g["dz_v"] == 0)
+    # dB^K_h = dK_h^T Z^K_h with the library's per-head key gradient
+    dk_h = np.transpose(tk.grad.numpy(), (0, 2, 1, 3))                 # [B, L, H, d_h]
+    want = np.einsum("blhd,blhr->hdr", dk_h, z_k)
+    assert rel_err(g["db_k"], want) < TIGHT
+
+
+def pin_backward_single_token(O):
+    # L = 1: the softmax over one key is constant, so nothing upstream of the
+    # logits gets a gradient; the value path is linear.
+    rng = np.random.default_rng(71)
+    q, k_s, v_s, z_k, z_v, b_k, b_v = _rand_prefill(71, B=2, L=1, H=3, d_h=4, r=2)
+    d_out = rng.standard_normal(q.shape)
+    g = O.prefill_backward(q, k_s, v_s, z_k, z_v, b_k, b_v, d_out)
+    for name in ("dq", "dk_s", "dz_k", "db_k"):
+        assert np.max(np.abs(g[name])) < 1e-14, name
+    assert rel_err(g["dv_s"], d_out.sum(axis=2)) < TIGHT
+    assert rel_err(g["dz_v"], np.einsum("blhd,hdr->blhr", d_out, b_v)) < TIGHT
+    assert rel_err(g["db_v"], np.einsum("blhd,blhr->hdr", d_out, z_v)) < TIGHT
+
+
 ALL_PINS = [
     pin_cache_counts_printed, pin_cache_ratios_printed, pin_cache_ratio_boxed_form,
     pin_table12_megabytes, pin_kv_param_count_matches_arrays, pin_decode_mqa_reduction,
@@ -473,5 +584,6 @@ ALL_PINS = [
     pin_prefill_mqa_causal_sdpa, pin_prefill_mha_causal_sdpa, pin_prefill_rows_are_decodes,
     pin_prefill_with_past_rows_are_decodes, pin_prefill_with_past_mqa_sdpa, pin_chunked_prefill_equals_full,
     pin_append_slots, pin_projected_rows_brute_force, pin_projected_rows_identity_inputs,
-    pin_projected_rows_decode_like_weights,
+    pin_projected_rows_decode_like_weights, pin_forward_lse_brute_force, pin_backward_finite_differences,
+    pin_backward_torch_autograd, pin_backward_mqa_sdpa, pin_backward_single_token,
 ]

@@ -108,6 +108,49 @@ def _projected(kind):
         return _orig_projected(X, Wk_shared, Wv_shared, Uk_shift, Uv)
     return mutant
 
+_orig_backward = O.prefill_backward
+_orig_lse = O.prefill_forward_lse
+
+
+def _backward(kind):
+    """The oracle's backward pass with one planted slip."""
+    def mutant(q, k_s, v_s, z_k, z_v, b_k, b_v, d_out, scale=None):
+        q, d_out, z_k, z_v, b_k, b_v = (np.asarray(a, np.float64) for a in (q, d_out, z_k, z_v, b_k, b_v))
+        B, L, H, d_h = q.shape
+        r = b_k.shape[2]
+        sc = 1.0 / math.sqrt(d_h)
+        g = {"dq": np.zeros_like(q), "dk_s": np.zeros((B, L, d_h)), "dv_s": np.zeros((B, L, d_h)),
+             "dz_k": np.zeros((B, L, H, r)), "dz_v": np.zeros((B, L, H, r)),
+             "db_k": np.zeros((H, d_h, r)), "db_v": np.zeros((H, d_h, r))}
+        future = np.triu(np.ones((L, L), dtype=bool), k=1)
+        for b in range(B):
+            K, V = O.implied_kv(k_s[b], v_s[b], z_k[b], z_v[b], b_k, b_v)
+            for h in range(H):
+                Qh, dO = q[b, :, h, :], d_out[b, :, h, :]
+                S = (Qh @ K[h].T) * sc
+                S[future] = -np.inf
+                E = np.exp(S - S.max(axis=1, keepdims=True))
+                A = E / E.sum(axis=1, keepdims=True)
+                dV = A.T @ dO
+                dA = dO @ V[h].T
+                dS = A * dA if kind == "no_softmax_rowsum" else A * (dA - (A * dA).sum(axis=1, keepdims=True))
+                g["dq"][b, :, h, :] = sc * (dS @ (V[h] if kind == "dq_uses_values" else K[h]))
+                dK = (1.0 if kind == "dk_without_scale" else sc) * (dS.T @ Qh)
+                g["dk_s"][b] += dK
+                g["dv_s"][b] += dV
+                g["dz_k"][b, :, h, :] = dK @ (b_v[h] if kind == "dz_k_uses_value_factor" else b_k[h])
+                g["dz_v"][b, :, h, :] = dV @ b_v[h]
+                g["db_k"][h] += dK.T @ z_k[b, :, h, :]
+                g["db_v"][h] += dV.T @ z_v[b, :, h, :]
+        return g
+    return mutant
+
+
+def _lse_mutant(q, k_s, v_s, z_k, z_v, b_k, b_v, scale=None):
+    out, lse = _orig_lse(q, k_s, v_s, z_k, z_v, b_k, b_v, scale)
+    return out, lse / math.log(2.0)          # log2 where the natural log is meant
+
+
 MUTANTS = {
     "lrkv_count_without_heads": ("cache_elems_per_token", _count_without_heads),
     "drop_key_latent": ("implied_kv", _implied(fk=lambda k, z, bk, bv, h: k)),
@@ -128,6 +171,11 @@ MUTANTS = {
     "past_mask_excludes_diagonal": ("prefill_with_past", _past("excludes_diagonal")),
     "projection_kv_swapped": ("projected_rows", _projected("kv_swapped")),
     "projection_latent_of_previous_head": ("projected_rows", _projected("head_shift")),
+    "backward_no_softmax_rowsum": ("prefill_backward", _backward("no_softmax_rowsum")),
+    "backward_dq_uses_values": ("prefill_backward", _backward("dq_uses_values")),
+    "backward_dk_without_scale": ("prefill_backward", _backward("dk_without_scale")),
+    "backward_dz_k_uses_value_factor": ("prefill_backward", _backward("dz_k_uses_value_factor")),
+    "lse_in_log2": ("prefill_forward_lse", _lse_mutant),
 }
 
 
