@@ -271,6 +271,60 @@ lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, 
                                const void* z_k_new, const void* z_v_new,
                                const void* b_k, const void* b_v, float scale, void* out, void* stream);
 
+/* Training forward: the causal prefill of lrkv_prefill over fresh sequences
+ * (no cache), also returning each query row's log-sum-exp for the backward
+ * pass (slide "Training learns the base and residuals together": the base
+ * and the residual factors are trained jointly, so the attention's
+ * gradients reach K_s, V_s, the latents and B_h).
+ *   q, out   [batch][seq_len][num_heads][head_dim];
+ *   k_s, v_s [batch][seq_len][head_dim];  z_k, z_v [batch][seq_len][num_heads][rank];
+ *   b_k, b_v [num_heads][head_dim][rank];
+ *   lse      fp32 [batch][seq_len][num_heads], caller-allocated:
+ *            lse[b][i][h] = ln sum_{j <= i} exp(scale * q_{b,i,h} . k_{h,j}).
+ * Envelope: dtype LRKV_BF16, head_dim 64 or 128, rank 0, 8, 16 or 32,
+ * num_heads a multiple of 4; else LRKV_ERR_SHAPE (LRKV_ERR_DTYPE for an
+ * unknown dtype).  batch*seq_len below 2^31 and one sequence's rows and
+ * latents under 4 GiB, else LRKV_ERR_SHAPE.  scale <= 0 or not finite means
+ * 1/sqrt(head_dim).  Tensors 16-byte aligned, lse 4-byte aligned.  batch or
+ * seq_len 0 writes nothing. */
+lrkv_status lrkv_train_forward(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                               int32_t rank, int32_t seq_len, const void* q,
+                               const void* k_s, const void* v_s, const void* z_k, const void* z_v,
+                               const void* b_k, const void* b_v, float scale, void* out, float* lse,
+                               void* stream);
+
+/* Workspace bytes lrkv_train_backward needs for these sizes (same envelope
+ * and errors as lrkv_train_forward; NULL bytes gives LRKV_ERR_NULL). */
+lrkv_status lrkv_train_backward_workspace_size(int32_t dtype, int32_t batch, int32_t num_heads,
+                                               int32_t head_dim, int32_t rank, int32_t seq_len,
+                                               size_t* bytes);
+
+/* Training backward: the vector-Jacobian product of lrkv_train_forward's
+ * output with the upstream gradient d_out (same layout and dtype as out),
+ * through the absorbed forms of Eqs. (6)-(7) and then through
+ * K_h = K_s + Z^K_h (B^K_h)^T and V_h = V_s + Z^V_h (B^V_h)^T (slide
+ * "LRKV constrains differences between heads"):
+ *   dq   fp32 [batch][seq_len][num_heads][head_dim];
+ *   dk_s, dv_s fp32 [batch][seq_len][head_dim]   (summed over heads);
+ *   dz_k, dz_v fp32 [batch][seq_len][num_heads][rank];
+ *   db_k, db_v fp32 [num_heads][head_dim][rank]  (summed over sequences and tokens).
+ * out and lse are the forward's outputs for the same inputs and scale.
+ * Every gradient is overwritten (not accumulated into).  The probabilities
+ * and their gradients enter bf16 MFMAs; all sums are fp32, in a fixed order
+ * (results are deterministic).  workspace: at least
+ * lrkv_train_backward_workspace_size bytes, 16-byte aligned, contents on
+ * entry ignored.  batch or seq_len 0 only sets db_k and db_v to zero (rank
+ * > 0).  Envelope and errors as lrkv_train_forward, plus
+ * LRKV_ERR_WORKSPACE; gradient pointers need 4-byte alignment, dq 16. */
+lrkv_status lrkv_train_backward(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                int32_t rank, int32_t seq_len, const void* q,
+                                const void* k_s, const void* v_s, const void* z_k, const void* z_v,
+                                const void* b_k, const void* b_v, const void* out, const float* lse,
+                                const void* d_out, float scale,
+                                float* dq, float* dk_s, float* dv_s, float* dz_k, float* dz_v,
+                                float* db_k, float* db_v,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Packs the key/value projection weights into the output-major matrix that
  * lrkv_project_append reads (slide "LRKV constrains differences between
  * heads", Eqs. (2)-(3): each head's projection is W_shared + U_h B_h^T, and

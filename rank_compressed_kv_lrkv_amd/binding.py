@@ -28,7 +28,8 @@ EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
             "lrkv_decode_combine", "lrkv_decode_noalloc", "lrkv_decode_workspace_size_ex", "lrkv_decode_ex", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
             "lrkv_project_kernel", "lrkv_project_workspace_size", "lrkv_project_append",
-            "lrkv_mha_decode_workspace_size", "lrkv_mha_decode")
+            "lrkv_mha_decode_workspace_size", "lrkv_mha_decode", "lrkv_train_forward",
+            "lrkv_train_backward_workspace_size", "lrkv_train_backward")
 
 
 class LrkvError(RuntimeError):
@@ -94,6 +95,14 @@ def library() -> ctypes.CDLL:
         lib.lrkv_mha_decode.argtypes = [_i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _i64, _vp, _f32, _i32, _vp, _vp,
                                         _sz, _vp]
         lib.lrkv_mha_decode.restype = _i32
+        lib.lrkv_train_forward.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _f32, _vp, _vp, _vp]
+        lib.lrkv_train_forward.restype = _i32
+        lib.lrkv_train_backward_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+        lib.lrkv_train_backward_workspace_size.restype = _i32
+        lib.lrkv_train_backward.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        lib.lrkv_train_backward.restype = _i32
         _lib = lib
     return _lib
 
@@ -478,6 +487,78 @@ def lrkv_mha_decode(k: torch.Tensor, v: torch.Tensor, seq_lens: torch.Tensor, ma
                                      _ptr(workspace, "workspace"), workspace.numel(), _stream()),
            "lrkv_mha_decode")
     return out
+
+
+def _train_shapes(q, k_s, v_s, z_k, z_v, b_k, b_v):
+    B, L, H, d_h = q.shape
+    r = z_k.shape[-1]
+    _shape(k_s, "k_s", (B, L, d_h))
+    _shape(v_s, "v_s", (B, L, d_h))
+    _shape(z_k, "z_k", (B, L, H, r))
+    _shape(z_v, "z_v", (B, L, H, r))
+    _shape(b_k, "b_k", (H, d_h, r))
+    _shape(b_v, "b_v", (H, d_h, r))
+    return B, L, H, d_h, r
+
+
+def lrkv_train_forward(q, k_s, v_s, z_k, z_v, b_k, b_v, scale: Optional[float] = None,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Causal LRKV attention over fresh sequences, returning (out, lse) with
+    lse[b, i, h] the natural log-sum-exp of row i's scaled logits (fp32)."""
+    dt = q.dtype
+    B, L, H, d_h, r = _train_shapes(q, k_s, v_s, z_k, z_v, b_k, b_v)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(B, L, H, dtype=torch.float32, device=q.device)
+    _shape(out, "out", (B, L, H, d_h))
+    _shape(lse, "lse", (B, L, H))
+    _check(library().lrkv_train_forward(_dtype_code(dt), B, H, d_h, r, L, _ptr(q, "q", dt), _ptr(k_s, "k_s", dt),
+                                        _ptr(v_s, "v_s", dt), _ptr(z_k, "z_k", dt), _ptr(z_v, "z_v", dt),
+                                        _ptr(b_k, "b_k", dt), _ptr(b_v, "b_v", dt),
+                                        0.0 if scale is None else float(scale), _ptr(out, "out", dt),
+                                        _ptr(lse, "lse", torch.float32), _stream()),
+           "lrkv_train_forward")
+    return out, lse
+
+
+def lrkv_train_backward_workspace_size(dtype: torch.dtype, batch: int, heads: int, head_dim: int, rank: int,
+                                       seq_len: int) -> int:
+    n = _sz(0)
+    _check(library().lrkv_train_backward_workspace_size(_dtype_code(dtype), batch, heads, head_dim, rank, seq_len,
+                                                        ctypes.byref(n)), "lrkv_train_backward_workspace_size")
+    return n.value
+
+
+def lrkv_train_backward(q, k_s, v_s, z_k, z_v, b_k, b_v, out, lse, d_out, scale: Optional[float] = None,
+                        workspace: Optional[torch.Tensor] = None, grads: Optional[dict] = None) -> dict:
+    """Gradients (fp32) of the loss with upstream gradient d_out through
+    lrkv_train_forward: dict with dq, dk_s, dv_s, dz_k, dz_v, db_k, db_v."""
+    dt = q.dtype
+    B, L, H, d_h, r = _train_shapes(q, k_s, v_s, z_k, z_v, b_k, b_v)
+    _shape(out, "out", (B, L, H, d_h))
+    _shape(lse, "lse", (B, L, H))
+    _shape(d_out, "d_out", (B, L, H, d_h))
+    dev, f32 = q.device, torch.float32
+    if grads is None:
+        grads = {"dq": torch.empty(B, L, H, d_h, dtype=f32, device=dev),
+                 "dk_s": torch.empty(B, L, d_h, dtype=f32, device=dev),
+                 "dv_s": torch.empty(B, L, d_h, dtype=f32, device=dev),
+                 "dz_k": torch.empty(B, L, H, r, dtype=f32, device=dev),
+                 "dz_v": torch.empty(B, L, H, r, dtype=f32, device=dev),
+                 "db_k": torch.empty(H, d_h, r, dtype=f32, device=dev),
+                 "db_v": torch.empty(H, d_h, r, dtype=f32, device=dev)}
+    need = lrkv_train_backward_workspace_size(dt, B, H, d_h, r, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    g = {k: _ptr(v, k, f32) for k, v in grads.items()}
+    _check(library().lrkv_train_backward(
+        _dtype_code(dt), B, H, d_h, r, L, _ptr(q, "q", dt), _ptr(k_s, "k_s", dt), _ptr(v_s, "v_s", dt),
+        _ptr(z_k, "z_k", dt), _ptr(z_v, "z_v", dt), _ptr(b_k, "b_k", dt), _ptr(b_v, "b_v", dt),
+        _ptr(out, "out", dt), _ptr(lse, "lse", f32), _ptr(d_out, "d_out", dt),
+        0.0 if scale is None else float(scale), g["dq"], g["dk_s"], g["dv_s"], g["dz_k"], g["dz_v"], g["db_k"],
+        g["db_v"], _ptr(workspace, "workspace"), workspace.numel(), _stream()), "lrkv_train_backward")
+    return grads
 
 
 def default_scale(head_dim: int) -> float:

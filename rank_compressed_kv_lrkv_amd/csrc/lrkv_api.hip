@@ -375,6 +375,91 @@ lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, 
   return lrkv::launch_prefill(p, s) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
 }
 
+namespace {
+
+// Shared validation of the training entry points' sizes.
+lrkv_status check_train_sizes(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
+                              int32_t seq_len) {
+  const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, 1);
+  if (st != LRKV_OK) return st;
+  if (!lrkv::train_supported(dtype, head_dim, rank, num_heads)) return LRKV_ERR_SHAPE;
+  if (seq_len < 0) return LRKV_ERR_SHAPE;
+  if (int64_t(batch) * seq_len >= (int64_t(1) << 31)) return LRKV_ERR_SHAPE;
+  if (int64_t(seq_len) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >= (int64_t(1) << 32))
+    return LRKV_ERR_SHAPE;
+  return LRKV_OK;
+}
+
+float resolve_scale(float scale, int32_t head_dim) {
+  return (scale > 0.f && std::isfinite(scale)) ? scale : 1.0f / std::sqrt(float(head_dim));
+}
+
+}  // namespace
+
+lrkv_status lrkv_train_forward(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
+                               int32_t seq_len, const void* q, const void* k_s, const void* v_s, const void* z_k,
+                               const void* z_v, const void* b_k, const void* b_v, float scale, void* out, float* lse,
+                               void* stream) {
+  const lrkv_status st = check_train_sizes(dtype, batch, num_heads, head_dim, rank, seq_len);
+  if (st != LRKV_OK) return st;
+  if (batch == 0 || seq_len == 0) return LRKV_OK;
+  if (!q || !k_s || !v_s || !out || !lse) return LRKV_ERR_NULL;
+  if (rank > 0 && (!z_k || !z_v || !b_k || !b_v)) return LRKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_s) || !aligned16(v_s) || !aligned16(out) || !aligned4(lse)) return LRKV_ERR_ALIGN;
+  if (rank > 0 && (!aligned16(z_k) || !aligned16(z_v) || !aligned16(b_k) || !aligned16(b_v))) return LRKV_ERR_ALIGN;
+  lrkv::PrefillArgs p;
+  p.batch = batch; p.heads = num_heads; p.head_dim = head_dim; p.rank = rank; p.seq_len = seq_len;
+  p.q = q; p.k_s = k_s; p.v_s = v_s; p.z_k = z_k; p.z_v = z_v; p.b_k = b_k; p.b_v = b_v;
+  p.scale_log2 = resolve_scale(scale, head_dim) * 1.4426950408889634f;
+  p.out = out;
+  p.kv_stride = seq_len; p.start = nullptr; p.max_start = 0;
+  p.lse = lse;
+  return lrkv::launch_prefill(p, static_cast<hipStream_t>(stream)) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+}
+
+lrkv_status lrkv_train_backward_workspace_size(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
+                                               int32_t rank, int32_t seq_len, size_t* bytes) {
+  if (!bytes) return LRKV_ERR_NULL;
+  const lrkv_status st = check_train_sizes(dtype, batch, num_heads, head_dim, rank, seq_len);
+  if (st != LRKV_OK) return st;
+  *bytes = lrkv::train_backward_ws_bytes(batch, num_heads, head_dim, rank, seq_len);
+  return LRKV_OK;
+}
+
+lrkv_status lrkv_train_backward(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
+                                int32_t seq_len, const void* q, const void* k_s, const void* v_s, const void* z_k,
+                                const void* z_v, const void* b_k, const void* b_v, const void* out, const float* lse,
+                                const void* d_out, float scale, float* dq, float* dk_s, float* dv_s, float* dz_k,
+                                float* dz_v, float* db_k, float* db_v, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  const lrkv_status st = check_train_sizes(dtype, batch, num_heads, head_dim, rank, seq_len);
+  if (st != LRKV_OK) return st;
+  const size_t need = lrkv::train_backward_ws_bytes(batch, num_heads, head_dim, rank, seq_len);
+  const bool empty = batch == 0 || seq_len == 0;
+  if (rank > 0 && (!db_k || !db_v)) return LRKV_ERR_NULL;
+  if (rank > 0 && (!aligned4(db_k) || !aligned4(db_v))) return LRKV_ERR_ALIGN;
+  if (!empty) {
+    if (!q || !k_s || !v_s || !out || !lse || !d_out || !dq || !dk_s || !dv_s) return LRKV_ERR_NULL;
+    if (rank > 0 && (!z_k || !z_v || !b_k || !b_v || !dz_k || !dz_v)) return LRKV_ERR_NULL;
+    if (!workspace) return LRKV_ERR_NULL;
+    if (workspace_bytes < need) return LRKV_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_s) || !aligned16(v_s) || !aligned16(out) || !aligned16(lse) ||
+        !aligned16(d_out) || !aligned16(dq) || !aligned4(dk_s) || !aligned4(dv_s) || !aligned16(workspace))
+      return LRKV_ERR_ALIGN;
+    if (rank > 0 && (!aligned16(z_k) || !aligned16(z_v) || !aligned16(b_k) || !aligned16(b_v) || !aligned4(dz_k) ||
+                     !aligned4(dz_v)))
+      return LRKV_ERR_ALIGN;
+  }
+  lrkv::TrainArgs a;
+  a.batch = batch; a.heads = num_heads; a.head_dim = head_dim; a.rank = rank; a.seq_len = seq_len;
+  a.q = q; a.k_s = k_s; a.v_s = v_s; a.z_k = z_k; a.z_v = z_v; a.b_k = b_k; a.b_v = b_v;
+  a.out = out; a.lse = lse; a.d_out = d_out;
+  a.scale = resolve_scale(scale, head_dim);
+  a.dq = dq; a.dk_s = dk_s; a.dv_s = dv_s; a.dz_k = dz_k; a.dz_v = dz_v; a.db_k = db_k; a.db_v = db_v;
+  a.ws = workspace;
+  return lrkv::launch_train_backward(a, static_cast<hipStream_t>(stream)) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+}
+
 lrkv_status lrkv_pack_projection(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank,
                                  int32_t d_model, const void* wk_shared, const void* wv_shared,
                                  const void* u_k, const void* u_v, void* w_packed, void* stream) {

@@ -85,9 +85,25 @@ struct PrefillArgs {
   int kv_stride;           // tokens per sequence in k_s/v_s/z_k/z_v (seq_len, or the cache capacity)
   const int32_t* start;    // device [batch] history lengths, or NULL (no history)
   int max_start;           // start is clamped to [0, max_start]
+  float* lse = nullptr;    // optional [batch][seq_len][heads] natural log-sum-exp of each row's logits
 };
 bool prefill_supported(int dtype, int head_dim, int rank, int heads);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+struct TrainArgs {
+  int batch, heads, head_dim, rank, seq_len;
+  const void* q; const void* k_s; const void* v_s; const void* z_k; const void* z_v;   // bf16, fresh tokens
+  const void* b_k; const void* b_v;
+  const void* out; const float* lse; const void* d_out;   // forward output (bf16), its lse, upstream gradient (bf16)
+  float scale;
+  float* dq; float* dk_s; float* dv_s; float* dz_k; float* dz_v; float* db_k; float* db_v;   // fp32 gradients
+  void* ws;                // train_backward_ws_bytes bytes
+};
+// Shapes the training backward takes: bf16, head_dim 64 or 128, rank 0/8/16/32,
+// heads a multiple of 4.
+bool train_supported(int dtype, int head_dim, int rank, int heads);
+size_t train_backward_ws_bytes(int batch, int heads, int head_dim, int rank, int seq_len);
+hipError_t launch_train_backward(const TrainArgs& a, hipStream_t stream);
 
 struct ProjectArgs {
   int dtype, batch, heads, head_dim, rank, d_model, n_new;

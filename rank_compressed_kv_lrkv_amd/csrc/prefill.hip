@@ -86,6 +86,9 @@ struct PrefillKernelParams {
   const int32_t* start;
   int max_start;
   float scale_log2;
+  // Optional: the natural log-sum-exp of each query row's scaled logits,
+  // [batch][seq_len][heads] fp32 (NULL: not written).
+  float* lse;
 };
 
 // This lane's source offsets (bytes from the first row of a tile) for the
@@ -475,6 +478,8 @@ void prefill_kernel(PrefillKernelParams p) {
   }
   if (q0 + n >= L) return;
   const float inv = 1.f / lsum;
+  // log-sum-exp of this row: ln(2^m * lsum), m the running max in log2 units
+  if (p.lse && half == 0) p.lse[(size_t(b) * L + q0 + n) * H + h] = (m + __builtin_amdgcn_logf(lsum)) * 0.6931471805599453f;
   uint16_t* orow = p.out + ((size_t(b) * L + q0 + n) * H + h) * DH;
 #pragma unroll
   for (int f = 0; f < DH / 32; ++f)
@@ -508,6 +513,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   kp.kv_stride = a.kv_stride;
   kp.start = a.start;
   kp.max_start = a.max_start;
+  kp.lse = a.lse;
   const long long blocks = (long long)kp.n_qblocks * kp.n_hgroups * a.batch;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid{static_cast<unsigned>(blocks)};

@@ -30,7 +30,7 @@ import numpy as np
 __all__ = [
     "DecodeWorkload", "PrefillWorkload", "DECODE_WORKLOADS", "PREFILL_WORKLOADS",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "decode_inputs", "prefill_inputs",
-    "append_inputs", "as_f64", "projection_inputs", "mha_inputs",
+    "append_inputs", "as_f64", "projection_inputs", "mha_inputs", "train_inputs",
 ]
 
 
@@ -157,6 +157,19 @@ def prefill_inputs(wl: PrefillWorkload, *, batch: Optional[int] = None, seq_len:
     return dict(q=_store(q, dt), k_s=_store(k_s, dt), v_s=_store(v_s, dt), z_k=_store(z_k, dt),
                 z_v=_store(z_v, dt), b_k=_store(b_k, dt), b_v=_store(b_v, dt),
                 dtype=dt, heads=H, head_dim=d_h, rank=r, seq_len=L)
+
+
+def train_inputs(wl: PrefillWorkload, *, batch: Optional[int] = None, seq_len: Optional[int] = None,
+                 seed: Optional[int] = None) -> dict:
+    """A prefill workload plus the upstream gradient of its output for a
+    training step: d_out [B, L, H, d_h] ~ N(0, 1), drawn from a stream of its
+    own (seed, 1) so that the forward inputs equal ``prefill_inputs``'s."""
+    d = prefill_inputs(wl, batch=batch, seq_len=seq_len, seed=seed)
+    B, L = d["q"].shape[0], d["q"].shape[1]
+    rng = np.random.default_rng([wl.seed if seed is None else seed, 1])
+    d_out = rng.standard_normal((B, L, wl.heads, wl.head_dim), dtype=np.float32)
+    d["d_out"] = _store(d_out, wl.dtype)
+    return d
 
 
 def append_inputs(B: int, n: int, H: int, d_h: int, r: int, dtype: str, seed: int) -> dict:

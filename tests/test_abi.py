@@ -337,3 +337,59 @@ def test_decode_ex_validation():
         st = lib.lrkv_decode_ex(1, phases, BF16, 2, 32, 128, 16, 256, p, p, p, p, p, 256, p, p, p,
                                 ctypes.c_float(0.0), 0, p, p, 1 << 30, None)
         assert st == SHAPE, (phases, st)
+
+
+def train_bwd_call(**over):
+    a = dict(dtype=BF16, B=1, H=8, d_h=64, r=8, L=64, q=FAKE, ks=FAKE, vs=FAKE, zk=FAKE, zv=FAKE, bk=FAKE, bv=FAKE,
+             out=FAKE, lse=FAKE, dout=FAKE, scale=0.0, dq=FAKE, dks=FAKE, dvs=FAKE, dzk=FAKE, dzv=FAKE, dbk=FAKE,
+             dbv=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return L.library().lrkv_train_backward(
+        a["dtype"], a["B"], a["H"], a["d_h"], a["r"], a["L"], a["q"], a["ks"], a["vs"], a["zk"], a["zv"], a["bk"],
+        a["bv"], a["out"], a["lse"], a["dout"], a["scale"], a["dq"], a["dks"], a["dvs"], a["dzk"], a["dzv"], a["dbk"],
+        a["dbv"], a["ws"], a["wsb"], None)
+
+
+def test_train_workspace_size():
+    lib = L.library()
+    n = ctypes.c_size_t(0)
+    assert lib.lrkv_train_backward_workspace_size(BF16, 4, 32, 128, 16, 4096, ctypes.byref(n)) == OK
+    al = lambda x: (x + 255) // 256 * 256
+    B, H, D, R, Lq = 4, 32, 128, 16, 4096
+    nb, ng = (Lq + 31) // 32, (H + 3) // 4
+    want = 2 * al(B * Lq * H * R * 2) + 2 * al(B * H * nb * 32 * 4) + 2 * al(ng * B * Lq * D * 4) + \
+        2 * al(B * nb * H * D * R * 4)
+    assert n.value == want
+    assert lib.lrkv_train_backward_workspace_size(BF16, 4, 30, 128, 16, 4096, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_train_backward_workspace_size(F32, 4, 32, 128, 16, 4096, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_train_backward_workspace_size(BF16, 4, 32, 96, 16, 4096, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_train_backward_workspace_size(BF16, 4, 32, 128, 24, 4096, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_train_backward_workspace_size(BF16, 4, 32, 128, 16, -1, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_train_backward_workspace_size(BF16, 4, 32, 128, 16, 4096, None) == NULL
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=F32), SHAPE), (dict(dtype=7), DTYPE), (dict(H=6), SHAPE), (dict(d_h=32), SHAPE),
+    (dict(r=4), SHAPE), (dict(L=-1), SHAPE), (dict(B=1 << 20, L=1 << 12), SHAPE),
+    (dict(q=None), NULL), (dict(lse=None), NULL), (dict(dout=None), NULL), (dict(dbk=None), NULL),
+    (dict(dzv=None), NULL), (dict(ws=None), NULL), (dict(wsb=1024), WS),
+    (dict(q=MIS), ALIGN), (dict(dq=FAKE + 4), ALIGN), (dict(dks=FAKE + 2), ALIGN), (dict(ws=MIS), ALIGN),
+])
+def test_train_backward_rejects_before_launch(kw, want):
+    assert train_bwd_call(**kw) == want
+
+
+@no_gpu
+def test_train_forward_rejects_before_launch():
+    lib = L.library()
+    call = lambda **o: lib.lrkv_train_forward(
+        o.get("dtype", BF16), 1, o.get("H", 8), 64, 8, o.get("L", 64), o.get("q", FAKE), FAKE, FAKE, FAKE, FAKE,
+        FAKE, FAKE, ctypes.c_float(0.0), FAKE, o.get("lse", FAKE), None)
+    assert call(dtype=F32) == SHAPE
+    assert call(H=6) == SHAPE
+    assert call(L=-1) == SHAPE
+    assert call(lse=None) == NULL
+    assert call(q=MIS) == ALIGN
+    assert call(lse=FAKE + 2) == ALIGN
+    assert call(L=0, q=None, lse=None) == OK
