@@ -50,12 +50,13 @@ def parse():
     ap.add_argument("--settle-s", type=float, default=0.5,
                     help="before the warmup steps, repeat the step (untimed) for this many seconds: "
                          "the GPU takes tens of ms of sustained work to reach its steady clock")
-    ap.add_argument("--mode", choices=("decode", "prefill", "chunk", "rank-sweep", "project", "vendor"),
+    ap.add_argument("--mode", choices=("decode", "prefill", "chunk", "rank-sweep", "project", "vendor", "train"),
                     default="decode",
                     help="decode (the headline line); the causal-prefill MFMA path; a prefill chunk over a "
                          "4096-token history; decode at ranks 0/8/16/32 and plain MHA on the headline shape; "
-                         "the fused projection + append of 4 x 4096 tokens from d = 4096; or the vendor "
-                         "libraries (hipBLASLt GEMM, PyTorch flash attention) timed beside the two MFMA kernels")
+                         "the fused projection + append of 4 x 4096 tokens from d = 4096; the vendor "
+                         "libraries (hipBLASLt GEMM, PyTorch flash attention) timed beside the two MFMA kernels; or "
+                         "one training step (forward with log-sum-exp, backward) of the prefill workload")
     ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
     ap.add_argument("--engine", type=int, default=0, choices=(0, 1, 2),
@@ -193,6 +194,8 @@ def main():
         return bench_project(args)
     if args.mode == "vendor":
         return bench_vendor(args)
+    if args.mode == "train":
+        return bench_train(args)
     wl = DECODE_WORKLOADS[args.workload or "mid_bf16_T8k"]
     d = decode_inputs(wl)
     m = measure_decode(args, wl, d, engine=args.engine)
@@ -335,6 +338,9 @@ def other_configs(args):
     res["prefill_bf16_L4k"] = prefill_record(args)
     torch.cuda.empty_cache()
     progress("prefill_bf16_L4k done")
+    res["train_bf16_L4k"] = train_record(args)
+    torch.cuda.empty_cache()
+    progress("train_bf16_L4k done")
     # Tiny fp32 decode: latency-bound (19 KB of cache).
     wl = DECODE_WORKLOADS["tiny_f32_T64"]
     d = decode_inputs(wl)
@@ -516,6 +522,105 @@ def prefill_record(args):
     if not args.no_cpu_baseline:
         rec.update(oracle_prefill_check(d, out, as_f64))
     return rec
+
+
+def train_record(args):
+    """One training step of LRKV attention on the 4 x 4096-token prefill
+    workload (H=32, d_h=128, r=16): lrkv_train_forward (the causal prefill
+    kernel, also writing each row's log-sum-exp) and lrkv_train_backward
+    (fp32 gradients of q, K_s, V_s, Z^K, Z^V, B^K, B^V), timed apart.  Their
+    TFLOP/s are priced against the bf16 MFMA peak with the algorithmic flops
+    of the absorbed products: 2 per causal pair and inner dimension (d_h + r)
+    for each of S and P.V in the forward, and of S, dP, dV, dK, dQ in the
+    backward.  Sampled (sequence, head) pairs of dq, dz_k, dz_v are checked
+    against the float64 gradient oracle, whose rate is reported beside."""
+    import torch
+    import rank_compressed_kv_lrkv_amd as L
+    from rank_compressed_kv_lrkv_amd.workloads import PREFILL_WORKLOADS, as_f64, train_inputs
+
+    wl = PREFILL_WORKLOADS["prefill_bf16_L4k"]
+    d = train_inputs(wl)
+    names = ("q", "k_s", "v_s", "z_k", "z_v", "b_k", "b_v")
+    t = {k: _dev(d[k], "bf16") for k in names + ("d_out",)}
+    B, Lq, H, d_h, r = wl.batch, wl.seq_len, wl.heads, wl.head_dim, wl.rank
+    ins = [t[k] for k in names]
+    out, lse = L.lrkv_train_forward(*ins)
+    ws = torch.empty(L.lrkv_train_backward_workspace_size(torch.bfloat16, B, H, d_h, r, Lq), dtype=torch.uint8,
+                     device="cuda")
+    grads = L.lrkv_train_backward(*ins, out, lse, t["d_out"], workspace=ws)
+
+    def fwd():
+        L.lrkv_train_forward(*ins, out=out, lse=lse)
+
+    def bwd():
+        L.lrkv_train_backward(*ins, out, lse, t["d_out"], workspace=ws, grads=grads)
+
+    def step():
+        fwd()
+        bwd()
+
+    settled = settle(step, args.settle_s)
+    for _ in range(max(1, args.warmup // 4)):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    steps = max(1, min(args.steps, 5))
+    step_ms, step_runs = timed_median(stream, steps, step, args.trials)
+    fwd_ms, _ = timed_median(stream, steps, fwd, args.trials)
+    bwd_ms, _ = timed_median(stream, steps, bwd, args.trials)
+    fwd(); bwd()
+    torch.cuda.synchronize()
+    pairs = B * H * Lq * (Lq + 1) // 2
+    fwd_flops = pairs * 4 * (d_h + r)
+    bwd_flops = pairs * 10 * (d_h + r)
+    tf = lambda fl, ms: fl / (ms * 1e-3) / 1e12
+    rec = {
+        "kind": "training step (forward + backward), throughput",
+        "value": B * Lq / (step_ms * 1e-3), "unit": "training tokens/s (forward + backward)",
+        "step_ms": step_ms, "step_ms_trials": step_runs, "settle": {"seconds": args.settle_s, "steps": settled},
+        "config": {"workload": wl.name, "batch": B, "seq_len": Lq, "heads": H, "head_dim": d_h, "rank": r},
+        "forward_ms": fwd_ms, "backward_ms": bwd_ms,
+        "forward_tflops": tf(fwd_flops, fwd_ms), "backward_tflops": tf(bwd_flops, bwd_ms),
+        "roofline": {"bound": "mfma", "achieved": tf(bwd_flops, bwd_ms), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf(bwd_flops, bwd_ms) / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "lrkv_train_backward (all its kernels)", "algorithmic_flops_per_launch": bwd_flops},
+    }
+    if not args.no_cpu_baseline:
+        sys.path.insert(0, ROOT)
+        import oracle as O
+        f = lambda k: as_f64(d[k], "bf16")
+        got = {k: v.cpu().numpy().astype(np.float64) for k, v in grads.items()}
+        err, secs, npairs = 0.0, 0.0, 0
+        for b, h in ((0, 0), (B - 1, H - 1)):
+            sl = lambda k: f(k)[b:b + 1][:, :, [h]]
+            t0 = time.perf_counter()
+            want = O.prefill_backward(sl("q"), f("k_s")[b:b + 1], f("v_s")[b:b + 1], sl("z_k"), sl("z_v"),
+                                      f("b_k")[[h]], f("b_v")[[h]], sl("d_out"))
+            secs += time.perf_counter() - t0
+            npairs += Lq * (Lq + 1) // 2
+            for k in ("dq", "dz_k", "dz_v"):
+                g = got[k][b:b + 1][:, :, [h]]
+                err = max(err, float(np.max(np.abs(g - want[k])) / np.max(np.abs(want[k]))))
+        rec["gpu_vs_oracle_max_err_over_inf_norm"] = err
+        rec["checked"] = "dq, dz_k, dz_v of (sequence, head) = (0, 0) and (3, 31), every query and key"
+        rec["oracle"] = {"value": npairs / secs, "unit": "causal pairs/s (forward recompute + backward)",
+                         "cores": thread_count(), "kind": "oracle",
+                         "sample": f"float64 numpy backward of 2 (sequence, head) pairs at 4096 tokens, {secs:.1f} s"}
+    return rec
+
+
+def bench_train(args):
+    """--mode train: the training step as the headline line."""
+    r = train_record(args)
+    rec = {
+        "metric": "LRKV attention training step: tokens/s, forward and backward TFLOP/s",
+        "value": r.pop("value"), "unit": r.pop("unit"), "n_gpus": 1, "steps": max(1, min(args.steps, 5)),
+        "warmup": args.warmup, "trials": args.trials, "ms_per_step": r.pop("step_ms"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) queries, bases, latents and upstream gradient; B ~ N(0, 1/r))",
+        **r,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def oracle_prefill_check(d, out_dev, as_f64, budget_s=8.0):
