@@ -38,13 +38,16 @@
  *       residual factors   b_k, b_v            [num_heads][head_dim][rank]
  *     so the cache holds exactly 2(head_dim + num_heads*rank) elements per
  *     token slot.
- *   - Every pointer must be 16-byte aligned, and head_dim and rank must make
- *     rows whole 16-byte units: head_dim*elem_bytes % 16 == 0 and
- *     rank*elem_bytes % 16 == 0 (rank == 0 is allowed and is MQA).
- *   - Supported envelope: head_dim in {16, 32, 64, 128}; rank in
- *     {0, 4, 8, 16, 32, 64} (bf16 needs rank % 8 == 0); 1 <= num_heads <= 64.
- *     Anything else returns
- *     LRKV_ERR_SHAPE before any launch.
+ *   - Every pointer must be 16-byte aligned, and shared rows must be whole
+ *     16-byte units: head_dim*elem_bytes % 16 == 0.  The latent run of a
+ *     token (num_heads*rank elements) may have any length; rank == 0 is
+ *     allowed and is MQA.
+ *   - Decode envelope: head_dim in {16, 32, 64, 128}, and either a tuned
+ *     scan's shape (rank in {0, 4, 8, 16, 32, 64}, bf16 needing rank % 8 ==
+ *     0, 1 <= num_heads <= 64) or the any-rank scan's (rank 0..128, 1 <=
+ *     num_heads <= 1024).  Prefill, chunk and training calls state their
+ *     own envelopes.  Anything else returns LRKV_ERR_SHAPE before any
+ *     launch.
  *   - Validation happens on the host before anything is enqueued; a call
  *     that returns an error has launched nothing.  A failed launch returns
  *     LRKV_ERR_DEVICE (from hipGetLastError).  No exception or abort crosses
@@ -114,9 +117,12 @@ lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num
 /* Name of the kernel that runs the split-K scan of lrkv_decode for these
  * sizes: "decode_mfma_kernel" (bf16, head_dim 64 or 128, rank 0/8/16/32,
  * num_heads a multiple of 32 up to 64: the shared term runs on bf16 MFMA
- * across 32 heads) or "decode_split_kernel" (every other supported shape:
- * vector-ALU dot products).  Returns NULL for a shape outside the supported
- * envelope.  Host-only: launches nothing; the string is static. */
+ * across 32 heads), "decode_split_kernel" (the other shapes of the tuned
+ * envelope: vector-ALU dot products) or "decode_generic_kernel" (any other
+ * rank up to 128 and up to 1024 heads, at the pages' ranks such as 46, 54,
+ * 55: vector-ALU, latents read element by element).  Returns NULL for a
+ * shape outside the supported envelope.  Host-only: launches nothing; the
+ * string is static. */
 const char* lrkv_decode_scan_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank);
 
 /* One decode step: for every sequence b and head h,
@@ -201,10 +207,12 @@ lrkv_status lrkv_decode_noalloc(int32_t dtype, int32_t batch, int32_t num_heads,
 /* lrkv_decode with an explicit choice of scan kernel, and of the phases to
  * run (for comparing the two scans on one shape, and timing them apart).
  *   engine  0: the default for the shape (as lrkv_decode_scan_kernel names);
- *           1: the vector-ALU scan, decode_split_kernel (every supported
- *              shape), with its fixed splits;
+ *           1: the vector-ALU scan, decode_split_kernel (the shapes of the
+ *              tuned envelope), with its fixed splits;
  *           2: the MFMA scan, decode_mfma_kernel (only its shapes; others
- *              return LRKV_ERR_SHAPE).
+ *              return LRKV_ERR_SHAPE);
+ *           3: the any-rank scan, decode_generic_kernel, with its merge
+ *              (every shape of the decode envelope).
  *   phases  1: the split-K scan (as lrkv_decode_partial), 2: the merge (as
  *           lrkv_decode_combine), 3: both (as lrkv_decode).
  * The remaining arguments are lrkv_decode's.  The workspace must be at least

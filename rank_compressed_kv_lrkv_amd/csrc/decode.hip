@@ -629,6 +629,7 @@ bool decode_supported(int dtype, int head_dim, int rank, int heads) {
 }
 
 hipError_t launch_decode(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
+  if (pl.generic) return launch_decode_generic(pl, a, phase, st);
   return pl.dtype == 1 ? dispatch_dim<BF16>(pl, a, phase, st) : dispatch_dim<F32>(pl, a, phase, st);
 }
 

@@ -39,32 +39,42 @@ lrkv_status check_sizes(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
   if (dtype != LRKV_F32 && dtype != LRKV_BF16) return LRKV_ERR_DTYPE;
   if (batch < 0 || heads < 1 || head_dim < 1 || rank < 0 || capacity < 1) return LRKV_ERR_SHAPE;
   if (capacity > INT32_MAX) return LRKV_ERR_SHAPE;
+  // shared rows are copied and staged in 16-byte chunks; latents may have any
+  // rank (each kernel states the ranks it takes)
   const int es = elem_bytes(dtype);
-  if ((int64_t(head_dim) * es) % 16 != 0 || (int64_t(rank) * es) % 16 != 0) return LRKV_ERR_SHAPE;
+  if ((int64_t(head_dim) * es) % 16 != 0) return LRKV_ERR_SHAPE;
+  if (rank > INT32_MAX / std::max(heads, 1) / 4) return LRKV_ERR_SHAPE;
   return LRKV_OK;
 }
 
 // engine: 0 = the default for the shape, 1 = the vector-ALU scan
-// (decode_split_kernel), 2 = the MFMA scan (decode_mfma_kernel).
+// (decode_split_kernel), 2 = the MFMA scan (decode_mfma_kernel), 3 = the
+// any-rank scan (decode_generic_kernel).  The default takes the MFMA scan
+// where it applies, else the vector-ALU scan, else the any-rank scan.
 lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t head_dim, int32_t rank,
                         int64_t capacity, int64_t max_len, int32_t split_tokens, DecodePlan* pl, int32_t engine = 0) {
   lrkv_status st = check_sizes(dtype, batch, heads, head_dim, rank, capacity);
   if (st != LRKV_OK) return st;
-  if (engine < 0 || engine > 2) return LRKV_ERR_SHAPE;
-  if (!lrkv::decode_supported(dtype, head_dim, rank, heads)) return LRKV_ERR_SHAPE;
+  if (engine < 0 || engine > 3) return LRKV_ERR_SHAPE;
+  const bool tuned = lrkv::decode_supported(dtype, head_dim, rank, heads);
+  const bool any = lrkv::decode_generic_supported(dtype, head_dim, rank, heads);
+  if (engine == 1 && !tuned) return LRKV_ERR_SHAPE;
   if (engine == 2 && !lrkv::decode_mfma_supported(dtype, head_dim, rank, heads)) return LRKV_ERR_SHAPE;
+  if (engine == 3 && !any) return LRKV_ERR_SHAPE;
+  if (engine == 0 && !tuned && !any) return LRKV_ERR_SHAPE;
   if (max_len < 0 || split_tokens < 0) return LRKV_ERR_SHAPE;
   if (max_len > capacity) return LRKV_ERR_CAPACITY;
   if (split_tokens != 0 && split_tokens % lrkv::kDecodeTile != 0) return LRKV_ERR_SHAPE;
 
   pl->batch = batch; pl->heads = heads; pl->head_dim = head_dim; pl->rank = rank; pl->dtype = dtype;
   pl->capacity = capacity; pl->max_len = int(max_len);
-  pl->mfma = engine != 1 && lrkv::decode_mfma_supported(dtype, head_dim, rank, heads);
+  pl->generic = engine == 3 || (engine == 0 && !tuned);
+  pl->mfma = !pl->generic && engine != 1 && lrkv::decode_mfma_supported(dtype, head_dim, rank, heads);
   pl->group = (rank == 4 || heads > 32) ? 4 : 8;
   int hp = 1;
   while (hp < heads) hp <<= 1;
   pl->heads_pow2 = hp;
-  pl->slots = pl->mfma ? lrkv::kMfmaSlots : lrkv::kDecodeThreads / (hp * pl->group);
+  pl->slots = (pl->mfma || pl->generic) ? 1 : lrkv::kDecodeThreads / (hp * pl->group);
   if (pl->slots < 1) return LRKV_ERR_SHAPE;
 
   const int tile = lrkv::kDecodeTile;
@@ -73,9 +83,11 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
     // Workgroups over the whole batch: about two per compute unit for the
     // vector-ALU scan; for the MFMA scan (one resident workgroup per compute
     // unit) about one, in whole 32-token tiles per wave.
-    const int64_t groups = pl->mfma ? heads / 32 : 1;
+    // The any-rank scan runs one workgroup per 32 heads with two or three
+    // resident per compute unit: about eight per compute unit.
+    const int64_t groups = pl->mfma ? heads / 32 : pl->generic ? (heads + 31) / 32 : 1;
     const int64_t total = int64_t(batch) * max_len * groups;
-    const int64_t target = (pl->mfma ? 1 : 2) * int64_t(device_cu_count());
+    const int64_t target = (pl->mfma ? 1 : pl->generic ? 8 : 2) * int64_t(device_cu_count());
     const int64_t unit = pl->mfma ? 2 * tile : tile;
     int64_t s = (total + target - 1) / (target > 0 ? target : 1);
     s = (s + unit - 1) / unit * unit;
@@ -169,7 +181,8 @@ int64_t lrkv_cache_elems_per_token(int32_t num_heads, int32_t head_dim, int32_t 
 
 const char* lrkv_decode_scan_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank) {
   if (check_sizes(dtype, 1, num_heads, head_dim, rank, 1) != LRKV_OK) return nullptr;
-  if (!lrkv::decode_supported(dtype, head_dim, rank, num_heads)) return nullptr;
+  if (!lrkv::decode_supported(dtype, head_dim, rank, num_heads))
+    return lrkv::decode_generic_supported(dtype, head_dim, rank, num_heads) ? "decode_generic_kernel" : nullptr;
   return lrkv::decode_mfma_supported(dtype, head_dim, rank, num_heads) ? "decode_mfma_kernel" : "decode_split_kernel";
 }
 

@@ -38,6 +38,7 @@ struct DecodePlan {
   int slots;          // independent token streams per workgroup
   int partials;       // n_splits * slots partial states per (sequence, head)
   bool mfma;          // scan on the MFMA kernel (one partial state per workgroup: slots = 1)
+  bool generic;       // scan and merge of the any-rank kernels (one partial state per split: slots = 1)
   bool balanced;      // length-balanced items computed on the device (MFMA scan, default split):
                       // n_splits = partials = max(bal_cap, batch) items, state index item * heads + h
   int bal_cap;        // items the partition aims for (resident scan workgroups)
@@ -61,6 +62,13 @@ bool decode_supported(int dtype, int head_dim, int rank, int heads);
 // heads a multiple of 32 up to 64.
 bool decode_mfma_supported(int dtype, int head_dim, int rank, int heads);
 constexpr int kMfmaSlots = 1;        // partial states per MFMA-scan workgroup
+// The any-rank scan (decode_generic.hip): bf16 or fp32, head_dim 16/32/64/128,
+// any rank up to kGenericMaxRank, up to kGenericMaxHeads heads.
+constexpr int kGenericMaxRank = 128;
+constexpr int kGenericMaxHeads = 1024;
+constexpr int kGenericMaxDims = 128 + kGenericMaxRank;   // head_dim + rank
+bool decode_generic_supported(int dtype, int head_dim, int rank, int heads);
+hipError_t launch_decode_generic(const DecodePlan& plan, const DecodeArgs& args, int phase, hipStream_t stream);
 hipError_t launch_decode_mfma_scan(const DecodePlan& plan, const DecodeArgs& args, hipStream_t stream);
 // phase: 1 = split-K scan only, 2 = combine only, 3 = both.
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int phase, hipStream_t stream);

@@ -36,13 +36,13 @@ def device_cache(d):
     return L.LrkvCache(to_dev(d["k_s"], dt), to_dev(d["v_s"], dt), to_dev(d["z_k"], dt), to_dev(d["z_v"], dt))
 
 
-def run_decode(d, split_tokens=0, max_len=None, cache=None):
+def run_decode(d, split_tokens=0, max_len=None, cache=None, engine=0):
     dt = d["dtype"]
     cache = cache if cache is not None else device_cache(d)
     lens = torch.from_numpy(np.asarray(d["seq_lens"], np.int32)).cuda()
     ml = int(d["capacity"] if max_len is None else max_len)
     out = L.lrkv_decode(cache, lens, ml, to_dev(d["q"], dt), to_dev(d["b_k"], dt), to_dev(d["b_v"], dt),
-                        split_tokens=split_tokens)
+                        split_tokens=split_tokens, engine=engine)
     torch.cuda.synchronize()
     return from_dev(out)
 

@@ -58,6 +58,13 @@ def test_decode_scan_kernel_names():
     assert lib.lrkv_decode_scan_kernel(BF16, 32, 32, 16) == b"decode_split_kernel"   # head_dim 32
     assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 64) == b"decode_split_kernel"  # rank 64
     assert lib.lrkv_decode_scan_kernel(F32, 32, 128, 16) == b"decode_split_kernel"   # fp32 storage
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 54) == b"decode_generic_kernel"  # the pages' ranks
+    assert lib.lrkv_decode_scan_kernel(BF16, 18, 128, 55) == b"decode_generic_kernel"
+    assert lib.lrkv_decode_scan_kernel(F32, 6, 128, 128) == b"decode_generic_kernel"
+    assert lib.lrkv_decode_scan_kernel(BF16, 8, 64, 4) == b"decode_generic_kernel"    # bf16 rank 4
+    assert lib.lrkv_decode_scan_kernel(BF16, 96, 64, 8) == b"decode_generic_kernel"   # more than 64 heads
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 129) is None
+    assert lib.lrkv_decode_scan_kernel(BF16, 1025, 128, 8) is None
     assert lib.lrkv_decode_scan_kernel(BF16, 32, 24, 16) is None                     # unsupported head_dim
     assert lib.lrkv_decode_scan_kernel(7, 32, 128, 16) is None
     assert L.lrkv_decode_scan_kernel(torch.bfloat16, 32, 128, 16) == "decode_mfma_kernel"
@@ -67,6 +74,15 @@ def ws_size(dtype=BF16, B=2, H=8, d_h=64, r=8, cap=256, max_len=256, split=0):
     n = ctypes.c_size_t(0)
     st = L.library().lrkv_decode_workspace_size(dtype, B, H, d_h, r, cap, max_len, split, ctypes.byref(n))
     return st, n.value
+
+
+def test_workspace_size_formula_any_rank():
+    # the any-rank scan keeps one partial state per (split, head)
+    st, n = ws_size(BF16, B=2, H=18, d_h=128, r=55, cap=1024, max_len=1000, split=128)
+    assert st == OK
+    states = 2 * -(-1000 // 128) * 18
+    pad = lambda x: -(-x // 256) * 256
+    assert n == pad(states * 2 * 4) + pad(states * (128 + 55) * 4)
 
 
 def test_workspace_size_formula():
@@ -84,9 +100,8 @@ def test_workspace_size_formula():
     (dict(dtype=2), DTYPE),
     (dict(H=0), SHAPE), (dict(d_h=0), SHAPE), (dict(r=-1), SHAPE), (dict(cap=0), SHAPE),
     (dict(d_h=24), SHAPE),                       # unsupported head width
-    (dict(r=4), SHAPE),                          # bf16 latent rows must be whole 16-byte units
-    (dict(r=12, dtype=F32), SHAPE),              # rank outside the compiled envelope
-    (dict(H=65), SHAPE),
+    (dict(r=129), SHAPE),                        # rank beyond the any-rank scan's 128
+    (dict(H=1025), SHAPE),                       # heads beyond the any-rank scan's 1024
     (dict(max_len=257), CAP), (dict(max_len=-1), SHAPE),
     (dict(split=100), SHAPE),                    # not a multiple of 64
 ])
@@ -325,8 +340,13 @@ def test_decode_ex_validation():
     # engine 2 (MFMA scan) only on its shapes; engine 1 everywhere the vector scan runs
     assert lib.lrkv_decode_workspace_size_ex(2, BF16, 2, 8, 64, 8, 256, 256, 0, ctypes.byref(n)) == SHAPE
     assert lib.lrkv_decode_workspace_size_ex(1, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == OK
-    assert lib.lrkv_decode_workspace_size_ex(3, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_decode_workspace_size_ex(4, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == SHAPE
     assert lib.lrkv_decode_workspace_size_ex(-1, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    # engine 3 (any-rank scan) takes every shape of the envelope; the tuned scans not the pages' odd ranks
+    assert lib.lrkv_decode_workspace_size_ex(3, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == OK
+    assert lib.lrkv_decode_workspace_size_ex(3, F32, 2, 18, 128, 55, 256, 256, 0, ctypes.byref(n)) == OK
+    assert lib.lrkv_decode_workspace_size_ex(1, BF16, 2, 18, 128, 55, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_decode_workspace_size_ex(2, BF16, 2, 32, 128, 54, 256, 256, 0, ctypes.byref(n)) == SHAPE
     # the default engine matches lrkv_decode_workspace_size
     m = ctypes.c_size_t(0)
     assert lib.lrkv_decode_workspace_size_ex(0, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == OK

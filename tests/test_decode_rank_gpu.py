@@ -1,0 +1,112 @@
+"""Decode at the ranks the LRKV slides sweep ("The rank directly sets the
+theoretical cache budget", Table 7; "Backup: the complete rank sweep
+clarifies the trade-off", Table 8), where a token's latent run of H*r
+elements is not a whole number of 16-byte chunks: the any-rank scan
+(decode_generic_kernel) through the C ABI against the float64 oracle, and
+the cache append at those ranks, bit-exact.
+
+Bar: max |gpu - oracle| <= 1e-5 * ||oracle||_inf (fp32 storage) or
+2e-2 * ||oracle||_inf (bf16 storage), as every decode test.
+"""
+import numpy as np
+import pytest
+import torch
+
+import rank_compressed_kv_lrkv_amd as L
+from rank_compressed_kv_lrkv_amd.workloads import DECODE_WORKLOADS, DecodeWorkload, decode_inputs
+from tests.gpu_util import TOL, TORCH_DT, err_ratio, oracle_decode, run_decode, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+PAGE_SHAPES = [(32, 54, 128), (18, 55, 128), (6, 128, 128)]   # (heads, rank, head_dim)
+
+
+def check(d, got, name, batches=None, heads=None):
+    want = oracle_decode(d, batches, heads)
+    sub = got
+    if batches is not None or heads is not None:
+        sub = got[np.ix_(list(batches if batches is not None else range(got.shape[0])),
+                         list(heads if heads is not None else range(got.shape[1])))]
+    e = err_ratio(sub, want)
+    say(f"  {name}: err/||out||inf = {e:.3e} (tol {TOL[d['dtype']]:.0e})")
+    assert np.all(np.isfinite(sub)) and e <= TOL[d["dtype"]], (name, e)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("H,r,d_h", PAGE_SHAPES, ids=[f"H{h}_r{r}_dh{d}" for h, r, d in PAGE_SHAPES])
+def test_page_ranks_full(H, r, d_h, dt):
+    name = f"H{H}_r{r}_dh{d_h}_{dt}"
+    assert L.lrkv_decode_scan_kernel(TORCH_DT[dt], H, d_h, r) == "decode_generic_kernel"
+    lens = np.array([700, 333, 1, 65], np.int32)           # several tiles, a ragged tail, one token
+    say(f"case {name} lens={lens.tolist()}")
+    d = decode_inputs(DecodeWorkload(name, 4, H, d_h, r, 700, dt, 4711 + H + r), lens=lens)
+    check(d, run_decode(d), name)
+    check(d, run_decode(d, split_tokens=128), name + " split 128")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_page_rank_long_context_sampled(dt):
+    """The 8K-context shape of the bandwidth workload (d_h = 128, 32 heads) at
+    the pages' rank 54, with the library's default split, sampled pairs."""
+    H, r, d_h, T = 32, 54, 128, 8192
+    say(f"case H{H}_r{r}_dh{d_h}_T{T}_{dt} batch=3 (sampled)")
+    d = decode_inputs(DecodeWorkload("rank54_T8k", 3, H, d_h, r, T, dt, 99), lens=np.array([8192, 5000, 8191], np.int32))
+    got = run_decode(d)
+    for b, h in ((0, 0), (1, 17), (2, 31)):
+        check(d, got, f"b={b} h={h}", [b], [h])
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_T64", "small_bf16_T2k"])
+def test_any_rank_engine_on_tuned_shapes(name):
+    """The any-rank scan (engine 3) on shapes the tuned scans take."""
+    wl = DECODE_WORKLOADS[name]
+    lens = None if name == "tiny_f32_T64" else np.array([2048, 1000, 1, 64, 65, 2047, 7, 1500], np.int32)
+    say(f"case {name} on the any-rank scan")
+    d = decode_inputs(wl, lens=lens)
+    check(d, run_decode(d, engine=3), name + " engine 3")
+
+
+def test_any_rank_many_heads():
+    """More than 32 heads: the grid runs a second group of heads."""
+    H, r, d_h = 40, 20, 64
+    d = decode_inputs(DecodeWorkload("many_heads", 2, H, d_h, r, 300, "bf16", 5), lens=np.array([300, 97], np.int32))
+    say("case H40_r20_dh64_bf16")
+    check(d, run_decode(d), "H40 r20")
+
+
+def test_rank_zero_and_empty_sequence_any_rank():
+    H, r, d_h = 6, 0, 64
+    d = decode_inputs(DecodeWorkload("mqa", 3, H, d_h, r, 130, "f32", 6), lens=np.array([130, 0, 1], np.int32))
+    got = run_decode(d, engine=3)
+    say("case rank 0 on the any-rank scan, an empty sequence")
+    assert np.all(got[1] == 0)
+    check(d, got, "rank 0", batches=[0, 2])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_append_then_decode_odd_latent_run(dt):
+    """Append at H*r = 990 elements per token (not whole 16-byte chunks):
+    bit-exact slots, untouched neighbours, then decode of the appended cache."""
+    B, H, r, d_h, T = 2, 18, 55, 128, 200
+    lens = np.array([200, 130], np.int32)
+    d = decode_inputs(DecodeWorkload("append55", B, H, d_h, r, T, dt, 77), lens=lens)
+    tdt = TORCH_DT[dt]
+    cache = L.LrkvCache.empty(B, H, d_h, r, T, dtype=tdt)
+    for t in (cache.k_s, cache.v_s, cache.z_k, cache.z_v):
+        t.fill_(-5.0)
+    filled = np.zeros(B, np.int32)
+    for n in (64, 1, 37, 100, 64):
+        rows = {k: np.zeros((B, n) + d[k].shape[2:], d[k].dtype) for k in ("k_s", "v_s", "z_k", "z_v")}
+        for b in range(B):
+            m = int(min(n, T - filled[b]))
+            for k in rows:
+                rows[k][b, :m] = d[k][b, filled[b]:filled[b] + m]
+        L.lrkv_append(cache, torch.from_numpy(filled.copy()).cuda(), *(to_dev(rows[k], dt) for k in rows))
+        filled = np.minimum(filled + n, T)
+    torch.cuda.synchronize()
+    view = np.int16 if dt == "bf16" else np.int32
+    for k, t in (("k_s", cache.k_s), ("v_s", cache.v_s), ("z_k", cache.z_k), ("z_v", cache.z_v)):
+        got = t.view(torch.int16 if dt == "bf16" else torch.int32).cpu().numpy()
+        assert np.array_equal(got, np.ascontiguousarray(d[k]).view(view)), k
+    say(f"case append H18 r55 {dt}: bit-exact")
+    check(d, run_decode(d, cache=cache), f"decode after append {dt}")
