@@ -28,7 +28,11 @@
  *     stream has drained.  Since the calls only launch kernels (no
  *     allocation, memset, copy or synchronisation), a caller may capture
  *     them on a stream into a HIP graph and replay it; every replay reads the
- *     buffers' contents at replay time.
+ *     buffers' contents at replay time.  The first launch of some kernels on
+ *     a device also raises their dynamic-LDS limit (a host-side attribute,
+ *     not stream work); lrkv_init does this for every kernel at once, so
+ *     after lrkv_init on a device no call needs an eager warm-up before
+ *     capture.
  *   - `dtype` (lrkv_dtype) is the storage type of q, the cache, B^K, B^V,
  *     the new rows and the output, one type per call.  Arithmetic is fp32
  *     (bf16 products accumulate in fp32).
@@ -82,6 +86,14 @@ typedef enum lrkv_dtype {
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* lrkv_status_string(int32_t status);
+
+/* Per-device set-up for the device current at the call: caches its compute
+ * unit count and raises the dynamic-LDS limit of every kernel that needs
+ * it.  Optional (each kernel's first launch does its own part); call it once
+ * per device, outside any stream capture, before capturing library calls
+ * into a HIP graph.  Idempotent and safe to call from several threads.
+ * Returns LRKV_ERR_DEVICE if a HIP call fails.  Launches nothing. */
+lrkv_status lrkv_init(void);
 
 /* Cache elements per token per layer, 2(head_dim + num_heads*rank)
  * (slide "Can heads share storage while keeping distinct K/V features?",

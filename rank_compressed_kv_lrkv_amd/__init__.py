@@ -6,7 +6,7 @@ workload generator used by the tests and the benchmark.
 """
 from .binding import (  # noqa: F401
     DecodeCall, EXPORTED, LRKV_BF16, LRKV_F32, LrkvCache, LrkvError, decode_workspace, default_scale, library,
-    lrkv_append, lrkv_cache_elems_per_token, lrkv_decode, lrkv_decode_noalloc, lrkv_decode_scan_kernel, lrkv_decode_workspace_size,
+    lrkv_append, lrkv_cache_elems_per_token, lrkv_init, lrkv_decode, lrkv_decode_noalloc, lrkv_decode_scan_kernel, lrkv_decode_workspace_size,
     lrkv_decode_workspace_size_ex,
     lrkv_mha_decode, lrkv_mha_decode_workspace_size,
     lrkv_pack_projection, lrkv_prefill, lrkv_prefill_chunk, lrkv_project_append, lrkv_project_kernel,

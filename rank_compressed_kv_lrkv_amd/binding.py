@@ -17,14 +17,16 @@ from typing import Optional
 import torch  # imported before the library so both share one HIP runtime
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "liblrkv.so")
+# LRKV_LIBRARY names another build of the library (the host-sanitizer build
+# of build.py --sanitize, for instance); by default the in-tree one.
+LIB_PATH = os.environ.get("LRKV_LIBRARY") or os.path.join(_HERE, "lib", "liblrkv.so")
 
 LRKV_F32 = 0
 LRKV_BF16 = 1
 STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DTYPE", 4: "LRKV_ERR_ALIGN",
           5: "LRKV_ERR_CAPACITY", 6: "LRKV_ERR_WORKSPACE", 7: "LRKV_ERR_DEVICE", 8: "LRKV_ERR_SCRATCH"}
 
-EXPORTED = ("lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
+EXPORTED = ("lrkv_init", "lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
             "lrkv_decode_combine", "lrkv_decode_noalloc", "lrkv_decode_workspace_size_ex", "lrkv_decode_ex", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
             "lrkv_project_kernel", "lrkv_project_workspace_size", "lrkv_project_append",
@@ -50,6 +52,8 @@ def library() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m rank_compressed_kv_lrkv_amd.build`")
         lib = ctypes.CDLL(LIB_PATH)
+        lib.lrkv_init.argtypes = []
+        lib.lrkv_init.restype = _i32
         lib.lrkv_status_string.argtypes = [_i32]
         lib.lrkv_status_string.restype = ctypes.c_char_p
         lib.lrkv_cache_elems_per_token.argtypes = [_i32, _i32, _i32]
@@ -105,6 +109,12 @@ def library() -> ctypes.CDLL:
         lib.lrkv_train_backward.restype = _i32
         _lib = lib
     return _lib
+
+
+def lrkv_init() -> None:
+    """Per-device set-up of the current device (kernel attributes, compute
+    unit count); call before capturing library calls into a HIP graph."""
+    _check(library().lrkv_init(), "lrkv_init")
 
 
 def lrkv_status_string(status: int) -> str:

@@ -620,4 +620,14 @@ hipError_t launch_decode_mfma_scan(const DecodePlan& pl, const DecodeArgs& a, hi
   return hipErrorInvalidValue;
 }
 
+hipError_t decode_mfma_prepare() {
+  hipError_t e = hipSuccess;
+#define LRKV_MF(DHV, RV) \
+  if (e == hipSuccess) e = allow_dynamic_lds<&decode_mfma_kernel<DHV, RV>>(MfShape<DHV, RV>::LDS);
+  LRKV_MF(64, 0) LRKV_MF(64, 8) LRKV_MF(64, 16) LRKV_MF(64, 32)
+  LRKV_MF(128, 0) LRKV_MF(128, 8) LRKV_MF(128, 16) LRKV_MF(128, 32)
+#undef LRKV_MF
+  return e;
+}
+
 }  // namespace lrkv

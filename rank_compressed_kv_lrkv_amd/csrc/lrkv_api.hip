@@ -174,6 +174,16 @@ const char* lrkv_status_string(int32_t s) {
   }
 }
 
+lrkv_status lrkv_init(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LRKV_ERR_DEVICE;
+  (void)device_cu_count();
+  for (hipError_t (*prep)() : {lrkv::decode_mfma_prepare, lrkv::prefill_prepare, lrkv::project_prepare,
+                               lrkv::train_prepare})
+    if (prep() != hipSuccess) return LRKV_ERR_DEVICE;
+  return LRKV_OK;
+}
+
 int64_t lrkv_cache_elems_per_token(int32_t num_heads, int32_t head_dim, int32_t rank) {
   if (num_heads < 1 || head_dim < 1 || rank < 0) return -1;
   return 2 * (int64_t(head_dim) + int64_t(num_heads) * int64_t(rank));

@@ -24,6 +24,14 @@ hipError_t allow_dynamic_lds(int bytes) {
   return e;
 }
 
+// Per-device set-up done at a kernel's first launch (the dynamic-LDS limit
+// of every kernel that needs more than the default), done for every kernel
+// at once; each returns the first failure.
+hipError_t decode_mfma_prepare();
+hipError_t prefill_prepare();
+hipError_t project_prepare();
+hipError_t train_prepare();
+
 constexpr int kDecodeThreads = 256;  // one workgroup = 4 wave64
 constexpr int kDecodeTile = 64;      // cache tokens staged in LDS per step
 

@@ -538,4 +538,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+hipError_t prefill_prepare() {
+  hipError_t e = hipSuccess;
+#define LRKV_PF(DHV, RV) \
+  if (e == hipSuccess) e = allow_dynamic_lds<&prefill_kernel<DHV, RV>>(PrefillShape<DHV, RV>::LDS);
+  LRKV_PF(64, 0) LRKV_PF(64, 8) LRKV_PF(64, 16) LRKV_PF(64, 32)
+  LRKV_PF(128, 0) LRKV_PF(128, 8) LRKV_PF(128, 16) LRKV_PF(128, 32)
+#undef LRKV_PF
+  return e;
+}
+
 }  // namespace lrkv

@@ -741,4 +741,10 @@ hipError_t launch_pack_projection(const PackArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t project_prepare() {
+  hipError_t e = allow_dynamic_lds<&project_gemm_kernel<4>>(PgShape<4>::LDS);
+  if (e == hipSuccess) e = allow_dynamic_lds<&project_gemm_kernel<5>>(PgShape<5>::LDS);
+  return e;
+}
+
 }  // namespace lrkv

@@ -52,6 +52,9 @@ struct TrShape {
   static constexpr int ZB = kTrWaves * R * 2, CZ = ZB / 16; // the 4 heads' latents of one token
   static constexpr int ROWS = kTrTile * RB;                 // a 32-row tile of d_h rows
   static constexpr int LATS = kTrTile * ZB;                 // a 32-token tile of latents
+  static constexpr int LDS_DQ = 2 * (ROWS + LATS);                     // dQ kernel: key and value tiles
+  static constexpr int LDS_RED = kTrWaves * (DH / 32) * 16 * 64 * 4;    // dK/dV kernel: head-sum exchange
+  static constexpr int LDS_KV = 2 * (kTrWaves * ROWS + LATS) > LDS_RED ? 2 * (kTrWaves * ROWS + LATS) : LDS_RED;
   static_assert(DH % 32 == 0 && R <= 32 && R % 8 == 0, "training envelope");
   static_assert(CR >= 4 && (R == 0 || CZ >= 4), "swizzle needs 4 chunks per row");
 };
@@ -560,14 +563,13 @@ static hipError_t launch_train_backward_t(const TrainArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = unsigned(size_t(kp.n_blocks) * kp.n_hgroups * B);
-  const int lds_dq = 2 * (P::ROWS + P::LATS);
+  const int lds_dq = P::LDS_DQ;
   e = allow_dynamic_lds<&train_dq_kernel<DH, R>>(lds_dq);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((train_dq_kernel<DH, R>), dim3(grid), dim3(kTrThreads), size_t(lds_dq), st, kp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int lds_red = kTrWaves * (DH / 32) * 16 * 64 * 4;
-  const int lds_kv = max(2 * (kTrWaves * P::ROWS + P::LATS), lds_red);
+  const int lds_kv = P::LDS_KV;
   e = allow_dynamic_lds<&train_dkv_kernel<DH, R>>(lds_kv);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((train_dkv_kernel<DH, R>), dim3(grid), dim3(kTrThreads), size_t(lds_kv), st, kp);
@@ -601,6 +603,17 @@ hipError_t launch_train_backward(const TrainArgs& a, hipStream_t st) {
   LRKV_TR(128, 0) LRKV_TR(128, 8) LRKV_TR(128, 16) LRKV_TR(128, 32)
 #undef LRKV_TR
   return hipErrorInvalidValue;
+}
+
+hipError_t train_prepare() {
+  hipError_t e = hipSuccess;
+#define LRKV_TR(DHV, RV)                                                                                      \
+  if (e == hipSuccess) e = allow_dynamic_lds<&train_dq_kernel<DHV, RV>>(TrShape<DHV, RV>::LDS_DQ);              \
+  if (e == hipSuccess) e = allow_dynamic_lds<&train_dkv_kernel<DHV, RV>>(TrShape<DHV, RV>::LDS_KV);
+  LRKV_TR(64, 0) LRKV_TR(64, 8) LRKV_TR(64, 16) LRKV_TR(64, 32)
+  LRKV_TR(128, 0) LRKV_TR(128, 8) LRKV_TR(128, 16) LRKV_TR(128, 32)
+#undef LRKV_TR
+  return e;
 }
 
 }  // namespace lrkv

@@ -216,3 +216,66 @@ def test_project_decode_step_graph(B, n, d, with_ws):
         for k in KEYS:
             assert same(getattr(cache, k), getattr(ref, k)), f"replay {i}: cache {k} differs from the eager call"
         cur = cur + n
+
+
+CAPTURE_AFTER_INIT = r'''
+import sys, torch
+import rank_compressed_kv_lrkv_amd as L
+torch.cuda.init()
+L.lrkv_init()                                   # the only set-up: no eager call before the capture
+g0 = torch.Generator(device="cuda").manual_seed(3)
+bf = torch.bfloat16
+rn = lambda *s, sc=1.0: (torch.randn(*s, device="cuda", generator=g0) * sc).to(bf)
+B, Lq, H, D, R, T = 2, 96, 32, 128, 16, 256
+q, ks, vs, zk, zv = rn(B, Lq, H, D), rn(B, Lq, D), rn(B, Lq, D), rn(B, Lq, H, R), rn(B, Lq, H, R)
+bk, bv, dout = rn(H, D, R, sc=0.25), rn(H, D, R, sc=0.25), rn(B, Lq, H, D)
+cache = L.LrkvCache(rn(B, T, D), rn(B, T, D), rn(B, T, H, R), rn(B, T, H, R))
+qd = rn(B, H, D)
+lens = torch.tensor([T, 77], dtype=torch.int32, device="cuda")
+ws = L.decode_workspace(cache, T)
+tws = torch.empty(L.lrkv_train_backward_workspace_size(bf, B, H, D, R, Lq), dtype=torch.uint8, device="cuda")
+def bufs():
+    return dict(po=torch.empty_like(q), do=torch.empty(B, H, D, dtype=bf, device="cuda"),
+                to=torch.empty_like(q), lse=torch.empty(B, Lq, H, device="cuda"),
+                g={k: torch.empty(s, device="cuda") for k, s in (("dq", (B, Lq, H, D)), ("dk_s", (B, Lq, D)),
+                   ("dv_s", (B, Lq, D)), ("dz_k", (B, Lq, H, R)), ("dz_v", (B, Lq, H, R)), ("db_k", (H, D, R)),
+                   ("db_v", (H, D, R)))})
+def step(o):
+    L.lrkv_prefill(q, ks, vs, zk, zv, bk, bv, out=o["po"])
+    L.lrkv_decode(cache, lens, T, qd, bk, bv, out=o["do"], workspace=ws)
+    L.lrkv_train_forward(q, ks, vs, zk, zv, bk, bv, out=o["to"], lse=o["lse"])
+    L.lrkv_train_backward(q, ks, vs, zk, zv, bk, bv, o["to"], o["lse"], dout, workspace=tws, grads=o["g"])
+cap, ref = bufs(), bufs()
+graph = torch.cuda.CUDAGraph()
+with torch.cuda.graph(graph):
+    step(cap)
+for i in range(3):
+    graph.replay()
+    torch.cuda.synchronize()
+    step(ref)
+    torch.cuda.synchronize()
+    for k in ("po", "do", "to", "lse"):
+        a, b = cap[k], ref[k]
+        assert torch.equal(a.view(torch.int16) if a.dtype == bf else a, b.view(torch.int16) if b.dtype == bf else b), (i, k)
+    for k in cap["g"]:
+        assert torch.equal(cap["g"][k], ref["g"][k]), (i, k)
+print("capture after lrkv_init: 3 replays bit-identical to eager calls", flush=True)
+'''
+
+
+def test_capture_after_init_in_a_fresh_process():
+    """In a fresh process, lrkv_init and then a capture of prefill, decode
+    (MFMA scan) and a training step with no eager call before it: every
+    kernel that raises its dynamic-LDS limit at first launch is set up by
+    lrkv_init.  Three replays are compared bit for bit with eager calls."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ)
+    env["PYTHONPATH"] = root + os.pathsep + env.get("PYTHONPATH", "")
+    say("case capture after lrkv_init, fresh process")
+    res = subprocess.run([sys.executable, "-c", CAPTURE_AFTER_INIT], cwd=root, env=env, capture_output=True,
+                         text=True, timeout=300)
+    say(res.stdout.strip()[-2000:])
+    assert res.returncode == 0, res.stderr[-4000:]
