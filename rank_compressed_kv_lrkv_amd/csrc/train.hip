@@ -24,11 +24,12 @@
 //   train_dq_kernel     per (query block, 4 heads): keys streamed through
 //                       LDS, S^T and dP^T on MFMA (lane = query), dQ^T
 //                       accumulated as Kaug^T dS^T, B^K epilogue;
-//   train_dkv_kernel    per (key block, 4 heads): queries and dO streamed
-//                       through LDS, S and dP on MFMA (lane = key), Kaug and
-//                       Vaug gradients accumulated as dS^T Qaug and P^T dOaug;
-//                       per-head-group partial sums of dK_s, dV_s and
-//                       per-key-block partial dB^K, dB^V;
+//   train_dkv_kernel    per (128 keys, head): the head's queries and dO
+//                       streamed through LDS (double buffered), S and dP on
+//                       MFMA (lane = key), Kaug and Vaug gradients
+//                       accumulated as dS^T Qaug and P^T dOaug; per-head
+//                       partials of dK_s, dV_s and per-key-block partial
+//                       dB^K, dB^V;
 //   train_reduce_kernel the partial sums added up (deterministic order).
 // P and dS enter MFMAs rounded to bf16; everything is accumulated in fp32.
 #include "lrkv_device.h"
@@ -53,11 +54,20 @@ struct TrShape {
   static constexpr int ROWS = kTrTile * RB;                 // a 32-row tile of d_h rows
   static constexpr int LATS = kTrTile * ZB;                 // a 32-token tile of latents
   static constexpr int LDS_DQ = 2 * (ROWS + LATS);                     // dQ kernel: key and value tiles
-  static constexpr int LDS_RED = kTrWaves * (DH / 32) * 16 * 64 * 4;    // dK/dV kernel: head-sum exchange
-  static constexpr int LDS_KV = 2 * (kTrWaves * ROWS + LATS) > LDS_RED ? 2 * (kTrWaves * ROWS + LATS) : LDS_RED;
+  // dK/dV kernel: two query-side tiles of one head (double buffer), each Q
+  // rows, Q B^K latents, dO rows, dO B^V latents, then lse and D of its 32
+  // queries; after them the B-gradient exchange area (32 x R fp32)
+  static constexpr int ZB1 = R * 2, CZ1 = ZB1 / 16;         // one head's latents of a token
+  static constexpr int LATS1 = kTrTile * ZB1;
+  static constexpr int KV_TILE1 = 2 * (ROWS + LATS1) + 2 * kTrTile * 4;
+  static constexpr int LDS_KV = 2 * KV_TILE1 + (R > 0 ? kTrTile * R * 4 : 16);
   static_assert(DH % 32 == 0 && R <= 32 && R % 8 == 0, "training envelope");
   static_assert(CR >= 4 && (R == 0 || CZ >= 4), "swizzle needs 4 chunks per row");
+  static_assert(LDS_KV <= 160 * 1024, "LDS");
 };
+
+constexpr int kTrKeyWaves = 4;                // dK/dV kernel: waves over the keys of a block
+constexpr int kTrKeyBlock = kTrKeyWaves * kTrTile;
 
 struct TrParams {
   const uint16_t* q; const uint16_t* k_s; const uint16_t* v_s; const uint16_t* z_k; const uint16_t* z_v;
@@ -67,9 +77,9 @@ struct TrParams {
   // workspace
   uint16_t* qb; uint16_t* dob;      // [B][L][H][R] bf16: Q B^K_h and dO B^V_h
   float* lse2; float* dd;           // [B][H][Lp]: lse * log2(e) and rowsum(dO o O); rows >= L hold 0
-  float* dks_part; float* dvs_part; // [n_hgroups][B][L][DH]
-  float* dbk_part; float* dbv_part; // [B][n_kblocks][H][DH][R]
-  int batch, heads, seq_len, seq_pad, n_blocks, n_hgroups;
+  float* dks_part; float* dvs_part; // [H][B][L][DH]: per-head dK_h, dV_h
+  float* dbk_part; float* dbv_part; // [B][n_kb][H][DH][R], key blocks of kTrKeyBlock tokens
+  int batch, heads, seq_len, seq_pad, n_blocks, n_hgroups, n_kb;
   float scale, scale_log2;
 };
 
@@ -89,15 +99,17 @@ __device__ __forceinline__ void tr_fill(unsigned char* dst, const unsigned char*
 
 // Per-lane LDS offsets of the operand reads (the layouts of the forward
 // prefill kernel): row-major 16-byte reads of chunk c of row n (koff) and of
-// this wave's head's latent chunk c (zoff); transpose reads of a 16-token
-// chunk of d_h rows (voff) and of latents (zvoff), giving lane (feature n,
-// half) the tokens {4half..+3, 8+4half..+3} of the chunk, the k-slot order
-// of an MFMA accumulator used as the other operand.
-template <int DH, int R>
+// latent chunk c (zoff) of head slot `slot` in a latent tile holding NH
+// heads' latents per token; transpose reads of a 16-token chunk of d_h rows
+// (voff) and of latents (zvoff), giving lane (feature n, half) the tokens
+// {4half..+3, 8+4half..+3} of the chunk, the k-slot order of an MFMA
+// accumulator used as the other operand.
+template <int DH, int R, int NH>
 struct TrOffsets {
   using P = TrShape<DH, R>;
+  static constexpr int ZB = NH * R * 2, CZ = ZB / 16;       // latent bytes and chunks per token
   int koff[DH / 16], zoff[P::ZCH], voff[DH / 32][2], zvoff[2][2];
-  __device__ __forceinline__ TrOffsets(int lane, int wave) {
+  __device__ __forceinline__ TrOffsets(int lane, int slot) {
     const int n = lane & 31, half = lane >> 5;
 #pragma unroll
     for (int c = 0; c < DH / 16; ++c) koff[c] = n * P::RB + ((2 * c + half) ^ lds_swz(n, P::CR)) * 16;
@@ -105,8 +117,8 @@ struct TrOffsets {
     for (int c = 0; c < P::ZCH; ++c) {
       zoff[c] = 0;
       if constexpr (R > 0) {
-        const int ch = wave * (R / 8) + (R == 8 ? 0 : 2 * c + half);
-        zoff[c] = n * P::ZB + (ch ^ lds_swz(n, P::CZ)) * 16;
+        const int ch = slot * (R / 8) + (R == 8 ? 0 : 2 * c + half);
+        zoff[c] = n * ZB + (ch ^ lds_swz(n, CZ)) * 16;
       }
     }
     const int tr_tok = 4 * half + ((lane >> 2) & 3);
@@ -126,19 +138,19 @@ struct TrOffsets {
         zvoff[c][j] = 0;
         if constexpr (R > 0) {
           const int feat = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-          const int byte = wave * R * 2 + (feat < R ? feat : 0) * 2;   // rows >= R: any valid row (unused)
+          const int byte = slot * R * 2 + (feat < R ? feat : 0) * 2;   // rows >= R: any valid row (unused)
           const int row = 16 * c + tr_tok + 8 * j;
-          zvoff[c][j] = row * P::ZB + ((byte / 16) ^ lds_swz(row, P::CZ)) * 16 + byte % 16;
+          zvoff[c][j] = row * ZB + ((byte / 16) ^ lds_swz(row, CZ)) * 16 + byte % 16;
         }
       }
   }
 };
 
 // Row-major operand chunk c of an augmented row: d_h part from `rows`, latent
-// part from `lats` (this wave's head).
-template <int DH, int R>
+// part from `lats` (the offsets' head slot).
+template <int DH, int R, int NH>
 __device__ __forceinline__ bf16x8_t tr_row_chunk(const unsigned char* rows, const unsigned char* lats,
-                                                 const TrOffsets<DH, R>& o, int c, int half) {
+                                                 const TrOffsets<DH, R, NH>& o, int c, int half) {
   if (c < DH / 16) return as_bf16x8(*reinterpret_cast<const u32x4*>(rows + o.koff[c]));
   if constexpr (R > 0) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(lats + o.zoff[c - DH / 16]);
@@ -148,9 +160,9 @@ __device__ __forceinline__ bf16x8_t tr_row_chunk(const unsigned char* rows, cons
 }
 
 // Transposed operand of 32-row block f of an augmented row, 16-token chunk c.
-template <int DH, int R>
+template <int DH, int R, int NH>
 __device__ __forceinline__ bf16x8_t tr_col_chunk(const unsigned char* rows, const unsigned char* lats,
-                                                 const TrOffsets<DH, R>& o, int f, int c) {
+                                                 const TrOffsets<DH, R, NH>& o, int f, int c) {
   if (f < DH / 32) {
     const uint2 lo = lds_read_tr16(rows + 16 * c * TrShape<DH, R>::RB + o.voff[f][0]);
     const uint2 hi = lds_read_tr16(rows + 16 * c * TrShape<DH, R>::RB + o.voff[f][1]);
@@ -234,7 +246,7 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
   const int q0 = qb * kTrTile;
   const int qrow = min(q0 + n, L - 1);
   const int kt_last = min(q0 + kTrTile - 1, L - 1) / kTrTile;
-  const TrOffsets<DH, R> o(lane, wave);
+  const TrOffsets<DH, R, kTrWaves> o(lane, wave);
 
   // B operands: the wave's query rows [Q | Q B^K_h] and [dO | dO B^V_h]
   bf16x8_t qop[P::KCH], dop[P::KCH];
@@ -269,8 +281,8 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
     f32x16_t s = {}, dp = {};
 #pragma unroll
     for (int c = 0; c < P::KCH; ++c) {
-      s = mfma32(tr_row_chunk<DH, R>(krows, klats, o, c, half), qop[c], s);
-      dp = mfma32(tr_row_chunk<DH, R>(vrows, vlats, o, c, half), dop[c], dp);
+      s = mfma32(tr_row_chunk(krows, klats, o, c, half), qop[c], s);
+      dp = mfma32(tr_row_chunk(vrows, vlats, o, c, half), dop[c], dp);
     }
     bf16x8_t pb[2];
 #pragma unroll
@@ -284,7 +296,7 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
 #pragma unroll
     for (int f = 0; f < P::VBLK; ++f)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) acc[f] = mfma32(tr_col_chunk<DH, R>(krows, klats, o, f, c), pb[c], acc[f]);
+      for (int c = 0; c < 2; ++c) acc[f] = mfma32(tr_col_chunk(krows, klats, o, f, c), pb[c], acc[f]);
     __syncthreads();
   }
   // dQ^T = scale (dQ_s^T + B^K_h dQ_z^T)
@@ -317,107 +329,174 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = (key block, 4 heads, sequence), one head per wave.
+// dK, dV: workgroup = (block of 128 keys, head, sequence); wave w owns keys
+// k0 + 32w .. k0 + 32w + 31.  The query blocks from the key block's diagonal
+// to the end stream through LDS as one tile (the head's Q rows and Q B^K
+// latents, dO rows and dO B^V latents, lse and D of the 32 queries) that all
+// four waves read; the next tile's global loads are in flight (in registers)
+// while the current one is computed, then stored to the other LDS buffer.  A
+// wave keeps its keys' [dK_h | dZ^K_h] and [dV_h | dZ^V_h] in registers; at
+// the end it writes dZ^K_h, dZ^V_h, the head's dK_h, dV_h as one partial of
+// dK_s, dV_s (summed over the heads afterwards) and its share of dB^K_h,
+// dB^V_h over the block (summed over the waves in a fixed order through LDS).
 // ---------------------------------------------------------------------------
 template <int DH, int R>
 __global__ __launch_bounds__(kTrThreads) void train_dkv_kernel(TrParams p) {
   using P = TrShape<DH, R>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  // query side: the 4 heads' Q rows, then [Q B^K] latents; dO side alike
-  unsigned char* const qrows = smem;                               // 4 x ROWS
-  unsigned char* const qlats = smem + kTrWaves * P::ROWS;
-  unsigned char* const drows = qlats + P::LATS;                    // 4 x ROWS
-  unsigned char* const dlats = drows + kTrWaves * P::ROWS;
+  float* const bx = reinterpret_cast<float*>(smem + 2 * P::KV_TILE1);   // B-gradient exchange
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, half = lane >> 5;
-  const int per_level = p.n_hgroups * p.batch;
-  const int kb = int(blockIdx.x) / per_level;                      // key block 0 scans every query block
-  const int rem = int(blockIdx.x) % per_level;
-  const int b = rem % p.batch, hg = rem / p.batch;
   const int H = p.heads, L = p.seq_len;
-  const int h = hg * kTrWaves + wave;
-  const int k0 = kb * kTrTile;
+  const int per_level = H * p.batch;
+  const int kb = int(blockIdx.x) / per_level;                // key block 0 (the heaviest) first
+  const int rem = int(blockIdx.x) % per_level;
+  const int b = rem % p.batch, h = rem / p.batch;
+  const int k0 = kb * kTrKeyBlock + wave * kTrTile;          // this wave's first key
   const int krow = min(k0 + n, L - 1);
-  const TrOffsets<DH, R> o(lane, wave);
+  const int nqb = (L + kTrTile - 1) / kTrTile;
+  const int qb_first = (kb * kTrKeyBlock) / kTrTile;
+  const TrOffsets<DH, R, 1> o(lane, 0);
 
-  // B operands: the wave's key rows [K_s | Z^K_h] and [V_s | Z^V_h] (lane = key n)
+  // the lane's key rows [K_s | Z^K_h] and [V_s | Z^V_h] (B operands, lane = key n)
   bf16x8_t kop[P::KCH], vop[P::KCH];
   {
-    const size_t r = size_t(b) * L + krow;
+    const size_t kr = size_t(b) * L + krow;
 #pragma unroll
     for (int c = 0; c < P::KCH; ++c) {
-      kop[c] = tr_global_chunk<DH, R>(p.k_s + r * DH, p.z_k + (r * H + h) * R, c, half);
-      vop[c] = tr_global_chunk<DH, R>(p.v_s + r * DH, p.z_v + (r * H + h) * R, c, half);
+      kop[c] = tr_global_chunk<DH, R>(p.k_s + kr * DH, p.z_k + (kr * H + h) * R, c, half);
+      vop[c] = tr_global_chunk<DH, R>(p.v_s + kr * DH, p.z_v + (kr * H + h) * R, c, half);
     }
   }
-  // accumulators C[key][feature], lane = feature column: [dK_h | dZ^K_h] / scale, [dV_h | dZ^V_h]
-  f32x16_t dk[P::VBLK], dv[P::VBLK];
-#pragma unroll
-  for (int f = 0; f < P::VBLK; ++f) dk[f] = dv[f] = f32x16_t{};
-  const int nqb = (L + kTrTile - 1) / kTrTile;
-  for (int qb = kb; qb < nqb; ++qb) {
+
+  // query-side tile qb: global loads into registers (rows >= valid are
+  // zero), then stores to LDS buffer `buf`
+  constexpr int NRL = kTrTile * P::CR / kTrThreads;         // row chunks per thread and array
+  static_assert(NRL >= 1 && (kTrTile * P::CR) % kTrThreads == 0, "row chunks per thread");
+  static_assert(kTrTile * P::CZ1 <= kTrThreads, "latent chunks per thread");
+  u32x4 pre_q[NRL], pre_d[NRL], pre_zq = {0u, 0u, 0u, 0u}, pre_zd = {0u, 0u, 0u, 0u};
+  float pre_l = 0.f;
+  const size_t lrow = (size_t(b) * H + h) * p.seq_pad;
+  auto tile_load = [&](int qb) __attribute__((always_inline)) {
     const int q0 = qb * kTrTile, valid = min(kTrTile, L - q0);
     const size_t tok = size_t(b) * L + q0;
 #pragma unroll
-    for (int w = 0; w < kTrWaves; ++w) {
-      const size_t hr = (tok * H + hg * kTrWaves + w) * DH;
-      tr_fill(qrows + w * P::ROWS, reinterpret_cast<const unsigned char*>(p.q + hr), size_t(H) * DH * 2, P::CR, valid,
-              tid);
-      tr_fill(drows + w * P::ROWS, reinterpret_cast<const unsigned char*>(p.d_out + hr), size_t(H) * DH * 2, P::CR,
-              valid, tid);
+    for (int i = 0; i < NRL; ++i) {
+      const int idx = tid + i * kTrThreads, t = idx / P::CR, ch = idx % P::CR;
+      pre_q[i] = pre_d[i] = u32x4{0u, 0u, 0u, 0u};
+      if (t < valid) {
+        const size_t off = ((tok + t) * H + h) * DH + ch * 8;
+        pre_q[i] = *reinterpret_cast<const u32x4*>(p.q + off);
+        pre_d[i] = *reinterpret_cast<const u32x4*>(p.d_out + off);
+      }
     }
     if constexpr (R > 0) {
-      tr_fill(qlats, reinterpret_cast<const unsigned char*>(p.qb + (tok * H + hg * kTrWaves) * R), size_t(H) * R * 2,
-              P::CZ, valid, tid);
-      tr_fill(dlats, reinterpret_cast<const unsigned char*>(p.dob + (tok * H + hg * kTrWaves) * R), size_t(H) * R * 2,
-              P::CZ, valid, tid);
+      const int t = tid / P::CZ1, ch = tid % P::CZ1;
+      pre_zq = pre_zd = u32x4{0u, 0u, 0u, 0u};
+      if (tid < kTrTile * P::CZ1 && t < valid) {
+        const size_t off = ((tok + t) * H + h) * R + ch * 8;
+        pre_zq = *reinterpret_cast<const u32x4*>(p.qb + off);
+        pre_zd = *reinterpret_cast<const u32x4*>(p.dob + off);
+      }
     }
-    __syncthreads();
-    const unsigned char* qw = qrows + wave * P::ROWS;
-    const unsigned char* dw = drows + wave * P::ROWS;
-    // S = Qaug Kaug^T and dP = dOaug Vaug^T: lane (key n, half) holds queries
-    // 8(i/4) + 4half + i%4
+    // lse and D of the 32 queries (padding rows hold 0)
+    if (tid < 2 * kTrTile) pre_l = (tid < kTrTile ? p.lse2 : p.dd)[lrow + q0 + (tid & (kTrTile - 1))];
+  };
+  auto tile_store = [&](int buf) __attribute__((always_inline)) {
+    unsigned char* const qrows = smem + buf * P::KV_TILE1;
+    unsigned char* const qlats = qrows + P::ROWS;
+    unsigned char* const drows = qlats + P::LATS1;
+    unsigned char* const dlats = drows + P::ROWS;
+#pragma unroll
+    for (int i = 0; i < NRL; ++i) {
+      const int idx = tid + i * kTrThreads, t = idx / P::CR, ch = idx % P::CR;
+      const int pos = t * P::RB + (ch ^ lds_swz(t, P::CR)) * 16;
+      *reinterpret_cast<u32x4*>(qrows + pos) = pre_q[i];
+      *reinterpret_cast<u32x4*>(drows + pos) = pre_d[i];
+    }
+    if constexpr (R > 0) {
+      if (tid < kTrTile * P::CZ1) {
+        const int t = tid / P::CZ1, ch = tid % P::CZ1;
+        const int pos = t * P::ZB1 + (ch ^ lds_swz(t, P::CZ1)) * 16;
+        *reinterpret_cast<u32x4*>(qlats + pos) = pre_zq;
+        *reinterpret_cast<u32x4*>(dlats + pos) = pre_zd;
+      }
+    }
+    if (tid < 2 * kTrTile) reinterpret_cast<float*>(dlats + P::LATS1)[tid] = pre_l;
+  };
+
+  f32x16_t dk[P::VBLK], dv[P::VBLK];
+#pragma unroll
+  for (int f = 0; f < P::VBLK; ++f) dk[f] = dv[f] = f32x16_t{};
+  tile_load(qb_first);
+  tile_store(0);
+  __syncthreads();
+  int buf = 0;
+  for (int qb = qb_first; qb < nqb; ++qb) {
+    if (qb + 1 < nqb) tile_load(qb + 1);
+    const unsigned char* const qrows = smem + buf * P::KV_TILE1;
+    const unsigned char* const qlats = qrows + P::ROWS;
+    const unsigned char* const drows = qlats + P::LATS1;
+    const unsigned char* const dlats = drows + P::ROWS;
+    const float* const lsd = reinterpret_cast<const float*>(dlats + P::LATS1);   // lse2[32], then D[32]
+    const int q0 = qb * kTrTile;
+    // S = Qaug Kaug^T and dP = dOaug Vaug^T: lane (key n, half) holds
+    // queries 8(i/4) + 4half + i%4
     f32x16_t s = {}, dp = {};
 #pragma unroll
     for (int c = 0; c < P::KCH; ++c) {
-      s = mfma32(tr_row_chunk<DH, R>(qw, qlats, o, c, half), kop[c], s);
-      dp = mfma32(tr_row_chunk<DH, R>(dw, dlats, o, c, half), vop[c], dp);
-    }
-    // the 16 rows' lse and D: 4 runs of 4 consecutive queries
-    const size_t lbase = (size_t(b) * H + h) * p.seq_pad + q0 + 4 * half;
-    float lse2[16], dd[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 l4 = *reinterpret_cast<const float4*>(p.lse2 + lbase + 8 * j);
-      const float4 d4 = *reinterpret_cast<const float4*>(p.dd + lbase + 8 * j);
-      lse2[4 * j] = l4.x; lse2[4 * j + 1] = l4.y; lse2[4 * j + 2] = l4.z; lse2[4 * j + 3] = l4.w;
-      dd[4 * j] = d4.x; dd[4 * j + 1] = d4.y; dd[4 * j + 2] = d4.z; dd[4 * j + 3] = d4.w;
+      s = mfma32(tr_row_chunk(qrows, qlats, o, c, half), kop[c], s);
+      dp = mfma32(tr_row_chunk(drows, dlats, o, c, half), vop[c], dp);
     }
     bf16x8_t pp[2], ps[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qi = q0 + 8 * (i >> 2) + 4 * half + (i & 3);
-      const bool ok = k0 + n <= qi && qi < L && k0 + n < L;
-      const float pv = ok ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -lse2[i])) : 0.f;
-      pp[i >> 3][i & 7] = (__bf16)pv;
-      ps[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dd[i]));
+    for (int j = 0; j < 4; ++j) {
+      const float4 l4 = *reinterpret_cast<const float4*>(lsd + 8 * j + 4 * half);
+      const float4 d4 = *reinterpret_cast<const float4*>(lsd + kTrTile + 8 * j + 4 * half);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * j + e;
+        const int qi = q0 + 8 * j + 4 * half + e;
+        const bool ok = k0 + n <= qi && qi < L && k0 + n < L;
+        const float pv = ok ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -lv[e])) : 0.f;
+        pp[i >> 3][i & 7] = (__bf16)pv;
+        ps[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dv4[e]));
+      }
     }
     // [dV_h | dZ^V_h] += P^T dOaug, [dK_h | dZ^K_h] / scale += dS^T Qaug
 #pragma unroll
     for (int f = 0; f < P::VBLK; ++f)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        dv[f] = mfma32(pp[c], tr_col_chunk<DH, R>(dw, dlats, o, f, c), dv[f]);
-        dk[f] = mfma32(ps[c], tr_col_chunk<DH, R>(qw, qlats, o, f, c), dk[f]);
+        dv[f] = mfma32(pp[c], tr_col_chunk(drows, dlats, o, f, c), dv[f]);
+        dk[f] = mfma32(ps[c], tr_col_chunk(qrows, qlats, o, f, c), dk[f]);
       }
+    // the other buffer was last read before the previous barrier
+    if (qb + 1 < nqb) tile_store(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
   for (int f = 0; f < P::VBLK; ++f) dk[f] *= p.scale;
 
-  // ---- per-key gradients of this head: dZ^K_h, dZ^V_h (columns n < R) ----
+  // ---- this head's dK_h, dV_h: one partial of dK_s, dV_s ----
+  const size_t part = (size_t(h) * p.batch + b) * size_t(L) * DH;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
+    if (key < L) {
+#pragma unroll
+      for (int f = 0; f < DH / 32; ++f) {
+        p.dks_part[part + size_t(key) * DH + 32 * f + n] = dk[f][i];
+        p.dvs_part[part + size_t(key) * DH + 32 * f + n] = dv[f][i];
+      }
+    }
+  }
+
   if constexpr (R > 0) {
+    // ---- dZ^K_h, dZ^V_h (columns n < R) ----
     if (n < R) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -429,9 +508,10 @@ __global__ __launch_bounds__(kTrThreads) void train_dkv_kernel(TrParams p) {
         }
       }
     }
-    // ---- dB^K_h, dB^V_h over this key block: C[d][j] = sum_key dK_h[key][d] Z^K[key][h][j] ----
+    // ---- dB^K_h, dB^V_h over the block: C[d][j] = sum_key dK_h[key][d] Z^K[key][h][j] ----
     // A = dK_h^T (lane = feature row, k-slots = keys in accumulator order),
-    // B = Z^K (lane = latent column n, the same keys).
+    // B = Z^K (lane = latent column n, the same keys).  The four waves'
+    // partials are added in wave order through LDS.
     bf16x8_t zk[2], zv[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -448,60 +528,41 @@ __global__ __launch_bounds__(kTrThreads) void train_dkv_kernel(TrParams p) {
         zk[c][s8] = __builtin_bit_cast(__bf16, zkv);
         zv[c][s8] = __builtin_bit_cast(__bf16, zvv);
       }
-    float* dbk = p.dbk_part + ((size_t(b) * p.n_blocks + kb) * H + h) * DH * R;
-    float* dbv = p.dbv_part + ((size_t(b) * p.n_blocks + kb) * H + h) * DH * R;
+    const size_t dbo = ((size_t(b) * p.n_kb + kb) * H + h) * DH * R;
 #pragma unroll
     for (int f = 0; f < DH / 32; ++f) {
-      f32x16_t ck = {}, cv = {};
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8_t ak, av;
+      for (int pass = 0; pass < 2; ++pass) {
+        f32x16_t cb = {};
 #pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-          ak[s8] = (__bf16)dk[f][8 * c + s8];
-          av[s8] = (__bf16)dv[f][8 * c + s8];
+        for (int c = 0; c < 2; ++c) {
+          bf16x8_t a;
+#pragma unroll
+          for (int s8 = 0; s8 < 8; ++s8) a[s8] = (__bf16)(pass ? dv[f][8 * c + s8] : dk[f][8 * c + s8]);
+          cb = mfma32(a, pass ? zv[c] : zk[c], cb);
         }
-        ck = mfma32(ak, zk[c], ck);
-        cv = mfma32(av, zv[c], cv);
-      }
-      if (n < R) {
+        float* dst = (pass ? p.dbv_part : p.dbk_part) + dbo;
+#pragma unroll 1
+        for (int w = 0; w < kTrKeyWaves; ++w) {
+          if (wave == w && n < R) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int d = 32 * f + 8 * (i >> 2) + 4 * half + (i & 3);
-          dbk[size_t(d) * R + n] = ck[i];
-          dbv[size_t(d) * R + n] = cv[i];
+            for (int i = 0; i < 16; ++i) {
+              const int dl = 8 * (i >> 2) + 4 * half + (i & 3);
+              const float v = w == 0 ? cb[i] : bx[dl * R + n] + cb[i];
+              if (w + 1 < kTrKeyWaves) bx[dl * R + n] = v;
+              else dst[size_t(32 * f + dl) * R + n] = v;
+            }
+          }
+          __syncthreads();                                   // this turn's sums are visible (and read)
         }
       }
     }
-  }
-
-  // ---- dK_s, dV_s: the 4 heads summed through LDS, one partial per head group ----
-  float* red = reinterpret_cast<float*>(smem);                     // [wave][f][16][64]
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int f = 0; f < DH / 32; ++f)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) red[((wave * (DH / 32) + f) * 16 + i) * 64 + lane] = pass ? dv[f][i] : dk[f][i];
-    __syncthreads();
-    float* part = (pass ? p.dvs_part : p.dks_part) + (size_t(hg) * p.batch + b) * size_t(L) * DH;
-    for (int f = wave; f < DH / 32; f += kTrWaves) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kTrWaves; ++w) sum += red[((w * (DH / 32) + f) * 16 + i) * 64 + lane];
-        const int key = k0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (key < L) part[size_t(key) * DH + 32 * f + n] = sum;
-      }
-    }
-    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
 // Sums of the partials, each output element added in a fixed order:
-// dK_s, dV_s over the head groups; dB^K, dB^V over (sequence, key block).
+// dK_s, dV_s over the heads; dB^K, dB^V over (sequence, key block).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void train_reduce_kernel(const float* part, float* out, long long n, int parts) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -513,9 +574,11 @@ __global__ __launch_bounds__(256) void train_reduce_kernel(const float* part, fl
 
 size_t train_backward_ws_bytes(int batch, int heads, int head_dim, int rank, int seq_len) {
   const size_t B = size_t(batch), H = size_t(heads), D = size_t(head_dim), R = size_t(rank), L = size_t(seq_len);
-  const size_t nb = (L + kTrTile - 1) / kTrTile, lp = nb * kTrTile, ng = (H + kTrWaves - 1) / kTrWaves;
+  const size_t nb = (L + kTrTile - 1) / kTrTile, lp = nb * kTrTile;
+  const size_t nkb = (L + kTrKeyBlock - 1) / kTrKeyBlock;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  return 2 * al(B * L * H * R * 2) + 2 * al(B * H * lp * 4) + 2 * al(ng * B * L * D * 4) + 2 * al(B * nb * H * D * R * 4);
+  return 2 * al(B * L * H * R * 2) + 2 * al(B * H * lp * 4) + 2 * al(H * B * L * D * 4) +
+         2 * al(B * nkb * H * D * R * 4);
 }
 
 template <int DH, int R>
@@ -546,6 +609,7 @@ static hipError_t launch_train_backward_t(const TrainArgs& a, hipStream_t st) {
   kp.n_blocks = int((L + kTrTile - 1) / kTrTile);
   kp.seq_pad = kp.n_blocks * kTrTile;
   kp.n_hgroups = int((H + kTrWaves - 1) / kTrWaves);
+  kp.n_kb = int((L + kTrKeyBlock - 1) / kTrKeyBlock);
   kp.scale = a.scale;
   kp.scale_log2 = a.scale * 1.4426950408889634f;
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -554,9 +618,9 @@ static hipError_t launch_train_backward_t(const TrainArgs& a, hipStream_t st) {
   kp.dob = reinterpret_cast<uint16_t*>(w); w += al(B * L * H * R * 2);
   kp.lse2 = reinterpret_cast<float*>(w); w += al(B * H * size_t(kp.seq_pad) * 4);
   kp.dd = reinterpret_cast<float*>(w); w += al(B * H * size_t(kp.seq_pad) * 4);
-  kp.dks_part = reinterpret_cast<float*>(w); w += al(size_t(kp.n_hgroups) * B * L * DH * 4);
-  kp.dvs_part = reinterpret_cast<float*>(w); w += al(size_t(kp.n_hgroups) * B * L * DH * 4);
-  kp.dbk_part = reinterpret_cast<float*>(w); w += al(B * size_t(kp.n_blocks) * H * DH * R * 4);
+  kp.dks_part = reinterpret_cast<float*>(w); w += al(H * B * L * DH * 4);
+  kp.dvs_part = reinterpret_cast<float*>(w); w += al(H * B * L * DH * 4);
+  kp.dbk_part = reinterpret_cast<float*>(w); w += al(B * size_t(kp.n_kb) * H * DH * R * 4);
   kp.dbv_part = reinterpret_cast<float*>(w);
 
   hipLaunchKernelGGL((train_prep_kernel<DH, R>), dim3(unsigned(B * L)), dim3(kTrThreads), 0, st, kp);
@@ -572,17 +636,18 @@ static hipError_t launch_train_backward_t(const TrainArgs& a, hipStream_t st) {
   const int lds_kv = P::LDS_KV;
   e = allow_dynamic_lds<&train_dkv_kernel<DH, R>>(lds_kv);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((train_dkv_kernel<DH, R>), dim3(grid), dim3(kTrThreads), size_t(lds_kv), st, kp);
+  const unsigned grid_kv = unsigned(size_t(kp.n_kb) * H * B);
+  hipLaunchKernelGGL((train_dkv_kernel<DH, R>), dim3(grid_kv), dim3(kTrThreads), size_t(lds_kv), st, kp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nrow = (long long)(B * L * DH);
   hipLaunchKernelGGL(train_reduce_kernel, dim3(unsigned((nrow + 255) / 256)), dim3(256), 0, st, kp.dks_part, a.dk_s,
-                     nrow, kp.n_hgroups);
+                     nrow, int(H));
   hipLaunchKernelGGL(train_reduce_kernel, dim3(unsigned((nrow + 255) / 256)), dim3(256), 0, st, kp.dvs_part, a.dv_s,
-                     nrow, kp.n_hgroups);
+                     nrow, int(H));
   if constexpr (R > 0) {
     const long long nb = (long long)(H * DH * R);
-    const int parts = int(B) * kp.n_blocks;
+    const int parts = int(B) * kp.n_kb;
     hipLaunchKernelGGL(train_reduce_kernel, dim3(unsigned((nb + 255) / 256)), dim3(256), 0, st, kp.dbk_part, a.db_k,
                        nb, parts);
     hipLaunchKernelGGL(train_reduce_kernel, dim3(unsigned((nb + 255) / 256)), dim3(256), 0, st, kp.dbv_part, a.db_v,

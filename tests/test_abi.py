@@ -376,9 +376,11 @@ def test_train_workspace_size():
     assert lib.lrkv_train_backward_workspace_size(BF16, 4, 32, 128, 16, 4096, ctypes.byref(n)) == OK
     al = lambda x: (x + 255) // 256 * 256
     B, H, D, R, Lq = 4, 32, 128, 16, 4096
-    nb, ng = (Lq + 31) // 32, (H + 3) // 4
-    want = 2 * al(B * Lq * H * R * 2) + 2 * al(B * H * nb * 32 * 4) + 2 * al(ng * B * Lq * D * 4) + \
-        2 * al(B * nb * H * D * R * 4)
+    nb, nkb = (Lq + 31) // 32, (Lq + 127) // 128       # 32-token query blocks, 128-token key blocks
+    # Q B^K and dO B^V (bf16), lse and D per padded row, per-head dK_h and
+    # dV_h, per-key-block dB^K and dB^V
+    want = 2 * al(B * Lq * H * R * 2) + 2 * al(B * H * nb * 32 * 4) + 2 * al(H * B * Lq * D * 4) + \
+        2 * al(B * nkb * H * D * R * 4)
     assert n.value == want
     assert lib.lrkv_train_backward_workspace_size(BF16, 4, 30, 128, 16, 4096, ctypes.byref(n)) == SHAPE
     assert lib.lrkv_train_backward_workspace_size(F32, 4, 32, 128, 16, 4096, ctypes.byref(n)) == SHAPE
