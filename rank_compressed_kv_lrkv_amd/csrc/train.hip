@@ -22,7 +22,8 @@
 // Kernels (one backward call):
 //   train_prep_kernel   Q B^K_h and dO B^V_h (bf16), D and log2-scaled lse;
 //   train_dq_kernel     per (query block, 4 heads): keys streamed through
-//                       LDS, S^T and dP^T on MFMA (lane = query), dQ^T
+//                       LDS (double buffered), S^T and dP^T on MFMA
+//                       (lane = query), dQ^T
 //                       accumulated as Kaug^T dS^T, B^K epilogue;
 //   train_dkv_kernel    per (128 keys, head): the head's queries and dO
 //                       streamed through LDS (double buffered), S and dP on
@@ -53,7 +54,8 @@ struct TrShape {
   static constexpr int ZB = kTrWaves * R * 2, CZ = ZB / 16; // the 4 heads' latents of one token
   static constexpr int ROWS = kTrTile * RB;                 // a 32-row tile of d_h rows
   static constexpr int LATS = kTrTile * ZB;                 // a 32-token tile of latents
-  static constexpr int LDS_DQ = 2 * (ROWS + LATS);                     // dQ kernel: key and value tiles
+  static constexpr int LDS_DQ1 = 2 * (ROWS + LATS);        // dQ kernel: a key and a value tile
+  static constexpr int LDS_DQ = 2 * LDS_DQ1;                // double buffered
   // dK/dV kernel: two query-side tiles of one head (double buffer), each Q
   // rows, Q B^K latents, dO rows, dO B^V latents, then lse and D of its 32
   // queries; after them the B-gradient exchange area (32 x R fp32)
@@ -82,20 +84,6 @@ struct TrParams {
   int batch, heads, seq_len, seq_pad, n_blocks, n_hgroups, n_kb;
   float scale, scale_log2;
 };
-
-// Copy a 32-row tile into LDS: row t (t < 32) is `chunks` 16-byte chunks at
-// src + t * stride (bytes); chunk ch of row t lands at position
-// ch ^ lds_swz(t, chunks).  Rows t >= valid are zero.  All threads of the
-// workgroup take part.
-__device__ __forceinline__ void tr_fill(unsigned char* dst, const unsigned char* src, size_t stride, int chunks,
-                                        int valid, int tid) {
-  for (int idx = tid; idx < kTrTile * chunks; idx += kTrThreads) {
-    const int t = idx / chunks, ch = idx % chunks;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (t < valid) v = *reinterpret_cast<const u32x4*>(src + size_t(t) * stride + size_t(ch) * 16);
-    *reinterpret_cast<u32x4*>(dst + t * chunks * 16 + (ch ^ lds_swz(t, chunks)) * 16) = v;
-  }
-}
 
 // Per-lane LDS offsets of the operand reads (the layouts of the forward
 // prefill kernel): row-major 16-byte reads of chunk c of row n (koff) and of
@@ -187,53 +175,97 @@ __device__ __forceinline__ bf16x8_t tr_global_chunk(const uint16_t* row, const u
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Per token row: Q B^K_h and dO B^V_h for every head (bf16), D = rowsum(dO o O)
-// and lse * log2(e) (fp32, [B][H][Lp]; the padding rows get 0).
+// Per (token, head): Q B^K_h and dO B^V_h (bf16), D = rowsum(dO o O) and
+// lse * log2(e) (fp32, [B][H][Lp]; the padding rows get 0).  Workgroup = 128
+// tokens (4 blocks of 32) x 4 heads, one head per wave.  The products run on
+// MFMA as C[j][token] = sum_d B_h[d][j] X[token][d]: A = B_h^T (lane = latent
+// column j, read once per wave), B = the tokens' rows straight from global
+// memory (lane = token), so lane (token n, half) ends up holding latent
+// columns 8(i/4) + 4half + i%4 of its token.
 // ---------------------------------------------------------------------------
+constexpr int kPrepBlocks = 4;                 // 32-token blocks per workgroup
+
 template <int DH, int R>
 __global__ __launch_bounds__(kTrThreads) void train_prep_kernel(TrParams p) {
-  const int row = int(blockIdx.x), tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, half = lane >> 5;
   const int H = p.heads, L = p.seq_len;
-  const int b = row / L, i = row % L;
-  const uint16_t* qr = p.q + size_t(row) * H * DH;
-  const uint16_t* dr = p.d_out + size_t(row) * H * DH;
-  const uint16_t* orow = p.out + size_t(row) * H * DH;
+  const int h = int(blockIdx.y) * kTrWaves + wave;
+  const long long ntok = (long long)p.batch * L;
+  constexpr int NC = DH / 16;
+  bf16x8_t wk[NC], wv[NC];
   if constexpr (R > 0) {
-    for (int idx = tid; idx < 2 * H * R; idx += kTrThreads) {
-      const int which = idx / (H * R), hj = idx % (H * R), h = hj / R, j = hj % R;
-      const uint16_t* x = (which ? dr : qr) + h * DH;
-      const uint16_t* w = (which ? p.b_v : p.b_k) + size_t(h) * DH * R + j;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < DH; ++d) acc = __builtin_fmaf(bf16_to_f32(x[d]), bf16_to_f32(w[size_t(d) * R]), acc);
-      (which ? p.dob : p.qb)[size_t(row) * H * R + hj] = f32_to_bf16(acc);
-    }
-  }
-  for (int h = tid; h < H; h += kTrThreads) {
-    float acc = 0.f;
-    for (int d = 0; d < DH; ++d) acc = __builtin_fmaf(bf16_to_f32(dr[h * DH + d]), bf16_to_f32(orow[h * DH + d]), acc);
-    const size_t o = (size_t(b) * H + h) * p.seq_pad + i;
-    p.dd[o] = acc;
-    p.lse2[o] = p.lse[size_t(row) * H + h] * 1.4426950408889634f;
-    if (i == L - 1)
-      for (int t = L; t < p.seq_pad; ++t) {
-        p.dd[o + (t - i)] = 0.f;
-        p.lse2[o + (t - i)] = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const size_t at = (size_t(h) * DH + 16 * c + 8 * half + e) * R + n;
+        wk[c][e] = __builtin_bit_cast(__bf16, n < R ? p.b_k[at] : uint16_t(0));
+        wv[c][e] = __builtin_bit_cast(__bf16, n < R ? p.b_v[at] : uint16_t(0));
       }
+  }
+#pragma unroll 1
+  for (int sb = 0; sb < kPrepBlocks; ++sb) {
+    const long long t = ((long long)blockIdx.x * kPrepBlocks + sb) * kTrTile + n;   // this lane's token
+    const bool ok = t < ntok;
+    const size_t row = (size_t(ok ? t : ntok - 1) * H + h) * DH + 8 * half;
+    f32x16_t cq = {}, cd = {};
+    float dsum = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(p.q + row + 16 * c);
+      const u32x4 dv = *reinterpret_cast<const u32x4*>(p.d_out + row + 16 * c);
+      const u32x4 ov = *reinterpret_cast<const u32x4*>(p.out + row + 16 * c);
+      if constexpr (R > 0) {
+        cq = mfma32(wk[c], as_bf16x8(qv), cq);
+        cd = mfma32(wv[c], as_bf16x8(dv), cd);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dsum = __builtin_fmaf(__uint_as_float(dv[e] << 16), __uint_as_float(ov[e] << 16), dsum);
+        dsum = __builtin_fmaf(__uint_as_float(dv[e] & 0xffff0000u), __uint_as_float(ov[e] & 0xffff0000u), dsum);
+      }
+    }
+    dsum += __shfl_xor(dsum, 32);
+    if (!ok) continue;
+    const int b = int(t / L), i = int(t % L);
+    if (half == 0) {
+      const size_t o = (size_t(b) * H + h) * p.seq_pad + i;
+      p.dd[o] = dsum;
+      p.lse2[o] = p.lse[size_t(t) * H + h] * 1.4426950408889634f;
+      if (i == L - 1)
+        for (int u = L; u < p.seq_pad; ++u) {
+          p.dd[o + (u - i)] = 0.f;
+          p.lse2[o + (u - i)] = 0.f;
+        }
+    }
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j0 = 8 * g + 4 * half;
+        if (j0 < R) {
+          const size_t zo = (size_t(t) * H + h) * R + j0;
+          *reinterpret_cast<uint2*>(p.qb + zo) = uint2{pack_bf16x2(cq[4 * g], cq[4 * g + 1]),
+                                                       pack_bf16x2(cq[4 * g + 2], cq[4 * g + 3])};
+          *reinterpret_cast<uint2*>(p.dob + zo) = uint2{pack_bf16x2(cd[4 * g], cd[4 * g + 1]),
+                                                        pack_bf16x2(cd[4 * g + 2], cd[4 * g + 3])};
+        }
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup = (query block, 4 heads, sequence), one head per wave.
+// dQ: workgroup = (query block, 4 heads, sequence), one head per wave.  The
+// key tiles from 0 to the diagonal (K_s and V_s rows, the 4 heads' Z^K and
+// Z^V latents) stream through two LDS buffers: the next tile's global loads
+// are in flight (in registers) while the current one is computed.
 // ---------------------------------------------------------------------------
 template <int DH, int R>
 __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
   using P = TrShape<DH, R>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  unsigned char* const krows = smem;
-  unsigned char* const klats = smem + P::ROWS;
-  unsigned char* const vrows = klats + P::LATS;
-  unsigned char* const vlats = vrows + P::ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, half = lane >> 5;
@@ -261,21 +293,77 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
   const size_t lrow = (size_t(b) * H + h) * p.seq_pad + qrow;
   const float lse2 = p.lse2[lrow], dd = p.dd[lrow];
 
+  // key tile kt: global loads into registers (rows >= valid are zero), then
+  // stores to LDS buffer `buf`
+  constexpr int NRL = kTrTile * P::CR / kTrThreads;         // row chunks per thread and array
+  constexpr int NZL = R > 0 ? (kTrTile * P::CZ + kTrThreads - 1) / kTrThreads : 1;   // latent chunks per thread
+  static_assert(NRL >= 1 && (kTrTile * P::CR) % kTrThreads == 0, "row chunks per thread");
+  u32x4 pre_k[NRL], pre_v[NRL], pre_zk[NZL], pre_zv[NZL];
+  auto tile_load = [&](int kt) __attribute__((always_inline)) {
+    const int t0 = kt * kTrTile, valid = min(kTrTile, L - t0);
+    const size_t tok = size_t(b) * L + t0;
+#pragma unroll
+    for (int i = 0; i < NRL; ++i) {
+      const int idx = tid + i * kTrThreads, t = idx / P::CR, ch = idx % P::CR;
+      pre_k[i] = pre_v[i] = u32x4{0u, 0u, 0u, 0u};
+      if (t < valid) {
+        const size_t off = (tok + t) * DH + ch * 8;
+        pre_k[i] = *reinterpret_cast<const u32x4*>(p.k_s + off);
+        pre_v[i] = *reinterpret_cast<const u32x4*>(p.v_s + off);
+      }
+    }
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int i = 0; i < NZL; ++i) {
+        const int idx = tid + i * kTrThreads, t = idx / P::CZ, ch = idx % P::CZ;
+        pre_zk[i] = pre_zv[i] = u32x4{0u, 0u, 0u, 0u};
+        if (idx < kTrTile * P::CZ && t < valid) {
+          const size_t off = ((tok + t) * H + hg * kTrWaves) * R + ch * 8;
+          pre_zk[i] = *reinterpret_cast<const u32x4*>(p.z_k + off);
+          pre_zv[i] = *reinterpret_cast<const u32x4*>(p.z_v + off);
+        }
+      }
+    }
+  };
+  auto tile_store = [&](int buf) __attribute__((always_inline)) {
+    unsigned char* const kr = smem + buf * P::LDS_DQ1;
+    unsigned char* const kl = kr + P::ROWS;
+    unsigned char* const vr = kl + P::LATS;
+    unsigned char* const vl = vr + P::ROWS;
+#pragma unroll
+    for (int i = 0; i < NRL; ++i) {
+      const int idx = tid + i * kTrThreads, t = idx / P::CR, ch = idx % P::CR;
+      const int pos = t * P::RB + (ch ^ lds_swz(t, P::CR)) * 16;
+      *reinterpret_cast<u32x4*>(kr + pos) = pre_k[i];
+      *reinterpret_cast<u32x4*>(vr + pos) = pre_v[i];
+    }
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int i = 0; i < NZL; ++i) {
+        const int idx = tid + i * kTrThreads, t = idx / P::CZ, ch = idx % P::CZ;
+        if (idx < kTrTile * P::CZ) {
+          const int pos = t * P::ZB + (ch ^ lds_swz(t, P::CZ)) * 16;
+          *reinterpret_cast<u32x4*>(kl + pos) = pre_zk[i];
+          *reinterpret_cast<u32x4*>(vl + pos) = pre_zv[i];
+        }
+      }
+    }
+  };
+
   f32x16_t acc[P::VBLK];
 #pragma unroll
   for (int f = 0; f < P::VBLK; ++f) acc[f] = f32x16_t{};
+  tile_load(0);
+  tile_store(0);
+  __syncthreads();
+  int buf = 0;
   for (int kt = 0; kt <= kt_last; ++kt) {
-    const int t0 = kt * kTrTile, valid = min(kTrTile, L - t0);
-    const size_t tok = size_t(b) * L + t0;
-    tr_fill(krows, reinterpret_cast<const unsigned char*>(p.k_s + tok * DH), P::RB, P::CR, valid, tid);
-    tr_fill(vrows, reinterpret_cast<const unsigned char*>(p.v_s + tok * DH), P::RB, P::CR, valid, tid);
-    if constexpr (R > 0) {
-      tr_fill(klats, reinterpret_cast<const unsigned char*>(p.z_k + (tok * H + hg * kTrWaves) * R), size_t(H) * R * 2,
-              P::CZ, valid, tid);
-      tr_fill(vlats, reinterpret_cast<const unsigned char*>(p.z_v + (tok * H + hg * kTrWaves) * R), size_t(H) * R * 2,
-              P::CZ, valid, tid);
-    }
-    __syncthreads();
+    if (kt < kt_last) tile_load(kt + 1);
+    const unsigned char* const krows = smem + buf * P::LDS_DQ1;
+    const unsigned char* const klats = krows + P::ROWS;
+    const unsigned char* const vrows = klats + P::LATS;
+    const unsigned char* const vlats = vrows + P::ROWS;
+    const int t0 = kt * kTrTile;
     // S^T = Kaug Qaug^T and dP^T = Vaug dOaug^T: lane (query n, half) holds
     // keys 8(i/4) + 4half + i%4
     f32x16_t s = {}, dp = {};
@@ -297,7 +385,10 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
     for (int f = 0; f < P::VBLK; ++f)
 #pragma unroll
       for (int c = 0; c < 2; ++c) acc[f] = mfma32(tr_col_chunk(krows, klats, o, f, c), pb[c], acc[f]);
+    // the other buffer was last read before the previous barrier
+    if (kt < kt_last) tile_store(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
   // dQ^T = scale (dQ_s^T + B^K_h dQ_z^T)
   if constexpr (R > 0) {
@@ -623,7 +714,8 @@ static hipError_t launch_train_backward_t(const TrainArgs& a, hipStream_t st) {
   kp.dbk_part = reinterpret_cast<float*>(w); w += al(B * size_t(kp.n_kb) * H * DH * R * 4);
   kp.dbv_part = reinterpret_cast<float*>(w);
 
-  hipLaunchKernelGGL((train_prep_kernel<DH, R>), dim3(unsigned(B * L)), dim3(kTrThreads), 0, st, kp);
+  const dim3 grid_prep(unsigned((B * L + kPrepBlocks * kTrTile - 1) / (kPrepBlocks * kTrTile)), unsigned(H / kTrWaves));
+  hipLaunchKernelGGL((train_prep_kernel<DH, R>), grid_prep, dim3(kTrThreads), 0, st, kp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = unsigned(size_t(kp.n_blocks) * kp.n_hgroups * B);
