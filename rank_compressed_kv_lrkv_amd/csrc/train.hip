@@ -26,13 +26,15 @@
 //                       (lane = query), dQ^T
 //                       accumulated as Kaug^T dS^T, B^K epilogue;
 //   train_dkv_kernel    per (128 keys, head): the head's queries and dO
-//                       streamed through LDS (double buffered), S and dP on
+//                       streamed through LDS (software pipelined), S and dP on
 //                       MFMA (lane = key), Kaug and Vaug gradients
 //                       accumulated as dS^T Qaug and P^T dOaug; per-head
 //                       partials of dK_s, dV_s and per-key-block partial
 //                       dB^K, dB^V;
 //   train_reduce_kernel the partial sums added up (deterministic order).
 // P and dS enter MFMAs rounded to bf16; everything is accumulated in fp32.
+#include <type_traits>
+
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -56,13 +58,14 @@ struct TrShape {
   static constexpr int LATS = kTrTile * ZB;                 // a 32-token tile of latents
   static constexpr int LDS_DQ1 = 2 * (ROWS + LATS);        // dQ kernel: a key and a value tile
   static constexpr int LDS_DQ = 2 * LDS_DQ1;                // double buffered
-  // dK/dV kernel: two query-side tiles of one head (double buffer), each Q
-  // rows, Q B^K latents, dO rows, dO B^V latents, then lse and D of its 32
-  // queries; after them the B-gradient exchange area (32 x R fp32)
+  // dK/dV kernel: three query-side tiles of one head (a software pipeline),
+  // each Q rows, Q B^K latents, dO rows, dO B^V latents, then lse and D of
+  // its 32 queries; after them the B-gradient exchange area (32 x R fp32)
   static constexpr int ZB1 = R * 2, CZ1 = ZB1 / 16;         // one head's latents of a token
   static constexpr int LATS1 = kTrTile * ZB1;
   static constexpr int KV_TILE1 = 2 * (ROWS + LATS1) + 2 * kTrTile * 4;
-  static constexpr int LDS_KV = 2 * KV_TILE1 + (R > 0 ? kTrTile * R * 4 : 16);
+  static constexpr int KV_BUFS = 3;
+  static constexpr int LDS_KV = KV_BUFS * KV_TILE1 + (R > 0 ? kTrTile * R * 4 : 16);
   static_assert(DH % 32 == 0 && R <= 32 && R % 8 == 0, "training envelope");
   static_assert(CR >= 4 && (R == 0 || CZ >= 4), "swizzle needs 4 chunks per row");
   static_assert(LDS_KV <= 160 * 1024, "LDS");
@@ -78,7 +81,7 @@ struct TrParams {
   float* dq; float* dz_k; float* dz_v;
   // workspace
   uint16_t* qb; uint16_t* dob;      // [B][L][H][R] bf16: Q B^K_h and dO B^V_h
-  float* lse2; float* dd;           // [B][H][Lp]: lse * log2(e) and rowsum(dO o O); rows >= L hold 0
+  float* lse2; float* dd;           // [B][H][Lp]: lse * log2(e) and rowsum(dO o O); rows >= L: +inf, 0
   float* dks_part; float* dvs_part; // [H][B][L][DH]: per-head dK_h, dV_h
   float* dbk_part; float* dbv_part; // [B][n_kb][H][DH][R], key blocks of kTrKeyBlock tokens
   int batch, heads, seq_len, seq_pad, n_blocks, n_hgroups, n_kb;
@@ -176,7 +179,7 @@ __device__ __forceinline__ bf16x8_t tr_global_chunk(const uint16_t* row, const u
 
 // ---------------------------------------------------------------------------
 // Per (token, head): Q B^K_h and dO B^V_h (bf16), D = rowsum(dO o O) and
-// lse * log2(e) (fp32, [B][H][Lp]; the padding rows get 0).  Workgroup = 128
+// lse * log2(e) (fp32, [B][H][Lp]; the padding rows get D = 0, lse = +inf).  Workgroup = 128
 // tokens (4 blocks of 32) x 4 heads, one head per wave.  The products run on
 // MFMA as C[j][token] = sum_d B_h[d][j] X[token][d]: A = B_h^T (lane = latent
 // column j, read once per wave), B = the tokens' rows straight from global
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(kTrThreads) void train_prep_kernel(TrParams p) {
       if (i == L - 1)
         for (int u = L; u < p.seq_pad; ++u) {
           p.dd[o + (u - i)] = 0.f;
-          p.lse2[o + (u - i)] = 0.f;
+          p.lse2[o + (u - i)] = __builtin_inff();   // probability 0 for every key
         }
     }
     if constexpr (R > 0) {
@@ -424,8 +427,9 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
 // k0 + 32w .. k0 + 32w + 31.  The query blocks from the key block's diagonal
 // to the end stream through LDS as one tile (the head's Q rows and Q B^K
 // latents, dO rows and dO B^V latents, lse and D of the 32 queries) that all
-// four waves read; the next tile's global loads are in flight (in registers)
-// while the current one is computed, then stored to the other LDS buffer.  A
+// four waves read.  Three LDS buffers carry a software pipeline: tile qb's
+// probabilities (vector ALU) overlap tile qb + 1's scores (MFMA), and tile
+// qb + 2's global loads are in flight in registers.  A
 // wave keeps its keys' [dK_h | dZ^K_h] and [dV_h | dZ^V_h] in registers; at
 // the end it writes dZ^K_h, dZ^V_h, the head's dK_h, dV_h as one partial of
 // dK_s, dV_s (summed over the heads afterwards) and its share of dB^K_h,
@@ -435,7 +439,7 @@ template <int DH, int R>
 __global__ __launch_bounds__(kTrThreads) void train_dkv_kernel(TrParams p) {
   using P = TrShape<DH, R>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  float* const bx = reinterpret_cast<float*>(smem + 2 * P::KV_TILE1);   // B-gradient exchange
+  float* const bx = reinterpret_cast<float*>(smem + P::KV_BUFS * P::KV_TILE1);   // B-gradient exchange
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, half = lane >> 5;
@@ -461,37 +465,56 @@ __global__ __launch_bounds__(kTrThreads) void train_dkv_kernel(TrParams p) {
     }
   }
 
-  // query-side tile qb: global loads into registers (rows >= valid are
-  // zero), then stores to LDS buffer `buf`
+  // query-side tile qb: global loads into registers, then stores to LDS
+  // buffer `buf`.  Rows past the sequence repeat its last row: their
+  // probabilities are 0 and every value is finite, so they add nothing.
   constexpr int NRL = kTrTile * P::CR / kTrThreads;         // row chunks per thread and array
   static_assert(NRL >= 1 && (kTrTile * P::CR) % kTrThreads == 0, "row chunks per thread");
   static_assert(kTrTile * P::CZ1 <= kTrThreads, "latent chunks per thread");
   u32x4 pre_q[NRL], pre_d[NRL], pre_zq = {0u, 0u, 0u, 0u}, pre_zd = {0u, 0u, 0u, 0u};
   float pre_l = 0.f;
   const size_t lrow = (size_t(b) * H + h) * p.seq_pad;
-  auto tile_load = [&](int qb) __attribute__((always_inline)) {
-    const int q0 = qb * kTrTile, valid = min(kTrTile, L - q0);
-    const size_t tok = size_t(b) * L + q0;
+  // element offsets of this thread's chunks from a tile's first token
+  uint32_t roff[NRL], zoff1 = 0;
 #pragma unroll
-    for (int i = 0; i < NRL; ++i) {
-      const int idx = tid + i * kTrThreads, t = idx / P::CR, ch = idx % P::CR;
-      pre_q[i] = pre_d[i] = u32x4{0u, 0u, 0u, 0u};
-      if (t < valid) {
-        const size_t off = ((tok + t) * H + h) * DH + ch * 8;
+  for (int i = 0; i < NRL; ++i) {
+    const int idx = tid + i * kTrThreads;
+    roff[i] = uint32_t(((idx / P::CR) * H + h) * DH + (idx % P::CR) * 8);
+  }
+  if constexpr (R > 0) zoff1 = uint32_t(((tid / P::CZ1) * H + h) * R + (tid % P::CZ1) * 8);
+  auto tile_load = [&](int qb) __attribute__((always_inline)) {
+    const int q0 = qb * kTrTile;
+    const size_t tok = size_t(b) * L + q0;
+    if (q0 + kTrTile <= L) {                                 // a whole tile: uniform base + offsets
+#pragma unroll
+      for (int i = 0; i < NRL; ++i) {
+        pre_q[i] = *reinterpret_cast<const u32x4*>(p.q + tok * H * DH + roff[i]);
+        pre_d[i] = *reinterpret_cast<const u32x4*>(p.d_out + tok * H * DH + roff[i]);
+      }
+      if constexpr (R > 0) {
+        if (tid < kTrTile * P::CZ1) {
+          pre_zq = *reinterpret_cast<const u32x4*>(p.qb + tok * H * R + zoff1);
+          pre_zd = *reinterpret_cast<const u32x4*>(p.dob + tok * H * R + zoff1);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NRL; ++i) {
+        const int idx = tid + i * kTrThreads, t = idx / P::CR, ch = idx % P::CR;
+        const size_t off = ((size_t(b) * L + min(q0 + t, L - 1)) * H + h) * DH + ch * 8;
         pre_q[i] = *reinterpret_cast<const u32x4*>(p.q + off);
         pre_d[i] = *reinterpret_cast<const u32x4*>(p.d_out + off);
       }
-    }
-    if constexpr (R > 0) {
-      const int t = tid / P::CZ1, ch = tid % P::CZ1;
-      pre_zq = pre_zd = u32x4{0u, 0u, 0u, 0u};
-      if (tid < kTrTile * P::CZ1 && t < valid) {
-        const size_t off = ((tok + t) * H + h) * R + ch * 8;
-        pre_zq = *reinterpret_cast<const u32x4*>(p.qb + off);
-        pre_zd = *reinterpret_cast<const u32x4*>(p.dob + off);
+      if constexpr (R > 0) {
+        if (tid < kTrTile * P::CZ1) {
+          const int t = tid / P::CZ1, ch = tid % P::CZ1;
+          const size_t off = ((size_t(b) * L + min(q0 + t, L - 1)) * H + h) * R + ch * 8;
+          pre_zq = *reinterpret_cast<const u32x4*>(p.qb + off);
+          pre_zd = *reinterpret_cast<const u32x4*>(p.dob + off);
+        }
       }
     }
-    // lse and D of the 32 queries (padding rows hold 0)
+    // lse and D of the 32 queries (padding rows: +inf and 0)
     if (tid < 2 * kTrTile) pre_l = (tid < kTrTile ? p.lse2 : p.dd)[lrow + q0 + (tid & (kTrTile - 1))];
   };
   auto tile_store = [&](int buf) __attribute__((always_inline)) {
@@ -516,45 +539,91 @@ __global__ __launch_bounds__(kTrThreads) void train_dkv_kernel(TrParams p) {
     }
     if (tid < 2 * kTrTile) reinterpret_cast<float*>(dlats + P::LATS1)[tid] = pre_l;
   };
-
-  f32x16_t dk[P::VBLK], dv[P::VBLK];
-#pragma unroll
-  for (int f = 0; f < P::VBLK; ++f) dk[f] = dv[f] = f32x16_t{};
-  tile_load(qb_first);
-  tile_store(0);
-  __syncthreads();
-  int buf = 0;
-  for (int qb = qb_first; qb < nqb; ++qb) {
-    if (qb + 1 < nqb) tile_load(qb + 1);
+  // S = Qaug Kaug^T and dP = dOaug Vaug^T of the tile in buffer `buf`: lane
+  // (key n, half) holds queries 8(i/4) + 4half + i%4
+  auto scores = [&](int buf, f32x16_t& s, f32x16_t& dp) __attribute__((always_inline)) {
     const unsigned char* const qrows = smem + buf * P::KV_TILE1;
     const unsigned char* const qlats = qrows + P::ROWS;
     const unsigned char* const drows = qlats + P::LATS1;
     const unsigned char* const dlats = drows + P::ROWS;
-    const float* const lsd = reinterpret_cast<const float*>(dlats + P::LATS1);   // lse2[32], then D[32]
-    const int q0 = qb * kTrTile;
-    // S = Qaug Kaug^T and dP = dOaug Vaug^T: lane (key n, half) holds
-    // queries 8(i/4) + 4half + i%4
-    f32x16_t s = {}, dp = {};
+    s = f32x16_t{};
+    dp = f32x16_t{};
 #pragma unroll
     for (int c = 0; c < P::KCH; ++c) {
       s = mfma32(tr_row_chunk(qrows, qlats, o, c, half), kop[c], s);
       dp = mfma32(tr_row_chunk(drows, dlats, o, c, half), vop[c], dp);
     }
-    bf16x8_t pp[2], ps[2];
+  };
+
+  // Software pipeline over the query tiles, three LDS buffers: while tile
+  // qb's probabilities are formed (vector ALU), the scores of tile qb + 1 run
+  // on MFMA; tile qb + 2 is in flight from global memory.
+  f32x16_t dk[P::VBLK], dv[P::VBLK];
+#pragma unroll
+  for (int f = 0; f < P::VBLK; ++f) dk[f] = dv[f] = f32x16_t{};
+  tile_load(qb_first);
+  tile_store(0);
+  tile_load(min(qb_first + 1, nqb - 1));
+  tile_store(1);
+  __syncthreads();
+  f32x16_t s, dp;
+  scores(0, s, dp);
+  // causal mask: query q0 + 8j + 4half + e sees key k0 + n iff
+  // (q0 - k0 + 4half - n) + 8j + e >= 0; queries past the sequence have
+  // lse = +inf (probability 0), keys past it are later than every query
+  const int mask_base = 4 * half - n - k0;
+  int cur = 0;
+  for (int qb = qb_first; qb < nqb; ++qb) {
+    const int nxt = cur == 2 ? 0 : cur + 1, nn = nxt == 2 ? 0 : nxt + 1;
+    if (qb + 2 < nqb) tile_load(qb + 2);
+    const unsigned char* const qrows = smem + cur * P::KV_TILE1;
+    const unsigned char* const qlats = qrows + P::ROWS;
+    const unsigned char* const drows = qlats + P::LATS1;
+    const unsigned char* const dlats = drows + P::ROWS;
+    const float* const lsd = reinterpret_cast<const float*>(dlats + P::LATS1);   // lse2[32], then D[32]
+    const int mb = qb * kTrTile + mask_base;
+    // P and dS of tile qb (bf16), formed between the MFMAs of tile qb + 1's
+    // scores (past the end: a stale buffer, not used): chunk c's two MFMAs,
+    // then elements [16c / KCH, 16(c + 1) / KCH) of the probabilities; the
+    // next chunk's operands are read from LDS one step ahead.  Scheduling
+    // barriers keep the groups in this order.
+    float4 l4[4], d4[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float4 l4 = *reinterpret_cast<const float4*>(lsd + 8 * j + 4 * half);
-      const float4 d4 = *reinterpret_cast<const float4*>(lsd + kTrTile + 8 * j + 4 * half);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      l4[j] = *reinterpret_cast<const float4*>(lsd + 8 * j + 4 * half);
+      d4[j] = *reinterpret_cast<const float4*>(lsd + kTrTile + 8 * j + 4 * half);
+    }
+    const unsigned char* const nq = smem + nxt * P::KV_TILE1;
+    const unsigned char* const nql = nq + P::ROWS;
+    const unsigned char* const nd = nql + P::LATS1;
+    const unsigned char* const ndl = nd + P::ROWS;
+    bf16x8_t pp[2], ps[2];
+    f32x16_t s2 = {}, dp2 = {};
+    bf16x8_t aq = tr_row_chunk(nq, nql, o, 0, half), ad = tr_row_chunk(nd, ndl, o, 0, half);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * j + e;
-        const int qi = q0 + 8 * j + 4 * half + e;
-        const bool ok = k0 + n <= qi && qi < L && k0 + n < L;
-        const float pv = ok ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -lv[e])) : 0.f;
-        pp[i >> 3][i & 7] = (__bf16)pv;
-        ps[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dv4[e]));
+    for (int c = 0; c < P::KCH; ++c) {
+      bf16x8_t aq1 = aq, ad1 = ad;
+      if (c + 1 < P::KCH) {
+        aq1 = tr_row_chunk(nq, nql, o, c + 1, half);
+        ad1 = tr_row_chunk(nd, ndl, o, c + 1, half);
       }
+      s2 = mfma32(aq, kop[c], s2);
+      dp2 = mfma32(ad, vop[c], dp2);
+#pragma unroll
+      for (int i = 16 * c / P::KCH; i < 16 * (c + 1) / P::KCH; ++i) {
+        const int j = i >> 2, e = i & 3;
+        const float lv = e == 0 ? l4[j].x : e == 1 ? l4[j].y : e == 2 ? l4[j].z : l4[j].w;
+        const float dd = e == 0 ? d4[j].x : e == 1 ? d4[j].y : e == 2 ? d4[j].z : d4[j].w;
+        const float ev = fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -lv));
+        float pv = mb + 8 * j + e >= 0 ? ev : 0.f;
+        float sv = pv * (dp[i] - dd);
+        asm volatile("" : "+v"(pv), "+v"(sv));
+        pp[i >> 3][i & 7] = (__bf16)pv;
+        ps[i >> 3][i & 7] = (__bf16)sv;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      aq = aq1;
+      ad = ad1;
     }
     // [dV_h | dZ^V_h] += P^T dOaug, [dK_h | dZ^K_h] / scale += dS^T Qaug
 #pragma unroll
@@ -564,10 +633,12 @@ __global__ __launch_bounds__(kTrThreads) void train_dkv_kernel(TrParams p) {
         dv[f] = mfma32(pp[c], tr_col_chunk(drows, dlats, o, f, c), dv[f]);
         dk[f] = mfma32(ps[c], tr_col_chunk(qrows, qlats, o, f, c), dk[f]);
       }
-    // the other buffer was last read before the previous barrier
-    if (qb + 1 < nqb) tile_store(buf ^ 1);
+    // buffer nn held tile qb - 1, read before the previous barrier
+    if (qb + 2 < nqb) tile_store(nn);
     __syncthreads();
-    buf ^= 1;
+    s = s2;
+    dp = dp2;
+    cur = nxt;
   }
 #pragma unroll
   for (int f = 0; f < P::VBLK; ++f) dk[f] *= p.scale;
