@@ -22,7 +22,7 @@
 // Kernels (one backward call):
 //   train_prep_kernel   Q B^K_h and dO B^V_h (bf16), D and log2-scaled lse;
 //   train_dq_kernel     per (query block, 4 heads): keys streamed through
-//                       LDS (double buffered), S^T and dP^T on MFMA
+//                       LDS (software pipelined), S^T and dP^T on MFMA
 //                       (lane = query), dQ^T
 //                       accumulated as Kaug^T dS^T, B^K epilogue;
 //   train_dkv_kernel    per (128 keys, head): the head's queries and dO
@@ -57,7 +57,7 @@ struct TrShape {
   static constexpr int ROWS = kTrTile * RB;                 // a 32-row tile of d_h rows
   static constexpr int LATS = kTrTile * ZB;                 // a 32-token tile of latents
   static constexpr int LDS_DQ1 = 2 * (ROWS + LATS);        // dQ kernel: a key and a value tile
-  static constexpr int LDS_DQ = 2 * LDS_DQ1;                // double buffered
+  static constexpr int LDS_DQ = 3 * LDS_DQ1;                // a three-stage pipeline
   // dK/dV kernel: three query-side tiles of one head (a software pipeline),
   // each Q rows, Q B^K latents, dO rows, dO B^V latents, then lse and D of
   // its 32 queries; after them the B-gradient exchange area (32 x R fp32)
@@ -262,8 +262,9 @@ __global__ __launch_bounds__(kTrThreads) void train_prep_kernel(TrParams p) {
 // ---------------------------------------------------------------------------
 // dQ: workgroup = (query block, 4 heads, sequence), one head per wave.  The
 // key tiles from 0 to the diagonal (K_s and V_s rows, the 4 heads' Z^K and
-// Z^V latents) stream through two LDS buffers: the next tile's global loads
-// are in flight (in registers) while the current one is computed.
+// Z^V latents) stream through three LDS buffers: tile kt's dS (vector ALU)
+// overlaps tile kt + 1's scores (MFMA), tile kt + 2's global loads are in
+// flight in registers.
 // ---------------------------------------------------------------------------
 template <int DH, int R>
 __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
@@ -296,34 +297,55 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
   const size_t lrow = (size_t(b) * H + h) * p.seq_pad + qrow;
   const float lse2 = p.lse2[lrow], dd = p.dd[lrow];
 
-  // key tile kt: global loads into registers (rows >= valid are zero), then
-  // stores to LDS buffer `buf`
+  // key tile kt: global loads into registers, then stores to LDS buffer
+  // `buf`.  Rows past the sequence repeat its last row (finite values; those
+  // keys are later than every query, so the causal mask removes them).
   constexpr int NRL = kTrTile * P::CR / kTrThreads;         // row chunks per thread and array
   constexpr int NZL = R > 0 ? (kTrTile * P::CZ + kTrThreads - 1) / kTrThreads : 1;   // latent chunks per thread
   static_assert(NRL >= 1 && (kTrTile * P::CR) % kTrThreads == 0, "row chunks per thread");
   u32x4 pre_k[NRL], pre_v[NRL], pre_zk[NZL], pre_zv[NZL];
-  auto tile_load = [&](int kt) __attribute__((always_inline)) {
-    const int t0 = kt * kTrTile, valid = min(kTrTile, L - t0);
-    const size_t tok = size_t(b) * L + t0;
+  // element offsets of this thread's latent chunks from a tile's first token
+  uint32_t zoffs[NZL];
 #pragma unroll
-    for (int i = 0; i < NRL; ++i) {
-      const int idx = tid + i * kTrThreads, t = idx / P::CR, ch = idx % P::CR;
-      pre_k[i] = pre_v[i] = u32x4{0u, 0u, 0u, 0u};
-      if (t < valid) {
-        const size_t off = (tok + t) * DH + ch * 8;
+  for (int i = 0; i < NZL; ++i) {
+    const int idx = tid + i * kTrThreads;
+    zoffs[i] = R > 0 ? uint32_t(((idx / P::CZ) * H + hg * kTrWaves) * R + (idx % P::CZ) * 8) : 0u;
+  }
+  auto tile_load = [&](int kt) __attribute__((always_inline)) {
+    const int t0 = kt * kTrTile;
+    const size_t tok = size_t(b) * L + t0;
+    if (t0 + kTrTile <= L) {                                 // a whole tile: uniform base + offsets
+#pragma unroll
+      for (int i = 0; i < NRL; ++i) {
+        const uint32_t off = uint32_t(tid + i * kTrThreads) * 8;
+        pre_k[i] = *reinterpret_cast<const u32x4*>(p.k_s + tok * DH + off);
+        pre_v[i] = *reinterpret_cast<const u32x4*>(p.v_s + tok * DH + off);
+      }
+      if constexpr (R > 0) {
+#pragma unroll
+        for (int i = 0; i < NZL; ++i)
+          if (tid + i * kTrThreads < kTrTile * P::CZ) {
+            pre_zk[i] = *reinterpret_cast<const u32x4*>(p.z_k + tok * H * R + zoffs[i]);
+            pre_zv[i] = *reinterpret_cast<const u32x4*>(p.z_v + tok * H * R + zoffs[i]);
+          }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NRL; ++i) {
+        const int idx = tid + i * kTrThreads, t = idx / P::CR, ch = idx % P::CR;
+        const size_t off = (size_t(b) * L + min(t0 + t, L - 1)) * DH + ch * 8;
         pre_k[i] = *reinterpret_cast<const u32x4*>(p.k_s + off);
         pre_v[i] = *reinterpret_cast<const u32x4*>(p.v_s + off);
       }
-    }
-    if constexpr (R > 0) {
+      if constexpr (R > 0) {
 #pragma unroll
-      for (int i = 0; i < NZL; ++i) {
-        const int idx = tid + i * kTrThreads, t = idx / P::CZ, ch = idx % P::CZ;
-        pre_zk[i] = pre_zv[i] = u32x4{0u, 0u, 0u, 0u};
-        if (idx < kTrTile * P::CZ && t < valid) {
-          const size_t off = ((tok + t) * H + hg * kTrWaves) * R + ch * 8;
-          pre_zk[i] = *reinterpret_cast<const u32x4*>(p.z_k + off);
-          pre_zv[i] = *reinterpret_cast<const u32x4*>(p.z_v + off);
+        for (int i = 0; i < NZL; ++i) {
+          const int idx = tid + i * kTrThreads, t = idx / P::CZ, ch = idx % P::CZ;
+          if (idx < kTrTile * P::CZ) {
+            const size_t off = ((size_t(b) * L + min(t0 + t, L - 1)) * H + hg * kTrWaves) * R + ch * 8;
+            pre_zk[i] = *reinterpret_cast<const u32x4*>(p.z_k + off);
+            pre_zv[i] = *reinterpret_cast<const u32x4*>(p.z_v + off);
+          }
         }
       }
     }
@@ -353,45 +375,82 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
     }
   };
 
+  // Software pipeline over the key tiles, three LDS buffers: while tile
+  // kt's dS is formed (vector ALU), the scores of tile kt + 1 run on MFMA;
+  // tile kt + 2 is in flight from global memory.
+  auto rows_of = [&](int buf) __attribute__((always_inline)) { return smem + buf * P::LDS_DQ1; };
   f32x16_t acc[P::VBLK];
 #pragma unroll
   for (int f = 0; f < P::VBLK; ++f) acc[f] = f32x16_t{};
   tile_load(0);
   tile_store(0);
+  tile_load(min(1, kt_last));
+  tile_store(1);
   __syncthreads();
-  int buf = 0;
-  for (int kt = 0; kt <= kt_last; ++kt) {
-    if (kt < kt_last) tile_load(kt + 1);
-    const unsigned char* const krows = smem + buf * P::LDS_DQ1;
-    const unsigned char* const klats = krows + P::ROWS;
-    const unsigned char* const vrows = klats + P::LATS;
-    const unsigned char* const vlats = vrows + P::ROWS;
-    const int t0 = kt * kTrTile;
-    // S^T = Kaug Qaug^T and dP^T = Vaug dOaug^T: lane (query n, half) holds
-    // keys 8(i/4) + 4half + i%4
-    f32x16_t s = {}, dp = {};
+  // S^T = Kaug Qaug^T and dP^T = Vaug dOaug^T: lane (query n, half) holds
+  // keys 8(i/4) + 4half + i%4
+  f32x16_t s = {}, dp = {};
+  {
+    const unsigned char* const kr = rows_of(0);
 #pragma unroll
     for (int c = 0; c < P::KCH; ++c) {
-      s = mfma32(tr_row_chunk(krows, klats, o, c, half), qop[c], s);
-      dp = mfma32(tr_row_chunk(vrows, vlats, o, c, half), dop[c], dp);
+      s = mfma32(tr_row_chunk(kr, kr + P::ROWS, o, c, half), qop[c], s);
+      dp = mfma32(tr_row_chunk(kr + P::ROWS + P::LATS, kr + 2 * P::ROWS + P::LATS, o, c, half), dop[c], dp);
     }
+  }
+  // causal mask: key t0 + 8j + 4half + e is seen by query q0 + n iff
+  // (q0 + n - 4half - t0) - (8j + e) >= 0 (keys past the sequence are later
+  // than every query)
+  const int mask_base = q0 + n - 4 * half;
+  int cur = 0;
+  for (int kt = 0; kt <= kt_last; ++kt) {
+    const int nxt = cur == 2 ? 0 : cur + 1, nn = nxt == 2 ? 0 : nxt + 1;
+    if (kt + 2 <= kt_last) tile_load(kt + 2);
+    const unsigned char* const krows = rows_of(cur);
+    const unsigned char* const klats = krows + P::ROWS;
+    const int mb = mask_base - kt * kTrTile;
+    // dS of tile kt (bf16), formed between the MFMAs of tile kt + 1's scores
+    // (past the end: a stale buffer, not used): chunk c's two MFMAs, then
+    // elements [16c / KCH, 16(c + 1) / KCH); the next chunk's operands are
+    // read one step ahead.  Scheduling barriers keep the groups in order.
+    const unsigned char* const nk = rows_of(nxt);
+    const unsigned char* const nkl = nk + P::ROWS;
+    const unsigned char* const nv = nkl + P::LATS;
+    const unsigned char* const nvl = nv + P::ROWS;
     bf16x8_t pb[2];
+    f32x16_t s2 = {}, dp2 = {};
+    bf16x8_t ak = tr_row_chunk(nk, nkl, o, 0, half), av = tr_row_chunk(nv, nvl, o, 0, half);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = t0 + 8 * (i >> 2) + 4 * half + (i & 3);
-      const bool ok = key <= q0 + n && key < L;
-      const float pv = ok ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -lse2)) : 0.f;
-      pb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dd));
+    for (int c = 0; c < P::KCH; ++c) {
+      bf16x8_t ak1 = ak, av1 = av;
+      if (c + 1 < P::KCH) {
+        ak1 = tr_row_chunk(nk, nkl, o, c + 1, half);
+        av1 = tr_row_chunk(nv, nvl, o, c + 1, half);
+      }
+      s2 = mfma32(ak, qop[c], s2);
+      dp2 = mfma32(av, dop[c], dp2);
+#pragma unroll
+      for (int i = 16 * c / P::KCH; i < 16 * (c + 1) / P::KCH; ++i) {
+        const float ev = fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -lse2));
+        float sv = mb >= 8 * (i >> 2) + (i & 3) ? ev * (dp[i] - dd) : 0.f;
+        asm volatile("" : "+v"(sv));
+        pb[i >> 3][i & 7] = (__bf16)sv;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      ak = ak1;
+      av = av1;
     }
     // dQaug^T += Kaug^T dS^T
 #pragma unroll
     for (int f = 0; f < P::VBLK; ++f)
 #pragma unroll
       for (int c = 0; c < 2; ++c) acc[f] = mfma32(tr_col_chunk(krows, klats, o, f, c), pb[c], acc[f]);
-    // the other buffer was last read before the previous barrier
-    if (kt < kt_last) tile_store(buf ^ 1);
+    // buffer nn held tile kt - 1, read before the previous barrier
+    if (kt + 2 <= kt_last) tile_store(nn);
     __syncthreads();
-    buf ^= 1;
+    s = s2;
+    dp = dp2;
+    cur = nxt;
   }
   // dQ^T = scale (dQ_s^T + B^K_h dQ_z^T)
   if constexpr (R > 0) {
