@@ -440,11 +440,24 @@ __global__ __launch_bounds__(kTrThreads) void train_dq_kernel(TrParams p) {
       ak = ak1;
       av = av1;
     }
-    // dQaug^T += Kaug^T dS^T
+    // dQaug^T += Kaug^T dS^T, block f's MFMAs with block f + 1's operands
+    // read one step ahead
+    bf16x8_t ok[2];
 #pragma unroll
-    for (int f = 0; f < P::VBLK; ++f)
+    for (int c = 0; c < 2; ++c) ok[c] = tr_col_chunk(krows, klats, o, 0, c);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) acc[f] = mfma32(tr_col_chunk(krows, klats, o, f, c), pb[c], acc[f]);
+    for (int f = 0; f < P::VBLK; ++f) {
+      bf16x8_t ok1[2] = {ok[0], ok[1]};
+      if (f + 1 < P::VBLK) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) ok1[c] = tr_col_chunk(krows, klats, o, f + 1, c);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[f] = mfma32(ok[c], pb[c], acc[f]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) ok[c] = ok1[c];
+    }
     // buffer nn held tile kt - 1, read before the previous barrier
     if (kt + 2 <= kt_last) tile_store(nn);
     __syncthreads();
@@ -684,14 +697,36 @@ __global__ __launch_bounds__(kTrThreads) void train_dkv_kernel(TrParams p) {
       aq = aq1;
       ad = ad1;
     }
-    // [dV_h | dZ^V_h] += P^T dOaug, [dK_h | dZ^K_h] / scale += dS^T Qaug
+    // [dV_h | dZ^V_h] += P^T dOaug, [dK_h | dZ^K_h] / scale += dS^T Qaug,
+    // block f's four MFMAs with block f + 1's operands read one step ahead
+    bf16x8_t od[2], oq[2];
 #pragma unroll
-    for (int f = 0; f < P::VBLK; ++f)
+    for (int c = 0; c < 2; ++c) {
+      od[c] = tr_col_chunk(drows, dlats, o, 0, c);
+      oq[c] = tr_col_chunk(qrows, qlats, o, 0, c);
+    }
+#pragma unroll
+    for (int f = 0; f < P::VBLK; ++f) {
+      bf16x8_t od1[2] = {od[0], od[1]}, oq1[2] = {oq[0], oq[1]};
+      if (f + 1 < P::VBLK) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          od1[c] = tr_col_chunk(drows, dlats, o, f + 1, c);
+          oq1[c] = tr_col_chunk(qrows, qlats, o, f + 1, c);
+        }
+      }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        dv[f] = mfma32(pp[c], tr_col_chunk(drows, dlats, o, f, c), dv[f]);
-        dk[f] = mfma32(ps[c], tr_col_chunk(qrows, qlats, o, f, c), dk[f]);
+        dv[f] = mfma32(pp[c], od[c], dv[f]);
+        dk[f] = mfma32(ps[c], oq[c], dk[f]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        od[c] = od1[c];
+        oq[c] = oq1[c];
+      }
+    }
     // buffer nn held tile qb - 1, read before the previous barrier
     if (qb + 2 < nqb) tile_store(nn);
     __syncthreads();
