@@ -59,8 +59,9 @@ def parse():
                          "one training step (forward with log-sum-exp, backward) of the prefill workload")
     ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
-    ap.add_argument("--engine", type=int, default=0, choices=(0, 1, 2),
-                    help="decode scan: 0 the default for the shape, 1 the vector-ALU scan, 2 the MFMA scan")
+    ap.add_argument("--engine", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="decode scan: 0 the default for the shape, 1 the vector-ALU scan, 2 the MFMA scan, "
+                         "3 the any-rank scan")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trials", type=int, default=5, help="timed trials per figure (the median is reported)")
@@ -78,6 +79,9 @@ KERNEL_SOURCES = {
     "decode_split_kernel": ("decode.hip", "lrkv_device.h"),
     "prefill_kernel": ("prefill.hip", "lrkv_device.h"),
     "project_gemm_kernel": ("project.hip", "lrkv_device.h"),
+    "decode_generic_kernel": ("decode_generic.hip", "lrkv_device.h"),
+    "train_dkv_kernel": ("train.hip", "lrkv_device.h"),
+    "train_dq_kernel": ("train.hip", "lrkv_device.h"),
 }
 
 
@@ -301,9 +305,11 @@ def measure_decode(args, wl, d, rotate_mb: float = 0.0, engine: int = 0):
     scan_bytes = cache_bytes + B * H * d_h * es + H * d_h * r * es          # cache + q + B^K
     step_bytes = cache_bytes + 2 * B * H * d_h * es + 2 * H * d_h * r * es  # + out + B^V
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
-    scan_kernel = {1: "decode_split_kernel", 2: "decode_mfma_kernel"}.get(engine) or \
+    scan_kernel = {1: "decode_split_kernel", 2: "decode_mfma_kernel", 3: "decode_generic_kernel"}.get(engine) or \
         L.lrkv_decode_scan_kernel(dt, H, d_h, r)
-    traffic = traffic_from_profiles("decode_scan_counters", scan_kernel, wl.name, args.split_tokens)
+    traffic = None
+    for rec_name in ("decode_scan_counters", "decode_valu_scan_counters"):
+        traffic = traffic or traffic_from_profiles(rec_name, scan_kernel, wl.name, args.split_tokens)
     return {
         "tokens": tokens, "tokens_per_s": tokens / (step_ms * 1e-3), "step_ms": step_ms,
         "step_ms_trials": step_runs, "wall_s_timed": wall, "settled": settled,
@@ -620,6 +626,7 @@ def bench_train(args):
         "data": "synthetic (seeded N(0,1) queries, bases, latents and upstream gradient; B ~ N(0, 1/r))",
         **r,
     }
+    copy_reference(args, rec)
     print(json.dumps(rec), flush=True)
 
 

@@ -29,15 +29,23 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def counter_means(path, counter):
-    """Mean value of `counter` per dispatch, keyed by kernel name (without arguments)."""
-    acc = {}
+    """Mean value of `counter` per dispatch, keyed by kernel name (without
+    arguments).  For the copy kernel only the dispatches of the largest grid
+    count: those are the reference copies; the program's own small copies
+    (uploads, staging) would dilute the calibration."""
+    rows = []
     with open(path) as f:
         for row in csv.DictReader(f):
-            if row["Counter_Name"] != counter:
-                continue
-            name = row["Kernel_Name"].split("(")[0].replace("void ", "").replace("lrkv::", "")
-            tot, n = acc.get(name, (0.0, 0))
-            acc[name] = (tot + float(row["Counter_Value"]), n + 1)
+            if row["Counter_Name"] == counter:
+                rows.append(row)
+    copy_grid = max((int(r["Grid_Size"]) for r in rows if COPY_KERNEL in r["Kernel_Name"]), default=None)
+    acc = {}
+    for row in rows:
+        if COPY_KERNEL in row["Kernel_Name"] and int(row["Grid_Size"]) != copy_grid:
+            continue
+        name = row["Kernel_Name"].split("(")[0].replace("void ", "").replace("lrkv::", "")
+        tot, n = acc.get(name, (0.0, 0))
+        acc[name] = (tot + float(row["Counter_Value"]), n + 1)
     return {k: t / n for k, (t, n) in acc.items()}
 
 
