@@ -820,12 +820,22 @@ __global__ __launch_bounds__(kTrThreads) void train_dkv_kernel(TrParams p) {
 // Sums of the partials, each output element added in a fixed order:
 // dK_s, dV_s over the heads; dB^K, dB^V over (sequence, key block).
 // ---------------------------------------------------------------------------
+// Eight running sums (partial k goes to sum k % 8), added pairwise at the
+// end: a fixed order, with eight loads in flight per thread.
 __global__ __launch_bounds__(256) void train_reduce_kernel(const float* part, float* out, long long n, int parts) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   if (e >= n) return;
-  float s = 0.f;
-  for (int k = 0; k < parts; ++k) s += part[(long long)k * n + e];
-  out[e] = s;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 8 <= parts; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = part[(long long)(k + j) * n + e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] += v[j];
+  }
+  for (; k < parts; ++k) s[k & 7] += part[(long long)k * n + e];
+  out[e] = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 }
 
 size_t train_backward_ws_bytes(int batch, int heads, int head_dim, int rank, int seq_len) {
