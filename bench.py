@@ -308,7 +308,7 @@ def measure_decode(args, wl, d, rotate_mb: float = 0.0, engine: int = 0):
     scan_kernel = {1: "decode_split_kernel", 2: "decode_mfma_kernel", 3: "decode_generic_kernel"}.get(engine) or \
         L.lrkv_decode_scan_kernel(dt, H, d_h, r)
     traffic = None
-    for rec_name in ("decode_scan_counters", "decode_valu_scan_counters"):
+    for rec_name in ("decode_scan_counters", "decode_valu_scan_counters", "decode_ragged_counters"):
         traffic = traffic or traffic_from_profiles(rec_name, scan_kernel, wl.name, args.split_tokens)
     return {
         "tokens": tokens, "tokens_per_s": tokens / (step_ms * 1e-3), "step_ms": step_ms,
