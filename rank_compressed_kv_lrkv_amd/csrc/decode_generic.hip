@@ -12,16 +12,22 @@
 // trade-off" (Table 8), where a token's latent run of H*r elements need not
 // fill whole 16-byte chunks.
 //
-// Work decomposition: a workgroup is 256 lanes = 32 heads x 8 lanes (grid.z
-// runs further groups of 32 heads), over one split of one sequence.  The
-// shared rows of 64 tokens are staged in LDS and read by every head; lane g
-// of a head owns shared dims [g d_h/8, (g+1) d_h/8) and latent dims j = g +
-// 8i.  Per token the head's 8 lanes add their partial logits through DPP,
-// run the online softmax (all 8 hold the same m and l) and fold the token
-// into their dims.  Latents are read element by element: the 64 lanes of a
-// wave cover 8 heads x 8 consecutive elements, so each load instruction
-// reads 8 runs of 8 contiguous elements.  The next token's latents are in
-// flight while a token is computed.
+// Work decomposition: a workgroup is 256 lanes = (256 / G) heads x G lanes
+// (G = 8, 16 or 32 lanes per head, more lanes per head when there are few
+// heads; grid.z runs further head groups), over one split of one sequence.
+// The split's tokens go through LDS in tiles of T tokens (T chosen on the
+// host so that a tile fits 64 KB): the shared rows, and for every token the
+// contiguous run of the group's latents, [h0 r, (h0 + heads) r) of its H r
+// elements, copied with 16-byte loads from the 16-byte boundary at or below
+// its start (the run's offset inside the copy is kept per token).  So every
+// global load is a whole 16-byte chunk whatever the rank, except the one
+// chunk that crosses the split's last byte, read in 2-byte pieces that each
+// lie inside the split.  Lane g of a head owns shared dims
+// [g d_h/G, (g+1) d_h/G) and latent dims j = g + G i.  Per token the head's
+// G lanes add their partial logits through DPP, run the online softmax (all
+// G hold the same m and l) and fold the token into their dims; two tokens
+// are interleaved.  Two or more workgroups are resident per compute unit,
+// so one's tile copy overlaps another's arithmetic.
 //
 // Numerics: fp32 throughout (the absorbed query B^K_h^T q_h is kept in fp32;
 // bf16 elements are widened exactly).
@@ -33,27 +39,18 @@ namespace lrkv {
 namespace {
 
 constexpr int kGnThreads = 256;
-constexpr int kGnG = 8;                          // lanes per head
-constexpr int kGnHeads = kGnThreads / kGnG;      // heads per workgroup
-constexpr int kGnTile = 64;                      // tokens staged per tile
-constexpr int kGnRPL = kGenericMaxRank / kGnG;   // latent dims per lane, at most
+constexpr int kGnTileMax = 64;                   // tokens per tile, at most
+constexpr int kGnLdsBudget = 64 * 1024;          // bytes of LDS per workgroup, at most
 
 struct GnParams {
   const void* k_s; const void* v_s; const void* z_k; const void* z_v;
   const int32_t* seq_lens; const void* q; const void* b_k;
   float scale_log2;
   int heads, rank, max_len, split_tokens, partials;
+  int tile, zrow;                                // tokens per tile; LDS bytes per token's latent copy
   int64_t capacity;
   float* ws_ml; float* ws_acc;
 };
-
-template <class E>
-__device__ __forceinline__ float gn_load(__amdgpu_buffer_rsrc_t res, uint32_t byte_off) {
-  if constexpr (E::kBytes == 2)
-    return bf16_to_f32(uint16_t(__builtin_amdgcn_raw_buffer_load_b16(res, int(byte_off), 0, kStream)));
-  else
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(res, int(byte_off), 0, kStream));
-}
 
 template <class E>
 __device__ __forceinline__ float gn_elem(const void* base, size_t i) {
@@ -61,19 +58,48 @@ __device__ __forceinline__ float gn_elem(const void* base, size_t i) {
   else return static_cast<const float*>(base)[i];
 }
 
+template <class E>
+__device__ __forceinline__ float gn_lds(const unsigned char* p) {
+  if constexpr (E::kBytes == 2) return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+  else return *reinterpret_cast<const float*>(p);
+}
+
+// Sum over aligned groups of G lanes (G up to 32): DPP within 8 lanes, row
+// mirror for 16, a bit-mode swizzle (xor 16) for 32.
+template <int G>
+__device__ __forceinline__ float gn_group_sum(float v) {
+  v = group_sum<(G < 8 ? G : 8)>(v);
+  if constexpr (G >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  if constexpr (G >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  return v;
+}
+
 }  // namespace
 
-template <class E, int DH>
+// Lanes per head of the any-rank scan.
+int generic_lanes_per_head(int heads, int head_dim) {
+  const int g = heads > 16 ? 8 : heads > 8 ? 16 : 32;
+  return g > head_dim ? head_dim : g;
+}
+
+template <class E, int DH, int G>
 __global__ __launch_bounds__(kGnThreads) void decode_generic_kernel(GnParams p) {
-  constexpr int G = kGnG, DPL = DH / G;
+  constexpr int DPL = DH / G, HW = kGnThreads / G;
   constexpr int ES = E::kBytes, ROW = DH * ES, ROW_CH = ROW / 16;
   static_assert(DH % G == 0 && ROW % 16 == 0, "shared rows");
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[kGnTile * ROW];
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[kGnTile * ROW];
-  const int tid = threadIdx.x, g = tid % G;
+  constexpr int RPL = (kGenericMaxRank + G - 1) / G;      // latent dims per lane, at most
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int T = p.tile, ZR = p.zrow;
+  unsigned char* const s_k = smem;
+  unsigned char* const s_v = s_k + T * ROW;
+  unsigned char* const s_zk = s_v + T * ROW;
+  unsigned char* const s_zv = s_zk + size_t(T) * ZR;
+  int* const s_off = reinterpret_cast<int*>(s_zv + size_t(T) * ZR);   // run offset inside each token's copy
+  const int tid = threadIdx.x, g = tid % G, hl = tid / G;
   const int split = blockIdx.x, b = blockIdx.y;
   const int H = p.heads, R = p.rank;
-  const int h = blockIdx.z * kGnHeads + tid / G;
+  const int h0 = blockIdx.z * HW;
+  const int h = h0 + hl;
   const bool active = h < H;
   const int hh = active ? h : H - 1;
 
@@ -90,123 +116,146 @@ __global__ __launch_bounds__(kGnThreads) void decode_generic_kernel(GnParams p) 
   float q[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) q[i] = gn_elem<E>(p.q, qbase + g * DPL + i);
-  float qt[kGnRPL];
+  float qt[RPL];
 #pragma unroll
-  for (int i = 0; i < kGnRPL; ++i) qt[i] = 0.f;
+  for (int i = 0; i < RPL; ++i) qt[i] = 0.f;
   if (R > 0) {
     const size_t bk0 = size_t(hh) * DH * R;
     for (int d = 0; d < DH; ++d) {
       const float qd = gn_elem<E>(p.q, qbase + d);
 #pragma unroll
-      for (int i = 0; i < kGnRPL; ++i)
+      for (int i = 0; i < RPL; ++i)
         if (i < nz) qt[i] = __builtin_fmaf(qd, gn_elem<E>(p.b_k, bk0 + size_t(d) * R + g + G * i), qt[i]);
     }
   }
 
   // ---- resources over the split's tokens ----
   const size_t row0 = size_t(b) * p.capacity + size_t(t0);
-  const uint32_t ztok = uint32_t(H) * uint32_t(R) * ES;     // latent bytes per token
+  const int nh = min(HW, H - h0);                           // heads of this group
+  const uint32_t ztok = uint32_t(H) * uint32_t(R) * ES;    // latent bytes per token (all heads)
+  const uint32_t zrun = uint32_t(nh) * uint32_t(R) * ES;   // the group's run in a token
+  const size_t zstart = (row0 * size_t(H) + size_t(h0)) * size_t(R) * ES;   // byte of the split's first run
+  const size_t zbase = zstart & ~size_t(15);
+  const uint32_t zlead = uint32_t(zstart - zbase);          // < 16
   const __amdgpu_buffer_rsrc_t kres =
       buffer_resource(static_cast<const unsigned char*>(p.k_s) + row0 * ROW, uint32_t(ntok) * ROW);
   const __amdgpu_buffer_rsrc_t vres =
       buffer_resource(static_cast<const unsigned char*>(p.v_s) + row0 * ROW, uint32_t(ntok) * ROW);
+  // the split's latent bytes from the aligned start to the end of its last run
+  const uint32_t zbytes = zlead + uint32_t(ntok - 1) * ztok + zrun;
   const __amdgpu_buffer_rsrc_t zkres =
-      buffer_resource(static_cast<const unsigned char*>(p.z_k) + row0 * ztok, uint32_t(ntok) * ztok);
+      buffer_resource(static_cast<const unsigned char*>(p.z_k) + (R > 0 ? zbase : 0), R > 0 ? zbytes : 0u);
   const __amdgpu_buffer_rsrc_t zvres =
-      buffer_resource(static_cast<const unsigned char*>(p.z_v) + row0 * ztok, uint32_t(ntok) * ztok);
-  const uint32_t zlane = (uint32_t(hh) * R + g) * ES;       // byte offset of latent dim g of head hh in a token
-
-  // latents of token tt (relative to t0) of this lane's dims
-  auto zload = [&](float (&zk)[kGnRPL], float (&zv)[kGnRPL], int tt) __attribute__((always_inline)) {
-    const uint32_t off = uint32_t(tt) * ztok + zlane;
-#pragma unroll
-    for (int i = 0; i < kGnRPL; ++i) {
-      if (i < nz) {
-        zk[i] = gn_load<E>(zkres, off + uint32_t(G * i * ES));
-        zv[i] = gn_load<E>(zvres, off + uint32_t(G * i * ES));
-      }
-    }
-  };
+      buffer_resource(static_cast<const unsigned char*>(p.z_v) + (R > 0 ? zbase : 0), R > 0 ? zbytes : 0u);
+  const int zch = ZR / 16;                                  // 16-byte chunks per token copy
+  const uint32_t zlane = (uint32_t(hl) * R + g) * ES;       // byte of latent dim g of this head in the run
 
   float m = -INFINITY, l = 0.f;
-  float acc_s[DPL], acc_z[kGnRPL];
+  float acc_s[DPL], acc_z[RPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc_s[i] = 0.f;
 #pragma unroll
-  for (int i = 0; i < kGnRPL; ++i) acc_z[i] = 0.f;
-  float zk[2][kGnRPL], zv[2][kGnRPL];
-#pragma unroll
-  for (int i = 0; i < kGnRPL; ++i) zk[0][i] = zv[0][i] = zk[1][i] = zv[1][i] = 0.f;
-  if (active) zload(zk[0], zv[0], 0);
+  for (int i = 0; i < RPL; ++i) acc_z[i] = 0.f;
 
-  // One token: logit, online softmax, aggregation.  Buffer `cur` holds its
-  // latents; the next token's go into the other buffer first.
-  auto token = [&](int tt, int j, float (&zkc)[kGnRPL], float (&zvc)[kGnRPL], float (&zkn)[kGnRPL],
-                   float (&zvn)[kGnRPL]) __attribute__((always_inline)) {
-    if (active && tt + 1 < ntok) zload(zkn, zvn, tt + 1);
+  // One token j of the tile: logit, online softmax, aggregation.
+  auto token = [&](int j) __attribute__((always_inline)) {
     float part = 0.f;
     {
       const unsigned char* kr = s_k + j * ROW + g * DPL * ES;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        const float kv = ES == 2 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(kr)[i])
-                                 : reinterpret_cast<const float*>(kr)[i];
-        part = __builtin_fmaf(q[i], kv, part);
-      }
+      for (int i = 0; i < DPL; ++i) part = __builtin_fmaf(q[i], gn_lds<E>(kr + i * ES), part);
     }
+    const unsigned char* zkr = s_zk + size_t(j) * ZR + s_off[j] + zlane;
 #pragma unroll
-    for (int i = 0; i < kGnRPL; ++i)
-      if (i < nz) part = __builtin_fmaf(qt[i], zkc[i], part);
-    const float s = group_sum<G>(part) * p.scale_log2;
+    for (int i = 0; i < RPL; ++i)
+      if (i < nz) part = __builtin_fmaf(qt[i], gn_lds<E>(zkr + G * i * ES), part);
+    const float s = gn_group_sum<G>(part) * p.scale_log2;
     if (s > m + 8.f) {                                       // lazy running max (log2 units)
       const float alpha = fast_exp2(m - s);                  // 0 on the first token (m = -inf)
       l *= alpha;
 #pragma unroll
       for (int i = 0; i < DPL; ++i) acc_s[i] *= alpha;
 #pragma unroll
-      for (int i = 0; i < kGnRPL; ++i) acc_z[i] *= alpha;
+      for (int i = 0; i < RPL; ++i) acc_z[i] *= alpha;
       m = s;
     }
     const float pe = fast_exp2(s - m);
     l += pe;
     const unsigned char* vr = s_v + j * ROW + g * DPL * ES;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-      const float vv = ES == 2 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(vr)[i])
-                               : reinterpret_cast<const float*>(vr)[i];
-      acc_s[i] = __builtin_fmaf(pe, vv, acc_s[i]);
-    }
+    for (int i = 0; i < DPL; ++i) acc_s[i] = __builtin_fmaf(pe, gn_lds<E>(vr + i * ES), acc_s[i]);
+    const unsigned char* zvr = s_zv + size_t(j) * ZR + s_off[j] + zlane;
 #pragma unroll
-    for (int i = 0; i < kGnRPL; ++i)
-      if (i < nz) acc_z[i] = __builtin_fmaf(pe, zvc[i], acc_z[i]);
+    for (int i = 0; i < RPL; ++i)
+      if (i < nz) acc_z[i] = __builtin_fmaf(pe, gn_lds<E>(zvr + G * i * ES), acc_z[i]);
   };
 
-  for (int tile0 = 0; tile0 < ntok; tile0 += kGnTile) {
-    const int nt = min(kGnTile, ntok - tile0);
+  for (int tile0 = 0; tile0 < ntok; tile0 += T) {
+    const int nt = min(T, ntok - tile0);
     __syncthreads();                                         // the previous tile is consumed
-    for (int idx = tid; idx < kGnTile * ROW_CH; idx += kGnThreads) {
+    // shared rows (rows past the split repeat its last token)
+    for (int idx = tid; idx < T * ROW_CH; idx += kGnThreads) {
       const int r = idx / ROW_CH, c = idx % ROW_CH;
       const uint32_t off = uint32_t(tile0 + min(r, nt - 1)) * ROW + uint32_t(c) * 16;
-      *reinterpret_cast<u32x4*>(s_k + r * ROW + c * 16) =
-          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, int(off), 0, kStream));
-      *reinterpret_cast<u32x4*>(s_v + r * ROW + c * 16) =
-          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, int(off), 0, kStream));
+      const u32x4 kv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kres, int(off), 0, kStream));
+      const u32x4 vv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vres, int(off), 0, kStream));
+      *reinterpret_cast<u32x4*>(s_k + r * ROW + c * 16) = kv;
+      *reinterpret_cast<u32x4*>(s_v + r * ROW + c * 16) = vv;
+    }
+    // latent runs: token r's run starts `lead` bytes into its 16-byte-aligned
+    // copy; bytes past the split's last run are zero
+    if (R > 0) {
+      for (int idx0 = tid; idx0 < T * zch; idx0 += 4 * kGnThreads) {
+        u32x4 zk4[4], zv4[4];
+        int at[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = idx0 + u * kGnThreads;
+          at[u] = -1;
+          zk4[u] = zv4[u] = u32x4{0u, 0u, 0u, 0u};
+          if (idx < T * zch) {
+            const int r = idx / zch, c = idx % zch;
+            const uint32_t rel = zlead + uint32_t(tile0 + min(r, nt - 1)) * ztok;
+            const uint32_t off = (rel & ~15u) + uint32_t(c) * 16;
+            if (off + 16 <= zbytes) {
+              zk4[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zkres, int(off), 0, kStream));
+              zv4[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zvres, int(off), 0, kStream));
+            } else if (off < zbytes) {
+              // the chunk that crosses the split's last byte: 2-byte loads,
+              // each inside the range (no load partly out of it)
+              uint32_t wk[4] = {0u, 0u, 0u, 0u}, wv[4] = {0u, 0u, 0u, 0u};
+              for (int e = 0; e < 8; ++e)
+                if (off + 2 * e < zbytes) {
+                  wk[e >> 1] |= uint32_t(uint16_t(__builtin_amdgcn_raw_buffer_load_b16(zkres, int(off + 2 * e), 0,
+                                                                                        kStream))) << (16 * (e & 1));
+                  wv[e >> 1] |= uint32_t(uint16_t(__builtin_amdgcn_raw_buffer_load_b16(zvres, int(off + 2 * e), 0,
+                                                                                        kStream))) << (16 * (e & 1));
+                }
+              zk4[u] = u32x4{wk[0], wk[1], wk[2], wk[3]};
+              zv4[u] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            }
+            at[u] = r * ZR + c * 16;
+            if (c == 0) s_off[r] = int(rel & 15u);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (at[u] >= 0) {
+            *reinterpret_cast<u32x4*>(s_zk + at[u]) = zk4[u];
+            *reinterpret_cast<u32x4*>(s_zv + at[u]) = zv4[u];
+          }
+      }
+    } else if (tid < T) {
+      s_off[tid] = 0;
     }
     __syncthreads();
     if (!active) continue;
     int j = 0;
     for (; j + 1 < nt; j += 2) {
-      token(tile0 + j, j, zk[0], zv[0], zk[1], zv[1]);
-      token(tile0 + j + 1, j + 1, zk[1], zv[1], zk[0], zv[0]);
+      token(j);
+      token(j + 1);
     }
-    if (j < nt) {                                            // odd tile length: swap the buffers' roles
-      token(tile0 + j, j, zk[0], zv[0], zk[1], zv[1]);
-#pragma unroll
-      for (int i = 0; i < kGnRPL; ++i) {
-        zk[0][i] = zk[1][i];
-        zv[0][i] = zv[1][i];
-      }
-    }
+    if (j < nt) token(j);
   }
 
   if (!active) return;
@@ -220,7 +269,7 @@ __global__ __launch_bounds__(kGnThreads) void decode_generic_kernel(GnParams p) 
 #pragma unroll
   for (int i = 0; i < DPL; ++i) dst[g * DPL + i] = acc_s[i];
 #pragma unroll
-  for (int i = 0; i < kGnRPL; ++i)
+  for (int i = 0; i < RPL; ++i)
     if (i < nz) dst[DH + g + G * i] = acc_z[i];
 }
 
@@ -274,7 +323,23 @@ bool decode_generic_supported(int dtype, int head_dim, int rank, int heads) {
          rank >= 0 && rank <= kGenericMaxRank && heads >= 1 && heads <= kGenericMaxHeads;
 }
 
-template <class E, int DH>
+// Tokens per tile and the LDS bytes of one token's latent copy, for lanes
+// per head G: the largest power of two up to kGnTileMax whose tile (shared
+// rows, the two latent copies, the run offsets) fits kGnLdsBudget.
+static void generic_tile(const DecodePlan& pl, int G, int* tile, int* zrow, int* lds) {
+  const int es = pl.dtype == 1 ? 2 : 4;
+  const int hw = kGnThreads / G;
+  const int nh = pl.heads < hw ? pl.heads : hw;
+  const int zr = pl.rank > 0 ? (nh * pl.rank * es + 15 + 15) / 16 * 16 : 0;
+  auto bytes = [&](int t) { return 2 * t * pl.head_dim * es + 2 * t * zr + 4 * t; };
+  int t = kGnTileMax;
+  while (t > 1 && bytes(t) > kGnLdsBudget) t /= 2;
+  *tile = t;
+  *zrow = zr;
+  *lds = bytes(t);
+}
+
+template <class E, int DH, int G>
 static hipError_t launch_generic_t(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
   if ((phase & 1) && pl.n_splits > 0) {
     GnParams kp;
@@ -284,8 +349,11 @@ static hipError_t launch_generic_t(const DecodePlan& pl, const DecodeArgs& a, in
     kp.heads = pl.heads; kp.rank = pl.rank; kp.max_len = pl.max_len; kp.split_tokens = pl.split_tokens;
     kp.partials = pl.partials; kp.capacity = pl.capacity;
     kp.ws_ml = a.ws_ml; kp.ws_acc = a.ws_acc;
-    const dim3 grid(unsigned(pl.n_splits), unsigned(pl.batch), unsigned((pl.heads + kGnHeads - 1) / kGnHeads));
-    hipLaunchKernelGGL((decode_generic_kernel<E, DH>), grid, dim3(kGnThreads), 0, st, kp);
+    int lds = 0;
+    generic_tile(pl, G, &kp.tile, &kp.zrow, &lds);
+    constexpr int HW = kGnThreads / G;
+    const dim3 grid(unsigned(pl.n_splits), unsigned(pl.batch), unsigned((pl.heads + HW - 1) / HW));
+    hipLaunchKernelGGL((decode_generic_kernel<E, DH, G>), grid, dim3(kGnThreads), size_t(lds), st, kp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -296,10 +364,22 @@ static hipError_t launch_generic_t(const DecodePlan& pl, const DecodeArgs& a, in
   return hipGetLastError();
 }
 
+template <class E, int DH>
+static hipError_t launch_generic_g(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
+  switch (generic_lanes_per_head(pl.heads, DH)) {
+    case 8: return launch_generic_t<E, DH, 8>(pl, a, phase, st);
+    case 16: return launch_generic_t<E, DH, 16>(pl, a, phase, st);
+    case 32:
+      if constexpr (DH >= 32) return launch_generic_t<E, DH, 32>(pl, a, phase, st);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_decode_generic(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
 #define LRKV_GN(DHV)                                                                                   \
   if (pl.head_dim == DHV)                                                                              \
-    return pl.dtype == 1 ? launch_generic_t<BF16, DHV>(pl, a, phase, st) : launch_generic_t<F32, DHV>(pl, a, phase, st);
+    return pl.dtype == 1 ? launch_generic_g<BF16, DHV>(pl, a, phase, st) : launch_generic_g<F32, DHV>(pl, a, phase, st);
   LRKV_GN(16) LRKV_GN(32) LRKV_GN(64) LRKV_GN(128)
 #undef LRKV_GN
   return hipErrorInvalidValue;

@@ -83,11 +83,13 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
     // Workgroups over the whole batch: about two per compute unit for the
     // vector-ALU scan; for the MFMA scan (one resident workgroup per compute
     // unit) about one, in whole 32-token tiles per wave.
-    // The any-rank scan runs one workgroup per 32 heads with two or three
-    // resident per compute unit: about eight per compute unit.
-    const int64_t groups = pl->mfma ? heads / 32 : pl->generic ? (heads + 31) / 32 : 1;
+    // The any-rank scan runs one workgroup per group of 256 / G heads (G
+    // lanes per head) with up to 64 KB of LDS, two resident per compute
+    // unit: about four per compute unit (two rounds).
+    const int64_t gh = 256 / lrkv::generic_lanes_per_head(heads, head_dim);
+    const int64_t groups = pl->mfma ? heads / 32 : pl->generic ? (heads + gh - 1) / gh : 1;
     const int64_t total = int64_t(batch) * max_len * groups;
-    const int64_t target = (pl->mfma ? 1 : pl->generic ? 8 : 2) * int64_t(device_cu_count());
+    const int64_t target = (pl->mfma ? 1 : pl->generic ? 4 : 2) * int64_t(device_cu_count());
     const int64_t unit = pl->mfma ? 2 * tile : tile;
     int64_t s = (total + target - 1) / (target > 0 ? target : 1);
     s = (s + unit - 1) / unit * unit;

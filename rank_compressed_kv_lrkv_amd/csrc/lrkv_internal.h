@@ -76,6 +76,8 @@ constexpr int kGenericMaxRank = 128;
 constexpr int kGenericMaxHeads = 1024;
 constexpr int kGenericMaxDims = 128 + kGenericMaxRank;   // head_dim + rank
 bool decode_generic_supported(int dtype, int head_dim, int rank, int heads);
+// Lanes per head of the any-rank scan (8, 16 or 32); 256 / that many heads per workgroup.
+int generic_lanes_per_head(int heads, int head_dim);
 hipError_t launch_decode_generic(const DecodePlan& plan, const DecodeArgs& args, int phase, hipStream_t stream);
 hipError_t launch_decode_mfma_scan(const DecodePlan& plan, const DecodeArgs& args, hipStream_t stream);
 // phase: 1 = split-K scan only, 2 = combine only, 3 = both.
