@@ -17,8 +17,10 @@ under `configs`, the other synthetic workloads: the tiny fp32 decode (a
 latency), the small bf16 decode (L2-resident latency, and throughput over
 rotated copies whose working set exceeds twice L2 plus the Infinity
 Cache), the ragged 1K-64K-token decode (checked in full against the
-oracle) and the causal prefill (TFLOP/s against the bf16 MFMA peak, sampled
-rows checked against the oracle), each with the oracle timed beside it.
+oracle), decode at rank 54 (a rank the pages train, on the any-rank scan),
+the causal prefill (TFLOP/s against the bf16 MFMA peak, sampled rows
+checked against the oracle) and a training step (forward and backward),
+each with the oracle timed beside it.
 
 Prints one JSON line.  `roofline` prices the dominant kernel (the scan)
 against the HBM peak using the algorithmic bytes of one launch and its
@@ -402,6 +404,20 @@ def other_configs(args):
     del m, d
     torch.cuda.empty_cache()
     progress("ragged_bf16_T1k_64k done")
+    # Decode at a rank the pages train (Table 7's largest model: 32 heads,
+    # rank 54), on the any-rank scan.
+    wl = DECODE_WORKLOADS["rank54_bf16_T8k"]
+    d = decode_inputs(wl)
+    m = measure_decode(args, wl, d)
+    o = oracle_decode_check(d, m["out"], as_f64, budget_s=5.0)
+    res[wl.name] = {"kind": "throughput (any-rank scan)", "cache_tokens": m["tokens"],
+                    "cache_tokens_per_s": m["tokens_per_s"], "step_ms": m["step_ms"], "kernels_ms": m["kernels_ms"],
+                    "hbm_GBps_step": m["hbm_GBps_step"], "hbm_frac_step": m["hbm_frac_step"],
+                    "roofline": m["roofline"], "config": m["config"],
+                    "gpu_vs_oracle_max_err_over_inf_norm": o["err"], "checked": o["checked"], "oracle": o["rate"]}
+    del m, d
+    torch.cuda.empty_cache()
+    progress("rank54_bf16_T8k done")
     return res
 
 

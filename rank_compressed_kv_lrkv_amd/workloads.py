@@ -85,6 +85,9 @@ DECODE_WORKLOADS = {
         DecodeWorkload("mid_bf16_T8k", 32, 32, 128, 16, 8192, "bf16", 20261204),
         DecodeWorkload("ragged_bf16_T1k_64k", 16, 32, 128, 32, 65536, "bf16", 20261205,
                        ragged=(1024, 65536)),
+        # a rank the pages train: the largest model of Table 7 (32 heads of
+        # width 128, rank 54) at 8K context; the any-rank scan takes it
+        DecodeWorkload("rank54_bf16_T8k", 16, 32, 128, 54, 8192, "bf16", 20261209),
     ]
 }
 
