@@ -61,9 +61,9 @@ def parse():
                          "one training step (forward with log-sum-exp, backward) of the prefill workload")
     ap.add_argument("--workload", default=None, help="default: mid_bf16_T8k (decode), prefill_bf16_L4k (prefill)")
     ap.add_argument("--split-tokens", type=int, default=0, help="0 = library default")
-    ap.add_argument("--engine", type=int, default=0, choices=(0, 1, 2, 3),
+    ap.add_argument("--engine", type=int, default=0, choices=(0, 1, 2, 3, 4),
                     help="decode scan: 0 the default for the shape, 1 the vector-ALU scan, 2 the MFMA scan, "
-                         "3 the any-rank scan")
+                         "3 the any-rank scan, 4 the any-rank MFMA scan")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall-clock budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trials", type=int, default=5, help="timed trials per figure (the median is reported)")
@@ -307,7 +307,8 @@ def measure_decode(args, wl, d, rotate_mb: float = 0.0, engine: int = 0):
     scan_bytes = cache_bytes + B * H * d_h * es + H * d_h * r * es          # cache + q + B^K
     step_bytes = cache_bytes + 2 * B * H * d_h * es + 2 * H * d_h * r * es  # + out + B^V
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
-    scan_kernel = {1: "decode_split_kernel", 2: "decode_mfma_kernel", 3: "decode_generic_kernel"}.get(engine) or \
+    scan_kernel = {1: "decode_split_kernel", 2: "decode_mfma_kernel", 3: "decode_generic_kernel",
+                   4: "decode_mfma_any_kernel"}.get(engine) or \
         L.lrkv_decode_scan_kernel(dt, H, d_h, r)
     traffic = None
     for rec_name in ("decode_scan_counters", "decode_valu_scan_counters", "decode_ragged_counters"):

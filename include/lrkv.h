@@ -121,7 +121,8 @@ lrkv_status lrkv_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t
 /* Bytes of device workspace lrkv_decode needs for these sizes and this
  * split (split_tokens == 0 selects the library's default for the device
  * that is current).  Written to *bytes.  The workspace holds the split-K
- * partial softmax states (fp32). */
+ * partial softmax states (fp32), and for decode_mfma_any_kernel also the
+ * absorbed queries B^K_h^T q (fp32, batch * num_heads * rank). */
 lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num_heads,
                                        int32_t head_dim, int32_t rank, int64_t capacity,
                                        int64_t max_len, int32_t split_tokens, size_t* bytes);
@@ -130,9 +131,14 @@ lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num
  * sizes: "decode_mfma_kernel" (bf16, head_dim 64 or 128, rank 0/8/16/32,
  * num_heads a multiple of 32 up to 64: the shared term runs on bf16 MFMA
  * across 32 heads), "decode_split_kernel" (the other shapes of the tuned
- * envelope: vector-ALU dot products) or "decode_generic_kernel" (any other
- * rank up to 128 and up to 1024 heads, at the pages' ranks such as 46, 54,
- * 55: vector-ALU, latents read element by element).  Returns NULL for a
+ * envelope: vector-ALU dot products), "decode_mfma_any_kernel" (bf16,
+ * head_dim 128, any other rank from 8 to 128 with num_heads * rank even, up
+ * to 1024 heads, except ranks above 112 with fewer than 32 heads; at the
+ * pages' ranks such as 46, 51, 54, 55: the shared term on bf16 MFMA as in
+ * decode_mfma_kernel, each lane's window of a latent row on 2-wide bf16
+ * dots) or "decode_generic_kernel" (the remaining shapes up to rank 128 and
+ * 1024 heads, fp32 included: vector-ALU, latents read element by element).
+ * Returns NULL for a
  * shape outside the supported envelope.  Host-only: launches nothing; the
  * string is static. */
 const char* lrkv_decode_scan_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank);
@@ -224,7 +230,9 @@ lrkv_status lrkv_decode_noalloc(int32_t dtype, int32_t batch, int32_t num_heads,
  *           2: the MFMA scan, decode_mfma_kernel (only its shapes; others
  *              return LRKV_ERR_SHAPE);
  *           3: the any-rank scan, decode_generic_kernel, with its merge
- *              (every shape of the decode envelope).
+ *              (every shape of the decode envelope);
+ *           4: the any-rank MFMA scan, decode_mfma_any_kernel, with the
+ *              any-rank merge (only its shapes).
  *   phases  1: the split-K scan (as lrkv_decode_partial), 2: the merge (as
  *           lrkv_decode_combine), 3: both (as lrkv_decode).
  * The remaining arguments are lrkv_decode's.  The workspace must be at least

@@ -257,7 +257,8 @@ def lrkv_decode(cache: LrkvCache, seq_lens: torch.Tensor, max_len: int, q: torch
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                 phase: str = "both", engine: int = 0) -> torch.Tensor:
     """phase: "both" (lrkv_decode), "partial" (lrkv_decode_partial) or "combine" (lrkv_decode_combine);
-    engine != 0 goes through lrkv_decode_ex (1: vector-ALU scan, 2: MFMA scan, 3: any-rank scan)."""
+    engine != 0 goes through lrkv_decode_ex (1: vector-ALU scan, 2: MFMA scan, 3: any-rank scan,
+    4: any-rank MFMA scan)."""
     dt = cache.dtype
     B, H, d_h, r = cache.batch, cache.heads, cache.head_dim, cache.rank
     _shape(q, "q", (B, H, d_h))

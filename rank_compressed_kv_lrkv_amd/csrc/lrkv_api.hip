@@ -49,18 +49,22 @@ lrkv_status check_sizes(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
 
 // engine: 0 = the default for the shape, 1 = the vector-ALU scan
 // (decode_split_kernel), 2 = the MFMA scan (decode_mfma_kernel), 3 = the
-// any-rank scan (decode_generic_kernel).  The default takes the MFMA scan
-// where it applies, else the vector-ALU scan, else the any-rank scan.
+// any-rank scan (decode_generic_kernel), 4 = the any-rank MFMA scan
+// (decode_mfma_any_kernel).  The default takes the MFMA scan where it
+// applies, else the vector-ALU scan, else the any-rank MFMA scan where it
+// is preferred, else the any-rank scan.
 lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t head_dim, int32_t rank,
                         int64_t capacity, int64_t max_len, int32_t split_tokens, DecodePlan* pl, int32_t engine = 0) {
   lrkv_status st = check_sizes(dtype, batch, heads, head_dim, rank, capacity);
   if (st != LRKV_OK) return st;
-  if (engine < 0 || engine > 3) return LRKV_ERR_SHAPE;
+  if (engine < 0 || engine > 4) return LRKV_ERR_SHAPE;
   const bool tuned = lrkv::decode_supported(dtype, head_dim, rank, heads);
   const bool any = lrkv::decode_generic_supported(dtype, head_dim, rank, heads);
+  const bool any_mfma = lrkv::decode_mfma_any_supported(dtype, head_dim, rank, heads);
   if (engine == 1 && !tuned) return LRKV_ERR_SHAPE;
   if (engine == 2 && !lrkv::decode_mfma_supported(dtype, head_dim, rank, heads)) return LRKV_ERR_SHAPE;
   if (engine == 3 && !any) return LRKV_ERR_SHAPE;
+  if (engine == 4 && !any_mfma) return LRKV_ERR_SHAPE;
   if (engine == 0 && !tuned && !any) return LRKV_ERR_SHAPE;
   if (max_len < 0 || split_tokens < 0) return LRKV_ERR_SHAPE;
   if (max_len > capacity) return LRKV_ERR_CAPACITY;
@@ -68,13 +72,16 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
 
   pl->batch = batch; pl->heads = heads; pl->head_dim = head_dim; pl->rank = rank; pl->dtype = dtype;
   pl->capacity = capacity; pl->max_len = int(max_len);
-  pl->generic = engine == 3 || (engine == 0 && !tuned);
-  pl->mfma = !pl->generic && engine != 1 && lrkv::decode_mfma_supported(dtype, head_dim, rank, heads);
+  const bool any_mfma_default = lrkv::decode_mfma_any_preferred(dtype, head_dim, rank, heads);
+  pl->mfma_any = engine == 4 || (engine == 0 && !tuned && any_mfma_default);
+  pl->generic = engine == 3 || (engine == 0 && !tuned && !any_mfma_default);
+  pl->mfma = !pl->generic && !pl->mfma_any && engine != 1 &&
+             lrkv::decode_mfma_supported(dtype, head_dim, rank, heads);
   pl->group = (rank == 4 || heads > 32) ? 4 : 8;
   int hp = 1;
   while (hp < heads) hp <<= 1;
   pl->heads_pow2 = hp;
-  pl->slots = (pl->mfma || pl->generic) ? 1 : lrkv::kDecodeThreads / (hp * pl->group);
+  pl->slots = (pl->mfma || pl->generic || pl->mfma_any) ? 1 : lrkv::kDecodeThreads / (hp * pl->group);
   if (pl->slots < 1) return LRKV_ERR_SHAPE;
 
   const int tile = lrkv::kDecodeTile;
@@ -85,12 +92,15 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
     // unit) about one, in whole 32-token tiles per wave.
     // The any-rank scan runs one workgroup per group of 256 / G heads (G
     // lanes per head) with up to 64 KB of LDS, two resident per compute
-    // unit: about four per compute unit (two rounds).
+    // unit: about four per compute unit (two rounds).  The any-rank MFMA
+    // scan runs one workgroup per group of 32 heads, one resident per
+    // compute unit: about one per compute unit, in whole 32-token tiles per
+    // wave.
     const int64_t gh = 256 / lrkv::generic_lanes_per_head(heads, head_dim);
-    const int64_t groups = pl->mfma ? heads / 32 : pl->generic ? (heads + gh - 1) / gh : 1;
+    const int64_t groups = pl->mfma ? heads / 32 : pl->mfma_any ? (heads + 31) / 32 : pl->generic ? (heads + gh - 1) / gh : 1;
     const int64_t total = int64_t(batch) * max_len * groups;
-    const int64_t target = (pl->mfma ? 1 : pl->generic ? 4 : 2) * int64_t(device_cu_count());
-    const int64_t unit = pl->mfma ? 2 * tile : tile;
+    const int64_t target = (pl->mfma || pl->mfma_any ? 1 : pl->generic ? 4 : 2) * int64_t(device_cu_count());
+    const int64_t unit = (pl->mfma || pl->mfma_any) ? 2 * tile : tile;
     int64_t s = (total + target - 1) / (target > 0 ? target : 1);
     s = (s + unit - 1) / unit * unit;
     // at least two tiles per split: a small cache split one tile at a time
@@ -106,11 +116,15 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
   pl->balanced = pl->mfma && split_tokens == 0 && batch <= lrkv::kBalMaxBatch && max_len < lrkv::kBalMaxLen;
   pl->bal_cap = device_cu_count();
   // The kernels address one split's rows and latents through 32-bit buffer
-  // offsets (a balanced item is at most max_len tokens).
+  // offsets (a balanced item is at most max_len tokens), with the top 1 KB of
+  // the offset range left for reads meant to fall outside every range.
   const int64_t es = dtype == 1 ? 2 : 4;
   const int64_t span = pl->balanced ? std::max<int64_t>(max_len, 1) : split;
-  if (span * std::max<int64_t>(int64_t(head_dim), int64_t(heads) * rank) * es >= (int64_t(1) << 32))
+  if (span * std::max<int64_t>(int64_t(head_dim), int64_t(heads) * rank) * es >= (int64_t(1) << 32) - 1024)
     return LRKV_ERR_SHAPE;
+  // the any-rank MFMA scan also forms offsets of up to 256 tokens past its
+  // split (zero reads of the tiles after the last)
+  if (pl->mfma_any && (span + 256) * int64_t(heads) * rank * es >= (int64_t(1) << 32)) return LRKV_ERR_SHAPE;
   pl->split_tokens = split;
   if (pl->balanced) {
     // the partition makes at most max(cap, non-empty sequences) items: no
@@ -126,7 +140,12 @@ lrkv_status plan_decode(int32_t dtype, int32_t batch, int32_t heads, int32_t hea
   pl->ws_ml_bytes = (states * 2 * sizeof(float) + 255) / 256 * 256;
   pl->ws_acc_bytes = (states * size_t(head_dim + rank) * sizeof(float) + 255) / 256 * 256;
   pl->ws_meta_bytes = pl->balanced ? (size_t(batch + 1) * sizeof(int) + 255) / 256 * 256 : 0;
+  pl->ws_qt_bytes = pl->mfma_any ? (size_t(batch) * heads * rank * sizeof(float) + 255) / 256 * 256 : 0;
   return LRKV_OK;
+}
+
+size_t workspace_bytes_of(const DecodePlan& pl) {
+  return pl.ws_ml_bytes + pl.ws_acc_bytes + pl.ws_meta_bytes + pl.ws_qt_bytes;
 }
 
 // Device scratch of lrkv_decode_noalloc: the split-K partial states of a
@@ -180,8 +199,8 @@ lrkv_status lrkv_init(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LRKV_ERR_DEVICE;
   (void)device_cu_count();
-  for (hipError_t (*prep)() : {lrkv::decode_mfma_prepare, lrkv::prefill_prepare, lrkv::project_prepare,
-                               lrkv::train_prepare})
+  for (hipError_t (*prep)() : {lrkv::decode_mfma_prepare, lrkv::decode_mfma_any_prepare, lrkv::prefill_prepare,
+                               lrkv::project_prepare, lrkv::train_prepare})
     if (prep() != hipSuccess) return LRKV_ERR_DEVICE;
   return LRKV_OK;
 }
@@ -193,8 +212,10 @@ int64_t lrkv_cache_elems_per_token(int32_t num_heads, int32_t head_dim, int32_t 
 
 const char* lrkv_decode_scan_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank) {
   if (check_sizes(dtype, 1, num_heads, head_dim, rank, 1) != LRKV_OK) return nullptr;
-  if (!lrkv::decode_supported(dtype, head_dim, rank, num_heads))
+  if (!lrkv::decode_supported(dtype, head_dim, rank, num_heads)) {
+    if (lrkv::decode_mfma_any_preferred(dtype, head_dim, rank, num_heads)) return "decode_mfma_any_kernel";
     return lrkv::decode_generic_supported(dtype, head_dim, rank, num_heads) ? "decode_generic_kernel" : nullptr;
+  }
   return lrkv::decode_mfma_supported(dtype, head_dim, rank, num_heads) ? "decode_mfma_kernel" : "decode_split_kernel";
 }
 
@@ -205,7 +226,7 @@ lrkv_status lrkv_decode_workspace_size(int32_t dtype, int32_t batch, int32_t num
   DecodePlan pl;
   const lrkv_status st = plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl);
   if (st != LRKV_OK) return st;
-  *bytes = pl.ws_ml_bytes + pl.ws_acc_bytes + pl.ws_meta_bytes;
+  *bytes = workspace_bytes_of(pl);
   return LRKV_OK;
 }
 
@@ -217,7 +238,7 @@ lrkv_status lrkv_decode_workspace_size_ex(int32_t engine, int32_t dtype, int32_t
   const lrkv_status st =
       plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl, engine);
   if (st != LRKV_OK) return st;
-  *bytes = pl.ws_ml_bytes + pl.ws_acc_bytes + pl.ws_meta_bytes;
+  *bytes = workspace_bytes_of(pl);
   return LRKV_OK;
 }
 
@@ -238,7 +259,7 @@ static lrkv_status decode_phases(int phase, int32_t dtype, int32_t batch, int32_
   if (scan && (!k_shared || !v_shared || !q)) return LRKV_ERR_NULL;
   if (scan && rank > 0 && (!z_k || !z_v || !b_k)) return LRKV_ERR_NULL;
   if (combine && (!out || (rank > 0 && !b_v))) return LRKV_ERR_NULL;
-  const size_t need = pl.ws_ml_bytes + pl.ws_acc_bytes + pl.ws_meta_bytes;
+  const size_t need = workspace_bytes_of(pl);
   if (!workspace || workspace_bytes < need) return LRKV_ERR_WORKSPACE;
   if (!aligned16(workspace) || !aligned4(seq_lens)) return LRKV_ERR_ALIGN;
   if (scan && (!aligned16(k_shared) || !aligned16(v_shared) || !aligned16(q))) return LRKV_ERR_ALIGN;
@@ -254,7 +275,10 @@ static lrkv_status decode_phases(int phase, int32_t dtype, int32_t batch, int32_
   a.ws_ml = static_cast<float*>(workspace);
   a.ws_acc = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + pl.ws_ml_bytes);
   a.ws_meta = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + pl.ws_ml_bytes + pl.ws_acc_bytes);
-  const hipError_t e = lrkv::launch_decode(pl, a, phase, static_cast<hipStream_t>(stream));
+  a.ws_qt = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + pl.ws_ml_bytes + pl.ws_acc_bytes +
+                                     pl.ws_meta_bytes);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const hipError_t e = pl.mfma_any ? lrkv::launch_decode_mfma_any(pl, a, phase, hs) : lrkv::launch_decode(pl, a, phase, hs);
   return e == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
 }
 
@@ -280,7 +304,7 @@ lrkv_status lrkv_decode_noalloc(int32_t dtype, int32_t batch, int32_t num_heads,
   DecodePlan pl;
   const lrkv_status st = plan_decode(dtype, batch, num_heads, head_dim, rank, capacity, max_len, split_tokens, &pl);
   if (st != LRKV_OK) return st;
-  if (pl.ws_ml_bytes + pl.ws_acc_bytes + pl.ws_meta_bytes > kScratchBytes) return LRKV_ERR_SCRATCH;
+  if (workspace_bytes_of(pl) > kScratchBytes) return LRKV_ERR_SCRATCH;
   if (batch == 0) return LRKV_OK;
   void* ws = nullptr;
   if (scratch_address(&ws) != hipSuccess) return LRKV_ERR_DEVICE;

@@ -28,6 +28,7 @@ hipError_t allow_dynamic_lds(int bytes) {
 // of every kernel that needs more than the default), done for every kernel
 // at once; each returns the first failure.
 hipError_t decode_mfma_prepare();
+hipError_t decode_mfma_any_prepare();
 hipError_t prefill_prepare();
 hipError_t project_prepare();
 hipError_t train_prepare();
@@ -47,10 +48,12 @@ struct DecodePlan {
   int partials;       // n_splits * slots partial states per (sequence, head)
   bool mfma;          // scan on the MFMA kernel (one partial state per workgroup: slots = 1)
   bool generic;       // scan and merge of the any-rank kernels (one partial state per split: slots = 1)
+  bool mfma_any;      // scan on the any-rank MFMA kernel, merge of the any-rank kernels (fixed splits)
   bool balanced;      // length-balanced items computed on the device (MFMA scan, default split):
                       // n_splits = partials = max(bal_cap, batch) items, state index item * heads + h
   int bal_cap;        // items the partition aims for (resident scan workgroups)
   size_t ws_ml_bytes, ws_acc_bytes, ws_meta_bytes;
+  size_t ws_qt_bytes;  // any-rank MFMA scan: the absorbed query [batch][heads][rank] fp32
 };
 
 struct DecodeArgs {
@@ -62,6 +65,7 @@ struct DecodeArgs {
   float* ws_ml;       // [batch][partials][heads] x (m, l)
   float* ws_acc;      // [batch][partials][heads][head_dim + rank]
   int* ws_meta;       // balanced partition: first item of each sequence [batch], then the item size
+  float* ws_qt;       // any-rank MFMA scan: absorbed query [batch][heads][rank]
 };
 
 // Returns false if (dtype, head_dim, rank, heads) is outside the compiled envelope.
@@ -80,7 +84,14 @@ bool decode_generic_supported(int dtype, int head_dim, int rank, int heads);
 int generic_lanes_per_head(int heads, int head_dim);
 hipError_t launch_decode_generic(const DecodePlan& plan, const DecodeArgs& args, int phase, hipStream_t stream);
 hipError_t launch_decode_mfma_scan(const DecodePlan& plan, const DecodeArgs& args, hipStream_t stream);
-// phase: 1 = split-K scan only, 2 = combine only, 3 = both.
+// The any-rank MFMA scan (decode_mfma_any.hip): bf16, head_dim 128, ranks 8 to
+// kGenericMaxRank with heads * rank even; its merge is the any-rank merge.
+bool decode_mfma_any_supported(int dtype, int head_dim, int rank, int heads);
+// Supported, and the default over decode_generic_kernel.
+bool decode_mfma_any_preferred(int dtype, int head_dim, int rank, int heads);
+hipError_t launch_decode_mfma_any(const DecodePlan& plan, const DecodeArgs& args, int phase, hipStream_t stream);
+// phase: 1 = split-K scan only, 2 = combine only, 3 = both (every plan but
+// the any-rank MFMA scan's, which launch_decode_mfma_any runs).
 hipError_t launch_decode(const DecodePlan& plan, const DecodeArgs& args, int phase, hipStream_t stream);
 
 struct AppendArgs {

@@ -58,9 +58,16 @@ def test_decode_scan_kernel_names():
     assert lib.lrkv_decode_scan_kernel(BF16, 32, 32, 16) == b"decode_split_kernel"   # head_dim 32
     assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 64) == b"decode_split_kernel"  # rank 64
     assert lib.lrkv_decode_scan_kernel(F32, 32, 128, 16) == b"decode_split_kernel"   # fp32 storage
-    assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 54) == b"decode_generic_kernel"  # the pages' ranks
-    assert lib.lrkv_decode_scan_kernel(BF16, 18, 128, 55) == b"decode_generic_kernel"
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 54) == b"decode_mfma_any_kernel"  # the pages' ranks
+    assert lib.lrkv_decode_scan_kernel(BF16, 18, 128, 55) == b"decode_mfma_any_kernel"
+    assert lib.lrkv_decode_scan_kernel(BF16, 12, 128, 51) == b"decode_mfma_any_kernel"
+    assert lib.lrkv_decode_scan_kernel(BF16, 6, 128, 128) == b"decode_generic_kernel"   # rank > 112, < 32 heads
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 128) == b"decode_mfma_any_kernel"
+    assert lib.lrkv_decode_scan_kernel(BF16, 6, 128, 112) == b"decode_mfma_any_kernel"
     assert lib.lrkv_decode_scan_kernel(F32, 6, 128, 128) == b"decode_generic_kernel"
+    assert lib.lrkv_decode_scan_kernel(BF16, 7, 128, 55) == b"decode_generic_kernel"   # heads * rank odd
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 7) == b"decode_generic_kernel"   # rank below 8
+    assert lib.lrkv_decode_scan_kernel(BF16, 32, 64, 54) == b"decode_generic_kernel"   # head_dim 64
     assert lib.lrkv_decode_scan_kernel(BF16, 8, 64, 4) == b"decode_generic_kernel"    # bf16 rank 4
     assert lib.lrkv_decode_scan_kernel(BF16, 96, 64, 8) == b"decode_generic_kernel"   # more than 64 heads
     assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 129) is None
@@ -77,12 +84,14 @@ def ws_size(dtype=BF16, B=2, H=8, d_h=64, r=8, cap=256, max_len=256, split=0):
 
 
 def test_workspace_size_formula_any_rank():
-    # the any-rank scan keeps one partial state per (split, head)
-    st, n = ws_size(BF16, B=2, H=18, d_h=128, r=55, cap=1024, max_len=1000, split=128)
-    assert st == OK
-    states = 2 * -(-1000 // 128) * 18
+    # the any-rank scans keep one partial state per (split, head); the MFMA one (the default
+    # for bf16 at head_dim 128) also the absorbed queries, batch * heads * rank fp32
     pad = lambda x: -(-x // 256) * 256
-    assert n == pad(states * 2 * 4) + pad(states * (128 + 55) * 4)
+    for dt, qt in ((F32, 0), (BF16, pad(2 * 18 * 55 * 4))):
+        st, n = ws_size(dt, B=2, H=18, d_h=128, r=55, cap=1024, max_len=1000, split=128)
+        assert st == OK
+        states = 2 * -(-1000 // 128) * 18
+        assert n == pad(states * 2 * 4) + pad(states * (128 + 55) * 4) + qt, dt
 
 
 def test_workspace_size_formula():
@@ -340,13 +349,25 @@ def test_decode_ex_validation():
     # engine 2 (MFMA scan) only on its shapes; engine 1 everywhere the vector scan runs
     assert lib.lrkv_decode_workspace_size_ex(2, BF16, 2, 8, 64, 8, 256, 256, 0, ctypes.byref(n)) == SHAPE
     assert lib.lrkv_decode_workspace_size_ex(1, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == OK
-    assert lib.lrkv_decode_workspace_size_ex(4, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_decode_workspace_size_ex(5, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == SHAPE
     assert lib.lrkv_decode_workspace_size_ex(-1, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == SHAPE
     # engine 3 (any-rank scan) takes every shape of the envelope; the tuned scans not the pages' odd ranks
     assert lib.lrkv_decode_workspace_size_ex(3, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == OK
     assert lib.lrkv_decode_workspace_size_ex(3, F32, 2, 18, 128, 55, 256, 256, 0, ctypes.byref(n)) == OK
     assert lib.lrkv_decode_workspace_size_ex(1, BF16, 2, 18, 128, 55, 256, 256, 0, ctypes.byref(n)) == SHAPE
     assert lib.lrkv_decode_workspace_size_ex(2, BF16, 2, 32, 128, 54, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    # engine 4 (any-rank MFMA scan): bf16, head_dim 128, ranks 8..128 with heads * rank even; its
+    # workspace adds the absorbed queries (batch * heads * rank fp32) to the partial states
+    assert lib.lrkv_decode_workspace_size_ex(4, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == OK
+    assert lib.lrkv_decode_workspace_size_ex(4, F32, 2, 32, 128, 54, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_decode_workspace_size_ex(4, BF16, 2, 32, 64, 54, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_decode_workspace_size_ex(4, BF16, 2, 7, 128, 55, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_decode_workspace_size_ex(4, BF16, 2, 32, 128, 7, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    assert lib.lrkv_decode_workspace_size_ex(4, BF16, 2, 32, 128, 129, 256, 256, 0, ctypes.byref(n)) == SHAPE
+    w3, w4 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.lrkv_decode_workspace_size_ex(3, BF16, 2, 32, 128, 54, 256, 256, 128, ctypes.byref(w3)) == OK
+    assert lib.lrkv_decode_workspace_size_ex(4, BF16, 2, 32, 128, 54, 256, 256, 128, ctypes.byref(w4)) == OK
+    assert w4.value == w3.value + (2 * 32 * 54 * 4 + 255) // 256 * 256
     # the default engine matches lrkv_decode_workspace_size
     m = ctypes.c_size_t(0)
     assert lib.lrkv_decode_workspace_size_ex(0, BF16, 2, 32, 128, 16, 256, 256, 0, ctypes.byref(n)) == OK

@@ -1,8 +1,9 @@
 """Decode at the ranks the LRKV slides sweep ("The rank directly sets the
 theoretical cache budget", Table 7; "Backup: the complete rank sweep
 clarifies the trade-off", Table 8), where a token's latent run of H*r
-elements is not a whole number of 16-byte chunks: the any-rank scan
-(decode_generic_kernel) through the C ABI against the float64 oracle, and
+elements is not a whole number of 16-byte chunks: the any-rank scans
+(decode_mfma_any_kernel, the bf16 default at head_dim 128, and
+decode_generic_kernel) through the C ABI against the float64 oracle, and
 the cache append at those ranks, bit-exact.
 
 Bar: max |gpu - oracle| <= 1e-5 * ||oracle||_inf (fp32 storage) or
@@ -14,7 +15,7 @@ import torch
 
 import rank_compressed_kv_lrkv_amd as L
 from rank_compressed_kv_lrkv_amd.workloads import DECODE_WORKLOADS, DecodeWorkload, decode_inputs
-from tests.gpu_util import TOL, TORCH_DT, err_ratio, oracle_decode, run_decode, say, to_dev
+from tests.gpu_util import TOL, TORCH_DT, device_cache, err_ratio, from_dev, oracle_decode, run_decode, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -36,12 +37,62 @@ def check(d, got, name, batches=None, heads=None):
 @pytest.mark.parametrize("H,r,d_h", PAGE_SHAPES, ids=[f"H{h}_r{r}_dh{d}" for h, r, d in PAGE_SHAPES])
 def test_page_ranks_full(H, r, d_h, dt):
     name = f"H{H}_r{r}_dh{d_h}_{dt}"
-    assert L.lrkv_decode_scan_kernel(TORCH_DT[dt], H, d_h, r) == "decode_generic_kernel"
+    want = "decode_mfma_any_kernel" if dt == "bf16" and r <= 112 else "decode_generic_kernel"
+    assert L.lrkv_decode_scan_kernel(TORCH_DT[dt], H, d_h, r) == want
     lens = np.array([700, 333, 1, 65], np.int32)           # several tiles, a ragged tail, one token
-    say(f"case {name} lens={lens.tolist()}")
+    say(f"case {name} lens={lens.tolist()} ({want})")
     d = decode_inputs(DecodeWorkload(name, 4, H, d_h, r, 700, dt, 4711 + H + r), lens=lens)
     check(d, run_decode(d), name)
     check(d, run_decode(d, split_tokens=128), name + " split 128")
+    if dt == "bf16":
+        other = 3 if want == "decode_mfma_any_kernel" else 4
+        say(f"case {name} on engine {other}")
+        check(d, run_decode(d, engine=other), f"{name} engine {other}")
+        check(d, run_decode(d, engine=other, split_tokens=128), f"{name} engine {other} split 128")
+
+
+# (heads, rank) for the any-rank MFMA scan: every window size (8 to 32 words
+# per lane), odd ranks (windows starting mid-word for odd heads), fewer than
+# 32 heads (idle lanes), more than 32 (a partial second group of heads), an
+# odd head count at an even rank, and the ranks the tuned scans also take.
+MFMA_ANY_SHAPES = [(2, 9), (4, 12), (6, 13), (32, 17), (8, 23), (32, 31), (10, 33), (12, 46), (12, 51),
+                   (32, 54), (18, 55), (16, 63), (4, 65), (40, 51), (33, 54), (2, 77), (6, 96), (2, 101),
+                   (2, 127), (6, 128), (32, 16), (64, 32)]
+
+
+@pytest.mark.parametrize("H,r", MFMA_ANY_SHAPES, ids=[f"H{h}_r{r}" for h, r in MFMA_ANY_SHAPES])
+def test_mfma_any_rank_sweep(H, r):
+    """The any-rank MFMA scan (engine 4) at bf16, head_dim 128: several tiles
+    per wave, ragged tails, one token, an empty sequence; default split and
+    two fixed ones."""
+    name = f"H{H}_r{r}_mfma_any"
+    lens = np.array([300, 97, 1, 0, 33], np.int32)
+    say(f"case {name} lens={lens.tolist()}")
+    d = decode_inputs(DecodeWorkload(name, 5, H, 128, r, 300, "bf16", 900 + 7 * H + r), lens=lens)
+    live = [0, 1, 2, 4]
+    for split in (0, 128, 256):
+        got = run_decode(d, engine=4, split_tokens=split)
+        assert np.all(got[3] == 0), "empty sequence"
+        check(d, got, f"{name} split {split}", batches=live)
+
+
+def test_mfma_any_phases_and_tail_tiles():
+    """Scan and merge called apart (lrkv_decode_partial / lrkv_decode_combine
+    through engine 4), at lengths that leave every wave of a split a
+    different number of tiles and a partial last tile."""
+    H, r = 12, 51
+    lens = np.array([1, 31, 32, 33, 127, 128, 129, 511], np.int32)
+    d = decode_inputs(DecodeWorkload("phases", len(lens), H, 128, r, 512, "bf16", 4242), lens=lens)
+    cache = device_cache(d)
+    dl = torch.from_numpy(lens).cuda()
+    q, bk, bv = (to_dev(d[k], "bf16") for k in ("q", "b_k", "b_v"))
+    for split in (0, 128, 512):
+        call = L.DecodeCall(cache, dl, 512, q, bk, bv, split_tokens=split, engine=4)
+        call.partial()
+        call.combine()
+        torch.cuda.synchronize()
+        say(f"case phases H{H} r{r} split {split}")
+        check(d, from_dev(call.out), f"phases split {split}")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])

@@ -64,6 +64,19 @@ def test_noalloc_matches_workspace_vector_scan_then_smaller():
                split_tokens=64)
 
 
+def test_noalloc_matches_workspace_any_rank_mfma_then_smaller():
+    # the any-rank MFMA scan keeps the absorbed queries in the scratch too
+    wl = DECODE_WORKLOADS["rank54_bf16_T8k"]
+    assert L.lrkv_decode_scan_kernel(torch.bfloat16, wl.heads, wl.head_dim, wl.rank) == "decode_mfma_any_kernel"
+    lens = np.array([1000, 999, 513, 1, 64, 65], np.int32)
+    say(f"case noalloc {wl.name} batch=6 capacity=1000 lens={lens.tolist()}")
+    check_pair(decode_inputs(wl, batch=6, capacity=1000, lens=lens, seed=34), "any-rank mfma scan, first call")
+    lens2 = np.array([300, 0], np.int32)
+    say(f"case noalloc {wl.name} batch=2 capacity=300 lens={lens2.tolist()} split=128")
+    check_pair(decode_inputs(wl, batch=2, capacity=300, lens=lens2, seed=35), "any-rank mfma scan, smaller",
+               split_tokens=128)
+
+
 def test_noalloc_rejects_requests_beyond_scratch():
     # host validation only: the workspace this fixed split needs (73 MiB) is
     # above the 16 MiB scratch, so the call returns before any launch
