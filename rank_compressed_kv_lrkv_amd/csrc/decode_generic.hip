@@ -275,14 +275,37 @@ __global__ __launch_bounds__(kGnThreads) void decode_generic_kernel(GnParams p) 
 
 // Merge of the partial states of one (sequence, head), with the residual
 // up-projection applied once (Eq. (7)): o = (sum_j w_j acc_s_j + B^V_h sum_j
-// w_j acc_z_j) / L, w_j = 2^(m_j - M), L = sum_j w_j l_j.  Thread t folds
-// merged dims t, t + 256, ... (d_h + r of them).
+// w_j acc_z_j) / L, w_j = 2^(m_j - M), L = sum_j w_j l_j.  The partials' maxima
+// and weights are spread over the threads (block reductions), each thread
+// folds merged dims t, t + 256, ... (d_h + r of them) with the weights from
+// LDS, and for bf16 B^V_h is staged in LDS (coalesced) before thread d < d_h
+// forms its row's product.
+constexpr int kMgW = 1024;                          // partial weights held in LDS per pass
+
+static __device__ __forceinline__ float block_reduce(float v, float* s_red, bool is_max) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float u = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();                                  // s_red free from any earlier use
+  if ((threadIdx.x & 63) == 0) s_red[w] = v;
+  __syncthreads();
+  return is_max ? fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]))
+                : (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+}
+
 template <class E>
 __global__ __launch_bounds__(kGnThreads) void decode_merge_generic_kernel(
     const float* __restrict__ ws_ml, const float* __restrict__ ws_acc, const int32_t* __restrict__ seq_lens,
     const void* b_v, void* out, int heads, int head_dim, int rank, int partials, int split_tokens, int max_len) {
   using T = typename E::T;
+  static_assert(kGnThreads == 256, "four waves");
+  constexpr bool kStageBv = E::kBytes == 2;
   __shared__ float s_a[kGenericMaxDims];
+  __shared__ float s_w[kMgW];
+  __shared__ float s_red[4];
+  __shared__ __attribute__((aligned(16))) uint16_t s_bv[kStageBv ? 128 * kGenericMaxRank : 8];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int D = head_dim + rank;
   int len = seq_lens[b];
@@ -292,28 +315,82 @@ __global__ __launch_bounds__(kGnThreads) void decode_merge_generic_kernel(
     for (int d = tid; d < head_dim; d += kGnThreads) o[d] = E::from_f32(0.f);
     return;
   }
+  // B^V_h staged while the partial states are merged: head_dim rows of rank
+  // bf16, 16-byte aligned as a whole (head_dim a multiple of 16), in 16-byte
+  // chunks, all of a thread's loads issued before any store
+  constexpr int kMaxCh = kStageBv ? 128 * kGenericMaxRank * 2 / 16 / kGnThreads : 1;
+  const int nch = kStageBv ? head_dim * rank * 2 / 16 : 0;
+  u32x4 c[kMaxCh];
+  if constexpr (kStageBv) {
+    const u32x4* bv = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(b_v) + size_t(h) * head_dim * rank);
+#pragma unroll
+    for (int k = 0; k < kMaxCh; ++k) {
+      const int i = tid + k * kGnThreads;
+      if (i < nch) c[k] = bv[i];
+    }
+  }
   const int n = (len + split_tokens - 1) / split_tokens;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + size_t(b) * partials * heads + h;
-  float M = -INFINITY;
-  for (int j = 0; j < n; ++j) M = fmaxf(M, ml[size_t(j) * heads].x);
-  float L = 0.f;
-  for (int j = 0; j < n; ++j) {
-    const float2 v = ml[size_t(j) * heads];
-    L = __builtin_fmaf(fast_exp2(v.x - M), v.y, L);
-  }
-  for (int d = tid; d < D; d += kGnThreads) {
-    float a = 0.f;
-    for (int j = 0; j < n; ++j) {
-      const size_t st = (size_t(b) * partials + j) * heads + h;
-      a = __builtin_fmaf(fast_exp2(ml[size_t(j) * heads].x - M), ws_acc[st * D + d], a);
+  float mloc = -INFINITY;
+  for (int j = tid; j < n; j += kGnThreads) mloc = fmaxf(mloc, ml[size_t(j) * heads].x);
+  if constexpr (kStageBv) {                         // stored once the partials' maxima are in flight
+#pragma unroll
+    for (int k = 0; k < kMaxCh; ++k) {
+      const int i = tid + k * kGnThreads;
+      if (i < nch) reinterpret_cast<u32x4*>(s_bv)[i] = c[k];
     }
-    s_a[d] = a;
+  }
+  const float M = block_reduce(mloc, s_red, true);
+  float acc[(kGenericMaxDims + kGnThreads - 1) / kGnThreads];
+#pragma unroll
+  for (int k = 0; k < (kGenericMaxDims + kGnThreads - 1) / kGnThreads; ++k) acc[k] = 0.f;
+  float lloc = 0.f;
+  for (int j0 = 0; j0 < n; j0 += kMgW) {
+    const int nj = min(kMgW, n - j0);
+    __syncthreads();                                // s_w free from the previous pass
+    for (int j = tid; j < nj; j += kGnThreads) {
+      const float2 v = ml[size_t(j0 + j) * heads];
+      const float w = fast_exp2(v.x - M);
+      s_w[j] = w;
+      lloc = __builtin_fmaf(w, v.y, lloc);
+    }
+    __syncthreads();
+    const float* src = ws_acc + ((size_t(b) * partials + j0) * heads + h) * D;
+    const size_t step = size_t(heads) * D;
+#pragma unroll
+    for (int k = 0; k < (kGenericMaxDims + kGnThreads - 1) / kGnThreads; ++k) {
+      const int d = tid + k * kGnThreads;
+      if (d < D) {
+        float a = acc[k];
+        int j = 0;
+        for (; j + 8 <= nj; j += 8) {               // eight partial loads in flight
+          float x[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) x[u] = src[size_t(j + u) * step + d];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) a = __builtin_fmaf(s_w[j + u], x[u], a);
+        }
+        for (; j < nj; ++j) a = __builtin_fmaf(s_w[j], src[size_t(j) * step + d], a);
+        acc[k] = a;
+      }
+    }
+  }
+  const float L = block_reduce(lloc, s_red, false);
+#pragma unroll
+  for (int k = 0; k < (kGenericMaxDims + kGnThreads - 1) / kGnThreads; ++k) {
+    const int d = tid + k * kGnThreads;
+    if (d < D) s_a[d] = acc[k];
   }
   __syncthreads();
   for (int d = tid; d < head_dim; d += kGnThreads) {
     float a = s_a[d];
-    for (int i = 0; i < rank; ++i)
-      a = __builtin_fmaf(gn_elem<E>(b_v, (size_t(h) * head_dim + d) * rank + i), s_a[head_dim + i], a);
+    if constexpr (kStageBv) {
+      const uint16_t* row = s_bv + d * rank;
+      for (int i = 0; i < rank; ++i) a = __builtin_fmaf(bf16_to_f32(row[i]), s_a[head_dim + i], a);
+    } else {
+      for (int i = 0; i < rank; ++i)
+        a = __builtin_fmaf(gn_elem<E>(b_v, (size_t(h) * head_dim + d) * rank + i), s_a[head_dim + i], a);
+    }
     o[d] = E::from_f32(a / L);
   }
 }

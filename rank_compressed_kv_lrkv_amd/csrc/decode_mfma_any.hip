@@ -130,32 +130,58 @@ struct MaParams {
 };
 
 // q~[b][h][e] = sum_d q[b][h][d] B^K_h[d][e] (the absorbed query of Eq. (6)),
-// fp32.  Grid (heads, ceil(batch / 4)); thread (e, s) takes element e < rank
-// for sequences 4y + 2s and 4y + 2s + 1.
+// fp32.  Grid (heads, ceil(batch / 8)), 256 threads: thread (e, g) takes
+// elements e, e + 64, ... below the rank and the 32 dims d = 32g .. 32g + 31
+// for 8 sequences (all 32 loads of a column slice in flight at once); the
+// four dim slices are added in LDS.
+constexpr int kAbSeq = 8;
 __global__ __launch_bounds__(256) void decode_absorb_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ b_k, float* __restrict__ qt,
                                                             int batch, int heads, int rank) {
-  constexpr int DH = kMaDH;
-  __shared__ float s_q[4][DH];
-  const int h = blockIdx.x, b0 = blockIdx.y * 4, tid = threadIdx.x;
-  for (int i = tid; i < 4 * DH; i += 256) {
-    const int s = i / DH, d = i % DH, bb = b0 + s;
-    s_q[s][d] = bb < batch ? bf16_to_f32(q[(size_t(bb) * heads + h) * DH + d]) : 0.f;
+  constexpr int DH = kMaDH, DS = DH / 4;
+  __shared__ float s_q[kAbSeq][DH];
+  __shared__ float s_part[4][kAbSeq][64];
+  const int h = blockIdx.x, b0 = blockIdx.y * kAbSeq, tid = threadIdx.x;
+  const int el = tid & 63, g = tid >> 6;
+  // column slice of B^K_h for elements e0 + el (every load unconditional)
+  float w[DS];
+  auto load_w = [&](int e0) {
+    const int e = e0 + el < rank ? e0 + el : rank - 1;
+#pragma unroll
+    for (int k = 0; k < DS; ++k) w[k] = bf16_to_f32(b_k[(size_t(h) * DH + DS * g + k) * rank + e]);
+  };
+  load_w(0);                                                 // in flight while the queries are staged
+  float qv[kAbSeq * DH / 256];
+#pragma unroll
+  for (int k = 0; k < kAbSeq * DH / 256; ++k) {          // all loads issued before any store
+    const int i = tid + 256 * k, s = i / DH, d = i % DH, bb = b0 + s < batch ? b0 + s : batch - 1;
+    qv[k] = bf16_to_f32(q[(size_t(bb) * heads + h) * DH + d]);
+  }
+#pragma unroll
+  for (int k = 0; k < kAbSeq * DH / 256; ++k) {
+    const int i = tid + 256 * k;
+    s_q[i / DH][i % DH] = qv[k];                             // rows past the batch: never written out
   }
   __syncthreads();
-  const int e = tid & 127, s = tid >> 7;
-  if (e >= rank) return;
-  const uint16_t* col = b_k + size_t(h) * DH * rank + e;
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll 16
-  for (int d = 0; d < DH; ++d) {
-    const float w = bf16_to_f32(col[size_t(d) * rank]);
-    a0 = __builtin_fmaf(s_q[2 * s][d], w, a0);
-    a1 = __builtin_fmaf(s_q[2 * s + 1][d], w, a1);
+  for (int e0 = 0; e0 < rank; e0 += 64) {                  // uniform
+    if (e0 > 0) load_w(e0);
+#pragma unroll
+    for (int s = 0; s < kAbSeq; ++s) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < DS; ++k) acc = __builtin_fmaf(s_q[s][DS * g + k], w[k], acc);
+      s_part[g][s][el] = acc;
+    }
+    __syncthreads();
+    // thread (el, g) adds the four slices for sequences 2g and 2g + 1
+    const int e = e0 + el;
+#pragma unroll
+    for (int s = 2 * g; s < 2 * g + 2; ++s) {
+      const float v = (s_part[0][s][el] + s_part[1][s][el]) + (s_part[2][s][el] + s_part[3][s][el]);
+      if (e < rank && b0 + s < batch) qt[(size_t(b0 + s) * heads + h) * rank + e] = v;
+    }
+    __syncthreads();
   }
-  const int bb = b0 + 2 * s;
-  if (bb < batch) qt[(size_t(bb) * heads + h) * rank + e] = a0;
-  if (bb + 1 < batch) qt[(size_t(bb + 1) * heads + h) * rank + e] = a1;
 }
 
 template <int NAB, bool ODD>
@@ -571,7 +597,7 @@ bool decode_mfma_any_preferred(int dtype, int head_dim, int rank, int heads) {
 
 hipError_t launch_decode_mfma_any(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
   if ((phase & 1) && pl.n_splits > 0) {
-    const dim3 agrid(pl.heads, (pl.batch + 3) / 4);
+    const dim3 agrid(pl.heads, (pl.batch + kAbSeq - 1) / kAbSeq);
     hipLaunchKernelGGL(decode_absorb_kernel, agrid, dim3(256), 0, st, static_cast<const uint16_t*>(a.q),
                        static_cast<const uint16_t*>(a.b_k), a.ws_qt, pl.batch, pl.heads, pl.rank);
     hipError_t e = hipGetLastError();
