@@ -82,6 +82,7 @@ KERNEL_SOURCES = {
     "prefill_kernel": ("prefill.hip", "lrkv_device.h"),
     "project_gemm_kernel": ("project.hip", "lrkv_device.h"),
     "decode_generic_kernel": ("decode_generic.hip", "lrkv_device.h"),
+    "decode_mfma_any_kernel": ("decode_mfma_any.hip", "lrkv_device.h"),
     "train_dkv_kernel": ("train.hip", "lrkv_device.h"),
     "train_dq_kernel": ("train.hip", "lrkv_device.h"),
 }
@@ -310,8 +311,13 @@ def measure_decode(args, wl, d, rotate_mb: float = 0.0, engine: int = 0):
     scan_kernel = {1: "decode_split_kernel", 2: "decode_mfma_kernel", 3: "decode_generic_kernel",
                    4: "decode_mfma_any_kernel"}.get(engine) or \
         L.lrkv_decode_scan_kernel(dt, H, d_h, r)
+    # the any-rank scans merge with decode_merge_generic_kernel; the MFMA one's
+    # scan phase also runs decode_absorb_kernel (the absorbed queries) first
+    merge_kernel = ("decode_merge_generic_kernel" if scan_kernel in ("decode_generic_kernel", "decode_mfma_any_kernel")
+                    else "decode_merge_kernel")
     traffic = None
-    for rec_name in ("decode_scan_counters", "decode_valu_scan_counters", "decode_ragged_counters"):
+    for rec_name in ("decode_scan_counters", "decode_valu_scan_counters", "decode_ragged_counters",
+                     "decode_any_rank_counters"):
         traffic = traffic or traffic_from_profiles(rec_name, scan_kernel, wl.name, args.split_tokens)
     return {
         "tokens": tokens, "tokens_per_s": tokens / (step_ms * 1e-3), "step_ms": step_ms,
@@ -322,7 +328,9 @@ def measure_decode(args, wl, d, rotate_mb: float = 0.0, engine: int = 0):
                    "cache_MB": cache_bytes / 1e6},
         "hbm_GBps_step": step_bytes / (step_ms * 1e-3) / 1e9,
         "hbm_frac_step": step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "kernels_ms": {scan_kernel: scan_ms, "decode_merge_kernel": comb_ms},
+        "kernels_ms": {scan_kernel: scan_ms, merge_kernel: comb_ms},
+        "scan_phase_kernels": (["decode_absorb_kernel", scan_kernel] if scan_kernel == "decode_mfma_any_kernel"
+                               else [scan_kernel]),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": scan_kernel, "algorithmic_bytes_per_launch": scan_bytes},
@@ -406,12 +414,12 @@ def other_configs(args):
     torch.cuda.empty_cache()
     progress("ragged_bf16_T1k_64k done")
     # Decode at a rank the pages train (Table 7's largest model: 32 heads,
-    # rank 54), on the any-rank scan.
+    # rank 54), on the any-rank MFMA scan.
     wl = DECODE_WORKLOADS["rank54_bf16_T8k"]
     d = decode_inputs(wl)
     m = measure_decode(args, wl, d)
     o = oracle_decode_check(d, m["out"], as_f64, budget_s=5.0)
-    res[wl.name] = {"kind": "throughput (any-rank scan)", "cache_tokens": m["tokens"],
+    res[wl.name] = {"kind": "throughput (any-rank MFMA scan)", "cache_tokens": m["tokens"],
                     "cache_tokens_per_s": m["tokens_per_s"], "step_ms": m["step_ms"], "kernels_ms": m["kernels_ms"],
                     "hbm_GBps_step": m["hbm_GBps_step"], "hbm_frac_step": m["hbm_frac_step"],
                     "roofline": m["roofline"], "config": m["config"],

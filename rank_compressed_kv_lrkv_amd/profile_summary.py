@@ -28,6 +28,11 @@ ROOT = os.path.dirname(HERE)
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
+def short_name(name):
+    """Kernel name without `void`, the library namespace and an anonymous one."""
+    return name.replace("void ", "").replace("(anonymous namespace)::", "").replace("lrkv::", "")
+
+
 def counter_means(path, counter):
     """Mean value of `counter` per dispatch, keyed by kernel name (without
     arguments).  For the copy kernel only the dispatches of the largest grid
@@ -43,7 +48,7 @@ def counter_means(path, counter):
     for row in rows:
         if COPY_KERNEL in row["Kernel_Name"] and int(row["Grid_Size"]) != copy_grid:
             continue
-        name = row["Kernel_Name"].split("(")[0].replace("void ", "").replace("lrkv::", "")
+        name = short_name(row["Kernel_Name"]).split("(")[0]
         tot, n = acc.get(name, (0.0, 0))
         acc[name] = (tot + float(row["Counter_Value"]), n + 1)
     return {k: t / n for k, (t, n) in acc.items()}
@@ -59,7 +64,7 @@ def pick(means, kernel):
 def trace_stats(path, kernel):
     with open(path) as f:
         for row in csv.DictReader(f):
-            if row["Name"].replace("void ", "").replace("lrkv::", "").startswith(kernel):
+            if short_name(row["Name"]).startswith(kernel):
                 return {"calls": int(row["Calls"]), "avg_us": float(row["AverageNs"]) / 1e3,
                         "min_us": float(row["MinNs"]) / 1e3, "max_us": float(row["MaxNs"]) / 1e3}
     raise SystemExit(f"{kernel} not in {path}")
