@@ -21,21 +21,25 @@
 // tile ahead.  Lane l owns head l%32 of the group and, in every tile, the 16
 // tokens 8(i/4) + 4(l/32) + i%4 of the accumulator layout.
 //
-// Latent terms.  Lane (head j, half hf) covers a window of 2*NAB consecutive
-// elements of head j's latent row: half 0 the first 2*NAB, half 1 the last
-// 2*NAB.  Both windows lie inside the row; where they overlap, half 1 skips
-// its copy (zero absorbed query there, and those sums are not written).  For
-// each accumulator row the lane loads its window of the two tokens the row
-// holds in the two lane halves: NAB words from the 4-byte boundary at or
-// below the window, plus one word when the rank is odd (the window then
-// starts mid-word for odd heads, and v_alignbyte shifts each word pair back
-// onto bf16 pairs).  So no load reaches past the end of the row it serves,
-// and none is partly outside the split's buffer range; rows past the split's
-// end fall outside the split's buffer range (zeros).  Per token the lane
-// forms a 2-wide bf16 dot over its window, and one cross-half swap
-// (v_permlane32_swap) adds the two halves' dots of each token into the lane
-// that holds it; the weights go the other way for sum_t p_t z^V_{t,h}, with
-// 2-wide dots over token pairs.  Latents are loaded with the cached policy:
+// Latent terms.  With fewer heads than MFMA columns each head fills F = 1, 2
+// or 4 columns (column j holds head j % (32/F); the shared term is simply
+// computed F times), so a head owns 2F lanes: (column, half).  Lane slice k
+// = 2 (j / (32/F)) + hf covers a window of 2*NAB consecutive elements of the
+// head's latent row: slices 0..2F-2 start at k * 2*NAB, the last one ends at
+// the row's end.  All windows lie inside the row; where the last overlaps its
+// neighbour it skips its copy (zero absorbed query there, and those sums are
+// not written).  For each accumulator row the lane loads its window of the
+// two tokens the row holds in the two lane halves: NAB words from the 4-byte
+// boundary at or below the window, plus one word when the rank is odd (the
+// window then starts mid-word in some heads, and v_alignbyte shifts each
+// word pair back onto bf16 pairs).  So no load reaches past the end of the
+// row it serves, and none is partly outside the split's buffer range; rows
+// past the split's end fall outside the split's buffer range (zeros).  Per
+// token the lane forms a 2-wide bf16 dot over its window; xor-lane swizzles
+// add the F column copies, and one cross-half swap (v_permlane32_swap) adds
+// the two halves' dots of each token into the lanes that hold it; the
+// weights go the other way for sum_t p_t z^V_{t,h}, with 2-wide dots over
+// token pairs.  Latents are loaded with the cached policy:
 // a wave's loads for one token cover its contiguous run of all heads in
 // overlapping pieces, which the L1 then serves.
 //
@@ -88,13 +92,29 @@ __device__ __forceinline__ float sum_halves(float a, float b) {
   return __uint_as_float(x0) + __uint_as_float(x1);
 }
 
-// Words per lane window: half of a row's ceil(r/2) bf16 pairs, rounded up to
-// whole 16-byte loads.
-constexpr int window_words(int rank) { return ((((rank + 1) / 2 + 1) / 2) + 3) / 4 * 4; }
+// Words per lane window with F column copies per head: a 2F-th of a row's
+// ceil(r/2) bf16 pairs, rounded up to whole 16-byte loads.
+constexpr int window_words(int rank, int f) { return ((((rank + 1) / 2 + 2 * f - 1) / (2 * f)) + 3) / 4 * 4; }
 
-template <int NAB, bool ODD>
+// The 2F windows of 2*NAB elements fit a row as laid out (slices 0..2F-2 end
+// inside it, with the extra word of an odd rank) and cover it.
+constexpr bool windows_fit(int rank, int f) {
+  const int nab = window_words(rank, f);
+  return (2 * f - 1) * 2 * nab <= rank - (rank & 1) && 2 * f * 2 * nab >= rank;
+}
+
+// Column copies per head: as many as the head count allows (32 / F heads per
+// workgroup) and the windows fit.
+constexpr int column_copies(int rank, int heads) {
+  if (heads <= 8 && windows_fit(rank, 4)) return 4;
+  if (heads <= 16 && windows_fit(rank, 2)) return 2;
+  return 1;
+}
+
+template <int NAB, bool ODD, int F>
 struct MaShape {
   static constexpr int DH = kMaDH;
+  static constexpr int HP = kMaHeads / F;      // heads per workgroup
   static constexpr int KC = DH / 16;           // k-chunks of the score MFMA
   static constexpr int VB = DH / 32;           // 32-feature blocks of the value MFMA
   static constexpr int RB = DH * 2;            // bytes per shared row
@@ -115,6 +135,7 @@ struct MaShape {
   static constexpr int FOLD = (kMaWaves * 64 * P + kMaWaves * kMaHeads) * 4;
   static constexpr int LDS = TILES > FOLD ? TILES : FOLD;
   static_assert(NAB % 4 == 0 && NAB >= 4 && NAB <= 32, "window of whole 16-byte loads");
+  static_assert(F == 1 || F == 2 || F == 4, "column copies");
   static_assert((2 * NG) % D == 0, "ring slots repeat every tile");
 };
 
@@ -184,10 +205,10 @@ __global__ __launch_bounds__(256) void decode_absorb_kernel(const uint16_t* __re
   }
 }
 
-template <int NAB, bool ODD>
+template <int NAB, bool ODD, int F>
 __global__ __attribute__((amdgpu_flat_work_group_size(kMaThreads, kMaThreads), amdgpu_waves_per_eu(1)))
 void decode_mfma_any_kernel(MaParams p) {
-  using S = MaShape<NAB, ODD>;
+  using S = MaShape<NAB, ODD, F>;
   constexpr int DH = S::DH;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
@@ -195,8 +216,10 @@ void decode_mfma_any_kernel(MaParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, hf = lane >> 5;
   const int H = p.heads, R = p.rank;
-  const int h = int(blockIdx.y) * kMaHeads + j;
+  const int copy = j / S::HP;                                // column copy of this lane's head
+  const int h = int(blockIdx.y) * S::HP + j % S::HP;
   const bool hv = h < H;                                     // lanes past the last head compute nothing kept
+  const int slice = 2 * copy + hf;                           // this lane's window of the head's latent row
   const int b = blockIdx.z;
 
   // This workgroup's split: tokens [lo, hi) of sequence b (uniform exits).
@@ -226,10 +249,12 @@ void decode_mfma_any_kernel(MaParams p) {
       buffer_resource(static_cast<const unsigned char*>(p.z_v) + row0 * ztok, uint32_t(nwg) * ztok);
 
   // This lane's window: elements [wofs, wofs + 2 NAB) of head h's row.  Its
-  // byte in token 0 is wbyte (2 mod 4 for odd heads at an odd rank); loads
+  // byte in token 0 is wbyte (2 mod 4 where h * r + wofs is odd); loads
   // start at the boundary below, and `sh` is the byte shift back onto the
   // window's pairs.
-  const int wofs = hf ? R - 2 * NAB : 0;
+  const bool last = slice == 2 * F - 1;
+  const int wofs = last ? R - 2 * NAB : slice * 2 * NAB;
+  const int ov = last ? 2 * F * 2 * NAB - R : 0;             // leading elements the previous slice covers
   const uint32_t wbyte = (uint32_t(h) * uint32_t(R) + uint32_t(wofs)) * 2;
   const uint32_t wload = wbyte & ~3u;
   const uint32_t sh = wbyte & 3u;
@@ -306,7 +331,6 @@ void decode_mfma_any_kernel(MaParams p) {
   __builtin_amdgcn_sched_barrier(0);
   uint32_t qh[NAB];                                          // the window of q~_h as bf16 pairs
   {
-    const int ov = hf ? 4 * NAB - R : 0;                     // leading window elements half 0 covers
 #pragma unroll
     for (int w = 0; w < NAB; ++w) {
       const float x0 = (hv && 2 * w >= ov) ? qv[2 * w] : 0.f;
@@ -378,6 +402,14 @@ void decode_mfma_any_kernel(MaParams p) {
           for (int w = 0; w < NAB; ++w) {
             pa = BF16::dot2(pa, qh[w], wword(ring[slot][t][0], w));
             pb = BF16::dot2(pb, qh[w], wword(ring[slot][t][1], w));
+          }
+          if constexpr (F >= 4) {                             // copies j, j ^ 8 (within each half)
+            pa += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(pa), 0x201F));
+            pb += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(pb), 0x201F));
+          }
+          if constexpr (F >= 2) {                             // copies j, j ^ 16
+            pa += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(pa), 0x401F));
+            pb += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(pb), 0x401F));
           }
           s[a * S::KG + t] += sum_halves(pa, pb);
         }
@@ -532,11 +564,10 @@ void decode_mfma_any_kernel(MaParams p) {
         const float4 v = *reinterpret_cast<const float4*>(src0 + w * 64 * P + 16 * f + 4 * r4);
         a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
       }
-      if (hv) *reinterpret_cast<float4*>(out_acc + 32 * f + 8 * r4 + 4 * hf) = a;
+      if (hv && copy == 0) *reinterpret_cast<float4*>(out_acc + 32 * f + 8 * r4 + 4 * hf) = a;
     }
   }
   if (S::VB % kMaWaves == wave) {
-    const int ov = hf ? 4 * NAB - R : 0;
 #pragma unroll
     for (int i = 0; i < 2 * NAB; ++i) {
       float a = src0[16 * S::VB + i];
@@ -550,13 +581,13 @@ void decode_mfma_any_kernel(MaParams p) {
     uint32_t x0 = __float_as_uint(ls), x1 = x0;
     swap_halves(x0, x1);                                     // the two halves' sums of this head
     ls = __uint_as_float(x0) + __uint_as_float(x1);
-    if (hf == 0 && hv) *reinterpret_cast<float2*>(p.ws_ml + 2 * pidx) = make_float2(M, ls);
+    if (hf == 0 && copy == 0 && hv) *reinterpret_cast<float2*>(p.ws_ml + 2 * pidx) = make_float2(M, ls);
   }
 }
 
-template <int NAB, bool ODD>
+template <int NAB, bool ODD, int F>
 static hipError_t launch_any_t(const DecodePlan& pl, const DecodeArgs& a, hipStream_t st) {
-  using S = MaShape<NAB, ODD>;
+  using S = MaShape<NAB, ODD, F>;
   MaParams kp;
   kp.k_s = a.k_s; kp.v_s = a.v_s; kp.z_k = a.z_k; kp.z_v = a.z_v;
   kp.seq_lens = a.seq_lens; kp.q = a.q; kp.qt = a.ws_qt;
@@ -565,16 +596,50 @@ static hipError_t launch_any_t(const DecodePlan& pl, const DecodeArgs& a, hipStr
   kp.max_len = pl.max_len; kp.split_tokens = pl.split_tokens;
   kp.capacity = pl.capacity;
   kp.ws_ml = a.ws_ml; kp.ws_acc = a.ws_acc;
-  const hipError_t attr = allow_dynamic_lds<&decode_mfma_any_kernel<NAB, ODD>>(S::LDS);
+  const hipError_t attr = allow_dynamic_lds<&decode_mfma_any_kernel<NAB, ODD, F>>(S::LDS);
   if (attr != hipSuccess) return attr;
-  const dim3 grid(pl.n_splits, (pl.heads + kMaHeads - 1) / kMaHeads, pl.batch);
-  hipLaunchKernelGGL((decode_mfma_any_kernel<NAB, ODD>), grid, dim3(kMaThreads), size_t(S::LDS), st, kp);
+  const dim3 grid(pl.n_splits, (pl.heads + S::HP - 1) / S::HP, pl.batch);
+  hipLaunchKernelGGL((decode_mfma_any_kernel<NAB, ODD, F>), grid, dim3(kMaThreads), size_t(S::LDS), st, kp);
   return hipGetLastError();
 }
 
-template <int NAB>
-static hipError_t launch_any_odd(const DecodePlan& pl, const DecodeArgs& a, hipStream_t st) {
-  return (pl.rank & 1) ? launch_any_t<NAB, true>(pl, a, st) : launch_any_t<NAB, false>(pl, a, st);
+// Instances: window words NAB up to 32 / F (a 2F-th of a rank-128 row).
+template <int F, int NAB>
+static hipError_t launch_any_nab(const DecodePlan& pl, const DecodeArgs& a, hipStream_t st) {
+  if constexpr (NAB * F <= 32) {
+    return (pl.rank & 1) ? launch_any_t<NAB, true, F>(pl, a, st) : launch_any_t<NAB, false, F>(pl, a, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <int F>
+static hipError_t launch_any_f(const DecodePlan& pl, const DecodeArgs& a, hipStream_t st) {
+  switch (window_words(pl.rank, F)) {
+    case 4: return launch_any_nab<F, 4>(pl, a, st);
+    case 8: return launch_any_nab<F, 8>(pl, a, st);
+    case 12: return launch_any_nab<F, 12>(pl, a, st);
+    case 16: return launch_any_nab<F, 16>(pl, a, st);
+    case 20: return launch_any_nab<F, 20>(pl, a, st);
+    case 24: return launch_any_nab<F, 24>(pl, a, st);
+    case 28: return launch_any_nab<F, 28>(pl, a, st);
+    case 32: return launch_any_nab<F, 32>(pl, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int F, int... N>
+static hipError_t prepare_f(std::integer_sequence<int, N...>) {
+  hipError_t e = hipSuccess;
+  auto one = [&](auto nab_c) {
+    constexpr int NAB = 4 * (decltype(nab_c)::value + 1);
+    if constexpr (NAB * F <= 32) {
+      if (e == hipSuccess) e = allow_dynamic_lds<&decode_mfma_any_kernel<NAB, false, F>>(MaShape<NAB, false, F>::LDS);
+      if (e == hipSuccess) e = allow_dynamic_lds<&decode_mfma_any_kernel<NAB, true, F>>(MaShape<NAB, true, F>::LDS);
+    }
+  };
+  (one(std::integral_constant<int, N>{}), ...);
+  return e;
 }
 
 }  // namespace
@@ -582,17 +647,16 @@ static hipError_t launch_any_odd(const DecodePlan& pl, const DecodeArgs& a, hipS
 bool decode_mfma_any_supported(int dtype, int head_dim, int rank, int heads) {
   if (dtype != 1 || head_dim != kMaDH || rank < 8 || rank > kGenericMaxRank) return false;
   if (heads < 1 || heads > kGenericMaxHeads || (int64_t(heads) * rank) % 2 != 0) return false;
-  // both windows inside the row, and half 0's extra word (odd rank) too
-  return 2 * window_words(rank) <= rank - (rank & 1);
+  return windows_fit(rank, 1);                              // one copy per head always fits
 }
 
 // The default scan for the shapes both any-rank scans take: this one, but for
-// 32-word windows (ranks above 112) with fewer than 32 heads, where most lanes
-// idle and the per-lane chain is longest (B = 32, 8K context: 16 heads at
-// rank 128 708 us here against 563 us on decode_generic_kernel; 32 heads 880
-// against 1872).
+// 32-word windows (ranks above 112 with one column per head) with fewer than
+// 32 heads, where most lanes idle and each lane's chain is longest (B = 32,
+// 8K context, 20 heads at rank 128: the vector scan is faster).
 bool decode_mfma_any_preferred(int dtype, int head_dim, int rank, int heads) {
-  return decode_mfma_any_supported(dtype, head_dim, rank, heads) && (window_words(rank) < 32 || heads >= 32);
+  if (!decode_mfma_any_supported(dtype, head_dim, rank, heads)) return false;
+  return window_words(rank, column_copies(rank, heads)) < 32 || heads >= 32;
 }
 
 hipError_t launch_decode_mfma_any(const DecodePlan& pl, const DecodeArgs& a, int phase, hipStream_t st) {
@@ -602,16 +666,10 @@ hipError_t launch_decode_mfma_any(const DecodePlan& pl, const DecodeArgs& a, int
                        static_cast<const uint16_t*>(a.b_k), a.ws_qt, pl.batch, pl.heads, pl.rank);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    switch (window_words(pl.rank)) {
-      case 4: e = launch_any_odd<4>(pl, a, st); break;
-      case 8: e = launch_any_odd<8>(pl, a, st); break;
-      case 12: e = launch_any_odd<12>(pl, a, st); break;
-      case 16: e = launch_any_odd<16>(pl, a, st); break;
-      case 20: e = launch_any_odd<20>(pl, a, st); break;
-      case 24: e = launch_any_odd<24>(pl, a, st); break;
-      case 28: e = launch_any_odd<28>(pl, a, st); break;
-      case 32: e = launch_any_odd<32>(pl, a, st); break;
-      default: return hipErrorInvalidValue;
+    switch (column_copies(pl.rank, pl.heads)) {
+      case 4: e = launch_any_f<4>(pl, a, st); break;
+      case 2: e = launch_any_f<2>(pl, a, st); break;
+      default: e = launch_any_f<1>(pl, a, st); break;
     }
     if (e != hipSuccess) return e;
   }
@@ -620,12 +678,9 @@ hipError_t launch_decode_mfma_any(const DecodePlan& pl, const DecodeArgs& a, int
 }
 
 hipError_t decode_mfma_any_prepare() {
-  hipError_t e = hipSuccess;
-#define LRKV_MA(N)                                                                                          \
-  if (e == hipSuccess) e = allow_dynamic_lds<&decode_mfma_any_kernel<N, false>>(MaShape<N, false>::LDS);   \
-  if (e == hipSuccess) e = allow_dynamic_lds<&decode_mfma_any_kernel<N, true>>(MaShape<N, true>::LDS);
-  LRKV_MA(4) LRKV_MA(8) LRKV_MA(12) LRKV_MA(16) LRKV_MA(20) LRKV_MA(24) LRKV_MA(28) LRKV_MA(32)
-#undef LRKV_MA
+  hipError_t e = prepare_f<1>(std::make_integer_sequence<int, 8>{});
+  if (e == hipSuccess) e = prepare_f<2>(std::make_integer_sequence<int, 8>{});
+  if (e == hipSuccess) e = prepare_f<4>(std::make_integer_sequence<int, 8>{});
   return e;
 }
 

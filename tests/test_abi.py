@@ -61,7 +61,8 @@ def test_decode_scan_kernel_names():
     assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 54) == b"decode_mfma_any_kernel"  # the pages' ranks
     assert lib.lrkv_decode_scan_kernel(BF16, 18, 128, 55) == b"decode_mfma_any_kernel"
     assert lib.lrkv_decode_scan_kernel(BF16, 12, 128, 51) == b"decode_mfma_any_kernel"
-    assert lib.lrkv_decode_scan_kernel(BF16, 6, 128, 128) == b"decode_generic_kernel"   # rank > 112, < 32 heads
+    assert lib.lrkv_decode_scan_kernel(BF16, 6, 128, 128) == b"decode_mfma_any_kernel"  # four column copies
+    assert lib.lrkv_decode_scan_kernel(BF16, 20, 128, 128) == b"decode_generic_kernel"  # 32-word windows, < 32 heads
     assert lib.lrkv_decode_scan_kernel(BF16, 32, 128, 128) == b"decode_mfma_any_kernel"
     assert lib.lrkv_decode_scan_kernel(BF16, 6, 128, 112) == b"decode_mfma_any_kernel"
     assert lib.lrkv_decode_scan_kernel(F32, 6, 128, 128) == b"decode_generic_kernel"

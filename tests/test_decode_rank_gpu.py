@@ -37,7 +37,7 @@ def check(d, got, name, batches=None, heads=None):
 @pytest.mark.parametrize("H,r,d_h", PAGE_SHAPES, ids=[f"H{h}_r{r}_dh{d}" for h, r, d in PAGE_SHAPES])
 def test_page_ranks_full(H, r, d_h, dt):
     name = f"H{H}_r{r}_dh{d_h}_{dt}"
-    want = "decode_mfma_any_kernel" if dt == "bf16" and r <= 112 else "decode_generic_kernel"
+    want = "decode_mfma_any_kernel" if dt == "bf16" else "decode_generic_kernel"
     assert L.lrkv_decode_scan_kernel(TORCH_DT[dt], H, d_h, r) == want
     lens = np.array([700, 333, 1, 65], np.int32)           # several tiles, a ragged tail, one token
     say(f"case {name} lens={lens.tolist()} ({want})")
@@ -51,13 +51,14 @@ def test_page_ranks_full(H, r, d_h, dt):
         check(d, run_decode(d, engine=other, split_tokens=128), f"{name} engine {other} split 128")
 
 
-# (heads, rank) for the any-rank MFMA scan: every window size (8 to 32 words
-# per lane), odd ranks (windows starting mid-word for odd heads), fewer than
-# 32 heads (idle lanes), more than 32 (a partial second group of heads), an
-# odd head count at an even rank, and the ranks the tuned scans also take.
+# (heads, rank) for the any-rank MFMA scan: every window size (4 to 32 words
+# per lane), odd ranks (windows starting mid-word for odd heads), 1, 2, 4 and
+# 8 heads (four column copies per head), 9-16 heads (two), 17-31 heads (one,
+# idle lanes), more than 32 (a partial second group of heads), an odd head
+# count at an even rank, and the ranks the tuned scans also take.
 MFMA_ANY_SHAPES = [(2, 9), (4, 12), (6, 13), (32, 17), (8, 23), (32, 31), (10, 33), (12, 46), (12, 51),
                    (32, 54), (18, 55), (16, 63), (4, 65), (40, 51), (33, 54), (2, 77), (6, 96), (2, 101),
-                   (2, 127), (6, 128), (32, 16), (64, 32)]
+                   (2, 127), (6, 128), (32, 16), (64, 32), (16, 128), (8, 54), (20, 128), (1, 40)]
 
 
 @pytest.mark.parametrize("H,r", MFMA_ANY_SHAPES, ids=[f"H{h}_r{r}" for h, r in MFMA_ANY_SHAPES])
