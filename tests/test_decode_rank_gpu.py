@@ -77,6 +77,20 @@ def test_mfma_any_rank_sweep(H, r):
         check(d, got, f"{name} split {split}", batches=live)
 
 
+@pytest.mark.parametrize("H,r", [(7, 55), (20, 128)], ids=["H7_r55", "H20_r128"])
+def test_any_rank_default_vector_scan_shapes(H, r):
+    """bf16 shapes the default leaves on the any-rank vector scan: an odd
+    heads * rank (token runs not on 4-byte boundaries), and 32-word windows
+    with fewer than 32 heads."""
+    assert L.lrkv_decode_scan_kernel(torch.bfloat16, H, 128, r) == "decode_generic_kernel"
+    lens = np.array([300, 97, 1], np.int32)
+    say(f"case H{H}_r{r} default engine lens={lens.tolist()}")
+    d = decode_inputs(DecodeWorkload(f"H{H}_r{r}", 3, H, 128, r, 300, "bf16", 31 * H + r), lens=lens)
+    check(d, run_decode(d), f"H{H} r{r} default")
+    if H * r % 2 == 0:
+        check(d, run_decode(d, engine=4), f"H{H} r{r} engine 4")
+
+
 def test_mfma_any_phases_and_tail_tiles():
     """Scan and merge called apart (lrkv_decode_partial / lrkv_decode_combine
     through engine 4), at lengths that leave every wave of a split a
