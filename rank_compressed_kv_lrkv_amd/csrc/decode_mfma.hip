@@ -112,8 +112,8 @@ __device__ __forceinline__ constexpr int acc_row(int i, int hf) { return 8 * (i 
 // half replaced by the lower half of x1, x1 with its lower half replaced by
 // the upper half of x0).  For x0 = x1 = x the two results hold, in every
 // lane, the lower half's and the upper half's x; for (x0, x1) the sum of the
-// results in lane l is x0[l] + x1[l ^ 32] for l < 32 and x0[l ^ 32] + x1[l]
-// above.
+// results in lane l is x0[l] + x0[l ^ 32] for l < 32 and x1[l ^ 32] + x1[l]
+// above (the lower half gets x0 summed over both halves, the upper half x1).
 __device__ __forceinline__ void swap_halves(uint32_t& x0, uint32_t& x1) {
   const auto r = __builtin_amdgcn_permlane32_swap(x0, x1, false, false);
   x0 = r[0];

@@ -12,13 +12,13 @@
 // on a 4-byte boundary when r is odd.
 //
 // Work decomposition and the shared term follow decode_mfma_kernel: a
-// workgroup is 4 wave64 over one split of one sequence and one group of 32
-// heads (lanes of heads past the last one idle); the split's 32-token tiles
-// are dealt to the waves round-robin, and per tile
-//   S^T[t][h] = K_s[t][:] . Q[h][:]          (32 x d_h by d_h x 32)
-//   O_s^T[d][h] += V_s[t][d]^T . P^T[t][h]   (d_h x 32 by 32 x 32)
+// workgroup is 4 wave64 over one split of one sequence and one group of
+// 32/F heads (F below; lanes of heads past the last one idle); the split's
+// 32-token tiles are dealt to the waves round-robin, and per tile
+//   S^T[t][c] = K_s[t][:] . Q[c][:]          (32 x d_h by d_h x 32 columns)
+//   O_s^T[d][c] += V_s[t][d]^T . P^T[t][c]   (d_h x 32 by 32 x 32)
 // run on v_mfma_f32_32x32x16_bf16, the shared rows copied global -> LDS one
-// tile ahead.  Lane l owns head l%32 of the group and, in every tile, the 16
+// tile ahead.  Lane l owns MFMA column l%32 and, in every tile, the 16
 // tokens 8(i/4) + 4(l/32) + i%4 of the accumulator layout.
 //
 // Latent terms.  With fewer heads than MFMA columns each head fills F = 1, 2
@@ -39,9 +39,9 @@
 // add the F column copies, and one cross-half swap (v_permlane32_swap) adds
 // the two halves' dots of each token into the lanes that hold it; the
 // weights go the other way for sum_t p_t z^V_{t,h}, with 2-wide dots over
-// token pairs.  Latents are loaded with the cached policy:
-// a wave's loads for one token cover its contiguous run of all heads in
-// overlapping pieces, which the L1 then serves.
+// token pairs.  Latents are loaded with the cached policy: a wave's loads
+// for one token cover its contiguous run of all heads in overlapping
+// pieces, which the L1 then serves.
 //
 // The absorbed query q~_h = B^K_h^T q_h comes from decode_absorb_kernel (fp32
 // in the workspace), rounded once to bf16 here.  Partial states use the
