@@ -61,7 +61,7 @@ namespace {
 
 constexpr int kMaWaves = 4;
 constexpr int kMaThreads = 64 * kMaWaves;
-constexpr int kMaHeads = 32;            // heads per wave: the N dimension of the MFMA
+constexpr int kMaHeads = 32;            // MFMA columns per wave (heads times their copies): the N dimension
 constexpr int kMaTile = 32;             // cache tokens per tile: the M dimension
 constexpr int kMaDH = 128;              // head dimension
 constexpr float kMaStale = 8.f;         // running-max refresh threshold (log2 units)
@@ -129,7 +129,9 @@ struct MaShape {
   static constexpr int KG = NAB <= 20 ? 2 : 1;
   static constexpr int NG = 16 / KG;           // latent groups per tile and side
   static constexpr int GL = KG * 2 * LPW;      // loads per latent group
-  static constexpr int D = KG * WL <= 8 ? 4 : KG * WL <= 17 ? 2 : 1;   // latent groups in flight (register budget)
+  // latent groups in flight, by the registers a group holds (one at 16-word
+  // windows: deeper rings measured no faster there)
+  static constexpr int D = KG * WL <= 8 ? 4 : KG * WL <= 17 ? 2 : 1;
   static constexpr int TILES = kMaWaves * 2 * VT;
   static constexpr int P = 16 * VB + 2 * NAB + 4;          // floats per lane in the fold
   static constexpr int FOLD = (kMaWaves * 64 * P + kMaWaves * kMaHeads) * 4;
