@@ -77,6 +77,25 @@ def test_mfma_any_rank_sweep(H, r):
         check(d, got, f"{name} split {split}", batches=live)
 
 
+@pytest.mark.parametrize("B,H,r", [(19, 32, 54), (3, 1024, 8), (9, 96, 21), (17, 128, 10)],
+                         ids=["B19_H32_r54", "B3_H1024_r8", "B9_H96_r21", "B17_H128_r10"])
+def test_mfma_any_batches_and_many_heads(B, H, r):
+    """The any-rank MFMA scan with more than eight sequences (several
+    workgroup rows of the absorbed-query kernel, one of them partial) and with
+    many head groups, up to the 1024-head limit; ragged lengths."""
+    rng = np.random.default_rng(7 * B + H + r)
+    lens = rng.integers(1, 260, size=B).astype(np.int32)
+    lens[B // 2] = 0
+    name = f"B{B}_H{H}_r{r}_mfma_any"
+    say(f"case {name} lens={lens.tolist()}")
+    d = decode_inputs(DecodeWorkload(name, B, H, 128, r, 260, "bf16", 77 * B + H + r), lens=lens)
+    live = [b for b in range(B) if lens[b] > 0]
+    for split in (0, 128):
+        got = run_decode(d, engine=4, split_tokens=split)
+        assert np.all(got[B // 2] == 0), "empty sequence"
+        check(d, got, f"{name} split {split}", batches=live)
+
+
 @pytest.mark.parametrize("H,r", [(7, 55), (20, 128)], ids=["H7_r55", "H20_r128"])
 def test_any_rank_default_vector_scan_shapes(H, r):
     """bf16 shapes the default leaves on the any-rank vector scan: an odd
