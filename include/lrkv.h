@@ -251,15 +251,26 @@ lrkv_status lrkv_decode_ex(int32_t engine, int32_t phases,
                            int32_t split_tokens, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Name of the kernel lrkv_prefill and lrkv_prefill_chunk run for these
+ * sizes: "prefill_kernel" (bf16 MFMA: head_dim 64 or 128, rank 0, 8, 16 or
+ * 32) or "prefill_generic_kernel" (vector ALU, fp32 arithmetic: fp32, or any
+ * rank up to 128, head_dim 16-128 a multiple of 8, at most 65535 heads).
+ * NULL outside both.  Host-only: launches nothing; the string is static. */
+const char* lrkv_prefill_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank);
+
 /* Causal prefill of seq_len fresh tokens per sequence (slides "Compute
  * logits without expanding historical keys" and "Aggregate values before
  * the residual up-projection" with seq_len queries; query i sees keys
  * j <= i):
  *   q   [batch][seq_len][num_heads][head_dim];  out same shape.
  *   k_s, v_s [batch][seq_len][head_dim];  z_k, z_v [batch][seq_len][num_heads][rank].
- * Only dtype LRKV_BF16 is supported (bf16 MFMA with fp32 accumulation).
- * One sequence's rows and latents must each span less than 4 GiB
- * (seq_len * max(head_dim, num_heads*rank) * 2 bytes), else LRKV_ERR_SHAPE.
+ * bf16 with head_dim 64 or 128 and rank 0, 8, 16 or 32 runs on bf16 MFMA
+ * with fp32 accumulation; there one sequence's rows and latents must each
+ * span less than 4 GiB (seq_len * max(head_dim, num_heads*rank) * 2 bytes),
+ * else LRKV_ERR_SHAPE.  Other shapes (fp32, or bf16 at any rank up to 128;
+ * head_dim 16-128, a multiple of 8; at most 65535 heads and sequences) run
+ * on a vector-ALU kernel with fp32 arithmetic (lrkv_prefill_kernel names
+ * the kernel); anything else is LRKV_ERR_SHAPE.
  * If the cache pointers are all non-NULL (k_shared, v_shared, and for
  * rank > 0 also z_k, z_v) the tokens are also written, bit-exactly, to cache
  * slots [0, seq_len) of every sequence (seq_len must then be <= capacity);
@@ -278,7 +289,8 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
  * with s = start_pos[b] tokens already cached:
  *   1. the new tokens are written, bit-exactly, to cache slots [s, s + n_new);
  *   2. new token i (position s + i) attends to cache tokens j <= s + i, in the
- *      absorbed form of Eqs. (6)-(7) on bf16 MFMA with fp32 accumulation.
+ *      absorbed form of Eqs. (6)-(7), on the same kernel lrkv_prefill takes
+ *      for the shape.
  *   start_pos  device int32 [batch]; each value is clamped to [0, max_start].
  *   max_start  host upper bound on start_pos; max_start + n_new <= capacity
  *              (else LRKV_ERR_CAPACITY).
@@ -286,11 +298,11 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
  *   k_s, v_s [batch][n_new][head_dim];  z_k_new, z_v_new [batch][n_new][num_heads][rank].
  *   The cache pointers are required (the cache is read and written; z_k and
  *   z_v may be NULL when rank == 0).
- * Only dtype LRKV_BF16 and the prefill envelope (head_dim 64 or 128, rank
- * 0/8/16/32) are supported.  One sequence's history and new tokens must
- * span less than 4 GiB ((max_start + n_new) * max(head_dim, num_heads*rank)
- * * 2 bytes), else LRKV_ERR_SHAPE.  With start_pos all zero and an empty
- * cache this is lrkv_prefill with the cache written. */
+ * The shapes are those of lrkv_prefill.  On the MFMA kernel one sequence's
+ * history and new tokens must span less than 4 GiB ((max_start + n_new) *
+ * max(head_dim, num_heads*rank) * 2 bytes), else LRKV_ERR_SHAPE.  With
+ * start_pos all zero and an empty cache this is lrkv_prefill with the cache
+ * written. */
 lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
                                int32_t rank, int64_t capacity,
                                void* k_shared, void* v_shared, void* z_k, void* z_v,

@@ -9,7 +9,7 @@ from .binding import (  # noqa: F401
     lrkv_append, lrkv_cache_elems_per_token, lrkv_init, lrkv_decode, lrkv_decode_noalloc, lrkv_decode_scan_kernel, lrkv_decode_workspace_size,
     lrkv_decode_workspace_size_ex,
     lrkv_mha_decode, lrkv_mha_decode_workspace_size,
-    lrkv_pack_projection, lrkv_prefill, lrkv_prefill_chunk, lrkv_project_append, lrkv_project_kernel,
+    lrkv_pack_projection, lrkv_prefill, lrkv_prefill_chunk, lrkv_prefill_kernel, lrkv_project_append, lrkv_project_kernel,
     lrkv_project_workspace_size, lrkv_status_string, lrkv_train_backward, lrkv_train_backward_workspace_size,
     lrkv_train_forward,
 )

@@ -28,7 +28,7 @@ STATUS = {0: "LRKV_OK", 1: "LRKV_ERR_NULL", 2: "LRKV_ERR_SHAPE", 3: "LRKV_ERR_DT
 
 EXPORTED = ("lrkv_init", "lrkv_status_string", "lrkv_cache_elems_per_token", "lrkv_append",
             "lrkv_decode_workspace_size", "lrkv_decode_scan_kernel", "lrkv_decode", "lrkv_decode_partial",
-            "lrkv_decode_combine", "lrkv_decode_noalloc", "lrkv_decode_workspace_size_ex", "lrkv_decode_ex", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
+            "lrkv_decode_combine", "lrkv_decode_noalloc", "lrkv_decode_workspace_size_ex", "lrkv_decode_ex", "lrkv_prefill_kernel", "lrkv_prefill", "lrkv_prefill_chunk", "lrkv_pack_projection",
             "lrkv_project_kernel", "lrkv_project_workspace_size", "lrkv_project_append",
             "lrkv_mha_decode_workspace_size", "lrkv_mha_decode", "lrkv_train_forward",
             "lrkv_train_backward_workspace_size", "lrkv_train_backward")
@@ -63,6 +63,8 @@ def library() -> ctypes.CDLL:
         lib.lrkv_append.restype = _i32
         lib.lrkv_decode_scan_kernel.argtypes = [_i32, _i32, _i32, _i32]
         lib.lrkv_decode_scan_kernel.restype = ctypes.c_char_p
+        lib.lrkv_prefill_kernel.argtypes = [_i32, _i32, _i32, _i32]
+        lib.lrkv_prefill_kernel.restype = ctypes.c_char_p
         lib.lrkv_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _i64, _i32,
                                                    ctypes.POINTER(_sz)]
         lib.lrkv_decode_workspace_size.restype = _i32
@@ -351,6 +353,12 @@ class DecodeCall:
 
     def combine(self):
         self._call(2)
+
+
+def lrkv_prefill_kernel(dtype: torch.dtype, num_heads: int, head_dim: int, rank: int) -> Optional[str]:
+    """Name of the kernel lrkv_prefill runs on for these sizes (None if unsupported)."""
+    name = library().lrkv_prefill_kernel(_dtype_code(dtype), num_heads, head_dim, rank)
+    return None if name is None else name.decode()
 
 
 def lrkv_prefill(q, k_s, v_s, z_k, z_v, b_k, b_v, scale: Optional[float] = None,

@@ -200,7 +200,7 @@ lrkv_status lrkv_init(void) {
   if (hipGetDevice(&dev) != hipSuccess) return LRKV_ERR_DEVICE;
   (void)device_cu_count();
   for (hipError_t (*prep)() : {lrkv::decode_mfma_prepare, lrkv::decode_mfma_any_prepare, lrkv::prefill_prepare,
-                               lrkv::project_prepare, lrkv::train_prepare})
+                               lrkv::prefill_generic_prepare, lrkv::project_prepare, lrkv::train_prepare})
     if (prep() != hipSuccess) return LRKV_ERR_DEVICE;
   return LRKV_OK;
 }
@@ -338,6 +338,27 @@ lrkv_status lrkv_append(int32_t dtype, int32_t batch, int32_t num_heads, int32_t
   return e == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
 }
 
+namespace {
+
+// Shapes outside the MFMA prefill's envelope run on the vector-ALU kernel
+// (one workgroup per 32 queries of a head and sequence: grid limits).
+bool prefill_generic_ok(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank) {
+  return lrkv::prefill_generic_supported(dtype, head_dim, rank, num_heads) && batch <= 65535;
+}
+
+lrkv_status run_prefill(bool mfma, int32_t dtype, const lrkv::PrefillArgs& p, hipStream_t s) {
+  const hipError_t e = mfma ? lrkv::launch_prefill(p, s) : lrkv::launch_prefill_generic(dtype, p, s);
+  return e == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+}
+
+}  // namespace
+
+const char* lrkv_prefill_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank) {
+  if (check_sizes(dtype, 1, num_heads, head_dim, rank, 1) != LRKV_OK) return nullptr;
+  if (lrkv::prefill_supported(dtype, head_dim, rank, num_heads)) return "prefill_kernel";
+  return prefill_generic_ok(dtype, 1, num_heads, head_dim, rank) ? "prefill_generic_kernel" : nullptr;
+}
+
 lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
                          int64_t capacity, void* k_shared, void* v_shared, void* z_k, void* z_v, int32_t seq_len,
                          const void* q, const void* k_s, const void* v_s, const void* z_k_new,
@@ -345,10 +366,12 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
                          void* stream) {
   const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, capacity);
   if (st != LRKV_OK) return st;
-  if (!lrkv::prefill_supported(dtype, head_dim, rank, num_heads)) return LRKV_ERR_SHAPE;
+  const bool mfma = lrkv::prefill_supported(dtype, head_dim, rank, num_heads);
+  if (!mfma && !prefill_generic_ok(dtype, batch, num_heads, head_dim, rank)) return LRKV_ERR_SHAPE;
   if (seq_len < 0) return LRKV_ERR_SHAPE;
-  // one sequence's rows and latents are addressed through 32-bit buffer offsets
-  if (int64_t(seq_len) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >= (int64_t(1) << 32))
+  // the MFMA kernel addresses one sequence's rows and latents through 32-bit buffer offsets
+  if (mfma &&
+      int64_t(seq_len) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >= (int64_t(1) << 32))
     return LRKV_ERR_SHAPE;
   // the cache is written when its pointers are given (the latent ones only count for rank > 0)
   const int want = rank > 0 ? 4 : 2;
@@ -381,7 +404,7 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
   p.scale_log2 = sc * 1.4426950408889634f;
   p.out = out;
   p.kv_stride = seq_len; p.start = nullptr; p.max_start = 0;
-  return lrkv::launch_prefill(p, s) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+  return run_prefill(mfma, dtype, p, s);
 }
 
 lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
@@ -391,12 +414,13 @@ lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, 
                                const void* b_k, const void* b_v, float scale, void* out, void* stream) {
   const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, capacity);
   if (st != LRKV_OK) return st;
-  if (!lrkv::prefill_supported(dtype, head_dim, rank, num_heads)) return LRKV_ERR_SHAPE;
+  const bool mfma = lrkv::prefill_supported(dtype, head_dim, rank, num_heads);
+  if (!mfma && !prefill_generic_ok(dtype, batch, num_heads, head_dim, rank)) return LRKV_ERR_SHAPE;
   if (n_new < 0 || max_start < 0) return LRKV_ERR_SHAPE;
   if (int64_t(max_start) + n_new > capacity) return LRKV_ERR_CAPACITY;
-  // one sequence's keys (history and new tokens) are addressed through 32-bit buffer offsets
-  if ((int64_t(max_start) + n_new) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >=
-      (int64_t(1) << 32))
+  // the MFMA kernel addresses one sequence's keys (history and new tokens) through 32-bit buffer offsets
+  if (mfma && (int64_t(max_start) + n_new) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >=
+                  (int64_t(1) << 32))
     return LRKV_ERR_SHAPE;
   if (batch == 0 || n_new == 0) return LRKV_OK;
   if (!k_shared || !v_shared || !start_pos || !q || !k_s || !v_s || !out) return LRKV_ERR_NULL;
@@ -421,7 +445,7 @@ lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, 
   p.scale_log2 = sc * 1.4426950408889634f;
   p.out = out;
   p.kv_stride = int(capacity); p.start = start_pos; p.max_start = max_start;
-  return lrkv::launch_prefill(p, s) == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
+  return run_prefill(mfma, dtype, p, s);
 }
 
 namespace {

@@ -118,6 +118,13 @@ struct PrefillArgs {
 };
 bool prefill_supported(int dtype, int head_dim, int rank, int heads);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// The vector-ALU prefill for the other shapes: bf16 or fp32, head_dim 16-128
+// (a multiple of 8), any rank up to kPrefillGenericMaxRank, at most 65535
+// heads and sequences.
+constexpr int kPrefillGenericMaxRank = 128;
+bool prefill_generic_supported(int dtype, int head_dim, int rank, int heads);
+hipError_t launch_prefill_generic(int dtype, const PrefillArgs& a, hipStream_t stream);
+hipError_t prefill_generic_prepare();
 
 struct TrainArgs {
   int batch, heads, head_dim, rank, seq_len;

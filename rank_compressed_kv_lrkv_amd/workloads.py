@@ -94,6 +94,9 @@ DECODE_WORKLOADS = {
 PREFILL_WORKLOADS = {
     w.name: w for w in [
         PrefillWorkload("prefill_bf16_L4k", 4, 4096, 32, 128, 16, "bf16", 20261206),
+        # one sequence of the same length at the rank of the trained 2.5B
+        # configuration (the vector-ALU prefill's shape)
+        PrefillWorkload("prefill_bf16_L4k_r54", 1, 4096, 32, 128, 54, "bf16", 20261210),
     ]
 }
 

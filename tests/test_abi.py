@@ -188,6 +188,22 @@ def test_append_zero_rows_is_noop():
     assert append_call(n=0, k=None, v=None, pos=None, nk=None, nv=None) == OK
 
 
+@no_gpu
+def test_prefill_kernel_names():
+    """bf16 at ranks 0/8/16/32 and head_dim 64/128 runs on MFMA; fp32 and
+    the other ranks up to 128 on the vector-ALU kernel; larger shapes on
+    neither."""
+    assert L.lrkv_prefill_kernel(torch.bfloat16, 32, 128, 16) == "prefill_kernel"
+    assert L.lrkv_prefill_kernel(torch.bfloat16, 4, 64, 0) == "prefill_kernel"
+    assert L.lrkv_prefill_kernel(torch.bfloat16, 32, 128, 54) == "prefill_generic_kernel"
+    assert L.lrkv_prefill_kernel(torch.bfloat16, 6, 128, 128) == "prefill_generic_kernel"
+    assert L.lrkv_prefill_kernel(torch.float32, 32, 128, 16) == "prefill_generic_kernel"
+    assert L.lrkv_prefill_kernel(torch.float32, 3, 16, 5) == "prefill_generic_kernel"
+    assert L.lrkv_prefill_kernel(torch.bfloat16, 32, 128, 129) is None
+    assert L.lrkv_prefill_kernel(torch.bfloat16, 32, 256, 16) is None
+    assert L.lrkv_prefill_kernel(torch.float32, 70000, 128, 16) is None   # grid limit of the vector-ALU kernel
+
+
 def prefill_call(**over):
     a = dict(dtype=BF16, B=1, H=8, d_h=64, r=8, cap=128, k=None, v=None, zk=None, zv=None, L=64, q=FAKE,
              ks=FAKE, vs=FAKE, zkn=FAKE, zvn=FAKE, bk=FAKE, bv=FAKE, scale=0.0, out=FAKE)
@@ -199,7 +215,8 @@ def prefill_call(**over):
 
 @no_gpu
 @pytest.mark.parametrize("kw,want", [
-    (dict(dtype=F32, r=4), SHAPE),               # prefill is bf16 only
+    (dict(r=130), SHAPE),                        # rank above 128: neither prefill kernel
+    (dict(d_h=256, r=16), SHAPE),                # head_dim above 128
     (dict(L=-1), SHAPE),
     (dict(k=FAKE), NULL),                        # cache pointers: all or none
     (dict(k=FAKE, v=FAKE, zk=FAKE, zv=FAKE, L=256), CAP),
@@ -219,8 +236,8 @@ def chunk_call(**over):
 
 @no_gpu
 @pytest.mark.parametrize("kw,want", [
-    (dict(dtype=F32, r=4), SHAPE),               # bf16 only
-    (dict(d_h=32), SHAPE),                       # outside the prefill envelope
+    (dict(r=130), SHAPE),                        # rank above 128: neither prefill kernel
+    (dict(d_h=256), SHAPE),                      # head_dim above 128
     (dict(max_start=-1), SHAPE), (dict(n=-1), SHAPE),
     (dict(max_start=200, n=64), CAP),            # history bound + new tokens past the capacity
     (dict(k=None), NULL), (dict(start=None), NULL), (dict(q=None), NULL), (dict(bk=None), NULL),
