@@ -15,8 +15,8 @@
 // LDS, lane j of a query's group scores keys j, j+8, j+16, j+24 of the tile
 // (16-byte LDS reads, the query's 4 columns reused for the 4 keys), the
 // group shares the running max by shuffles, and lane j accumulates the
-// augmented output dims 32c + 4j .. 32c + 4j + 3.  A correctness-first vector-ALU path:
-// the MFMA kernel stays the one for bf16 at ranks 0, 8, 16 and 32.
+// augmented output dims 32c + 4j .. 32c + 4j + 3.  The MFMA kernel stays
+// the one for bf16 at ranks 0, 8, 16 and 32.
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
