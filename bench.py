@@ -541,9 +541,10 @@ def prefill_record(args):
     flops = pairs * 4 * (d_h + r) + B * H * Lq * 4 * d_h * r  # Eq. (6)-(7) contractions + absorption
     tflops = flops / (kern_ms * 1e-3) / 1e12
     kernel = L.lrkv_prefill_kernel(torch.bfloat16, H, d_h, r)
-    # the MFMA kernel is priced against the bf16 MFMA peak, the vector-ALU
+    # the MFMA kernels are priced against the bf16 MFMA peak, the vector-ALU
     # kernel (fp32 FMAs) against the fp32 vector peak
-    bound, peak = ("mfma", MFMA_BF16_PEAK_TFLOPS) if kernel == "prefill_kernel" else ("alu", FP32_VECTOR_PEAK_TFLOPS)
+    mfma = kernel in ("prefill_kernel", "prefill_wide_kernel")
+    bound, peak = ("mfma", MFMA_BF16_PEAK_TFLOPS) if mfma else ("alu", FP32_VECTOR_PEAK_TFLOPS)
     rec = {
         "value": B * Lq / (step_ms * 1e-3), "unit": "prefill tokens/s (cache written)",
         "settle": {"seconds": args.settle_s, "steps": settled}, "ms_per_step": step_ms, "steps": steps,

@@ -200,7 +200,8 @@ lrkv_status lrkv_init(void) {
   if (hipGetDevice(&dev) != hipSuccess) return LRKV_ERR_DEVICE;
   (void)device_cu_count();
   for (hipError_t (*prep)() : {lrkv::decode_mfma_prepare, lrkv::decode_mfma_any_prepare, lrkv::prefill_prepare,
-                               lrkv::prefill_generic_prepare, lrkv::project_prepare, lrkv::train_prepare})
+                               lrkv::prefill_wide_prepare, lrkv::prefill_generic_prepare, lrkv::project_prepare,
+                               lrkv::train_prepare})
     if (prep() != hipSuccess) return LRKV_ERR_DEVICE;
   return LRKV_OK;
 }
@@ -346,8 +347,20 @@ bool prefill_generic_ok(int32_t dtype, int32_t batch, int32_t num_heads, int32_t
   return lrkv::prefill_generic_supported(dtype, head_dim, rank, num_heads) && batch <= 65535;
 }
 
-lrkv_status run_prefill(bool mfma, int32_t dtype, const lrkv::PrefillArgs& p, hipStream_t s) {
-  const hipError_t e = mfma ? lrkv::launch_prefill(p, s) : lrkv::launch_prefill_generic(dtype, p, s);
+// Which prefill kernel a shape runs on: the bf16 MFMA kernel at ranks 0, 8,
+// 16 and 32; its padded form at even ranks 34-64; else the vector-ALU kernel.
+enum class PrefillEngine { kMfma, kWide, kGeneric, kNone };
+
+PrefillEngine prefill_engine(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank) {
+  if (lrkv::prefill_supported(dtype, head_dim, rank, num_heads)) return PrefillEngine::kMfma;
+  if (lrkv::prefill_wide_supported(dtype, head_dim, rank, num_heads)) return PrefillEngine::kWide;
+  return prefill_generic_ok(dtype, batch, num_heads, head_dim, rank) ? PrefillEngine::kGeneric : PrefillEngine::kNone;
+}
+
+lrkv_status run_prefill(PrefillEngine eng, int32_t dtype, const lrkv::PrefillArgs& p, hipStream_t s) {
+  const hipError_t e = eng == PrefillEngine::kMfma   ? lrkv::launch_prefill(p, s)
+                       : eng == PrefillEngine::kWide ? lrkv::launch_prefill_wide(p, s)
+                                                     : lrkv::launch_prefill_generic(dtype, p, s);
   return e == hipSuccess ? LRKV_OK : LRKV_ERR_DEVICE;
 }
 
@@ -355,8 +368,12 @@ lrkv_status run_prefill(bool mfma, int32_t dtype, const lrkv::PrefillArgs& p, hi
 
 const char* lrkv_prefill_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank) {
   if (check_sizes(dtype, 1, num_heads, head_dim, rank, 1) != LRKV_OK) return nullptr;
-  if (lrkv::prefill_supported(dtype, head_dim, rank, num_heads)) return "prefill_kernel";
-  return prefill_generic_ok(dtype, 1, num_heads, head_dim, rank) ? "prefill_generic_kernel" : nullptr;
+  switch (prefill_engine(dtype, 1, num_heads, head_dim, rank)) {
+    case PrefillEngine::kMfma: return "prefill_kernel";
+    case PrefillEngine::kWide: return "prefill_wide_kernel";
+    case PrefillEngine::kGeneric: return "prefill_generic_kernel";
+    default: return nullptr;
+  }
 }
 
 lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
@@ -366,12 +383,14 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
                          void* stream) {
   const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, capacity);
   if (st != LRKV_OK) return st;
-  const bool mfma = lrkv::prefill_supported(dtype, head_dim, rank, num_heads);
-  if (!mfma && !prefill_generic_ok(dtype, batch, num_heads, head_dim, rank)) return LRKV_ERR_SHAPE;
+  const PrefillEngine eng = prefill_engine(dtype, batch, num_heads, head_dim, rank);
+  if (eng == PrefillEngine::kNone) return LRKV_ERR_SHAPE;
   if (seq_len < 0) return LRKV_ERR_SHAPE;
-  // the MFMA kernel addresses one sequence's rows and latents through 32-bit buffer offsets
-  if (mfma &&
-      int64_t(seq_len) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >= (int64_t(1) << 32))
+  // the MFMA kernels address one sequence's rows and latents through 32-bit
+  // buffer offsets (the padded one reads up to 128 bytes past a latent row)
+  if (eng != PrefillEngine::kGeneric &&
+      int64_t(seq_len) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >=
+          (int64_t(1) << 32) - 1024)
     return LRKV_ERR_SHAPE;
   // the cache is written when its pointers are given (the latent ones only count for rank > 0)
   const int want = rank > 0 ? 4 : 2;
@@ -404,7 +423,7 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
   p.scale_log2 = sc * 1.4426950408889634f;
   p.out = out;
   p.kv_stride = seq_len; p.start = nullptr; p.max_start = 0;
-  return run_prefill(mfma, dtype, p, s);
+  return run_prefill(eng, dtype, p, s);
 }
 
 lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank,
@@ -414,13 +433,14 @@ lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, 
                                const void* b_k, const void* b_v, float scale, void* out, void* stream) {
   const lrkv_status st = check_sizes(dtype, batch, num_heads, head_dim, rank, capacity);
   if (st != LRKV_OK) return st;
-  const bool mfma = lrkv::prefill_supported(dtype, head_dim, rank, num_heads);
-  if (!mfma && !prefill_generic_ok(dtype, batch, num_heads, head_dim, rank)) return LRKV_ERR_SHAPE;
+  const PrefillEngine eng = prefill_engine(dtype, batch, num_heads, head_dim, rank);
+  if (eng == PrefillEngine::kNone) return LRKV_ERR_SHAPE;
   if (n_new < 0 || max_start < 0) return LRKV_ERR_SHAPE;
   if (int64_t(max_start) + n_new > capacity) return LRKV_ERR_CAPACITY;
-  // the MFMA kernel addresses one sequence's keys (history and new tokens) through 32-bit buffer offsets
-  if (mfma && (int64_t(max_start) + n_new) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >=
-                  (int64_t(1) << 32))
+  // the MFMA kernels address one sequence's keys (history and new tokens) through 32-bit buffer offsets
+  if (eng != PrefillEngine::kGeneric &&
+      (int64_t(max_start) + n_new) * std::max<int64_t>(int64_t(head_dim), int64_t(num_heads) * rank) * 2 >=
+          (int64_t(1) << 32) - 1024)
     return LRKV_ERR_SHAPE;
   if (batch == 0 || n_new == 0) return LRKV_OK;
   if (!k_shared || !v_shared || !start_pos || !q || !k_s || !v_s || !out) return LRKV_ERR_NULL;
@@ -445,7 +465,7 @@ lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, 
   p.scale_log2 = sc * 1.4426950408889634f;
   p.out = out;
   p.kv_stride = int(capacity); p.start = start_pos; p.max_start = max_start;
-  return run_prefill(mfma, dtype, p, s);
+  return run_prefill(eng, dtype, p, s);
 }
 
 namespace {

@@ -118,6 +118,10 @@ struct PrefillArgs {
 };
 bool prefill_supported(int dtype, int head_dim, int rank, int heads);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// The bf16 MFMA prefill at even ranks 34-64 (latents padded to 64 in LDS).
+bool prefill_wide_supported(int dtype, int head_dim, int rank, int heads);
+hipError_t launch_prefill_wide(const PrefillArgs& a, hipStream_t stream);
+hipError_t prefill_wide_prepare();
 // The vector-ALU prefill for the other shapes: bf16 or fp32, head_dim 16-128
 // (a multiple of 8), any rank up to kPrefillGenericMaxRank, at most 65535
 // heads and sequences.

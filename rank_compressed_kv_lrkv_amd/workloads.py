@@ -94,9 +94,11 @@ DECODE_WORKLOADS = {
 PREFILL_WORKLOADS = {
     w.name: w for w in [
         PrefillWorkload("prefill_bf16_L4k", 4, 4096, 32, 128, 16, "bf16", 20261206),
-        # one sequence of the same length at the rank of the trained 2.5B
-        # configuration (the vector-ALU prefill's shape)
+        # one sequence of the same length at two of the trained ranks: the
+        # 2.5B configuration (32 heads, rank 54: the padded MFMA prefill) and
+        # an odd rank (18 heads, rank 55: the vector-ALU prefill)
         PrefillWorkload("prefill_bf16_L4k_r54", 1, 4096, 32, 128, 54, "bf16", 20261210),
+        PrefillWorkload("prefill_bf16_L4k_r55", 1, 4096, 18, 128, 55, "bf16", 20261211),
     ]
 }
 

@@ -1,11 +1,11 @@
-"""lrkv_prefill and lrkv_prefill_chunk on the vector-ALU prefill kernel (the
-shapes outside the bf16 MFMA kernel's envelope: fp32, and bf16 at the
-pages' trained ranks), through the C ABI, against the float64 oracle.
+"""lrkv_prefill and lrkv_prefill_chunk outside the rank 0/8/16/32 MFMA
+kernel's envelope, through the C ABI, against the float64 oracle: bf16 at
+even ranks 34-64 on the padded MFMA kernel (prefill_wide_kernel), fp32 and
+the other ranks up to 128 on the vector-ALU kernel (prefill_generic_kernel).
 
 Bar: max |gpu - oracle| <= 1e-5 * ||oracle||_inf for fp32 storage and
-2e-2 * ||oracle||_inf for bf16 storage (fp32 arithmetic throughout).
-Element by element, at sizes that span several 32-query blocks and key
-tiles with ragged tails.
+2e-2 * ||oracle||_inf for bf16 storage.  Element by element, at sizes that
+span several 32-query blocks and key tiles with ragged tails.
 """
 import numpy as np
 import pytest
@@ -32,7 +32,16 @@ SHAPES = [
     ("bf16_r46_h12", "bf16", 1, 40, 12, 128, 46),
     ("bf16_r51_h12", "bf16", 2, 31, 12, 128, 51),
     ("bf16_dh32_r16", "bf16", 1, 50, 4, 32, 16),
+    ("bf16_r64_dh64_h5", "bf16", 2, 77, 5, 64, 64),
+    ("bf16_r34_h8", "bf16", 1, 130, 8, 128, 34),
+    ("bf16_r54_L1", "bf16", 1, 1, 4, 128, 54),
 ]
+
+
+def expected_kernel(dt, d_h, r):
+    if dt == "bf16" and d_h in (64, 128) and r % 2 == 0 and 32 < r <= 64:
+        return "prefill_wide_kernel"
+    return "prefill_generic_kernel"
 
 
 def f64(d, k):
@@ -41,8 +50,9 @@ def f64(d, k):
 
 @pytest.mark.parametrize("name,dt,B,Lq,H,d_h,r", SHAPES, ids=[s[0] for s in SHAPES])
 def test_prefill_generic(name, dt, B, Lq, H, d_h, r):
-    assert L.lrkv_prefill_kernel(TORCH_DT[dt], H, d_h, r) == "prefill_generic_kernel"
-    say(f"case prefill (vector ALU) {name}")
+    kern = expected_kernel(dt, d_h, r)
+    assert L.lrkv_prefill_kernel(TORCH_DT[dt], H, d_h, r) == kern
+    say(f"case prefill ({kern}) {name}")
     d = prefill_inputs(PrefillWorkload(name, B, Lq, H, d_h, r, dt, 1000 + H + r))
     t = {k: to_dev(d[k], dt) for k in ("q",) + NEW + ("b_k", "b_v")}
     out = L.lrkv_prefill(t["q"], t["k_s"], t["v_s"], t["z_k"], t["z_v"], t["b_k"], t["b_v"])
@@ -76,13 +86,14 @@ CHUNKS = [
     # name, dtype, batch, heads, head_dim, rank, capacity, starts, n_new
     ("f32_r16", "f32", 3, 8, 128, 16, 320, [0, 37, 190], 100),
     ("bf16_r54", "bf16", 2, 32, 128, 54, 200, [64, 5], 33),
+    ("bf16_r46_long", "bf16", 2, 12, 128, 46, 700, [600, 130], 64),
     ("bf16_r55_one_token", "bf16", 2, 18, 128, 55, 300, [299, 0], 1),
 ]
 
 
 @pytest.mark.parametrize("name,dt,B,H,d_h,r,cap,starts,n", CHUNKS, ids=[c[0] for c in CHUNKS])
 def test_prefill_chunk_generic(name, dt, B, H, d_h, r, cap, starts, n):
-    say(f"case prefill chunk (vector ALU) {name} starts={starts} n_new={n}")
+    say(f"case prefill chunk ({expected_kernel(dt, d_h, r)}) {name} starts={starts} n_new={n}")
     d = chunk_inputs(batch=B, heads=H, head_dim=d_h, rank=r, capacity=cap, starts=starts, n_new=n, seed=40 + r,
                      dtype=dt)
     cache = L.LrkvCache(*(to_dev(d["cache_" + k], dt) for k in NEW))
