@@ -253,9 +253,11 @@ lrkv_status lrkv_decode_ex(int32_t engine, int32_t phases,
 
 /* Name of the kernel lrkv_prefill and lrkv_prefill_chunk run for these
  * sizes: "prefill_kernel" (bf16 MFMA: head_dim 64 or 128, rank 0, 8, 16 or
- * 32) or "prefill_generic_kernel" (vector ALU, fp32 arithmetic: fp32, or any
+ * 32), "prefill_wide_kernel" (the same at even ranks 34-64) or
+ * "prefill_generic_kernel" (vector ALU, fp32 arithmetic: fp32, or any other
  * rank up to 128, head_dim 16-128 a multiple of 8, at most 65535 heads).
- * NULL outside both.  Host-only: launches nothing; the string is static. */
+ * NULL outside all three.  Host-only: launches nothing; the string is
+ * static. */
 const char* lrkv_prefill_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank);
 
 /* Causal prefill of seq_len fresh tokens per sequence (slides "Compute
@@ -264,10 +266,11 @@ const char* lrkv_prefill_kernel(int32_t dtype, int32_t num_heads, int32_t head_d
  * j <= i):
  *   q   [batch][seq_len][num_heads][head_dim];  out same shape.
  *   k_s, v_s [batch][seq_len][head_dim];  z_k, z_v [batch][seq_len][num_heads][rank].
- * bf16 with head_dim 64 or 128 and rank 0, 8, 16 or 32 runs on bf16 MFMA
- * with fp32 accumulation; there one sequence's rows and latents must each
- * span less than 4 GiB (seq_len * max(head_dim, num_heads*rank) * 2 bytes),
- * else LRKV_ERR_SHAPE.  Other shapes (fp32, or bf16 at any rank up to 128;
+ * bf16 with head_dim 64 or 128 runs on bf16 MFMA with fp32 accumulation at
+ * ranks 0, 8, 16 and 32, and at even ranks 34-64 (latents padded to 64 dims
+ * per head); there one sequence's rows and latents must each span less than
+ * 4 GiB - 1 KiB (seq_len * max(head_dim, num_heads*rank) * 2 bytes), else
+ * LRKV_ERR_SHAPE.  Other shapes (fp32, or bf16 at any other rank up to 128;
  * head_dim 16-128, a multiple of 8; at most 65535 heads and sequences) run
  * on a vector-ALU kernel with fp32 arithmetic (lrkv_prefill_kernel names
  * the kernel); anything else is LRKV_ERR_SHAPE.
@@ -298,9 +301,9 @@ lrkv_status lrkv_prefill(int32_t dtype, int32_t batch, int32_t num_heads, int32_
  *   k_s, v_s [batch][n_new][head_dim];  z_k_new, z_v_new [batch][n_new][num_heads][rank].
  *   The cache pointers are required (the cache is read and written; z_k and
  *   z_v may be NULL when rank == 0).
- * The shapes are those of lrkv_prefill.  On the MFMA kernel one sequence's
- * history and new tokens must span less than 4 GiB ((max_start + n_new) *
- * max(head_dim, num_heads*rank) * 2 bytes), else LRKV_ERR_SHAPE.  With
+ * The shapes are those of lrkv_prefill.  On the MFMA kernels one sequence's
+ * history and new tokens must span less than 4 GiB - 1 KiB ((max_start +
+ * n_new) * max(head_dim, num_heads*rank) * 2 bytes), else LRKV_ERR_SHAPE.  With
  * start_pos all zero and an empty cache this is lrkv_prefill with the cache
  * written. */
 lrkv_status lrkv_prefill_chunk(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim,
