@@ -1,20 +1,22 @@
-// LRKV causal prefill on bf16 MFMA at ranks 34-64 (even): the trained ranks
-// of the pages' models (slide "The rank directly sets the theoretical cache
-// budget", Table 7: 46 and 54 among them).  Same method, arguments and
+// LRKV causal prefill on bf16 MFMA at even ranks 34-128: trained ranks of
+// the pages' models (slide "The rank directly sets the theoretical cache
+// budget", Table 7: 46 and 54; "Backup: the complete rank sweep clarifies
+// the trade-off", Table 8: up to 128).  Same method, arguments and
 // pipeline as prefill_wide_kernel (slides "Compute logits without expanding
 // historical keys", Eq. (6) with the causal mask, and "Aggregate values
 // before the residual up-projection", Eq. (7)); what differs:
-//   - the latent rows sit in LDS padded to RP = 64 dims per head: a tile
-//     transfer takes, for each head, 16-byte pieces starting at its row in
-//     HBM (4-byte aligned for an even rank), so the 64 - r dims past the
-//     rank hold finite data of the neighbouring row (or zeros past the
-//     array);
+//   - the latent rows sit in LDS padded to RP = 64 (ranks up to 64) or 128
+//     dims per head: a tile transfer takes, for each head, 16-byte pieces
+//     starting at its row in HBM (4-byte aligned for an even rank), so the
+//     RP - r dims past the rank hold finite data of the following rows (or
+//     zeros past the array);
 //   - the absorbed query and B^V are zero in those dims, so they add
 //     nothing to the logits and the output;
-//   - the value latents are two 32-row MFMA blocks; the softmax sum is
-//     added up on the vector ALUs;
-//   - the side is 24 KB, so one workgroup (one wave per SIMD) runs per
-//     compute unit, with up to 512 registers per lane.
+//   - the value latents are RP/32 MFMA blocks of 32 rows; the softmax sum
+//     is added up on the vector ALUs;
+//   - a side is 24 KB (RP = 64) or 40 KB (RP = 128) with d_h = 128, so one
+//     workgroup (one wave per SIMD) runs per compute unit, with up to 512
+//     registers per lane.
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
@@ -25,7 +27,7 @@ constexpr int kPwThreads = 64 * kPwWaves;
 constexpr int kPwTile = 32;                 // key tokens per tile, query rows per wave
 constexpr float kPwStale = 8.f;             // running-max refresh threshold (log2 units)
 constexpr int kPwVmcntZero = 0x0F70;          // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt not waited on
-constexpr int kPwPad = 64;                  // latent dims per head in LDS (ranks 34-64, even)
+constexpr int kPwMaxPad = 128;              // latent dims per head in LDS: 64 (ranks 34-64) or 128 (66-128)
 
 // LDS tiles keep rows unpadded, with 16-byte chunk ch of row r at position
 // ch ^ lds_swz(r, chunks per row); with it every read this kernel makes is
@@ -50,7 +52,7 @@ struct WideShape {
   static constexpr int NZ = kPwTile * CZ / 64;             // and latents
   static constexpr int NRW = (NR + kPwWaves - 1) / kPwWaves;          // per wave
   static constexpr int NZW = (NZ + kPwWaves - 1) / kPwWaves;
-  static_assert(DH % 32 == 0 && RP % 32 == 0 && RP <= 64, "wide prefill envelope");
+  static_assert(DH % 32 == 0 && RP % 32 == 0 && RP <= kPwMaxPad, "wide prefill envelope");
   static_assert(CR >= 4 && CZ >= 4, "swizzle needs 4 chunks per row");
 };
 
@@ -67,7 +69,7 @@ struct WideKernelParams {
   const int32_t* start;
   int max_start;
   float scale_log2;
-  int rank;                        // r, even, RP - 30 <= r <= RP: latent row length in HBM
+  int rank;                        // r, even, r <= RP: latent row length in HBM
 };
 
 // This lane's source offsets (bytes from the first row of a tile) for the
@@ -462,9 +464,9 @@ void prefill_wide_kernel(WideKernelParams p) {
     }
 }
 
-template <int DH>
+template <int DH, int RP>
 static hipError_t launch_wide_t(const PrefillArgs& a, hipStream_t st) {
-  using P = WideShape<DH, kPwPad>;
+  using P = WideShape<DH, RP>;
   WideKernelParams kp;
   kp.q = static_cast<const uint16_t*>(a.q);
   kp.k_s = static_cast<const uint16_t*>(a.k_s);
@@ -488,26 +490,29 @@ static hipError_t launch_wide_t(const PrefillArgs& a, hipStream_t st) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid{static_cast<unsigned>(blocks)};
   const size_t lds = size_t(P::LDS);
-  const hipError_t attr = allow_dynamic_lds<&prefill_wide_kernel<DH, kPwPad>>(int(lds));
+  const hipError_t attr = allow_dynamic_lds<&prefill_wide_kernel<DH, RP>>(int(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((prefill_wide_kernel<DH, kPwPad>), grid, dim3(kPwThreads), lds, st, kp);
+  hipLaunchKernelGGL((prefill_wide_kernel<DH, RP>), grid, dim3(kPwThreads), lds, st, kp);
   return hipGetLastError();
 }
 
 bool prefill_wide_supported(int dtype, int head_dim, int rank, int heads) {
-  return dtype == 1 && (head_dim == 64 || head_dim == 128) && rank % 2 == 0 && rank > 32 && rank <= kPwPad &&
+  return dtype == 1 && (head_dim == 64 || head_dim == 128) && rank % 2 == 0 && rank > 32 && rank <= kPwMaxPad &&
          heads >= 1;
 }
 
 hipError_t launch_prefill_wide(const PrefillArgs& a, hipStream_t st) {
   // the training forward's log-sum-exp output is the rank 0-32 kernel's only
   if (!prefill_wide_supported(1, a.head_dim, a.rank, a.heads) || a.lse) return hipErrorInvalidValue;
-  return a.head_dim == 64 ? launch_wide_t<64>(a, st) : launch_wide_t<128>(a, st);
+  if (a.rank <= 64) return a.head_dim == 64 ? launch_wide_t<64, 64>(a, st) : launch_wide_t<128, 64>(a, st);
+  return a.head_dim == 64 ? launch_wide_t<64, 128>(a, st) : launch_wide_t<128, 128>(a, st);
 }
 
 hipError_t prefill_wide_prepare() {
-  hipError_t e = allow_dynamic_lds<&prefill_wide_kernel<64, kPwPad>>(WideShape<64, kPwPad>::LDS);
-  if (e == hipSuccess) e = allow_dynamic_lds<&prefill_wide_kernel<128, kPwPad>>(WideShape<128, kPwPad>::LDS);
+  hipError_t e = allow_dynamic_lds<&prefill_wide_kernel<64, 64>>(WideShape<64, 64>::LDS);
+  if (e == hipSuccess) e = allow_dynamic_lds<&prefill_wide_kernel<128, 64>>(WideShape<128, 64>::LDS);
+  if (e == hipSuccess) e = allow_dynamic_lds<&prefill_wide_kernel<64, 128>>(WideShape<64, 128>::LDS);
+  if (e == hipSuccess) e = allow_dynamic_lds<&prefill_wide_kernel<128, 128>>(WideShape<128, 128>::LDS);
   return e;
 }
 

@@ -1,6 +1,6 @@
 """lrkv_prefill and lrkv_prefill_chunk outside the rank 0/8/16/32 MFMA
 kernel's envelope, through the C ABI, against the float64 oracle: bf16 at
-even ranks 34-64 on the padded MFMA kernel (prefill_wide_kernel), fp32 and
+even ranks 34-128 on the padded MFMA kernel (prefill_wide_kernel), fp32 and
 the other ranks up to 128 on the vector-ALU kernel (prefill_generic_kernel).
 
 Bar: max |gpu - oracle| <= 1e-5 * ||oracle||_inf for fp32 storage and
@@ -35,11 +35,14 @@ SHAPES = [
     ("bf16_r64_dh64_h5", "bf16", 2, 77, 5, 64, 64),
     ("bf16_r34_h8", "bf16", 1, 130, 8, 128, 34),
     ("bf16_r54_L1", "bf16", 1, 1, 4, 128, 54),
+    ("bf16_r66_h4", "bf16", 1, 70, 4, 128, 66),
+    ("bf16_r96_dh64_h7", "bf16", 2, 45, 7, 64, 96),
+    ("bf16_r127_h3", "bf16", 1, 40, 3, 128, 127),
 ]
 
 
 def expected_kernel(dt, d_h, r):
-    if dt == "bf16" and d_h in (64, 128) and r % 2 == 0 and 32 < r <= 64:
+    if dt == "bf16" and d_h in (64, 128) and r % 2 == 0 and 32 < r <= 128:
         return "prefill_wide_kernel"
     return "prefill_generic_kernel"
 
@@ -87,6 +90,7 @@ CHUNKS = [
     ("f32_r16", "f32", 3, 8, 128, 16, 320, [0, 37, 190], 100),
     ("bf16_r54", "bf16", 2, 32, 128, 54, 200, [64, 5], 33),
     ("bf16_r46_long", "bf16", 2, 12, 128, 46, 700, [600, 130], 64),
+    ("bf16_r128", "bf16", 2, 6, 128, 128, 160, [100, 7], 40),
     ("bf16_r55_one_token", "bf16", 2, 18, 128, 55, 300, [299, 0], 1),
 ]
 
