@@ -254,8 +254,8 @@ lrkv_status lrkv_decode_ex(int32_t engine, int32_t phases,
 /* Name of the kernel lrkv_prefill and lrkv_prefill_chunk run for these
  * sizes: "prefill_kernel" (bf16 MFMA: head_dim 64 or 128, rank 0, 8, 16 or
  * 32), "prefill_wide_kernel" (the same at even ranks 34-128) or
- * "prefill_generic_kernel" (vector ALU, fp32 arithmetic: fp32, or an odd
- * rank up to 127, head_dim 16-128 a multiple of 8, at most 65535 heads).
+ * "prefill_generic_kernel" (vector ALU, fp32 arithmetic: the other shapes
+ * with rank <= 128, head_dim 16-128 a multiple of 8, at most 65535 heads).
  * NULL outside all three.  Host-only: launches nothing; the string is
  * static. */
 const char* lrkv_prefill_kernel(int32_t dtype, int32_t num_heads, int32_t head_dim, int32_t rank);
@@ -270,10 +270,11 @@ const char* lrkv_prefill_kernel(int32_t dtype, int32_t num_heads, int32_t head_d
  * ranks 0, 8, 16 and 32, and at even ranks 34-128 (latents padded to 64 or
  * 128 dims per head); there one sequence's rows and latents must each span less than
  * 4 GiB - 1 KiB (seq_len * max(head_dim, num_heads*rank) * 2 bytes), else
- * LRKV_ERR_SHAPE.  Other shapes (fp32, or bf16 at an odd rank up to 127;
- * head_dim 16-128, a multiple of 8; at most 65535 heads and sequences) run
- * on a vector-ALU kernel with fp32 arithmetic (lrkv_prefill_kernel names
- * the kernel); anything else is LRKV_ERR_SHAPE.
+ * LRKV_ERR_SHAPE.  The other shapes with rank <= 128 and head_dim 16-128 (a
+ * multiple of 8), at most 65535 heads and sequences (fp32; bf16 at odd
+ * ranks, or at head_dim 16 or 32) run on a vector-ALU kernel with fp32
+ * arithmetic (lrkv_prefill_kernel names the kernel); anything else is
+ * LRKV_ERR_SHAPE.
  * If the cache pointers are all non-NULL (k_shared, v_shared, and for
  * rank > 0 also z_k, z_v) the tokens are also written, bit-exactly, to cache
  * slots [0, seq_len) of every sequence (seq_len must then be <= capacity);
