@@ -116,3 +116,31 @@ def test_prefill_chunk_generic(name, dt, B, H, d_h, r, cap, starts, n):
     e = err_ratio(got, want)
     say(f"  {name}: err/||out||inf = {e:.3e} (tol {TOL[dt]:.0e})")
     assert np.all(np.isfinite(got)) and e <= TOL[dt], (name, e)
+
+
+@pytest.mark.parametrize("wname", ["prefill_bf16_L4k_r54", "prefill_bf16_L4k_r128", "prefill_bf16_L4k_r55"])
+def test_prefill_trained_ranks_full_size_sampled_rows(wname):
+    """The 4096-token workloads at trained ranks, at full size (the padded
+    MFMA kernel at ranks 54 and 128, the vector-ALU kernel at rank 55):
+    sampled query rows, each computed by the oracle as a decode over its
+    causal prefix."""
+    from rank_compressed_kv_lrkv_amd.workloads import PREFILL_WORKLOADS
+    wl = PREFILL_WORKLOADS[wname]
+    say(f"case {wl} (full size, sampled rows, {L.lrkv_prefill_kernel(torch.bfloat16, wl.heads, wl.head_dim, wl.rank)})")
+    d = prefill_inputs(wl)
+    t = {k: to_dev(d[k], "bf16") for k in ("q",) + NEW + ("b_k", "b_v")}
+    out = L.lrkv_prefill(t["q"], t["k_s"], t["v_s"], t["z_k"], t["z_v"], t["b_k"], t["b_v"])
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    b_k, b_v = f64(d, "b_k"), f64(d, "b_v")
+    H = wl.heads
+    for h in (0, H // 2, H - 1):
+        for i in (0, 1, 31, 32, 33, 1000, 2047, 4095):
+            n = i + 1
+            want = O.decode(f64(d, "q")[0:1, i][:, [h]], f64(d, "k_s")[0:1, :n], f64(d, "v_s")[0:1, :n],
+                            f64(d, "z_k")[0:1, :n][:, :, [h]], f64(d, "z_v")[0:1, :n][:, :, [h]], b_k[[h]], b_v[[h]],
+                            [n])[0, 0]
+            e = float(np.max(np.abs(got[0, i, h] - want)) / np.max(np.abs(want)))
+            say(f"  h={h} row={i}: err/||row||inf = {e:.3e}")
+            assert e <= TOL["bf16"], (h, i, e)
