@@ -1,17 +1,20 @@
-// LRKV causal prefill on bf16 MFMA at even ranks 34-128: trained ranks of
-// the pages' models (slide "The rank directly sets the theoretical cache
-// budget", Table 7: 46 and 54; "Backup: the complete rank sweep clarifies
-// the trade-off", Table 8: up to 128).  Same method, arguments and
-// pipeline as prefill_wide_kernel (slides "Compute logits without expanding
-// historical keys", Eq. (6) with the causal mask, and "Aggregate values
-// before the residual up-projection", Eq. (7)); what differs:
-//   - the latent rows sit in LDS padded to RP = 64 (ranks up to 64) or 128
-//     dims per head: a tile transfer takes, for each head, 16-byte pieces
-//     starting at its row in HBM (4-byte aligned for an even rank), so the
-//     RP - r dims past the rank hold finite data of the following rows (or
+// LRKV causal prefill on bf16 MFMA at the ranks the rank-0/8/16/32 kernel
+// does not take, up to 128: the trained ranks of the pages' models (slide
+// "The rank directly sets the theoretical cache budget", Table 7: 46, 51,
+// 54, 55; "Backup: the complete rank sweep clarifies the trade-off", Table
+// 8: up to 128).  Same method, arguments and pipeline as prefill_kernel
+// (slides "Compute logits without expanding historical keys", Eq. (6) with
+// the causal mask, and "Aggregate values before the residual
+// up-projection", Eq. (7)); what differs:
+//   - a token's latent row in LDS is the run of the workgroup's 4 heads as
+//     in HBM (4r elements, 4-byte aligned when heads * r is even), padded
+//     to 4 RP elements (RP = 64 or 128) with the data that follows it (or
 //     zeros past the array);
-//   - the absorbed query and B^V are zero in those dims, so they add
-//     nothing to the logits and the output;
+//   - wave w reads its head through an RP-element window that starts at
+//     the 8-aligned element at or below w r: its first o_w = (w r) mod 8
+//     rows and those past o_w + r belong to other heads, and the absorbed
+//     query and B^V are zero there, so they add nothing to the logits and
+//     the output;
 //   - the value latents are RP/32 MFMA blocks of 32 rows; the softmax sum
 //     is added up on the vector ALUs;
 //   - a side is 24 KB (RP = 64) or 40 KB (RP = 128) with d_h = 128, so one
@@ -20,6 +23,8 @@
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
+#include <algorithm>
+
 namespace lrkv {
 
 constexpr int kPwWaves = 4;                 // heads per workgroup
@@ -27,7 +32,7 @@ constexpr int kPwThreads = 64 * kPwWaves;
 constexpr int kPwTile = 32;                 // key tokens per tile, query rows per wave
 constexpr float kPwStale = 8.f;             // running-max refresh threshold (log2 units)
 constexpr int kPwVmcntZero = 0x0F70;          // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt not waited on
-constexpr int kPwMaxPad = 128;              // latent dims per head in LDS: 64 (ranks 34-64) or 128 (66-128)
+constexpr int kPwMaxPad = 128;              // window of latent rows per head in LDS: 64 or 128
 
 // LDS tiles keep rows unpadded, with 16-byte chunk ch of row r at position
 // ch ^ lds_swz(r, chunks per row); with it every read this kernel makes is
@@ -69,7 +74,7 @@ struct WideKernelParams {
   const int32_t* start;
   int max_start;
   float scale_log2;
-  int rank;                        // r, even, r <= RP: latent row length in HBM
+  int rank;                        // r: latent row length in HBM (every window fits in RP)
 };
 
 // This lane's source offsets (bytes from the first row of a tile) for the
@@ -93,12 +98,12 @@ __device__ __forceinline__ PwDmaOffsets<WideShape<DH, RP>> pw_dma_offsets(int H,
   }
 #pragma unroll
   for (int i = 0; i < P::NZW; ++i) {
-    // padded chunk ch of token tok: dims 8(ch % (RP/8)) .. +7 of head ch / (RP/8),
-    // read from that head's row in HBM (past its r dims: the next row's data)
+    // chunk ch of token tok: elements 8ch .. 8ch+7 of the run of the 4
+    // heads' latents in HBM (4r of the row's 4 RP; past the run: the next
+    // token's data, or zeros past the array)
     const int q = (wave + i * kPwWaves) * 64 + lane, tok = q / P::CZ, pos = q % P::CZ;
     const int ch = pos ^ lds_swz(tok, P::CZ);
-    const int hh = min(hg * kPwWaves + ch / (RP / 8), H - 1);
-    d.lat[i] = uint32_t(((tok * H + hh) * r + (ch % (RP / 8)) * 8) * 2);
+    d.lat[i] = uint32_t(((tok * H + hg * kPwWaves) * r + 8 * ch) * 2);
   }
   return d;
 }
@@ -159,8 +164,7 @@ __device__ __forceinline__ void pw_dma(unsigned char* side, const PwSources& src
       const int q = j * 64 + lane, tok = q / P::CZ, pos = q % P::CZ;
       const int ch = pos ^ lds_swz(tok, P::CZ);
       const int t = min(kt * kPwTile + tok, L - 1);
-      const int hh = min(hg * kPwWaves + ch / (RP / 8), H - 1);
-      dma16(src.lat, uint32_t(((t * H + hh) * r + (ch % (RP / 8)) * 8) * 2), 0u, side + kPwTile * P::RB + j * 1024);
+      dma16(src.lat, uint32_t(((t * H + hg * kPwWaves) * r + 8 * ch) * 2), 0u, side + kPwTile * P::RB + j * 1024);
     }
   }
 }
@@ -234,9 +238,14 @@ void prefill_wide_kernel(WideKernelParams p) {
   int koff[DH / 16], zoff[P::ZCH];
 #pragma unroll
   for (int c = 0; c < DH / 16; ++c) koff[c] = n * P::RB + ((2 * c + half) ^ lds_swz(n, P::CR)) * 16;
+  // This wave's head sits at elements [wave r, wave r + r) of the run; it
+  // reads the RP-element window from the 8-aligned element at or below,
+  // whose first o_w elements belong to the previous head (o_w < 8, and
+  // r + o_w <= RP: the host picks RP so).
+  const int wstart = (wave * rk) & ~7, o_w = wave * rk - wstart;
 #pragma unroll
   for (int c = 0; c < P::ZCH; ++c) {
-    const int ch = wave * (RP / 8) + 2 * c + half;
+    const int ch = wstart / 8 + 2 * c + half;
     zoff[c] = kPwTile * P::RB + n * P::ZB + (ch ^ lds_swz(n, P::CZ)) * 16;
   }
   // Transpose reads of a 16-token value chunk: this lane addresses token
@@ -260,7 +269,7 @@ void prefill_wide_kernel(WideKernelParams p) {
 #pragma unroll
   for (int v = 0; v < P::LB; ++v) {
     const int feat = 32 * v + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int byte = wave * RP * 2 + feat * 2;
+    const int byte = (wstart + feat) * 2;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -286,14 +295,15 @@ void prefill_wide_kernel(WideKernelParams p) {
 #pragma unroll
     for (int v = 0; v < P::LB; ++v) {
       qt[v] = f32x16_t{};
-      const int j = 32 * v + n;
+      const int j = 32 * v + n - o_w;                   // window row -> latent dim
 #pragma unroll
       for (int c = 0; c < DH / 16; ++c) {
         bf16x8_t a;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const uint16_t x = bk[size_t(16 * c + 8 * half + i) * rk + (j < rk ? j : 0)];
-          a[i] = __builtin_bit_cast(__bf16, j < rk ? x : uint16_t(0));
+          const bool ok = j >= 0 && j < rk;
+          const uint16_t x = bk[size_t(16 * c + 8 * half + i) * rk + (ok ? j : 0)];
+          a[i] = __builtin_bit_cast(__bf16, ok ? x : uint16_t(0));
         }
         qt[v] = mfma32(a, qop[c], qt[v]);
       }
@@ -431,8 +441,8 @@ void prefill_wide_kernel(WideKernelParams p) {
   // softmax sum of query n: the two halves' partial sums
   lsum += __shfl_xor(lsum, 32);
   // ---- epilogue: O_s += B^V_h . O_z^T, then divide by the softmax sum ----
-  // B^V_h is zero in the padded dims j >= r (O_z holds finite values there);
-  // with r even, each pair of dims is whole on one side of r.
+  // B^V_h is zero outside the head's dims (window rows o_w .. o_w + r - 1;
+  // O_z holds finite values in the others).
 #pragma unroll
   for (int c = 0; c < P::ZCH; ++c) {
     bf16x8_t bz;                                          // O_z^T k-slots, accumulator order
@@ -444,8 +454,10 @@ void prefill_wide_kernel(WideKernelParams p) {
       uint32_t w[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int j = 16 * c + 8 * (k >> 1) + 4 * half + 2 * (k & 1);
-        w[k] = j < rk ? *reinterpret_cast<const uint32_t*>(bv + j) : 0u;
+        // window rows e, e + 1 -> latent dims e - o_w, e + 1 - o_w
+        const int j = 16 * c + 8 * (k >> 1) + 4 * half + 2 * (k & 1) - o_w;
+        const uint32_t lo = (j >= 0 && j < rk) ? bv[j] : 0u, hi = (j + 1 >= 0 && j + 1 < rk) ? bv[j + 1] : 0u;
+        w[k] = lo | (hi << 16);
       }
       oacc[f] = mfma32(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}), bz, oacc[f]);
     }
@@ -496,15 +508,26 @@ static hipError_t launch_wide_t(const PrefillArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Latent dims per head in LDS for rank r: the smallest of 64 and 128 that
+// holds every head's window (r plus its offset o_w = (w r) mod 8, w < 4);
+// 0 if neither does.
+static int wide_pad(int r) {
+  int need = r;
+  for (int w = 1; w < kPwWaves; ++w) need = std::max(need, r + ((w * r) & 7));
+  return need <= 64 ? 64 : need <= kPwMaxPad ? kPwMaxPad : 0;
+}
+
+// Any rank 1-128 whose windows fit, with the 4-head runs 4-byte aligned in
+// HBM (heads * rank even makes every run start at an even element).
 bool prefill_wide_supported(int dtype, int head_dim, int rank, int heads) {
-  return dtype == 1 && (head_dim == 64 || head_dim == 128) && rank % 2 == 0 && rank > 32 && rank <= kPwMaxPad &&
-         heads >= 1;
+  return dtype == 1 && (head_dim == 64 || head_dim == 128) && rank >= 1 && rank <= kPwMaxPad && heads >= 1 &&
+         (heads % 2 == 0 || rank % 2 == 0) && wide_pad(rank) > 0;
 }
 
 hipError_t launch_prefill_wide(const PrefillArgs& a, hipStream_t st) {
   // the training forward's log-sum-exp output is the rank 0-32 kernel's only
   if (!prefill_wide_supported(1, a.head_dim, a.rank, a.heads) || a.lse) return hipErrorInvalidValue;
-  if (a.rank <= 64) return a.head_dim == 64 ? launch_wide_t<64, 64>(a, st) : launch_wide_t<128, 64>(a, st);
+  if (wide_pad(a.rank) == 64) return a.head_dim == 64 ? launch_wide_t<64, 64>(a, st) : launch_wide_t<128, 64>(a, st);
   return a.head_dim == 64 ? launch_wide_t<64, 128>(a, st) : launch_wide_t<128, 128>(a, st);
 }
 

@@ -94,13 +94,15 @@ DECODE_WORKLOADS = {
 PREFILL_WORKLOADS = {
     w.name: w for w in [
         PrefillWorkload("prefill_bf16_L4k", 4, 4096, 32, 128, 16, "bf16", 20261206),
-        # one sequence of the same length at trained ranks: the 2.5B
-        # configuration (32 heads, rank 54: the padded MFMA prefill) and an
-        # odd rank (18 heads, rank 55: the vector-ALU prefill)
+        # one sequence of the same length at trained ranks (the windowed
+        # MFMA prefill): the 2.5B configuration (32 heads, rank 54), an odd
+        # rank (18 heads, rank 55) and the top of the rank sweep (16 heads,
+        # rank 128); and an odd number of heads at an odd rank (9 heads,
+        # rank 55: the vector-ALU prefill)
         PrefillWorkload("prefill_bf16_L4k_r54", 1, 4096, 32, 128, 54, "bf16", 20261210),
         PrefillWorkload("prefill_bf16_L4k_r55", 1, 4096, 18, 128, 55, "bf16", 20261211),
-        # the top of the rank sweep: 16 heads of rank 128 (128-dim padding)
         PrefillWorkload("prefill_bf16_L4k_r128", 1, 4096, 16, 128, 128, "bf16", 20261212),
+        PrefillWorkload("prefill_bf16_L4k_h9_r55", 1, 4096, 9, 128, 55, "bf16", 20261213),
     ]
 }
 

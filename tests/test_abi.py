@@ -190,17 +190,18 @@ def test_append_zero_rows_is_noop():
 
 @no_gpu
 def test_prefill_kernel_names():
-    """bf16 at ranks 0/8/16/32 and head_dim 64/128 runs on MFMA, at even
-    ranks 34-128 on its padded form; fp32 and the other ranks up to 128 on
+    """bf16 at ranks 0/8/16/32 and head_dim 64/128 runs on MFMA, at the
+    other ranks up to 128 on its windowed form where the windows fit; fp32 and the other ranks up to 128 on
     the vector-ALU kernel; larger shapes on neither."""
     assert L.lrkv_prefill_kernel(torch.bfloat16, 32, 128, 16) == "prefill_kernel"
     assert L.lrkv_prefill_kernel(torch.bfloat16, 4, 64, 0) == "prefill_kernel"
     assert L.lrkv_prefill_kernel(torch.bfloat16, 32, 128, 54) == "prefill_wide_kernel"
     assert L.lrkv_prefill_kernel(torch.bfloat16, 12, 64, 46) == "prefill_wide_kernel"
-    assert L.lrkv_prefill_kernel(torch.bfloat16, 12, 128, 51) == "prefill_generic_kernel"   # odd rank
+    assert L.lrkv_prefill_kernel(torch.bfloat16, 12, 128, 51) == "prefill_wide_kernel"      # odd rank, even heads
+    assert L.lrkv_prefill_kernel(torch.bfloat16, 9, 128, 55) == "prefill_generic_kernel"    # odd heads x odd rank
     assert L.lrkv_prefill_kernel(torch.bfloat16, 12, 32, 54) == "prefill_generic_kernel"    # head_dim 32
     assert L.lrkv_prefill_kernel(torch.bfloat16, 6, 128, 128) == "prefill_wide_kernel"
-    assert L.lrkv_prefill_kernel(torch.bfloat16, 6, 128, 127) == "prefill_generic_kernel"
+    assert L.lrkv_prefill_kernel(torch.bfloat16, 6, 128, 127) == "prefill_generic_kernel"   # window past 128
     assert L.lrkv_prefill_kernel(torch.float32, 32, 128, 16) == "prefill_generic_kernel"
     assert L.lrkv_prefill_kernel(torch.float32, 3, 16, 5) == "prefill_generic_kernel"
     assert L.lrkv_prefill_kernel(torch.bfloat16, 32, 128, 129) is None

@@ -1,7 +1,8 @@
 """lrkv_prefill and lrkv_prefill_chunk outside the rank 0/8/16/32 MFMA
 kernel's envelope, through the C ABI, against the float64 oracle: bf16 at
-even ranks 34-128 on the padded MFMA kernel (prefill_wide_kernel), fp32 and
-the other ranks up to 128 on the vector-ALU kernel (prefill_generic_kernel).
+the other ranks up to 128 on the windowed MFMA kernel (prefill_wide_kernel)
+where every head's window fits and heads * rank is even, fp32 and the rest
+on the vector-ALU kernel (prefill_generic_kernel).
 
 Bar: max |gpu - oracle| <= 1e-5 * ||oracle||_inf for fp32 storage and
 2e-2 * ||oracle||_inf for bf16 storage.  Element by element, at sizes that
@@ -38,12 +39,20 @@ SHAPES = [
     ("bf16_r66_h4", "bf16", 1, 70, 4, 128, 66),
     ("bf16_r96_dh64_h7", "bf16", 2, 45, 7, 64, 96),
     ("bf16_r127_h3", "bf16", 1, 40, 3, 128, 127),
+    ("bf16_r55_h9", "bf16", 1, 60, 9, 128, 55),
+    ("bf16_r126_h4", "bf16", 1, 33, 4, 128, 126),
+    ("bf16_r5_dh64_h4", "bf16", 2, 50, 4, 64, 5),
+    ("bf16_r51_h6_dh64", "bf16", 1, 90, 6, 64, 51),
 ]
 
 
-def expected_kernel(dt, d_h, r):
-    if dt == "bf16" and d_h in (64, 128) and r % 2 == 0 and 32 < r <= 128:
-        return "prefill_wide_kernel"
+def expected_kernel(dt, d_h, r, H):
+    """bf16 at head_dim 64/128 and a rank other than 0/8/16/32 runs on the
+    windowed MFMA kernel when every head's window (r plus (w r) mod 8, w < 4)
+    fits in 128 rows and heads * rank is even; the rest on the vector ALUs."""
+    if dt == "bf16" and d_h in (64, 128) and 1 <= r <= 128 and (H % 2 == 0 or r % 2 == 0):
+        if max(r + ((w * r) & 7) for w in range(4)) <= 128:
+            return "prefill_wide_kernel"
     return "prefill_generic_kernel"
 
 
@@ -53,7 +62,7 @@ def f64(d, k):
 
 @pytest.mark.parametrize("name,dt,B,Lq,H,d_h,r", SHAPES, ids=[s[0] for s in SHAPES])
 def test_prefill_generic(name, dt, B, Lq, H, d_h, r):
-    kern = expected_kernel(dt, d_h, r)
+    kern = expected_kernel(dt, d_h, r, H)
     assert L.lrkv_prefill_kernel(TORCH_DT[dt], H, d_h, r) == kern
     say(f"case prefill ({kern}) {name}")
     d = prefill_inputs(PrefillWorkload(name, B, Lq, H, d_h, r, dt, 1000 + H + r))
@@ -91,13 +100,15 @@ CHUNKS = [
     ("bf16_r54", "bf16", 2, 32, 128, 54, 200, [64, 5], 33),
     ("bf16_r46_long", "bf16", 2, 12, 128, 46, 700, [600, 130], 64),
     ("bf16_r128", "bf16", 2, 6, 128, 128, 160, [100, 7], 40),
+    ("bf16_r51_h12", "bf16", 2, 12, 128, 51, 300, [250, 3], 37),
+    ("bf16_r55_h9", "bf16", 1, 9, 128, 55, 120, [70], 20),
     ("bf16_r55_one_token", "bf16", 2, 18, 128, 55, 300, [299, 0], 1),
 ]
 
 
 @pytest.mark.parametrize("name,dt,B,H,d_h,r,cap,starts,n", CHUNKS, ids=[c[0] for c in CHUNKS])
 def test_prefill_chunk_generic(name, dt, B, H, d_h, r, cap, starts, n):
-    say(f"case prefill chunk ({expected_kernel(dt, d_h, r)}) {name} starts={starts} n_new={n}")
+    say(f"case prefill chunk ({expected_kernel(dt, d_h, r, H)}) {name} starts={starts} n_new={n}")
     d = chunk_inputs(batch=B, heads=H, head_dim=d_h, rank=r, capacity=cap, starts=starts, n_new=n, seed=40 + r,
                      dtype=dt)
     cache = L.LrkvCache(*(to_dev(d["cache_" + k], dt) for k in NEW))
@@ -118,10 +129,12 @@ def test_prefill_chunk_generic(name, dt, B, H, d_h, r, cap, starts, n):
     assert np.all(np.isfinite(got)) and e <= TOL[dt], (name, e)
 
 
-@pytest.mark.parametrize("wname", ["prefill_bf16_L4k_r54", "prefill_bf16_L4k_r128", "prefill_bf16_L4k_r55"])
+@pytest.mark.parametrize("wname", ["prefill_bf16_L4k_r54", "prefill_bf16_L4k_r128", "prefill_bf16_L4k_r55",
+                                   "prefill_bf16_L4k_h9_r55"])
 def test_prefill_trained_ranks_full_size_sampled_rows(wname):
-    """The 4096-token workloads at trained ranks, at full size (the padded
-    MFMA kernel at ranks 54 and 128, the vector-ALU kernel at rank 55):
+    """The 4096-token workloads at trained ranks, at full size (the windowed
+    MFMA kernel at ranks 54, 55 and 128; the vector-ALU kernel at rank 55
+    with 9 heads):
     sampled query rows, each computed by the oracle as a decode over its
     causal prefix."""
     from rank_compressed_kv_lrkv_amd.workloads import PREFILL_WORKLOADS
