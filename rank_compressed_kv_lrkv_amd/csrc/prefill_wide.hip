@@ -77,6 +77,22 @@ struct WideKernelParams {
   int rank;                        // r: latent row length in HBM (every window fits in RP)
 };
 
+// Source byte offset (from the tile's first token) of latent chunk ch of
+// token tok: with WIN, elements 8ch .. 8ch+7 of the run of the 4 heads'
+// latents (4r of the row's 4 RP elements; past the run: the next token's
+// data, or zeros past the array); without, dims 8(ch % (RP/8)) .. +7 of
+// head ch / (RP/8) from that head's own row (past its r dims: the next
+// row's data).
+template <int RP, bool WIN>
+__device__ __forceinline__ uint32_t pw_lat_src(int tok, int H, int r, int hg, int ch) {
+  if constexpr (WIN) {
+    return uint32_t(((tok * H + hg * kPwWaves) * r + 8 * ch) * 2);
+  } else {
+    const int hh = min(hg * kPwWaves + ch / (RP / 8), H - 1);
+    return uint32_t(((tok * H + hh) * r + (ch % (RP / 8)) * 8) * 2);
+  }
+}
+
 // This lane's source offsets (bytes from the first row of a tile) for the
 // wave's share of one side's 1 KB transfers; the same for every tile, and for
 // the key side and the value side.  Transfer j carries LDS bytes
@@ -87,7 +103,7 @@ struct PwDmaOffsets {
   uint32_t row[P::NRW], lat[P::NZW];
 };
 
-template <int DH, int RP>
+template <int DH, int RP, bool WIN>
 __device__ __forceinline__ PwDmaOffsets<WideShape<DH, RP>> pw_dma_offsets(int H, int r, int hg, int wave, int lane) {
   using P = WideShape<DH, RP>;
   PwDmaOffsets<P> d;
@@ -98,12 +114,9 @@ __device__ __forceinline__ PwDmaOffsets<WideShape<DH, RP>> pw_dma_offsets(int H,
   }
 #pragma unroll
   for (int i = 0; i < P::NZW; ++i) {
-    // chunk ch of token tok: elements 8ch .. 8ch+7 of the run of the 4
-    // heads' latents in HBM (4r of the row's 4 RP; past the run: the next
-    // token's data, or zeros past the array)
     const int q = (wave + i * kPwWaves) * 64 + lane, tok = q / P::CZ, pos = q % P::CZ;
     const int ch = pos ^ lds_swz(tok, P::CZ);
-    d.lat[i] = uint32_t(((tok * H + hg * kPwWaves) * r + 8 * ch) * 2);
+    d.lat[i] = pw_lat_src<RP, WIN>(tok, H, r, hg, ch);
   }
   return d;
 }
@@ -128,7 +141,7 @@ __device__ __forceinline__ PwSources pw_sources(const uint16_t* rows, const uint
 // a uniform tile offset to each lane's fixed offset; a tile reaching past the
 // last token clamps its rows to token L-1 (their values are masked out of the
 // softmax).  Each wave issues its share of the 1 KB transfers.
-template <int DH, int RP>
+template <int DH, int RP, bool WIN>
 __device__ __forceinline__ void pw_dma(unsigned char* side, const PwSources& src, const PwDmaOffsets<WideShape<DH, RP>>& d,
                                        const WideKernelParams& p, int hg, int kt, int wave, int lane, int L) {
   using P = WideShape<DH, RP>;
@@ -164,7 +177,7 @@ __device__ __forceinline__ void pw_dma(unsigned char* side, const PwSources& src
       const int q = j * 64 + lane, tok = q / P::CZ, pos = q % P::CZ;
       const int ch = pos ^ lds_swz(tok, P::CZ);
       const int t = min(kt * kPwTile + tok, L - 1);
-      dma16(src.lat, uint32_t(((t * H + hg * kPwWaves) * r + 8 * ch) * 2), 0u, side + kPwTile * P::RB + j * 1024);
+      dma16(src.lat, pw_lat_src<RP, WIN>(t, H, r, hg, ch), 0u, side + kPwTile * P::RB + j * 1024);
     }
   }
 }
@@ -204,7 +217,7 @@ __device__ __forceinline__ f32x16_t pw_scores(const unsigned char* side, const b
   return s;
 }
 
-template <int DH, int RP>
+template <int DH, int RP, bool WIN>
 __global__ __attribute__((amdgpu_flat_work_group_size(kPwThreads, kPwThreads), amdgpu_waves_per_eu(1)))
 void prefill_wide_kernel(WideKernelParams p) {
   using P = WideShape<DH, RP>;
@@ -238,11 +251,11 @@ void prefill_wide_kernel(WideKernelParams p) {
   int koff[DH / 16], zoff[P::ZCH];
 #pragma unroll
   for (int c = 0; c < DH / 16; ++c) koff[c] = n * P::RB + ((2 * c + half) ^ lds_swz(n, P::CR)) * 16;
-  // This wave's head sits at elements [wave r, wave r + r) of the run; it
-  // reads the RP-element window from the 8-aligned element at or below,
-  // whose first o_w elements belong to the previous head (o_w < 8, and
-  // r + o_w <= RP: the host picks RP so).
-  const int wstart = (wave * rk) & ~7, o_w = wave * rk - wstart;
+  // With WIN this wave's head sits at elements [wave r, wave r + r) of the
+  // run; it reads the RP-element window from the 8-aligned element at or
+  // below, whose first o_w elements belong to the previous head (o_w < 8,
+  // and r + o_w <= RP: the host picks RP so).  Without, its padded row.
+  const int wstart = WIN ? (wave * rk) & ~7 : wave * RP, o_w = WIN ? wave * rk - wstart : 0;
 #pragma unroll
   for (int c = 0; c < P::ZCH; ++c) {
     const int ch = wstart / 8 + 2 * c + half;
@@ -278,7 +291,7 @@ void prefill_wide_kernel(WideKernelParams p) {
         zvoff[v][c][j] = kPwTile * P::RB + row * P::ZB + ((byte / 16) ^ lds_swz(row, P::CZ)) * 16 + byte % 16;
       }
   }
-  const PwDmaOffsets<P> dma = pw_dma_offsets<DH, RP>(H, rk, hg, wave, lane);
+  const PwDmaOffsets<P> dma = pw_dma_offsets<DH, RP, WIN>(H, rk, hg, wave, lane);
 
   // ---- query rows (B operands, K-dim = features): lane (query n, half) ----
   bf16x8_t qop[P::KCH];
@@ -340,9 +353,9 @@ void prefill_wide_kernel(WideKernelParams p) {
   unsigned char* const vside0 = smem + 2 * P::SIDE;
   const PwSources ksrc = pw_sources<DH, RP>(p.k_s, p.z_k, p, b, nkeys);
   const PwSources vsrc = pw_sources<DH, RP>(p.v_s, p.z_v, p, b, nkeys);
-  pw_dma<DH, RP>(kside0, ksrc, dma, p, hg, 0, wave, lane, nkeys);
-  pw_dma<DH, RP>(vside0, vsrc, dma, p, hg, 0, wave, lane, nkeys);
-  if (kt_last >= 1) pw_dma<DH, RP>(kside0 + P::SIDE, ksrc, dma, p, hg, 1, wave, lane, nkeys);
+  pw_dma<DH, RP, WIN>(kside0, ksrc, dma, p, hg, 0, wave, lane, nkeys);
+  pw_dma<DH, RP, WIN>(vside0, vsrc, dma, p, hg, 0, wave, lane, nkeys);
+  if (kt_last >= 1) pw_dma<DH, RP, WIN>(kside0 + P::SIDE, ksrc, dma, p, hg, 1, wave, lane, nkeys);
   __builtin_amdgcn_s_waitcnt(kPwVmcntZero);
   __syncthreads();
   f32x16_t s0 = pw_scores<DH, RP>(kside0, qop, koff, zoff, half);
@@ -377,8 +390,8 @@ void prefill_wide_kernel(WideKernelParams p) {
     // Refill the buffers read in the previous step.  Issued after this step's
     // LDS reads, which therefore never wait on the transfers; they overlap
     // the softmax and the value MFMAs.
-    if (next_k) pw_dma<DH, RP>(kside0 + (kt & 1) * P::SIDE, ksrc, dma, p, hg, kt + 2, wave, lane, nkeys);
-    if (next_v) pw_dma<DH, RP>(vside0 + ((kt + 1) & 1) * P::SIDE, vsrc, dma, p, hg, kt + 1, wave, lane, nkeys);
+    if (next_k) pw_dma<DH, RP, WIN>(kside0 + (kt & 1) * P::SIDE, ksrc, dma, p, hg, kt + 2, wave, lane, nkeys);
+    if (next_v) pw_dma<DH, RP, WIN>(vside0 + ((kt + 1) & 1) * P::SIDE, vsrc, dma, p, hg, kt + 1, wave, lane, nkeys);
 
     // online softmax (log2 domain) for the query at position qpos0 + n.
     // Only tiles reaching past the block's first query position (the
@@ -454,10 +467,15 @@ void prefill_wide_kernel(WideKernelParams p) {
       uint32_t w[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        // window rows e, e + 1 -> latent dims e - o_w, e + 1 - o_w
+        // window rows e, e + 1 -> latent dims e - o_w, e + 1 - o_w (without
+        // WIN: o_w = 0 and r even, so the pair is whole on one side of r)
         const int j = 16 * c + 8 * (k >> 1) + 4 * half + 2 * (k & 1) - o_w;
-        const uint32_t lo = (j >= 0 && j < rk) ? bv[j] : 0u, hi = (j + 1 >= 0 && j + 1 < rk) ? bv[j + 1] : 0u;
-        w[k] = lo | (hi << 16);
+        if constexpr (WIN) {
+          const uint32_t lo = (j >= 0 && j < rk) ? bv[j] : 0u, hi = (j + 1 >= 0 && j + 1 < rk) ? bv[j + 1] : 0u;
+          w[k] = lo | (hi << 16);
+        } else {
+          w[k] = j < rk ? *reinterpret_cast<const uint32_t*>(bv + j) : 0u;
+        }
       }
       oacc[f] = mfma32(as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}), bz, oacc[f]);
     }
@@ -476,7 +494,7 @@ void prefill_wide_kernel(WideKernelParams p) {
     }
 }
 
-template <int DH, int RP>
+template <int DH, int RP, bool WIN>
 static hipError_t launch_wide_t(const PrefillArgs& a, hipStream_t st) {
   using P = WideShape<DH, RP>;
   WideKernelParams kp;
@@ -502,23 +520,26 @@ static hipError_t launch_wide_t(const PrefillArgs& a, hipStream_t st) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid{static_cast<unsigned>(blocks)};
   const size_t lds = size_t(P::LDS);
-  const hipError_t attr = allow_dynamic_lds<&prefill_wide_kernel<DH, RP>>(int(lds));
+  const hipError_t attr = allow_dynamic_lds<&prefill_wide_kernel<DH, RP, WIN>>(int(lds));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((prefill_wide_kernel<DH, RP>), grid, dim3(kPwThreads), lds, st, kp);
+  hipLaunchKernelGGL((prefill_wide_kernel<DH, RP, WIN>), grid, dim3(kPwThreads), lds, st, kp);
   return hipGetLastError();
 }
 
-// Latent dims per head in LDS for rank r: the smallest of 64 and 128 that
-// holds every head's window (r plus its offset o_w = (w r) mod 8, w < 4);
-// 0 if neither does.
+// Latent rows per head in LDS for rank r: the smallest of 64 and 128 that
+// holds the head's rows: r for an even rank (each head's own row, padded),
+// r plus the window offset o_w = (w r) mod 8, w < 4, for an odd one; 0 if
+// neither does.
 static int wide_pad(int r) {
   int need = r;
-  for (int w = 1; w < kPwWaves; ++w) need = std::max(need, r + ((w * r) & 7));
+  if (r % 2)
+    for (int w = 1; w < kPwWaves; ++w) need = std::max(need, r + ((w * r) & 7));
   return need <= 64 ? 64 : need <= kPwMaxPad ? kPwMaxPad : 0;
 }
 
-// Any rank 1-128 whose windows fit, with the 4-head runs 4-byte aligned in
-// HBM (heads * rank even makes every run start at an even element).
+// Ranks 1-128 with the transfers' sources 4-byte aligned in HBM: an even
+// rank (every head's row), or an odd one with an even number of heads
+// (every 4-head run starts at an even element), whose windows fit.
 bool prefill_wide_supported(int dtype, int head_dim, int rank, int heads) {
   return dtype == 1 && (head_dim == 64 || head_dim == 128) && rank >= 1 && rank <= kPwMaxPad && heads >= 1 &&
          (heads % 2 == 0 || rank % 2 == 0) && wide_pad(rank) > 0;
@@ -527,15 +548,22 @@ bool prefill_wide_supported(int dtype, int head_dim, int rank, int heads) {
 hipError_t launch_prefill_wide(const PrefillArgs& a, hipStream_t st) {
   // the training forward's log-sum-exp output is the rank 0-32 kernel's only
   if (!prefill_wide_supported(1, a.head_dim, a.rank, a.heads) || a.lse) return hipErrorInvalidValue;
-  if (wide_pad(a.rank) == 64) return a.head_dim == 64 ? launch_wide_t<64, 64>(a, st) : launch_wide_t<128, 64>(a, st);
-  return a.head_dim == 64 ? launch_wide_t<64, 128>(a, st) : launch_wide_t<128, 128>(a, st);
+  const bool odd = a.rank % 2, d64 = a.head_dim == 64;
+  if (wide_pad(a.rank) == 64) {
+    if (odd) return d64 ? launch_wide_t<64, 64, true>(a, st) : launch_wide_t<128, 64, true>(a, st);
+    return d64 ? launch_wide_t<64, 64, false>(a, st) : launch_wide_t<128, 64, false>(a, st);
+  }
+  if (odd) return d64 ? launch_wide_t<64, 128, true>(a, st) : launch_wide_t<128, 128, true>(a, st);
+  return d64 ? launch_wide_t<64, 128, false>(a, st) : launch_wide_t<128, 128, false>(a, st);
 }
 
 hipError_t prefill_wide_prepare() {
-  hipError_t e = allow_dynamic_lds<&prefill_wide_kernel<64, 64>>(WideShape<64, 64>::LDS);
-  if (e == hipSuccess) e = allow_dynamic_lds<&prefill_wide_kernel<128, 64>>(WideShape<128, 64>::LDS);
-  if (e == hipSuccess) e = allow_dynamic_lds<&prefill_wide_kernel<64, 128>>(WideShape<64, 128>::LDS);
-  if (e == hipSuccess) e = allow_dynamic_lds<&prefill_wide_kernel<128, 128>>(WideShape<128, 128>::LDS);
+  hipError_t e = hipSuccess;
+#define LRKV_PW(DHV, RPV, W) \
+  if (e == hipSuccess) e = allow_dynamic_lds<&prefill_wide_kernel<DHV, RPV, W>>(WideShape<DHV, RPV>::LDS);
+  LRKV_PW(64, 64, false) LRKV_PW(128, 64, false) LRKV_PW(64, 128, false) LRKV_PW(128, 128, false)
+  LRKV_PW(64, 64, true) LRKV_PW(128, 64, true) LRKV_PW(64, 128, true) LRKV_PW(128, 128, true)
+#undef LRKV_PW
   return e;
 }
 

@@ -1,8 +1,8 @@
 """lrkv_prefill and lrkv_prefill_chunk outside the rank 0/8/16/32 MFMA
 kernel's envelope, through the C ABI, against the float64 oracle: bf16 at
-the other ranks up to 128 on the windowed MFMA kernel (prefill_wide_kernel)
-where every head's window fits and heads * rank is even, fp32 and the rest
-on the vector-ALU kernel (prefill_generic_kernel).
+the other ranks up to 128 on the padded MFMA kernel (prefill_wide_kernel:
+every even rank; odd ranks with an even number of heads whose windows fit),
+fp32 and the rest on the vector-ALU kernel (prefill_generic_kernel).
 
 Bar: max |gpu - oracle| <= 1e-5 * ||oracle||_inf for fp32 storage and
 2e-2 * ||oracle||_inf for bf16 storage.  Element by element, at sizes that
@@ -41,6 +41,8 @@ SHAPES = [
     ("bf16_r127_h3", "bf16", 1, 40, 3, 128, 127),
     ("bf16_r55_h9", "bf16", 1, 60, 9, 128, 55),
     ("bf16_r126_h4", "bf16", 1, 33, 4, 128, 126),
+    ("bf16_r121_h2", "bf16", 1, 40, 2, 128, 121),
+    ("bf16_r123_h2", "bf16", 1, 40, 2, 128, 123),
     ("bf16_r5_dh64_h4", "bf16", 2, 50, 4, 64, 5),
     ("bf16_r51_h6_dh64", "bf16", 1, 90, 6, 64, 51),
 ]
@@ -48,10 +50,13 @@ SHAPES = [
 
 def expected_kernel(dt, d_h, r, H):
     """bf16 at head_dim 64/128 and a rank other than 0/8/16/32 runs on the
-    windowed MFMA kernel when every head's window (r plus (w r) mod 8, w < 4)
-    fits in 128 rows and heads * rank is even; the rest on the vector ALUs."""
-    if dt == "bf16" and d_h in (64, 128) and 1 <= r <= 128 and (H % 2 == 0 or r % 2 == 0):
-        if max(r + ((w * r) & 7) for w in range(4)) <= 128:
+    padded MFMA kernel: an even rank always, an odd one with an even number
+    of heads when every head's window (r plus (w r) mod 8, w < 4) fits in
+    128 rows; the rest on the vector ALUs."""
+    if dt == "bf16" and d_h in (64, 128) and 1 <= r <= 128:
+        if r % 2 == 0:
+            return "prefill_wide_kernel"
+        if H % 2 == 0 and max(r + ((w * r) & 7) for w in range(4)) <= 128:
             return "prefill_wide_kernel"
     return "prefill_generic_kernel"
 
