@@ -253,7 +253,8 @@ lrkv_status lrkv_decode_ex(int32_t engine, int32_t phases,
 
 /* Name of the kernel lrkv_prefill and lrkv_prefill_chunk run for these
  * sizes: "prefill_kernel" (bf16 MFMA: head_dim 64 or 128, rank 0, 8, 16 or
- * 32), "prefill_wide_kernel" (the same at even ranks 34-128) or
+ * 32), "prefill_wide_kernel" (the same with padded latents at the other
+ * ranks up to 128, see lrkv_prefill) or
  * "prefill_generic_kernel" (vector ALU, fp32 arithmetic: the other shapes
  * with rank <= 128, head_dim 16-128 a multiple of 8, at most 65535 heads).
  * NULL outside all three.  Host-only: launches nothing; the string is
@@ -267,14 +268,15 @@ const char* lrkv_prefill_kernel(int32_t dtype, int32_t num_heads, int32_t head_d
  *   q   [batch][seq_len][num_heads][head_dim];  out same shape.
  *   k_s, v_s [batch][seq_len][head_dim];  z_k, z_v [batch][seq_len][num_heads][rank].
  * bf16 with head_dim 64 or 128 runs on bf16 MFMA with fp32 accumulation at
- * ranks 0, 8, 16 and 32, and at even ranks 34-128 (latents padded to 64 or
- * 128 dims per head); there one sequence's rows and latents must each span less than
- * 4 GiB - 1 KiB (seq_len * max(head_dim, num_heads*rank) * 2 bytes), else
- * LRKV_ERR_SHAPE.  The other shapes with rank <= 128 and head_dim 16-128 (a
- * multiple of 8), at most 65535 heads and sequences (fp32; bf16 at odd
- * ranks, or at head_dim 16 or 32) run on a vector-ALU kernel with fp32
- * arithmetic (lrkv_prefill_kernel names the kernel); anything else is
- * LRKV_ERR_SHAPE.
+ * ranks 0, 8, 16 and 32, and with latents padded to 64 or 128 rows per head
+ * at every other rank up to 128 except: an odd rank with an odd number of
+ * heads, and ranks 123, 125 and 127.  There one sequence's rows and latents
+ * must each span less than 4 GiB - 1 KiB (seq_len * max(head_dim,
+ * num_heads*rank) * 2 bytes), else LRKV_ERR_SHAPE.  The other shapes with
+ * rank <= 128 and head_dim 16-128 (a multiple of 8), at most 65535 heads and
+ * sequences (fp32; the bf16 exceptions above; bf16 at head_dim 16 or 32)
+ * run on a vector-ALU kernel with fp32 arithmetic (lrkv_prefill_kernel
+ * names the kernel); anything else is LRKV_ERR_SHAPE.
  * If the cache pointers are all non-NULL (k_shared, v_shared, and for
  * rank > 0 also z_k, z_v) the tokens are also written, bit-exactly, to cache
  * slots [0, seq_len) of every sequence (seq_len must then be <= capacity);

@@ -348,7 +348,7 @@ bool prefill_generic_ok(int32_t dtype, int32_t batch, int32_t num_heads, int32_t
 }
 
 // Which prefill kernel a shape runs on: the bf16 MFMA kernel at ranks 0, 8,
-// 16 and 32; its padded form at even ranks 34-128; else the vector-ALU kernel.
+// 16 and 32; its padded form at the other ranks it takes; else the vector-ALU kernel.
 enum class PrefillEngine { kMfma, kWide, kGeneric, kNone };
 
 PrefillEngine prefill_engine(int32_t dtype, int32_t batch, int32_t num_heads, int32_t head_dim, int32_t rank) {

@@ -118,7 +118,7 @@ struct PrefillArgs {
 };
 bool prefill_supported(int dtype, int head_dim, int rank, int heads);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-// The bf16 MFMA prefill at even ranks 34-128 (latents padded to 64 or 128 in LDS).
+// The bf16 MFMA prefill at the other ranks up to 128 (latents padded to 64 or 128 rows in LDS).
 bool prefill_wide_supported(int dtype, int head_dim, int rank, int heads);
 hipError_t launch_prefill_wide(const PrefillArgs& a, hipStream_t stream);
 hipError_t prefill_wide_prepare();
