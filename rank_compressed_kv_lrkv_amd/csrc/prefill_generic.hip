@@ -1,6 +1,7 @@
-// LRKV causal prefill for the shapes the MFMA prefill does not take: fp32
-// storage, any rank up to 128 (the trained ranks 46-128 among them), head
-// widths 16-128.  Same operation and arguments as prefill_kernel (slides
+// LRKV causal prefill for the shapes the MFMA prefills do not take: fp32
+// storage, head widths 16 and 32, an odd number of heads at an odd rank,
+// and ranks 123, 125 and 127 (any rank up to 128, head widths 16-128 are
+// accepted).  Same operation and arguments as prefill_kernel (slides
 // "Compute logits without expanding historical keys", Eq. (6) with the
 // causal mask, and "Aggregate values before the residual up-projection",
 // Eq. (7)), in the absorbed form with fp32 arithmetic throughout:
@@ -15,8 +16,7 @@
 // LDS, lane j of a query's group scores keys j, j+8, j+16, j+24 of the tile
 // (16-byte LDS reads, the query's 4 columns reused for the 4 keys), the
 // group shares the running max by shuffles, and lane j accumulates the
-// augmented output dims 32c + 4j .. 32c + 4j + 3.  The MFMA kernel stays
-// the one for bf16 at ranks 0, 8, 16 and 32.
+// augmented output dims 32c + 4j .. 32c + 4j + 3.
 #include "lrkv_device.h"
 #include "lrkv_internal.h"
 
